@@ -1,0 +1,271 @@
+"""CPU oracle for decode attention over a budget-limited per-head KV cache.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark use this package; the HIP library never does.  The arithmetic
+lives in ``oracle.c`` (plain C, double precision, one thread); this module
+loads it with ctypes and keeps a canonical per-head state (entries in
+ascending position order) for multi-step trajectories.
+
+Pages cited in the C source: the KV-cache-compression guide (sections on the
+capacity formula and on StreamingLLM / H2O) and the eviction-in-practice blog
+(sections on per-head random eviction and its reference hook).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Dict, List, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build() -> str:
+    """Compile oracle.c with gcc (strict IEEE double, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        c_i32p = ctypes.POINTER(ctypes.c_int32)
+        c_dp = ctypes.POINTER(ctypes.c_double)
+        c_u8p = ctypes.POINTER(ctypes.c_uint8)
+        L.orc_bytes_per_token.restype = ctypes.c_uint64
+        L.orc_bytes_per_token.argtypes = [ctypes.c_int64] * 4
+        L.orc_bf16_to_f64.restype = None
+        L.orc_bf16_to_f64.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16), c_dp]
+        L.orc_philox4x32_10.restype = None
+        L.orc_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32)] * 3
+        L.orc_random_key.restype = ctypes.c_uint32
+        L.orc_random_key.argtypes = [ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint32,
+                                     ctypes.c_uint32, ctypes.c_uint32]
+        L.orc_attend.restype = None
+        L.orc_attend.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                 c_dp, c_dp, c_dp, c_dp, c_dp]
+        L.orc_select_streaming.restype = None
+        L.orc_select_streaming.argtypes = [ctypes.c_int32, c_i32p, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_int32, c_u8p]
+        L.orc_select_h2o.restype = None
+        L.orc_select_h2o.argtypes = [ctypes.c_int32, c_i32p, c_dp, ctypes.c_int64,
+                                     ctypes.c_int32, ctypes.c_int32, c_u8p]
+        L.orc_select_random.restype = None
+        L.orc_select_random.argtypes = [ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                        ctypes.c_uint32, c_u8p]
+        L.orc_n_keep.restype = ctypes.c_int64
+        L.orc_n_keep.argtypes = [ctypes.c_int64, ctypes.c_double]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ct):
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+# ----------------------------------------------------------------------------
+# thin wrappers
+# ----------------------------------------------------------------------------
+
+def bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype_bytes: int) -> int:
+    return int(lib().orc_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes))
+
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage array (bf16 bit patterns or float32) -> float64, exactly."""
+    if dtype == "f32":
+        return np.asarray(x, np.float32).astype(np.float64)
+    bits = np.ascontiguousarray(x, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float64)
+    lib().orc_bf16_to_f64(bits.size, _p(bits, ctypes.c_uint16), _p(out, ctypes.c_double))
+    return out
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    o = np.empty(4, np.uint32)
+    lib().orc_philox4x32_10(_p(c, ctypes.c_uint32), _p(k, ctypes.c_uint32), _p(o, ctypes.c_uint32))
+    return o
+
+
+def random_key(pos: int, seed: int, seq: int, head: int, step: int) -> int:
+    return int(lib().orc_random_key(pos, seed, seq, head, step))
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: Optional[float] = None,
+           want_p: bool = False):
+    """q [G, D], K [n, D], V [n, D] float64 -> out [G, D] (and p [G, n])."""
+    q = np.ascontiguousarray(q, np.float64)
+    K = np.ascontiguousarray(K, np.float64)
+    V = np.ascontiguousarray(V, np.float64)
+    G, D = q.shape
+    n = K.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.empty((G, D), np.float64)
+    p = np.empty((G, max(n, 1)), np.float64) if want_p else None
+    lib().orc_attend(n, G, D, scale, _p(q, ctypes.c_double),
+                     _p(K if n else np.zeros((1, D)), ctypes.c_double),
+                     _p(V if n else np.zeros((1, D)), ctypes.c_double),
+                     _p(out, ctypes.c_double), _p(p, ctypes.c_double) if want_p else None)
+    if want_p:
+        return out, p[:, :n]
+    return out
+
+
+def select_streaming(pos, L: int, n_sink: int, n_recent: int) -> np.ndarray:
+    pos = np.ascontiguousarray(pos, np.int32)
+    keep = np.zeros(pos.size, np.uint8)
+    lib().orc_select_streaming(pos.size, _p(pos, ctypes.c_int32), L, n_sink, n_recent,
+                               _p(keep, ctypes.c_uint8))
+    return keep.astype(bool)
+
+
+def select_h2o(pos, score, L: int, n_heavy: int, n_recent: int) -> np.ndarray:
+    pos = np.ascontiguousarray(pos, np.int32)
+    score = np.ascontiguousarray(score, np.float64)
+    keep = np.zeros(pos.size, np.uint8)
+    lib().orc_select_h2o(pos.size, _p(pos, ctypes.c_int32), _p(score, ctypes.c_double), L,
+                         n_heavy, n_recent, _p(keep, ctypes.c_uint8))
+    return keep.astype(bool)
+
+
+def select_random(pos, prompt_len: int, n_keep: int, seed: int, seq: int, head: int,
+                  step: int) -> np.ndarray:
+    pos = np.ascontiguousarray(pos, np.int32)
+    keep = np.zeros(pos.size, np.uint8)
+    lib().orc_select_random(pos.size, _p(pos, ctypes.c_int32), prompt_len, n_keep,
+                            seed, seq, head, step, _p(keep, ctypes.c_uint8))
+    return keep.astype(bool)
+
+
+def n_keep(N: int, keep_ratio: float) -> int:
+    return int(lib().orc_n_keep(N, keep_ratio))
+
+
+# ----------------------------------------------------------------------------
+# multi-step trajectories
+# ----------------------------------------------------------------------------
+
+class Policy(dict):
+    """kind: 'full' | 'streaming' | 'h2o' | 'random' plus its parameters."""
+
+    @staticmethod
+    def streaming(n_sink=64, n_recent=448):
+        return Policy(kind="streaming", n_sink=n_sink, n_recent=n_recent)
+
+    @staticmethod
+    def h2o(n_heavy=64, n_recent=448):
+        return Policy(kind="h2o", n_heavy=n_heavy, n_recent=n_recent)
+
+    @staticmethod
+    def random(prompt_len, n_keep, seed=0):
+        return Policy(kind="random", prompt_len=prompt_len, n_keep=n_keep, seed=seed)
+
+    @staticmethod
+    def full():
+        return Policy(kind="full")
+
+
+class Unit:
+    """Canonical state of one (sequence, kv head): entries in ascending position."""
+
+    __slots__ = ("pos", "k", "v", "s")
+
+    def __init__(self, pos, k, v, s=None):
+        self.pos = np.asarray(pos, np.int32)
+        self.k = np.asarray(k, np.float64)
+        self.v = np.asarray(v, np.float64)
+        self.s = np.zeros(self.pos.size) if s is None else np.asarray(s, np.float64)
+
+
+class Oracle:
+    """Whole-batch decode steps with eviction, one sequence at a time."""
+
+    def __init__(self, q_heads: int, kv_heads: int, head_dim: int, dtype: str,
+                 scale: Optional[float] = None):
+        assert q_heads % kv_heads == 0
+        self.Hq, self.Hkv, self.D, self.dtype = q_heads, kv_heads, head_dim, dtype
+        self.G = q_heads // kv_heads
+        self.scale = 1.0 / math.sqrt(head_dim) if scale is None else scale
+        self.units: Dict[int, List[Unit]] = {}
+        self.seen: Dict[int, int] = {}
+
+    def load(self, b: int, k_store: np.ndarray, v_store: np.ndarray, seen: Optional[int] = None,
+             pos: Optional[np.ndarray] = None, scores: Optional[np.ndarray] = None):
+        """Cache of sequence b: storage arrays [Hkv, n, D]; positions default to 0..n-1."""
+        k = decode(k_store, self.dtype)
+        v = decode(v_store, self.dtype)
+        n = k.shape[1]
+        units = []
+        for h in range(self.Hkv):
+            ph = np.arange(n, dtype=np.int32) if pos is None else np.asarray(pos[h], np.int32)
+            sh = None if scores is None else np.asarray(scores[h], np.float64)
+            order = np.argsort(ph, kind="stable")
+            units.append(Unit(ph[order], k[h][order], v[h][order],
+                              None if sh is None else sh[order]))
+        self.units[b] = units
+        self.seen[b] = int(n if seen is None else seen)
+
+    def step(self, b: int, q_store, knew_store, vnew_store, policy: Policy, step: int = 0,
+             seq_id: Optional[int] = None):
+        """One decode step of sequence b: attend (new token included), then evict.
+
+        Returns out [Hq, D] float64 and the per-head post-attention scores
+        (before eviction, keyed by position) for H2O.
+        """
+        q = decode(q_store, self.dtype).reshape(self.Hq, self.D)
+        kn = decode(knew_store, self.dtype).reshape(self.Hkv, self.D)
+        vn = decode(vnew_store, self.dtype).reshape(self.Hkv, self.D)
+        p_new = self.seen[b]
+        out = np.empty((self.Hq, self.D))
+        post = []
+        for h, u in enumerate(self.units[b]):
+            u.pos = np.append(u.pos, np.int32(p_new))
+            u.k = np.vstack([u.k, kn[h][None]])
+            u.v = np.vstack([u.v, vn[h][None]])
+            u.s = np.append(u.s, 0.0)
+            o, p = attend(q[h * self.G:(h + 1) * self.G], u.k, u.v, self.scale, want_p=True)
+            out[h * self.G:(h + 1) * self.G] = o
+            if policy["kind"] == "h2o":
+                u.s = u.s + p.sum(axis=0)
+            post.append((u.pos.copy(), u.s.copy()))
+        self.seen[b] = p_new + 1
+        L = self.seen[b]
+        for h, u in enumerate(self.units[b]):
+            keep = self.select(u, L, policy, step, b if seq_id is None else seq_id, h)
+            u.pos, u.k, u.v, u.s = u.pos[keep], u.k[keep], u.v[keep], u.s[keep]
+        return out, post
+
+    @staticmethod
+    def select(u: Unit, L: int, policy: Policy, step: int, seq: int, head: int) -> np.ndarray:
+        kind = policy["kind"]
+        if kind == "full":
+            return np.ones(u.pos.size, bool)
+        if kind == "streaming":
+            return select_streaming(u.pos, L, policy["n_sink"], policy["n_recent"])
+        if kind == "h2o":
+            return select_h2o(u.pos, u.s, L, policy["n_heavy"], policy["n_recent"])
+        if kind == "random":
+            return select_random(u.pos, policy["prompt_len"], policy["n_keep"],
+                                 policy.get("seed", 0), seq, head, step)
+        raise ValueError(kind)
+
+    def kept_positions(self, b: int) -> List[np.ndarray]:
+        return [u.pos.copy() for u in self.units[b]]
