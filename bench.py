@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Decode attention + eviction throughput on one MI355X.
+
+Workload (default): the heavy-load layer -- batch 512, 64 query / 8 kv heads,
+head_dim 128, bf16, 2,048-token prompts -- under H2O-512 (64 heavy + 448
+recent).  Step 1 trims every unit from 2,049 attended tokens to 512 and is
+reported on its own; the timed steps are the steady state, one whole decode
+step each: attention for every sequence (new token included), the H2O score
+update, the selection and the compaction, all on the GPU.
+
+Prints one JSON line (rank 0, N = 1):
+  value = decode steps/s (whole batch), roofline of the dominant kernel
+  (algorithmic bytes / its HIP-event duration vs 8 TB/s), and the CPU oracle
+  timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def per_unit_bytes(n: int, G: int, D: int, b: int, policy: str) -> int:
+    """Algorithmic HBM bytes of one unit (sequence x kv head) in one steady step.
+
+    n = cached slots before the step.  K and V of the n cached slots are read
+    once; the new token's k, v are read once and written once; the group's q
+    is read and its fp32 output written; H2O reads and writes one fp32 score
+    per attended slot; every policy but 'full' reads one int32 position per
+    cached slot (the selection), and the new slot's position is written.
+    """
+    kv = 2 * n * D * b
+    new = 4 * D * b
+    qo = G * D * (b + 4)
+    sc = 8 * (n + 1) if policy == "h2o" else 0
+    pos = 4 * n if policy != "full" else 0
+    return kv + new + qo + sc + pos + 4
+
+
+def cpu_baseline(w, n_cached: int, budget_s: float = 12.0):
+    """The oracle (single thread) on whole sequences of the same shape at the
+    steady-state length, as many as fit in about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+    import synth
+    orc = oracle.Oracle(w.q_heads, w.kv_heads, w.head_dim, w.dtype)
+    pol = oracle.Policy.h2o(w.n_heavy, w.n_recent)
+    t_work = 0.0
+    done = 0
+    b = 0
+    while t_work < budget_s and b < w.batch:
+        k, v = synth.prefill_kv(w, b, n_cached)
+        orc.load(b, k, v)
+        q, kn, vn = synth.step_inputs(w, b, 1)
+        t0 = time.perf_counter()
+        orc.step(b, q, kn, vn, pol, step=1)
+        t_work += time.perf_counter() - t0
+        del orc.units[b]
+        done += 1
+        b += 1
+    per_seq = t_work / done
+    steps_per_s = 1.0 / (per_seq * w.batch)
+    return {
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} of {w.batch} sequences, one steady H2O step each "
+                   f"({n_cached} cached + 1 new, fp64, one thread), {t_work:.1f} s of work; "
+                   f"steps/s = 1 / (mean seconds per sequence x {w.batch})"),
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_nproc": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="heavy_load_b512_l2048")
+    ap.add_argument("--policy", default="h2o", choices=["h2o", "streaming", "full"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1. "
+                                   "Units (sequence, kv head) are independent, so the path "
+                                   "shards by sequences or kv heads with no exchange."}))
+        sys.exit(2)
+
+    import torch
+
+    import compressed_decode_attention_amd as kvc
+    import synth
+
+    w = synth.workload(args.workload)
+    policy = args.policy
+    B, Hq, Hkv, D, P = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.prompt_len
+    G = Hq // Hkv
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cap = P + 1 if policy != "full" else P + 2 + args.warmup + 2 * args.steps
+    log(f"workload {w.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} prompt={P} policy={policy} cap={cap}")
+
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    cache = kvc.KvCache(B, Hq, Hkv, D, cap, kvc.BF16, device=dev)
+    for b0 in range(0, B, 64):
+        sl = slice(b0, min(B, b0 + 64))
+        cache.k[sl, :, :P] = torch.randn(cache.k[sl, :, :P].shape, generator=gen, device=dev,
+                                         dtype=torch.float32).to(torch.bfloat16)
+        cache.v[sl, :, :P] = torch.randn(cache.v[sl, :, :P].shape, generator=gen, device=dev,
+                                         dtype=torch.float32).to(torch.bfloat16)
+    cache.pos[:, :, :P] = torch.arange(P, dtype=torch.int32, device=dev)
+    cache.n_slots.fill_(P)
+    scores = torch.zeros((B, Hkv, cap), device=dev) if policy == "h2o" else None
+    n_pool = 4
+    pool = [(torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16),
+             torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16),
+             torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16))
+            for _ in range(n_pool)]
+    total_steps = 1 + args.warmup + 2 * args.steps
+    new_pos = (P + torch.arange(total_steps, dtype=torch.int32, device=dev)).view(-1, 1).expand(
+        total_steps, B).contiguous()
+    out = torch.empty((B, Hq, D), device=dev)
+    if policy == "h2o":
+        pol = kvc.policy_h2o(w.n_heavy, w.n_recent)
+    elif policy == "streaming":
+        pol = kvc.policy_streaming(w.n_sink, w.n_recent)
+    else:
+        pol = kvc.policy_full()
+    hint = cap
+    ws = cache.workspace(hint)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(t):
+        q, kn, vn = pool[t % n_pool]
+        kvc.decode_step(cache, pol, t, new_pos[t - 1], q, kn, vn, out, scores,
+                        max_len_hint=hint, workspace=ws, stream=stream)
+
+    # step 1: the over-budget trim, timed alone
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    step(1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    trim_ms = e0.elapsed_time(e1)
+    n_after = int(cache.n_slots[0, 0].item())
+    log(f"step 1 (trim to {n_after}): {trim_ms:.3f} ms")
+
+    t = 2
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, no host sync inside
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(t)
+        t += 1
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms ({ms_per_step * 1e3:.1f} us/step), "
+        f"wall {wall * 1e3:.1f} ms")
+
+    # per-launch duration of the step, bracketed by events on the same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(t)
+        evs[i][1].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    assert int(cache.flags.item()) == 0, "device contract flag raised"
+
+    n_cached = n_after if policy != "full" else P + t
+    unit_bytes = per_unit_bytes(n_cached, G, D, 2, policy)
+    step_bytes = unit_bytes * B * Hkv
+    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+    steps_per_s = 1e3 / ms_per_step
+
+    result = {
+        "metric": "decode steps/s and achieved HBM GB/s (% of peak), attn+evict, B=512 L=2048",
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+            "prompt": P, "policy": policy, "budget": "64+448" if policy != "full" else "none",
+            "cached_per_unit": n_cached, "kv_dtype": "bf16", "accumulate": "fp32",
+            "tokens_per_s": steps_per_s * B, "trim_step_ms": trim_ms,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "kvc_decode_step (whole step)",
+            "bytes_per_unit": unit_bytes, "units_per_launch": B * Hkv,
+            "launch_ms": launch_ms,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, n_cached if policy != "full" else P,
+                                              args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,294 @@
+"""Python binding of libkvc (decode attention over a budget-limited per-head KV
+cache with StreamingLLM / H2O / per-head random eviction, for MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libkvc.so; PyTorch provides device memory and the stream.  The functions carry
+the C ABI's names without the ``kvc_`` prefix.  There is no CPU fallback: if
+the library is missing, importing this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libkvc.so not found at {LIB_PATH}; build it with "
+        "`python -m compressed_decode_attention_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---------------------------------------------------------------------------
+# C types
+# ---------------------------------------------------------------------------
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_WORKSPACE, ERR_HIP = range(6)
+BF16, F32 = 0, 1
+FLAG_FULL, FLAG_BAD_COUNT, FLAG_BAD_BLOCK = 1, 2, 4
+POLICY_FULL, POLICY_STREAMING, POLICY_H2O, POLICY_RANDOM = range(4)
+
+EXPORTED = (
+    "kvc_bytes_per_token", "kvc_n_keep", "kvc_status_string", "kvc_last_error",
+    "kvc_workspace_bytes", "kvc_decode_attn", "kvc_h2o_accumulate", "kvc_evict_streaming",
+    "kvc_evict_h2o", "kvc_evict_random", "kvc_compact", "kvc_decode_step",
+)
+
+
+class kvc_cache(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("pos", ctypes.c_void_p), ("n_slots", ctypes.c_void_p), ("flags", ctypes.c_void_p),
+    ]
+
+
+class kvc_policy(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_heavy", ctypes.c_int32),
+        ("n_recent", ctypes.c_int32), ("prompt_len", ctypes.c_int32), ("n_keep", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+    ]
+
+
+_P = ctypes.c_void_p
+_CP = ctypes.POINTER(kvc_cache)
+_lib.kvc_bytes_per_token.restype = ctypes.c_size_t
+_lib.kvc_bytes_per_token.argtypes = [ctypes.c_int32] * 4
+_lib.kvc_n_keep.restype = ctypes.c_int64
+_lib.kvc_n_keep.argtypes = [ctypes.c_int64, ctypes.c_double]
+_lib.kvc_status_string.restype = ctypes.c_char_p
+_lib.kvc_status_string.argtypes = [ctypes.c_int]
+_lib.kvc_last_error.restype = ctypes.c_char_p
+_lib.kvc_last_error.argtypes = []
+_lib.kvc_workspace_bytes.restype = ctypes.c_size_t
+_lib.kvc_workspace_bytes.argtypes = [_CP, ctypes.c_int32]
+_lib.kvc_decode_attn.restype = ctypes.c_int
+_lib.kvc_decode_attn.argtypes = [_CP, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
+                                 _P, ctypes.c_size_t, _P]
+_lib.kvc_h2o_accumulate.restype = ctypes.c_int
+_lib.kvc_h2o_accumulate.argtypes = [_CP, _P, ctypes.c_int32, _P, _P, ctypes.c_float, _P]
+_lib.kvc_evict_streaming.restype = ctypes.c_int
+_lib.kvc_evict_streaming.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+_lib.kvc_evict_h2o.restype = ctypes.c_int
+_lib.kvc_evict_h2o.argtypes = [_CP, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+_lib.kvc_evict_random.restype = ctypes.c_int
+_lib.kvc_evict_random.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
+                                  ctypes.c_uint32, _P, _P, _P]
+_lib.kvc_compact.restype = ctypes.c_int
+_lib.kvc_compact.argtypes = [_CP, _P, _P, _P, _CP, _P]
+_lib.kvc_decode_step.restype = ctypes.c_int
+_lib.kvc_decode_step.argtypes = [_CP, ctypes.POINTER(kvc_policy), ctypes.c_uint32, _P, _P, _P,
+                                 _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
+                                 ctypes.c_size_t, _P]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_lib.kvc_status_string(status).decode()} ({status}): {detail}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != OK:
+        raise KvcError(status, _lib.kvc_last_error().decode())
+
+
+def library():
+    """The loaded ctypes library (for symbol checks)."""
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return _lib.kvc_status_string(s).decode()
+
+
+def last_error() -> str:
+    return _lib.kvc_last_error().decode()
+
+
+def bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype_bytes: int) -> int:
+    return int(_lib.kvc_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes))
+
+
+def n_keep(n_candidates: int, keep_ratio: float) -> int:
+    return int(_lib.kvc_n_keep(n_candidates, keep_ratio))
+
+
+# ---------------------------------------------------------------------------
+# tensors -> pointers
+# ---------------------------------------------------------------------------
+_TORCH_DTYPE = {BF16: torch.bfloat16, F32: torch.float32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libkvc must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+class KvCache:
+    """Device buffers of one cache (contiguous or paged) and its C descriptor.
+
+    The tensors belong to this object; libkvc only reads and writes them.
+    """
+
+    def __init__(self, batch: int, q_heads: int, kv_heads: int, head_dim: int, capacity: int,
+                 dtype: int = BF16, device="cuda", block_size: int = 0,
+                 num_blocks: int = 0, block_table: Optional[torch.Tensor] = None):
+        self.batch, self.q_heads, self.kv_heads = batch, q_heads, kv_heads
+        self.head_dim, self.capacity, self.dtype = head_dim, capacity, dtype
+        self.block_size = block_size
+        tdt = _TORCH_DTYPE[dtype]
+        if block_size:
+            assert capacity % block_size == 0
+            self.max_blocks = capacity // block_size
+            self.num_blocks = num_blocks
+            shape = (num_blocks, kv_heads, block_size, head_dim)
+            if block_table is None:
+                raise ValueError("paged cache needs a block table")
+            self.block_table = block_table.to(device=device, dtype=torch.int32).contiguous()
+        else:
+            self.max_blocks = 0
+            self.num_blocks = 0
+            shape = (batch, kv_heads, capacity, head_dim)
+            self.block_table = None
+        self.k = torch.zeros(shape, dtype=tdt, device=device)
+        self.v = torch.zeros(shape, dtype=tdt, device=device)
+        self.pos = torch.zeros((batch, kv_heads, capacity), dtype=torch.int32, device=device)
+        self.n_slots = torch.zeros((batch, kv_heads), dtype=torch.int32, device=device)
+        self.flags = torch.zeros((1,), dtype=torch.int32, device=device)
+        self._c = None
+
+    @property
+    def group(self) -> int:
+        return self.q_heads // self.kv_heads
+
+    def c(self) -> kvc_cache:
+        if self._c is None:
+            c = kvc_cache()
+            c.batch, c.q_heads, c.kv_heads = self.batch, self.q_heads, self.kv_heads
+            c.head_dim, c.capacity, c.dtype = self.head_dim, self.capacity, self.dtype
+            c.block_size, c.max_blocks, c.num_blocks = self.block_size, self.max_blocks, \
+                self.num_blocks
+            c.k, c.v = _ptr(self.k), _ptr(self.v)
+            c.block_table = _ptr(self.block_table)
+            c.pos, c.n_slots, c.flags = _ptr(self.pos), _ptr(self.n_slots), _ptr(self.flags)
+            self._c = c
+        return self._c
+
+    def rows(self, b: int, h: int, slots):
+        """(k, v) rows of unit (b, h) at the given slots (for inspection)."""
+        slots = torch.as_tensor(slots, dtype=torch.long, device=self.k.device)
+        if not self.block_size:
+            return self.k[b, h, slots], self.v[b, h, slots]
+        blk = self.block_table[b, slots // self.block_size].long()
+        off = slots % self.block_size
+        return self.k[blk, h, off], self.v[blk, h, off]
+
+    def workspace_bytes(self, max_len_hint: int = 0) -> int:
+        return int(_lib.kvc_workspace_bytes(ctypes.byref(self.c()), max_len_hint))
+
+    def workspace(self, max_len_hint: int = 0) -> torch.Tensor:
+        n = self.workspace_bytes(max_len_hint)
+        return torch.empty((max(n, 1),), dtype=torch.uint8, device=self.k.device)
+
+
+def _policy(kind: int, n_sink=0, n_heavy=0, n_recent=0, prompt_len=0, n_keep=0, seed=0):
+    p = kvc_policy()
+    p.kind, p.n_sink, p.n_heavy, p.n_recent = kind, n_sink, n_heavy, n_recent
+    p.prompt_len, p.n_keep, p.seed = prompt_len, n_keep, seed
+    return p
+
+
+def policy_full():
+    return _policy(POLICY_FULL)
+
+
+def policy_streaming(n_sink=64, n_recent=448):
+    return _policy(POLICY_STREAMING, n_sink=n_sink, n_recent=n_recent)
+
+
+def policy_h2o(n_heavy=64, n_recent=448):
+    return _policy(POLICY_H2O, n_heavy=n_heavy, n_recent=n_recent)
+
+
+def policy_random(prompt_len, n_keep, seed=0):
+    return _policy(POLICY_RANDOM, prompt_len=prompt_len, n_keep=n_keep, seed=seed)
+
+
+def _scale(cache: KvCache, scale):
+    return 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def decode_attn(cache: KvCache, new_pos, q, k_new, v_new, out, scores=None, scale=None,
+                max_len_hint: int = 0, workspace=None, stream=None):
+    wp, wn = _ws(workspace)
+    _check(_lib.kvc_decode_attn(ctypes.byref(cache.c()), _ptr(new_pos), _ptr(q), _ptr(k_new),
+                                _ptr(v_new), _ptr(out), _ptr(scores), _scale(cache, scale),
+                                max_len_hint, wp, wn, _stream(stream)))
+
+
+def h2o_accumulate(cache: KvCache, q_rows, m_rows: int, scores, q_pos=None, scale=None,
+                   stream=None):
+    _check(_lib.kvc_h2o_accumulate(ctypes.byref(cache.c()), _ptr(q_rows), m_rows, _ptr(q_pos),
+                                   _ptr(scores), _scale(cache, scale), _stream(stream)))
+
+
+def evict_streaming(cache: KvCache, n_sink: int, n_recent: int, keep_slots, n_out, stream=None):
+    _check(_lib.kvc_evict_streaming(ctypes.byref(cache.c()), n_sink, n_recent, _ptr(keep_slots),
+                                    _ptr(n_out), _stream(stream)))
+
+
+def evict_h2o(cache: KvCache, scores, n_heavy: int, n_recent: int, keep_slots, n_out,
+              stream=None):
+    _check(_lib.kvc_evict_h2o(ctypes.byref(cache.c()), _ptr(scores), n_heavy, n_recent,
+                              _ptr(keep_slots), _ptr(n_out), _stream(stream)))
+
+
+def evict_random(cache: KvCache, prompt_len: int, n_keep: int, seed: int, step: int, keep_slots,
+                 n_out, stream=None):
+    _check(_lib.kvc_evict_random(ctypes.byref(cache.c()), prompt_len, n_keep, seed, step,
+                                 _ptr(keep_slots), _ptr(n_out), _stream(stream)))
+
+
+def compact(cache: KvCache, keep_slots, n_out, scores=None, ordered_dst: Optional[KvCache] = None,
+            stream=None):
+    dst = ctypes.byref(ordered_dst.c()) if ordered_dst is not None else None
+    _check(_lib.kvc_compact(ctypes.byref(cache.c()), _ptr(keep_slots), _ptr(n_out), _ptr(scores),
+                            dst, _stream(stream)))
+
+
+def decode_step(cache: KvCache, policy: kvc_policy, step: int, new_pos, q, k_new, v_new, out,
+                scores=None, scale=None, max_len_hint: int = 0, workspace=None, stream=None):
+    wp, wn = _ws(workspace)
+    _check(_lib.kvc_decode_step(ctypes.byref(cache.c()), ctypes.byref(policy), step,
+                                _ptr(new_pos), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
+                                _ptr(scores), _scale(cache, scale), max_len_hint, wp, wn,
+                                _stream(stream)))

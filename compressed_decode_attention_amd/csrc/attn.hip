@@ -1,0 +1,381 @@
+// attn.hip -- decode attention over a per-head KV cache, split over
+// workgroups, with the H2O accumulated-attention update folded in.
+//
+// Per unit (sequence b, kv head h) the G query heads of the group attend the
+// n cached slots plus the new token: z = scale * q.k, p = softmax(z),
+// o = sum p v (KV cache compression guide, section 16, "prefill, decode, TP":
+// a decode step reads all kept history).  With H2O scores requested, every
+// slot's score grows by the group-summed probability (same guide, sections 2
+// and 16, "the 4 methods"; section 16 "limits" notes that fused attention
+// normally hides these probabilities -- here they are computed exactly, with
+// the final softmax normaliser).
+//
+// This file holds the generic VALU path: one workgroup per (unit, split),
+// logits kept in a global scratch row per (unit, query head), a combine pass
+// when a unit is split across workgroups.
+#include "kvc_internal.h"
+
+namespace kvc {
+
+constexpr int kAttnThreads = 256;
+constexpr int kMaxSplit = 64;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
+    const CacheDev &c = a.c;
+    const int G = c.G;
+    const int u = blockIdx.x / a.nsplit, s = blockIdx.x % a.nsplit;
+    const int b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    constexpr int kParts = kAttnThreads / D;
+
+    __shared__ float q_s[kMaxGroup * D];
+    __shared__ float st_m[kMaxGroup], st_l[kMaxGroup];
+    __shared__ float red[kAttnThreads / 64][kMaxGroup];
+    __shared__ float pv[kParts][kMaxGroup][D];
+
+    const int n = load_count(c, u, s == 0 && tid == 0);
+    const bool can_store = n < c.cap;
+    if (!can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
+    const int T_len = n + 1;
+    const int chunk = (T_len + a.nsplit - 1) / a.nsplit;
+    const int j0 = min(s * chunk, T_len), j1 = min(T_len, j0 + chunk);
+
+    const T *qp = (const T *)a.q + ((size_t)b * c.Hq + (size_t)h * G) * D;
+    for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<T>::get(qp, e);
+    __syncthreads();
+
+    const T *K = (const T *)c.k;
+    const T *V = (const T *)c.v;
+    const T *kn = (const T *)a.k_new + ((size_t)b * c.Hkv + h) * D;
+    const T *vn = (const T *)a.v_new + ((size_t)b * c.Hkv + h) * D;
+    const size_t ld = (size_t)c.cap + 1;
+    float *lg = a.logits + (size_t)u * G * ld;
+
+    // ---- logits and running max (thread owns keys j = j0 + tid + k*256)
+    float mloc[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) mloc[g] = -INFINITY;
+    for (int j = j0 + tid; j < j1; j += kAttnThreads) {
+        const T *row = (j < n) ? K + row_of(c, b, h, j) * D : kn;
+        float acc[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
+        for (int d = 0; d < D; ++d) {
+            const float kv = Elem<T>::get(row, d);
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g)
+            if (g < G) {
+                const float z = acc[g] * a.scale;
+                lg[g * ld + j] = z;
+                mloc[g] = fmaxf(mloc[g], z);
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+        const float w = wave_max(mloc[g]);
+        if (lane == 0) red[wv][g] = w;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float m = red[0][tid];
+        for (int w = 1; w < kAttnThreads / 64; ++w) m = fmaxf(m, red[w][tid]);
+        st_m[tid] = m;
+    }
+    __syncthreads();
+
+    // ---- unnormalised weights w = exp(z - m), row sums
+    float lloc[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) lloc[g] = 0.f;
+    for (int j = j0 + tid; j < j1; j += kAttnThreads) {
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g)
+            if (g < G) {
+                const float w = __expf(lg[g * ld + j] - st_m[g]);
+                lg[g * ld + j] = w;
+                lloc[g] += w;
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+        const float w = wave_sum(lloc[g]);
+        if (lane == 0) red[wv][g] = w;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float l = 0.f;
+        for (int w = 0; w < kAttnThreads / 64; ++w) l += red[w][tid];
+        st_l[tid] = l;
+    }
+    __syncthreads();
+
+    // ---- P.V: thread owns one dimension d and every kParts-th key
+    {
+        const int d = tid % D, part = tid / D;
+        float acc[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
+        for (int j = j0 + part; j < j1; j += kParts) {
+            const T *row = (j < n) ? V + row_of(c, b, h, j) * D : vn;
+            const float vv = Elem<T>::get(row, d);
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) acc[g] = fmaf(lg[g * ld + j], vv, acc[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) pv[part][g][d] = acc[g];
+    }
+    __syncthreads();
+
+    if (a.nsplit == 1) {
+        if (tid < D) {
+            for (int g = 0; g < G; ++g) {
+                float o = 0.f;
+                for (int p = 0; p < kParts; ++p) o += pv[p][g][tid];
+                a.out[((size_t)b * c.Hq + (size_t)h * G + g) * D + tid] = o / st_l[g];
+            }
+        }
+        if (a.scores) {
+            float *sc = a.scores + (size_t)u * c.cap;
+            for (int j = j0 + tid; j < j1; j += kAttnThreads) {
+                float ps = 0.f;
+                for (int g = 0; g < G; ++g) ps += lg[g * ld + j] / st_l[g];
+                if (j < n) sc[j] += ps;
+                else if (can_store) sc[n] = ps;
+            }
+        }
+    } else {
+        float *pp = a.part + ((size_t)u * a.nsplit + s) * G * (D + 2);
+        if (tid < D) {
+            for (int g = 0; g < G; ++g) {
+                float o = 0.f;
+                for (int p = 0; p < kParts; ++p) o += pv[p][g][tid];
+                pp[g * (D + 2) + tid] = o;
+            }
+        }
+        if (tid < G) {
+            pp[tid * (D + 2) + D] = st_m[tid];
+            pp[tid * (D + 2) + D + 1] = st_l[tid];
+        }
+    }
+
+    // ---- append the new token (the workgroup whose range holds index n)
+    if (can_store && j0 <= n && n < j1) {
+        T *Kw = (T *)c.k;
+        T *Vw = (T *)c.v;
+        const size_t r = row_of(c, b, h, n) * D;
+        for (int e = tid; e < D; e += kAttnThreads) {
+            Kw[r + e] = kn[e];
+            Vw[r + e] = vn[e];
+        }
+        if (tid == 0) c.pos[(size_t)u * c.cap + n] = a.new_pos[b];
+    }
+    if (a.nsplit == 1 && tid == 0 && can_store) c.n_slots[u] = n + 1;
+}
+
+// Combine the splits of one unit: rescale partial sums to the global max,
+// normalise, update scores and the slot count.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
+    const CacheDev &c = a.c;
+    const int G = c.G, ns = a.nsplit;
+    const int u = blockIdx.x, b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x;
+    __shared__ float fac[kMaxSplit][kMaxGroup];   // exp(m_s - M) / L
+    __shared__ float Mg[kMaxGroup], Lg[kMaxGroup];
+
+    const int n = load_count(c, u, false);
+    const bool can_store = n < c.cap;
+    const int T_len = n + 1;
+    const int chunk = (T_len + ns - 1) / ns;
+    const float *pp = a.part + (size_t)u * ns * G * (D + 2);
+
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, pp[(s * G + tid) * (D + 2) + D]);
+        float L = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            const float ms = pp[(s * G + tid) * (D + 2) + D];
+            const float ls = pp[(s * G + tid) * (D + 2) + D + 1];
+            L += (ms == -INFINITY) ? 0.f : ls * __expf(ms - M);
+        }
+        Mg[tid] = M;
+        Lg[tid] = L;
+        for (int s = 0; s < ns; ++s) {
+            const float ms = pp[(s * G + tid) * (D + 2) + D];
+            fac[s][tid] = (ms == -INFINITY) ? 0.f : __expf(ms - M) / L;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * D; e += kAttnThreads) {
+        const int g = e / D, d = e % D;
+        float o = 0.f;
+        for (int s = 0; s < ns; ++s) o += pp[(s * G + g) * (D + 2) + d] * fac[s][g];
+        a.out[((size_t)b * c.Hq + (size_t)h * G + g) * D + d] = o;
+    }
+    if (a.scores) {
+        const size_t ld = (size_t)c.cap + 1;
+        const float *lg = a.logits + (size_t)u * G * ld;
+        float *sc = a.scores + (size_t)u * c.cap;
+        for (int j = tid; j < T_len; j += kAttnThreads) {
+            const int s = j / chunk;
+            float ps = 0.f;
+            for (int g = 0; g < G; ++g) ps += lg[g * ld + j] * fac[s][g];
+            if (j < n) sc[j] += ps;
+            else if (can_store) sc[n] = ps;
+        }
+    }
+    if (tid == 0 && can_store) c.n_slots[u] = n + 1;
+}
+
+template <typename T, int D>
+static hipError_t launch_typed(const AttnArgs &a, hipStream_t s) {
+    const int units = a.c.B * a.c.Hkv;
+    hipLaunchKernelGGL((attn_valu_kernel<T, D>), dim3(units * a.nsplit), dim3(kAttnThreads), 0, s,
+                       a);
+    if (a.nsplit > 1)
+        hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(units), dim3(kAttnThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
+    if (dtype == KVC_BF16) {
+        if (a.c.D == 128) return launch_typed<uint16_t, 128>(a, s);
+        if (a.c.D == 64) return launch_typed<uint16_t, 64>(a, s);
+    } else {
+        if (a.c.D == 128) return launch_typed<float, 128>(a, s);
+        if (a.c.D == 64) return launch_typed<float, 64>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Unfused H2O score pass over m_rows query rows per sequence: each row's
+// group-summed probabilities are added to the scores (no append).  Two
+// traversals of K per row: one for the softmax statistics, one to add the
+// normalised probabilities.  The thread that owns a slot is the only writer of
+// its score, so the accumulation order is fixed.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kAttnThreads) void accumulate_kernel(AccumArgs a) {
+    const CacheDev &c = a.c;
+    const int G = c.G;
+    const int u = blockIdx.x, b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    __shared__ float q_s[kMaxGroup * D];
+    __shared__ float st_m[kMaxGroup], st_l[kMaxGroup];
+    __shared__ float red[kAttnThreads / 64][kMaxGroup];
+
+    const int n = load_count(c, u, tid == 0);
+    const T *K = (const T *)c.k;
+    const int32_t *P = c.pos + (size_t)u * c.cap;
+    float *sc = a.scores + (size_t)u * c.cap;
+
+    for (int r = 0; r < a.m_rows; ++r) {
+        const T *qp = (const T *)a.q_rows +
+                      (((size_t)b * a.m_rows + r) * c.Hq + (size_t)h * G) * D;
+        const int limit = a.q_pos ? a.q_pos[(size_t)b * a.m_rows + r] : 0x7FFFFFFF;
+        __syncthreads();
+        for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<T>::get(qp, e);
+        __syncthreads();
+        float mloc[kMaxGroup], lloc[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) {
+            mloc[g] = -INFINITY;
+            lloc[g] = 0.f;
+        }
+        // online max / sum over the thread's keys
+        for (int j = tid; j < n; j += kAttnThreads) {
+            if (P[j] > limit) continue;
+            const T *row = K + row_of(c, b, h, j) * D;
+            float acc[kMaxGroup];
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
+            for (int d = 0; d < D; ++d) {
+                const float kv = Elem<T>::get(row, d);
+#pragma unroll
+                for (int g = 0; g < kMaxGroup; ++g)
+                    if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
+            }
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) {
+                    const float z = acc[g] * a.scale;
+                    const float mn = fmaxf(mloc[g], z);
+                    lloc[g] = lloc[g] * __expf(mloc[g] - mn) + __expf(z - mn);
+                    mloc[g] = mn;
+                }
+        }
+        // merge (m, l) over the block
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) {
+            const float mw = wave_max(mloc[g]);
+            const float lw = wave_sum(mloc[g] == -INFINITY ? 0.f : lloc[g] * __expf(mloc[g] - mw));
+            if (lane == 0) {
+                red[wv][g] = mw;
+            }
+            lloc[g] = lw;
+            mloc[g] = mw;
+        }
+        __syncthreads();
+        if (tid < G) {
+            float M = red[0][tid];
+            for (int w = 1; w < kAttnThreads / 64; ++w) M = fmaxf(M, red[w][tid]);
+            st_m[tid] = M;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g)
+            if (lane == 0) red[wv][g] = (mloc[g] == -INFINITY || g >= G) ? 0.f : lloc[g] * __expf(mloc[g] - st_m[g]);
+        __syncthreads();
+        if (tid < G) {
+            float L = 0.f;
+            for (int w = 0; w < kAttnThreads / 64; ++w) L += red[w][tid];
+            st_l[tid] = L;
+        }
+        __syncthreads();
+        // add normalised probabilities
+        for (int j = tid; j < n; j += kAttnThreads) {
+            if (P[j] > limit) continue;
+            const T *row = K + row_of(c, b, h, j) * D;
+            float acc[kMaxGroup];
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
+            for (int d = 0; d < D; ++d) {
+                const float kv = Elem<T>::get(row, d);
+#pragma unroll
+                for (int g = 0; g < kMaxGroup; ++g)
+                    if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
+            }
+            float ps = 0.f;
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) ps += __expf(acc[g] * a.scale - st_m[g]) / st_l[g];
+            sc[j] += ps;
+        }
+    }
+}
+
+hipError_t launch_accumulate(const AccumArgs &a, int dtype, hipStream_t s) {
+    const int units = a.c.B * a.c.Hkv;
+    if (a.m_rows <= 0) return hipSuccess;
+    if (dtype == KVC_BF16) {
+        if (a.c.D == 128)
+            hipLaunchKernelGGL((accumulate_kernel<uint16_t, 128>), dim3(units), dim3(kAttnThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((accumulate_kernel<uint16_t, 64>), dim3(units), dim3(kAttnThreads), 0, s, a);
+    } else {
+        if (a.c.D == 128)
+            hipLaunchKernelGGL((accumulate_kernel<float, 128>), dim3(units), dim3(kAttnThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((accumulate_kernel<float, 64>), dim3(units), dim3(kAttnThreads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvc

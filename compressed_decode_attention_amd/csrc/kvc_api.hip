@@ -1,0 +1,383 @@
+// kvc_api.hip -- the extern "C" entry points of libkvc: host-side argument
+// validation (nothing is enqueued when a call fails), workspace layout,
+// split selection and kernel dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kvc_internal.h"
+
+#define KVC_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvc_status fail(kvc_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+kvc_status fail(kvc_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+kvc_status ok() {
+    g_err[0] = '\0';
+    return KVC_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+kvc_status check_cache(const kvc_cache *c, const char *what) {
+    if (!c) return fail(KVC_ERR_INVALID_ARG, "%s: cache is NULL", what);
+    if (c->batch <= 0 || c->q_heads <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 ||
+        c->capacity <= 0)
+        return fail(KVC_ERR_INVALID_ARG, "%s: batch, heads, head_dim and capacity must be > 0",
+                    what);
+    if (c->q_heads % c->kv_heads != 0)
+        return fail(KVC_ERR_SHAPE, "%s: q_heads %d is not a multiple of kv_heads %d", what,
+                    c->q_heads, c->kv_heads);
+    if (c->q_heads / c->kv_heads > kvc::kMaxGroup)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: group size %d > %d", what,
+                    c->q_heads / c->kv_heads, kvc::kMaxGroup);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", what, c->head_dim);
+    if (c->dtype != KVC_BF16 && c->dtype != KVC_F32)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: dtype %d", what, c->dtype);
+    if (c->capacity > kvc::kMaxCapacity)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: capacity %d > %d", what, c->capacity,
+                    kvc::kMaxCapacity);
+    if (!c->k || !c->v || !c->pos || !c->n_slots)
+        return fail(KVC_ERR_INVALID_ARG, "%s: k, v, pos and n_slots must not be NULL", what);
+    if ((uintptr_t)c->k % 16 || (uintptr_t)c->v % 16)
+        return fail(KVC_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", what);
+    if (c->block_size < 0)
+        return fail(KVC_ERR_INVALID_ARG, "%s: block_size < 0", what);
+    if (c->block_size > 0) {
+        if (!c->block_table)
+            return fail(KVC_ERR_INVALID_ARG, "%s: paged cache without block_table", what);
+        if (c->max_blocks <= 0 || c->num_blocks <= 0)
+            return fail(KVC_ERR_SHAPE, "%s: max_blocks and num_blocks must be > 0", what);
+        if ((int64_t)c->max_blocks * c->block_size != c->capacity)
+            return fail(KVC_ERR_SHAPE, "%s: capacity %d != max_blocks %d x block_size %d", what,
+                        c->capacity, c->max_blocks, c->block_size);
+    }
+    return KVC_OK;
+}
+
+int units_of(const kvc_cache *c) { return c->batch * c->kv_heads; }
+
+// Workgroups per unit for a unit length of up to `hint` attended entries:
+// at most 1024 keys per workgroup, and enough workgroups to cover the chip
+// when the batch is small (never below 256 keys per workgroup).
+int choose_nsplit(const kvc_cache *c, int hint) {
+    const int T = (hint <= 0 || hint > c->capacity + 1) ? c->capacity + 1 : hint;
+    const int units = units_of(c);
+    int ns = (T + 1023) / 1024;
+    if (units < 2048) {
+        int fill = (2048 + units - 1) / units;
+        int by_len = (T + 255) / 256;
+        fill = fill < by_len ? fill : by_len;
+        ns = ns > fill ? ns : fill;
+    }
+    if (ns < 1) ns = 1;
+    if (ns > 64) ns = 64;
+    return ns;
+}
+
+struct Workspace {
+    size_t part_off, part_bytes;
+    size_t logit_off, logit_bytes;
+    size_t keep_off, keep_bytes;
+    size_t nout_off, nout_bytes;
+    size_t total;
+    int nsplit;
+};
+
+Workspace layout(const kvc_cache *c, int hint) {
+    Workspace w;
+    const size_t units = (size_t)units_of(c);
+    const size_t G = (size_t)(c->q_heads / c->kv_heads);
+    w.nsplit = choose_nsplit(c, hint);
+    w.part_bytes = w.nsplit > 1 ? units * w.nsplit * G * (c->head_dim + 2) * sizeof(float) : 0;
+    w.logit_bytes = units * G * ((size_t)c->capacity + 1) * sizeof(float);
+    w.keep_bytes = units * (size_t)c->capacity * sizeof(int32_t);
+    w.nout_bytes = units * sizeof(int32_t);
+    size_t off = 0;
+    w.part_off = off;
+    off += align_up(w.part_bytes);
+    w.logit_off = off;
+    off += align_up(w.logit_bytes);
+    w.keep_off = off;
+    off += align_up(w.keep_bytes);
+    w.nout_off = off;
+    off += align_up(w.nout_bytes);
+    w.total = off;
+    return w;
+}
+
+kvc_status check_ws(const Workspace &w, void *ws, size_t bytes, const char *what) {
+    if (w.total == 0) return KVC_OK;
+    if (!ws) return fail(KVC_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", what, w.total);
+    if (bytes < w.total)
+        return fail(KVC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what, bytes, w.total);
+    if ((uintptr_t)ws % kAlign)
+        return fail(KVC_ERR_WORKSPACE, "%s: workspace must be %zu-byte aligned", what, kAlign);
+    return KVC_OK;
+}
+
+kvc_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+kvc_status check_policy(const kvc_policy *p, const float *scores, const char *what) {
+    if (!p) return fail(KVC_ERR_INVALID_ARG, "%s: policy is NULL", what);
+    switch (p->kind) {
+        case KVC_POLICY_FULL:
+            return KVC_OK;
+        case KVC_POLICY_STREAMING:
+            if (p->n_sink < 0 || p->n_recent < 0)
+                return fail(KVC_ERR_INVALID_ARG, "%s: n_sink and n_recent must be >= 0", what);
+            return KVC_OK;
+        case KVC_POLICY_H2O:
+            if (p->n_heavy < 0 || p->n_recent < 0)
+                return fail(KVC_ERR_INVALID_ARG, "%s: n_heavy and n_recent must be >= 0", what);
+            if (!scores) return fail(KVC_ERR_INVALID_ARG, "%s: H2O needs h2o_scores", what);
+            return KVC_OK;
+        case KVC_POLICY_RANDOM:
+            if (p->prompt_len < 0 || p->n_keep < 0)
+                return fail(KVC_ERR_INVALID_ARG, "%s: prompt_len and n_keep must be >= 0", what);
+            return KVC_OK;
+        default:
+            return fail(KVC_ERR_INVALID_ARG, "%s: unknown policy kind %d", what, p->kind);
+    }
+}
+
+kvc::AttnArgs attn_args(const kvc_cache *c, const int32_t *new_pos, const void *q,
+                        const void *k_new, const void *v_new, float *out, float *scores,
+                        float scale, const Workspace &w, void *ws) {
+    kvc::AttnArgs a;
+    a.c = kvc::make_dev(*c);
+    a.new_pos = new_pos;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.out = out;
+    a.scores = scores;
+    a.scale = scale;
+    a.nsplit = w.nsplit;
+    a.part = w.part_bytes ? (float *)((char *)ws + w.part_off) : nullptr;
+    a.logits = (float *)((char *)ws + w.logit_off);
+    return a;
+}
+
+kvc_status check_attn_args(const kvc_cache *c, const int32_t *new_pos, const void *q,
+                           const void *k_new, const void *v_new, const float *out, float scale,
+                           const char *what) {
+    kvc_status s = check_cache(c, what);
+    if (s != KVC_OK) return s;
+    if (!new_pos || !q || !k_new || !v_new || !out)
+        return fail(KVC_ERR_INVALID_ARG, "%s: new_pos, q, k_new, v_new and out must not be NULL",
+                    what);
+    if (!isfinite(scale)) return fail(KVC_ERR_INVALID_ARG, "%s: scale is not finite", what);
+    return KVC_OK;
+}
+
+kvc::SelectArgs select_args(const kvc_cache *c, const kvc_policy &p, uint32_t step,
+                            const float *scores, int32_t *keep, int32_t *nout) {
+    kvc::SelectArgs a;
+    a.c = kvc::make_dev(*c);
+    a.kind = p.kind;
+    a.n_sink = p.n_sink;
+    a.n_heavy = p.n_heavy;
+    a.n_recent = p.n_recent;
+    a.prompt_len = p.prompt_len;
+    a.n_keep = p.n_keep;
+    a.seed = p.seed;
+    a.step = step;
+    a.scores = scores;
+    a.keep_slots = keep;
+    a.n_out = nout;
+    return a;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+
+KVC_EXPORT size_t kvc_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                      int32_t dtype_bytes) {
+    if (layers <= 0 || kv_heads <= 0 || head_dim <= 0 || dtype_bytes <= 0) return 0;
+    return (size_t)2 * (size_t)layers * (size_t)kv_heads * (size_t)head_dim * (size_t)dtype_bytes;
+}
+
+KVC_EXPORT int64_t kvc_n_keep(int64_t n_candidates, double keep_ratio) {
+    if (n_candidates <= 0) return 0;
+    const double prod = (double)n_candidates * keep_ratio;
+    int64_t k = (prod >= 9.2e18) ? n_candidates : (int64_t)prod;   // truncation toward zero
+    if (k < 1) k = 1;
+    if (k > n_candidates) k = n_candidates;
+    return k;
+}
+
+KVC_EXPORT const char *kvc_status_string(kvc_status s) {
+    switch (s) {
+        case KVC_OK: return "ok";
+        case KVC_ERR_INVALID_ARG: return "invalid argument";
+        case KVC_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case KVC_ERR_SHAPE: return "inconsistent shapes";
+        case KVC_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVC_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+KVC_EXPORT const char *kvc_last_error(void) { return g_err; }
+
+KVC_EXPORT size_t kvc_workspace_bytes(const kvc_cache *c, int32_t max_len_hint) {
+    if (check_cache(c, "kvc_workspace_bytes") != KVC_OK) return 0;
+    return layout(c, max_len_hint).total;
+}
+
+KVC_EXPORT kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos, const void *q,
+                                      const void *k_new, const void *v_new, float *out,
+                                      float *h2o_scores, float scale, int32_t max_len_hint,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    const char *what = "kvc_decode_attn";
+    kvc_status s = check_attn_args(c, new_pos, q, k_new, v_new, out, scale, what);
+    if (s != KVC_OK) return s;
+    const Workspace w = layout(c, max_len_hint);
+    if ((s = check_ws(w, workspace, workspace_bytes, what)) != KVC_OK) return s;
+    kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, h2o_scores, scale, w, workspace);
+    return hip_status(kvc::launch_attn(a, c->dtype, (hipStream_t)stream), what);
+}
+
+KVC_EXPORT kvc_status kvc_h2o_accumulate(const kvc_cache *c, const void *q_rows, int32_t m_rows,
+                                         const int32_t *q_pos, float *h2o_scores, float scale,
+                                         void *stream) {
+    const char *what = "kvc_h2o_accumulate";
+    kvc_status s = check_cache(c, what);
+    if (s != KVC_OK) return s;
+    if (m_rows < 0) return fail(KVC_ERR_INVALID_ARG, "%s: m_rows < 0", what);
+    if (m_rows == 0) return ok();
+    if (!q_rows || !h2o_scores)
+        return fail(KVC_ERR_INVALID_ARG, "%s: q_rows and h2o_scores must not be NULL", what);
+    if (!isfinite(scale)) return fail(KVC_ERR_INVALID_ARG, "%s: scale is not finite", what);
+    kvc::AccumArgs a;
+    a.c = kvc::make_dev(*c);
+    a.q_rows = q_rows;
+    a.m_rows = m_rows;
+    a.q_pos = q_pos;
+    a.scores = h2o_scores;
+    a.scale = scale;
+    return hip_status(kvc::launch_accumulate(a, c->dtype, (hipStream_t)stream), what);
+}
+
+static kvc_status evict_common(const char *what, const kvc_cache *c, const kvc_policy &p,
+                               uint32_t step, const float *scores, int32_t *keep_slots,
+                               int32_t *n_out, void *stream) {
+    kvc_status s = check_cache(c, what);
+    if (s != KVC_OK) return s;
+    if ((s = check_policy(&p, scores, what)) != KVC_OK) return s;
+    if (!keep_slots || !n_out)
+        return fail(KVC_ERR_INVALID_ARG, "%s: keep_slots and n_out must not be NULL", what);
+    kvc::SelectArgs a = select_args(c, p, step, scores, keep_slots, n_out);
+    return hip_status(kvc::launch_select(a, (hipStream_t)stream), what);
+}
+
+KVC_EXPORT kvc_status kvc_evict_streaming(const kvc_cache *c, int32_t n_sink, int32_t n_recent,
+                                          int32_t *keep_slots, int32_t *n_out, void *stream) {
+    kvc_policy p = {};
+    p.kind = KVC_POLICY_STREAMING;
+    p.n_sink = n_sink;
+    p.n_recent = n_recent;
+    return evict_common("kvc_evict_streaming", c, p, 0, nullptr, keep_slots, n_out, stream);
+}
+
+KVC_EXPORT kvc_status kvc_evict_h2o(const kvc_cache *c, const float *h2o_scores, int32_t n_heavy,
+                                    int32_t n_recent, int32_t *keep_slots, int32_t *n_out,
+                                    void *stream) {
+    kvc_policy p = {};
+    p.kind = KVC_POLICY_H2O;
+    p.n_heavy = n_heavy;
+    p.n_recent = n_recent;
+    return evict_common("kvc_evict_h2o", c, p, 0, h2o_scores, keep_slots, n_out, stream);
+}
+
+KVC_EXPORT kvc_status kvc_evict_random(const kvc_cache *c, int32_t prompt_len, int32_t n_keep,
+                                       uint64_t seed, uint32_t step, int32_t *keep_slots,
+                                       int32_t *n_out, void *stream) {
+    kvc_policy p = {};
+    p.kind = KVC_POLICY_RANDOM;
+    p.prompt_len = prompt_len;
+    p.n_keep = n_keep;
+    p.seed = seed;
+    return evict_common("kvc_evict_random", c, p, step, nullptr, keep_slots, n_out, stream);
+}
+
+KVC_EXPORT kvc_status kvc_compact(const kvc_cache *c, const int32_t *keep_slots,
+                                  const int32_t *n_out, float *h2o_scores,
+                                  const kvc_cache *ordered_dst, void *stream) {
+    const char *what = "kvc_compact";
+    kvc_status s = check_cache(c, what);
+    if (s != KVC_OK) return s;
+    if (!keep_slots || !n_out)
+        return fail(KVC_ERR_INVALID_ARG, "%s: keep_slots and n_out must not be NULL", what);
+    kvc::CompactArgs a;
+    a.c = kvc::make_dev(*c);
+    a.keep_slots = keep_slots;
+    a.n_out = n_out;
+    a.scores = h2o_scores;
+    a.ordered = ordered_dst != nullptr;
+    if (ordered_dst) {
+        if ((s = check_cache(ordered_dst, what)) != KVC_OK) return s;
+        if (ordered_dst->batch != c->batch || ordered_dst->q_heads != c->q_heads ||
+            ordered_dst->kv_heads != c->kv_heads || ordered_dst->head_dim != c->head_dim ||
+            ordered_dst->dtype != c->dtype)
+            return fail(KVC_ERR_SHAPE, "%s: ordered_dst shape or dtype differs from the cache",
+                        what);
+        if (ordered_dst->k == c->k || ordered_dst->v == c->v)
+            return fail(KVC_ERR_INVALID_ARG, "%s: ordered_dst must not alias the cache", what);
+        a.dst = kvc::make_dev(*ordered_dst);
+    } else {
+        a.dst = a.c;
+    }
+    return hip_status(kvc::launch_compact(a, c->dtype, (hipStream_t)stream), what);
+}
+
+KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *policy, uint32_t step,
+                                      const int32_t *new_pos, const void *q, const void *k_new,
+                                      const void *v_new, float *out, float *h2o_scores,
+                                      float scale, int32_t max_len_hint, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    const char *what = "kvc_decode_step";
+    kvc_status s = check_attn_args(c, new_pos, q, k_new, v_new, out, scale, what);
+    if (s != KVC_OK) return s;
+    if ((s = check_policy(policy, h2o_scores, what)) != KVC_OK) return s;
+    const Workspace w = layout(c, max_len_hint);
+    if ((s = check_ws(w, workspace, workspace_bytes, what)) != KVC_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    float *scores = policy->kind == KVC_POLICY_H2O ? h2o_scores : nullptr;
+    kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, scores, scale, w, workspace);
+    hipError_t e = kvc::launch_attn(a, c->dtype, st);
+    if (e != hipSuccess) return hip_status(e, what);
+    if (policy->kind == KVC_POLICY_FULL) return ok();
+    int32_t *keep = (int32_t *)((char *)workspace + w.keep_off);
+    int32_t *nout = (int32_t *)((char *)workspace + w.nout_off);
+    kvc::SelectArgs sa = select_args(c, *policy, step, scores, keep, nout);
+    e = kvc::launch_select(sa, st);
+    if (e != hipSuccess) return hip_status(e, what);
+    kvc::CompactArgs ca;
+    ca.c = kvc::make_dev(*c);
+    ca.keep_slots = keep;
+    ca.n_out = nout;
+    ca.scores = scores;
+    ca.ordered = false;
+    ca.dst = ca.c;
+    return hip_status(kvc::launch_compact(ca, c->dtype, st), what);
+}

@@ -1,0 +1,218 @@
+// kvc_internal.h -- device-side view of the cache and small helpers shared by
+// the libkvc kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kMaxGroup = 16;       // q heads per kv head handled by one workgroup
+constexpr int kMaxCapacity = 65536; // slots per unit
+constexpr int kWave = 64;
+
+// Device copy of kvc_cache, passed by value to kernels.
+struct CacheDev {
+    int32_t B, Hq, Hkv, D, cap, G;
+    int32_t bs, max_blocks, num_blocks;
+    void *k, *v;
+    const int32_t *bt;
+    int32_t *pos, *n_slots, *flags;
+};
+
+inline CacheDev make_dev(const kvc_cache &c) {
+    CacheDev d;
+    d.B = c.batch;
+    d.Hq = c.q_heads;
+    d.Hkv = c.kv_heads;
+    d.D = c.head_dim;
+    d.cap = c.capacity;
+    d.G = c.q_heads / c.kv_heads;
+    d.bs = c.block_size;
+    d.max_blocks = c.max_blocks;
+    d.num_blocks = c.num_blocks;
+    d.k = c.k;
+    d.v = c.v;
+    d.bt = c.block_table;
+    d.pos = c.pos;
+    d.n_slots = c.n_slots;
+    d.flags = c.flags;
+    return d;
+}
+
+__device__ inline void raise_flag(const CacheDev &c, int32_t bit) {
+    if (c.flags) atomicOr(c.flags, bit);
+}
+
+// Row index (in units of head_dim elements) of slot j of unit (b, h).
+// Paged caches look the block up in the block table; an id outside the pool
+// is reported and redirected to block 0 so that no access leaves the pool.
+__device__ inline size_t row_of(const CacheDev &c, int b, int h, int j) {
+    if (c.bs == 0) return ((size_t)(b * c.Hkv + h)) * (size_t)c.cap + (size_t)j;
+    int blk = c.bt[(size_t)b * c.max_blocks + j / c.bs];
+    if (blk < 0 || blk >= c.num_blocks) {
+        raise_flag(c, KVC_FLAG_BAD_BLOCK);
+        blk = 0;
+    }
+    return ((size_t)blk * c.Hkv + h) * (size_t)c.bs + (size_t)(j % c.bs);
+}
+
+// Filled slots of unit u, clamped into [0, cap] (reported when clamped).
+__device__ inline int load_count(const CacheDev &c, int u, bool report) {
+    int n = c.n_slots[u];
+    if (n < 0 || n > c.cap) {
+        if (report) raise_flag(c, KVC_FLAG_BAD_COUNT);
+        n = n < 0 ? 0 : c.cap;
+    }
+    return n;
+}
+
+// ---------------------------------------------------------------------------
+// element access: bf16 is kept as raw 16-bit patterns; widening is exact
+// ---------------------------------------------------------------------------
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+    __device__ static inline float get(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
+};
+template <> struct Elem<float> {
+    __device__ static inline float get(const float *p, size_t i) { return p[i]; }
+};
+
+// ---------------------------------------------------------------------------
+// wave / block reductions
+// ---------------------------------------------------------------------------
+__device__ inline float wave_max(float x) {
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+__device__ inline float wave_sum(float x) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+__device__ inline int wave_sum_i(int x) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+__device__ inline int wave_max_i(int x) {
+    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+
+// Block-wide max of an int (blockDim.x a multiple of 64, <= 1024).
+__device__ inline int block_max_i(int x, int *red) {
+    x = wave_max_i(x);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[w] = x;
+    __syncthreads();
+    int r = red[0];
+    for (int i = 1; i < nw; ++i) r = max(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+// Block-wide exclusive prefix sum of small ints; returns the exclusive prefix
+// of the calling thread and writes the block total to *total.
+__device__ inline int block_excl_scan(int x, int *red, int *total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int incl = x;
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) red[w] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int i = 0; i < nw; ++i) {
+        if (i < w) base += red[i];
+        tot += red[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - x;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11): returns word 0 for counter (c0..c3) and key (k0, k1).
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                        uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t a = c0, cc = c2;
+        const uint32_t lo_a = a * 0xD2511F53u, hi_a = __umulhi(a, 0xD2511F53u);
+        const uint32_t lo_c = cc * 0xCD9E8D57u, hi_c = __umulhi(cc, 0xCD9E8D57u);
+        c0 = hi_c ^ c1 ^ k0;
+        c1 = lo_c;
+        c2 = hi_a ^ c3 ^ k1;
+        c3 = lo_a;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c0;
+}
+
+// order-preserving map float -> uint32 (larger float -> larger uint)
+__device__ inline uint32_t float_order_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace kvc
+
+// ---------------------------------------------------------------------------
+// host-side launchers (defined in the kernel files, called by kvc_api.hip)
+// ---------------------------------------------------------------------------
+namespace kvc {
+
+struct AttnArgs {
+    CacheDev c;
+    const int32_t *new_pos;
+    const void *q, *k_new, *v_new;
+    float *out;
+    float *scores;        // may be null
+    float scale;
+    int nsplit;
+    float *part;          // [units][nsplit][G][D+2] when nsplit > 1
+    float *logits;        // [units][G][cap+1] scratch (scores and/or nsplit > 1)
+};
+
+hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s);
+
+struct AccumArgs {
+    CacheDev c;
+    const void *q_rows;
+    int m_rows;
+    const int32_t *q_pos;
+    float *scores;
+    float scale;
+};
+hipError_t launch_accumulate(const AccumArgs &a, int dtype, hipStream_t s);
+
+struct SelectArgs {
+    CacheDev c;
+    int kind;             // kvc_policy_kind
+    int n_sink, n_heavy, n_recent, prompt_len, n_keep;
+    uint64_t seed;
+    uint32_t step;
+    const float *scores;
+    int32_t *keep_slots, *n_out;
+};
+hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+
+struct CompactArgs {
+    CacheDev c;
+    const int32_t *keep_slots, *n_out;
+    float *scores;        // may be null
+    bool ordered;
+    CacheDev dst;         // ordered destination
+};
+hipError_t launch_compact(const CompactArgs &a, int dtype, hipStream_t s);
+
+}  // namespace kvc

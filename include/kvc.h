@@ -1,0 +1,275 @@
+/*
+ * kvc.h -- C ABI of libkvc: one decode step of attention over a per-head,
+ * budget-limited KV cache on AMD Instinct MI355X (gfx950), and the eviction
+ * that keeps that cache at budget.
+ *
+ * Sources, cited by page and section:
+ *  [GUIDE] "Rethinking KV Cache Compression: from memory savings back to real
+ *          serving end-to-end gains" -- section 2 (cost structure of the four
+ *          baselines: 64 sink/heavy + 448 recent = cache 512) and section 16
+ *          (the KV capacity formula; the four methods step by step; prefill,
+ *          decode and TP accounting; limits -- H2O needs the attention
+ *          probabilities that a fused attention kernel does not expose).
+ *  [BLOG]  "KV Cache eviction in practice: when to drop the scorer and evict
+ *          at random" -- sections "scorers are overrated", "six steps to land
+ *          it" and "reference implementation" (per-head uniform eviction with
+ *          the prompt pinned, equal per-head counts, no union across heads).
+ *  [EMP]   "Practical Online KV Cache Compaction for LLM Agents: An Empirical
+ *          Study" -- section 4.2 (mark evicted tokens, then compact the
+ *          survivors, with a logical-to-physical index map).
+ *
+ * Conventions shared by every call
+ *  - All pointers in kvc_cache and all array arguments are DEVICE pointers
+ *    unless stated otherwise; the kvc_cache / kvc_policy structs themselves
+ *    are read on the host during the call and not retained.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    keeps a pointer after a call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Arguments are validated on the host first; a call that
+ *    returns an error has enqueued nothing.  Faults surface at the caller's
+ *    next synchronisation.
+ *  - A "unit" is one (sequence b, kv head h); units are independent.
+ *  - Query head i reads kv head floor(i / G), G = q_heads / kv_heads.
+ *  - Attention scale: the caller passes it (1/sqrt(head_dim) is the usual).
+ *  - Inputs must be finite; NaN/Inf are outside the contract.
+ *  - Device-side contract violations (a unit whose n_slots is negative, above
+ *    the capacity, or equal to the capacity when a token must be appended)
+ *    are clamped so that no access leaves the buffers, and reported by OR-ing
+ *    KVC_FLAG_* bits into *flags when kvc_cache.flags is not NULL.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_INVALID_ARG = 1, /* null pointer, bad count, inconsistent policy */
+    KVC_ERR_UNSUPPORTED = 2, /* head_dim / dtype / group size not built */
+    KVC_ERR_SHAPE = 3,       /* q_heads % kv_heads != 0, paged geometry, ... */
+    KVC_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+    KVC_ERR_HIP = 5          /* a HIP runtime call failed */
+} kvc_status;
+
+typedef enum kvc_dtype {
+    KVC_BF16 = 0, /* K, V, q, k_new, v_new stored as bfloat16 */
+    KVC_F32 = 1   /* ... as float32 */
+} kvc_dtype;
+
+/* bits OR-ed into *kvc_cache.flags by kernels */
+#define KVC_FLAG_FULL 1      /* n_slots == capacity at an append: token not stored */
+#define KVC_FLAG_BAD_COUNT 2 /* n_slots outside [0, capacity]: clamped */
+#define KVC_FLAG_BAD_BLOCK 4 /* block_table entry outside the pool: block 0 used */
+
+/*
+ * The cache.  Per unit, slots 0 .. n_slots-1 are filled; slot order is free
+ * (attention is permutation invariant because keys already carry their
+ * position encoding [BLOG "reference implementation", note on sort()]), and
+ * pos[] maps each slot to the token's original position [EMP 4.2].
+ *
+ * Contiguous layout (block_size == 0):
+ *   k, v       [batch, kv_heads, capacity, head_dim] of dtype
+ * Paged layout (block_size > 0, e.g. 16):
+ *   k, v       pool [num_blocks, kv_heads, block_size, head_dim]
+ *   block_table[batch, max_blocks]: slot j of sequence b, head h lives in
+ *              block block_table[b*max_blocks + j/block_size], row
+ *              j % block_size; capacity must equal max_blocks*block_size.
+ * Both layouts:
+ *   pos        [batch, kv_heads, capacity] int32 original token positions
+ *   n_slots    [batch, kv_heads] int32 filled slots per unit
+ *   flags      optional int32 word (see KVC_FLAG_*), may be NULL
+ */
+typedef struct kvc_cache {
+    int32_t batch;
+    int32_t q_heads;
+    int32_t kv_heads;
+    int32_t head_dim;
+    int32_t capacity;
+    int32_t dtype; /* kvc_dtype */
+    int32_t block_size;
+    int32_t max_blocks;
+    int32_t num_blocks;
+    int32_t reserved;
+    void *k;
+    void *v;
+    const int32_t *block_table;
+    int32_t *pos;
+    int32_t *n_slots;
+    int32_t *flags;
+} kvc_cache;
+
+typedef enum kvc_policy_kind {
+    KVC_POLICY_FULL = 0,      /* keep everything (no eviction) */
+    KVC_POLICY_STREAMING = 1, /* n_sink first + n_recent most recent */
+    KVC_POLICY_H2O = 2,       /* n_heavy by accumulated attention + n_recent */
+    KVC_POLICY_RANDOM = 3     /* prompt pinned + n_keep uniform per head */
+} kvc_policy_kind;
+
+typedef struct kvc_policy {
+    int32_t kind; /* kvc_policy_kind */
+    int32_t n_sink;
+    int32_t n_heavy;
+    int32_t n_recent;
+    int32_t prompt_len;
+    int32_t n_keep;
+    uint64_t seed;
+} kvc_policy;
+
+/* ------------------------------------------------------------------------
+ * Host-only helpers
+ * ---------------------------------------------------------------------- */
+
+/* KV bytes per token = 2 (K and V) x layers x kv_heads x head_dim x
+ * dtype_bytes [GUIDE 16, capacity formula; BLOG "six steps", memory
+ * accounting].  `layers` counts attention layers only (linear-attention
+ * layers of hybrid models hold no KV [BLOG "what are you compressing"]).
+ * Returns 0 if any argument is not positive. */
+size_t kvc_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                           int32_t dtype_bytes);
+
+/* Kept generated tokens of a one-shot random eviction over n_candidates
+ * tokens after the prompt: max(1, trunc(n_candidates * keep_ratio)), clamped
+ * to n_candidates; 0 when n_candidates <= 0 [BLOG "reference
+ * implementation"]. */
+int64_t kvc_n_keep(int64_t n_candidates, double keep_ratio);
+
+/* Static, never-freed description of a status code. */
+const char *kvc_status_string(kvc_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *kvc_last_error(void);
+
+/* Workspace (device bytes) that kvc_decode_attn / kvc_decode_step /
+ * kvc_h2o_accumulate need for `c` when no unit attends more than
+ * max_len_hint entries (n_slots + 1).  0 means no workspace is needed. */
+size_t kvc_workspace_bytes(const kvc_cache *c, int32_t max_len_hint);
+
+/* ------------------------------------------------------------------------
+ * Device calls
+ * ---------------------------------------------------------------------- */
+
+/*
+ * Decode attention for one new token per sequence [GUIDE 16, "prefill,
+ * decode, TP": a decode step reads all kept history].
+ *
+ * For every unit (b, h) with n = n_slots[b,h] and every query head i of the
+ * group of h:  out[b,i,:] = sum_j p_j v_j  with p = softmax(scale * q K^T)
+ * over the n cached slots AND the new token (k_new[b,h], v_new[b,h]).
+ * The new token is then stored at slot n with pos = new_pos[b], and
+ * n_slots[b,h] becomes n + 1 (capacity must exceed n; see KVC_FLAG_FULL).
+ *
+ * If h2o_scores ([batch, kv_heads, capacity] fp32) is not NULL, the group's
+ * summed probabilities are added to it: scores[b,h,j] += sum_i p_ij for every
+ * cached slot, and the new slot is set to its own probability sum -- the
+ * accumulated-attention statistic of H2O [GUIDE 2 and 16, "the 4 methods":
+ * accumulate attention scores and update the kept set; GUIDE 16 "limits":
+ * a fused kernel must expose these probabilities].
+ *
+ *   new_pos  [batch] int32 position of the new token
+ *   q        [batch, q_heads, head_dim]  dtype
+ *   k_new,v_new [batch, kv_heads, head_dim] dtype
+ *   out      [batch, q_heads, head_dim] fp32
+ *   max_len_hint  upper bound on n_slots + 1 over the batch (<= capacity+1);
+ *            sizes the split of long units over workgroups.  A unit longer
+ *            than the hint is still computed exactly (less parallel).
+ *   workspace     kvc_workspace_bytes(c, max_len_hint) device bytes (may be
+ *            NULL when that is 0).
+ */
+kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos,
+                           const void *q, const void *k_new, const void *v_new,
+                           float *out, float *h2o_scores, float scale,
+                           int32_t max_len_hint, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * Unfused H2O score pass: adds the group-summed softmax probabilities of
+ * m_rows query rows per sequence to h2o_scores, over each unit's current
+ * n_slots slots (no append).  Row r of sequence b sees the slots whose pos is
+ * <= q_pos[b*m_rows + r] when q_pos is not NULL (causal prompt scoring), all
+ * slots otherwise.  This is the "extra traversal" that maintaining H2O scores
+ * costs when attention does not expose its probabilities [GUIDE 16 "limits"],
+ * and the prefill scoring of H2O [GUIDE 16 "prefill, decode, TP"].
+ *   q_rows [batch, m_rows, q_heads, head_dim] dtype;  q_pos NULL or
+ *   [batch, m_rows] int32.
+ */
+kvc_status kvc_h2o_accumulate(const kvc_cache *c, const void *q_rows,
+                              int32_t m_rows, const int32_t *q_pos,
+                              float *h2o_scores, float scale, void *stream);
+
+/*
+ * Selection ("mark" of mark-then-compact [EMP 4.2]).  Reads each unit's
+ * n_slots and pos (and scores), writes the kept slot indices in ascending
+ * slot order to keep_slots[b,h, 0 .. n_out[b,h]-1] ([batch, kv_heads,
+ * capacity] int32) and the count to n_out ([batch, kv_heads] int32).  The
+ * cache is not modified.  L = 1 + the largest position in the unit (its
+ * newest token).
+ *
+ * StreamingLLM [GUIDE 2, 16 "the 4 methods"]: keep pos < n_sink and
+ * pos >= L - n_recent.
+ */
+kvc_status kvc_evict_streaming(const kvc_cache *c, int32_t n_sink,
+                               int32_t n_recent, int32_t *keep_slots,
+                               int32_t *n_out, void *stream);
+
+/* H2O [GUIDE 2, 16 "the 4 methods"]: keep pos >= L - n_recent, and among the
+ * other slots the n_heavy with the largest h2o_scores, ties to the lower
+ * position. */
+kvc_status kvc_evict_h2o(const kvc_cache *c, const float *h2o_scores,
+                         int32_t n_heavy, int32_t n_recent,
+                         int32_t *keep_slots, int32_t *n_out, void *stream);
+
+/* Per-head uniform random eviction with the prompt pinned [BLOG "scorers are
+ * overrated", "six steps", "reference implementation"]: slots with
+ * pos < prompt_len are kept; among the others each unit keeps the n_keep
+ * whose key is smallest (ties to the lower position), the key of a token
+ * being word 0 of Philox4x32-10 (Salmon et al., SC'11) with counter
+ * (pos, step, kv head, sequence) and key (seed low 32 bits, seed high 32
+ * bits).  Every unit draws its own set; nothing is merged across heads.  With
+ * at most n_keep candidates everything is kept. */
+kvc_status kvc_evict_random(const kvc_cache *c, int32_t prompt_len,
+                            int32_t n_keep, uint64_t seed, uint32_t step,
+                            int32_t *keep_slots, int32_t *n_out, void *stream);
+
+/*
+ * Compaction ("compact" of mark-then-compact [EMP 4.2]).
+ * In place (ordered_dst == NULL): with n_out kept of n slots, the kept slots
+ * at index >= n_out move, in ascending order, into the evicted slots below
+ * n_out, in ascending order; K row, V row, pos and (if h2o_scores is not
+ * NULL) score move together; n_slots becomes n_out.  Sources and
+ * destinations are disjoint.
+ * Ordered (ordered_dst != NULL): the kept entries are gathered into
+ * ordered_dst in ascending position, slot i holding the i-th kept position --
+ * the regular [kv_heads, prompt_len + n_keep, head_dim] layout of the
+ * blog's hook [BLOG "reference implementation"]; ordered_dst's n_slots is
+ * set, its scores are not written, the source cache is not modified.
+ * ordered_dst must have the same batch/heads/head_dim/dtype and a capacity
+ * of at least every n_out; at most 8192 kept entries per unit.
+ */
+kvc_status kvc_compact(const kvc_cache *c, const int32_t *keep_slots,
+                       const int32_t *n_out, float *h2o_scores,
+                       const kvc_cache *ordered_dst, void *stream);
+
+/*
+ * One whole decode step: kvc_decode_attn, then the policy's selection, then
+ * in-place compaction, with the same results as those three calls in that
+ * order (kept sets identical, the new token placed where the compaction
+ * would put it, identical outputs and scores).  For KVC_POLICY_H2O,
+ * h2o_scores is required; `step` keys the random draws.
+ */
+kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *policy,
+                           uint32_t step, const int32_t *new_pos,
+                           const void *q, const void *k_new, const void *v_new,
+                           float *out, float *h2o_scores, float scale,
+                           int32_t max_len_hint, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

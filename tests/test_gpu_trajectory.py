@@ -1,0 +1,244 @@
+"""Multi-step parity: whole decode steps (attention + eviction + compaction).
+
+* StreamingLLM and random eviction depend only on positions (and the random
+  keys), so the oracle runs its own full trajectory and every step's kept
+  position sets must match bit-exactly and every step's outputs within 2e-3.
+* H2O is checked state-synchronised: at every step the oracle attends over
+  the GPU's pre-step entries, its selection runs on the GPU's post-attention
+  score vector, and the kept set must match exactly (scores within 1e-5).
+* The one-launch step (kvc_decode_step) must leave exactly the state of the
+  three-call sequence; the paged layout exactly the state of the contiguous.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_decode_attention_amd as kvc
+import oracle
+import synth
+from kvc_harness import (OUT_ATOL, Snapshot, assert_scores_close, dev, make_cache,
+                         oracle_unit_attend, rows_by_pos)
+
+pytestmark = pytest.mark.gpu
+
+
+def _policy_pair(w):
+    if w.policy == "streaming":
+        return kvc.policy_streaming(w.n_sink, w.n_recent), oracle.Policy.streaming(w.n_sink,
+                                                                                    w.n_recent)
+    if w.policy == "h2o":
+        return kvc.policy_h2o(w.n_heavy, w.n_recent), oracle.Policy.h2o(w.n_heavy, w.n_recent)
+    if w.policy == "random":
+        return (kvc.policy_random(w.pinned, w.n_keep, w.seed),
+                oracle.Policy.random(w.pinned, w.n_keep, w.seed))
+    return kvc.policy_full(), oracle.Policy.full()
+
+
+def _trajectory(w, lengths, capacity, steps, fused=True, paged=0):
+    """Oracle trajectory vs GPU trajectory, kept sets and outputs every step."""
+    B = len(lengths)
+    cache = make_cache(w, lengths, capacity, paged=paged)
+    orc = oracle.Oracle(w.q_heads, w.kv_heads, w.head_dim, w.dtype)
+    for b, L in enumerate(lengths):
+        k, v = synth.prefill_kv(w, b, L)
+        orc.load(b, k, v)
+    pol_gpu, pol_orc = _policy_pair(w)
+    ws = cache.workspace(capacity)
+    out = torch.empty((B, w.q_heads, w.head_dim), device="cuda")
+    scores = torch.zeros((B, w.kv_heads, capacity), device="cuda") if w.policy == "h2o" else None
+    seen = list(lengths)
+    for t in range(1, steps + 1):
+        q, kn, vn = synth.batch_step_inputs(w, t, B)
+        new_pos = torch.tensor(seen, dtype=torch.int32, device="cuda")
+        qd, knd, vnd = dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype)
+        if fused:
+            kvc.decode_step(cache, pol_gpu, t, new_pos, qd, knd, vnd, out, scores,
+                            max_len_hint=capacity, workspace=ws)
+        else:
+            _three_calls(cache, w, pol_gpu, t, new_pos, qd, knd, vnd, out, scores, ws, capacity)
+        snap = Snapshot(cache, w.dtype)
+        o = out.cpu().numpy()
+        for b in range(B):
+            ref, _ = orc.step(b, q[b], kn[b], vn[b], pol_orc, step=t)
+            err = np.abs(o[b] - ref).max()
+            assert err <= OUT_ATOL, (t, b, err)
+            want = orc.kept_positions(b)
+            for h in range(w.kv_heads):
+                got = np.sort(snap.unit(b, h)["pos"])
+                np.testing.assert_array_equal(got, want[h], err_msg=f"step {t} seq {b} head {h}")
+            seen[b] += 1
+    assert int(cache.flags.item()) == 0
+    return cache
+
+
+def _three_calls(cache, w, pol, t, new_pos, q, kn, vn, out, scores, ws, hint):
+    kvc.decode_attn(cache, new_pos, q, kn, vn, out, scores, max_len_hint=hint, workspace=ws)
+    keep = torch.empty((cache.batch, cache.kv_heads, cache.capacity), dtype=torch.int32,
+                       device="cuda")
+    nout = torch.empty((cache.batch, cache.kv_heads), dtype=torch.int32, device="cuda")
+    if pol.kind == kvc.POLICY_STREAMING:
+        kvc.evict_streaming(cache, pol.n_sink, pol.n_recent, keep, nout)
+    elif pol.kind == kvc.POLICY_H2O:
+        kvc.evict_h2o(cache, scores, pol.n_heavy, pol.n_recent, keep, nout)
+    elif pol.kind == kvc.POLICY_RANDOM:
+        kvc.evict_random(cache, pol.prompt_len, pol.n_keep, pol.seed, t, keep, nout)
+    else:
+        return
+    kvc.compact(cache, keep, nout, scores)
+
+
+def test_tiny_streaming_fp32_workload_all_steps():
+    # 1 sequence, 8 MHA heads, head_dim 64, 1024 cached fp32, 64 + 448, 16 steps
+    w = synth.workload("tiny_mha_streaming_f32")
+    _trajectory(w, [w.prompt_len], capacity=w.prompt_len + 1, steps=w.steps)
+
+
+def test_tiny_streaming_three_call_path():
+    w = synth.workload("tiny_mha_streaming_f32")
+    _trajectory(w, [w.prompt_len], capacity=w.prompt_len + 1, steps=4, fused=False)
+
+
+def test_random_eviction_trajectory_reaches_steady_state():
+    # reasoning-trace shape, shortened: pinned prompt 64, 96 kept generated
+    w = synth.workload("reasoning_random_b32", pinned=64, n_keep=96)
+    _trajectory(w, [150, 170, 64], capacity=200, steps=24)
+
+
+def test_random_eviction_three_call_path():
+    w = synth.workload("reasoning_random_b32", pinned=64, n_keep=96)
+    _trajectory(w, [150, 170], capacity=200, steps=6, fused=False)
+
+
+def test_streaming_on_paged_cache():
+    w = synth.workload("mixed_paged_h2o_b128", policy="streaming", n_sink=8, n_recent=40)
+    _trajectory(w, [30, 47, 80, 200], capacity=208, steps=8, paged=16)
+
+
+def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None):
+    B = len(lengths)
+    G = w.group
+    cache = make_cache(w, lengths, capacity, paged=paged)
+    scores = torch.zeros((B, w.kv_heads, capacity), device="cuda")
+    ws = cache.workspace(capacity)
+    out = torch.empty((B, w.q_heads, w.head_dim), device="cuda")
+    keep = torch.empty((B, w.kv_heads, capacity), dtype=torch.int32, device="cuda")
+    nout = torch.empty((B, w.kv_heads), dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(w.head_dim)
+    units = check_units or [(b, h) for b in range(B) for h in range(w.kv_heads)]
+    seen = list(lengths)
+    for t in range(1, steps + 1):
+        q, kn, vn = synth.batch_step_inputs(w, t, B)
+        pre = Snapshot(cache, w.dtype, scores, units)
+        kvc.decode_attn(cache, torch.tensor(seen, dtype=torch.int32, device="cuda"),
+                        dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype), out, scores,
+                        max_len_hint=capacity, workspace=ws)
+        mid = Snapshot(cache, w.dtype, scores, units)
+        kvc.evict_h2o(cache, scores, w.n_heavy, w.n_recent, keep, nout)
+        kk, mm = keep.cpu().numpy(), nout.cpu().numpy()
+        kvc.compact(cache, keep, nout, scores)
+        post = Snapshot(cache, w.dtype, scores, units)
+        o = out.cpu().numpy()
+        for (b, h) in units:
+            u0, u1, u2 = pre.unit(b, h), mid.unit(b, h), post.unit(b, h)
+            ref, psum = oracle_unit_attend(w.dtype, q[b, h * G:(h + 1) * G], u0, kn[b, h],
+                                           vn[b, h], scale)
+            assert np.abs(o[b, h * G:(h + 1) * G] - ref).max() <= OUT_ATOL
+            n = u0["n"]
+            assert_scores_close(u1["s"][:n], u0["s"] + psum[:n])
+            assert_scores_close(u1["s"][n:n + 1], psum[n:])
+            # oracle selection on the GPU's own post-attention scores
+            L = seen[b] + 1
+            want = oracle.select_h2o(u1["pos"], u1["s"].astype(np.float64), L, w.n_heavy,
+                                     w.n_recent)
+            m = int(mm[b, h])
+            np.testing.assert_array_equal(kk[b, h, :m], np.flatnonzero(want))
+            # compaction: exactly the kept rows, bit-exact, with their scores
+            r1, r2 = rows_by_pos(u1), rows_by_pos(u2)
+            assert set(r2) == set(int(p) for p in u1["pos"][want])
+            for p in r2:
+                assert r1[p] == r2[p]
+        for b in range(B):
+            seen[b] += 1
+
+
+def test_h2o_state_synchronised_with_heavy_hitters():
+    # LLaMA-3-8B shape with 2% heavy keys, 64 + 448, a 2,048-token prompt
+    w = synth.workload("llama3_8b_h2o_b64")
+    _h2o_sync(w, [2048, 2048, 700], capacity=2049, steps=4)
+
+
+def test_h2o_small_budget_many_steps():
+    w = synth.workload("llama3_8b_h2o_b64", n_heavy=6, n_recent=20)
+    _h2o_sync(w, [40, 26, 3], capacity=48, steps=30)
+
+
+def test_h2o_on_paged_mixed_lengths():
+    w = synth.workload("mixed_paged_h2o_b128", n_heavy=16, n_recent=48)
+    _h2o_sync(w, [600, 64, 1000, 17], capacity=1008, steps=5, paged=16)
+
+
+def _state(cache, scores, dn):
+    s = Snapshot(cache, dn, scores)
+    return {k: rows_by_pos(v) for k, v in s.units.items()}, s
+
+
+@pytest.mark.parametrize("policy", ["h2o", "streaming", "random", "full"])
+def test_fused_step_equals_three_calls(policy):
+    w = synth.workload("llama3_8b_h2o_b64", policy=policy, n_heavy=8, n_recent=40,
+                       n_sink=4, pinned=50, n_keep=30) if policy != "h2o" else \
+        synth.workload("llama3_8b_h2o_b64", n_heavy=8, n_recent=40)
+    lengths, cap = [120, 60, 49, 0], 160
+    caches = [make_cache(w, lengths, cap), make_cache(w, lengths, cap)]
+    B = len(lengths)
+    scs = [torch.zeros((B, w.kv_heads, cap), device="cuda") for _ in range(2)]
+    outs = [torch.empty((B, w.q_heads, w.head_dim), device="cuda") for _ in range(2)]
+    pol, _ = _policy_pair(w)
+    wss = [c.workspace(cap) for c in caches]
+    for t in range(1, 7):
+        q, kn, vn = synth.batch_step_inputs(w, t, B)
+        new_pos = torch.tensor([L + t - 1 for L in lengths], dtype=torch.int32, device="cuda")
+        args = (new_pos, dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype))
+        sc0 = scs[0] if policy == "h2o" else None
+        sc1 = scs[1] if policy == "h2o" else None
+        kvc.decode_step(caches[0], pol, t, *args, outs[0], sc0, max_len_hint=cap,
+                        workspace=wss[0])
+        _three_calls(caches[1], w, pol, t, *args, outs[1], sc1, wss[1], cap)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
+        assert torch.equal(caches[0].n_slots, caches[1].n_slots)
+        assert torch.equal(caches[0].pos, caches[1].pos)
+        assert torch.equal(caches[0].k, caches[1].k)
+        assert torch.equal(caches[0].v, caches[1].v)
+        if policy == "h2o":
+            n = caches[0].n_slots.cpu()
+            for b in range(B):
+                for h in range(w.kv_heads):
+                    m = int(n[b, h])
+                    assert torch.equal(scs[0][b, h, :m], scs[1][b, h, :m])
+
+
+def test_paged_and_contiguous_give_identical_results():
+    w = synth.workload("mixed_paged_h2o_b128", n_heavy=16, n_recent=48)
+    lengths, cap = [300, 64, 17, 200], 320
+    a = make_cache(w, lengths, cap)
+    p = make_cache(w, lengths, cap, paged=16, extra_blocks=7, seed_blocks=3)
+    B = len(lengths)
+    sa = torch.zeros((B, w.kv_heads, cap), device="cuda")
+    sp = torch.zeros((B, w.kv_heads, cap), device="cuda")
+    oa = torch.empty((B, w.q_heads, w.head_dim), device="cuda")
+    op = torch.empty_like(oa)
+    pol = kvc.policy_h2o(16, 48)
+    for t in range(1, 6):
+        q, kn, vn = synth.batch_step_inputs(w, t, B)
+        new_pos = torch.tensor([L + t - 1 for L in lengths], dtype=torch.int32, device="cuda")
+        args = (new_pos, dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype))
+        kvc.decode_step(a, pol, t, *args, oa, sa, max_len_hint=cap, workspace=a.workspace(cap))
+        kvc.decode_step(p, pol, t, *args, op, sp, max_len_hint=cap, workspace=p.workspace(cap))
+        torch.cuda.synchronize()
+        assert torch.equal(oa, op)
+        assert torch.equal(a.pos, p.pos) and torch.equal(a.n_slots, p.n_slots)
+        sta, _ = _state(a, sa, "bf16")
+        stp, _ = _state(p, sp, "bf16")
+        assert sta == stp
