@@ -13,169 +13,14 @@
 // This file holds the generic VALU path: one workgroup per (unit, split),
 // logits kept in a global scratch row per (unit, query head), a combine pass
 // when a unit is split across workgroups.
-#include "kvc_internal.h"
+#include "generic.h"
 
 namespace kvc {
 
-constexpr int kAttnThreads = 256;
-constexpr int kMaxSplit = 64;
-
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
-    const CacheDev &c = a.c;
-    const int G = c.G;
-    const int u = blockIdx.x / a.nsplit, s = blockIdx.x % a.nsplit;
-    const int b = u / c.Hkv, h = u % c.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    constexpr int kParts = kAttnThreads / D;
-
-    __shared__ float q_s[kMaxGroup * D];
-    __shared__ float st_m[kMaxGroup], st_l[kMaxGroup];
-    __shared__ float red[kAttnThreads / 64][kMaxGroup];
-    __shared__ float pv[kParts][kMaxGroup][D];
-
-    const int n = load_count(c, u, s == 0 && tid == 0);
-    const bool can_store = n < c.cap;
-    if (!can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
-    const int T_len = n + 1;
-    const int chunk = (T_len + a.nsplit - 1) / a.nsplit;
-    const int j0 = min(s * chunk, T_len), j1 = min(T_len, j0 + chunk);
-
-    const T *qp = (const T *)a.q + ((size_t)b * c.Hq + (size_t)h * G) * D;
-    for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<T>::get(qp, e);
-    __syncthreads();
-
-    const T *K = (const T *)c.k;
-    const T *V = (const T *)c.v;
-    const T *kn = (const T *)a.k_new + ((size_t)b * c.Hkv + h) * D;
-    const T *vn = (const T *)a.v_new + ((size_t)b * c.Hkv + h) * D;
-    const size_t ld = (size_t)c.cap + 1;
-    float *lg = a.logits + (size_t)u * G * ld;
-
-    // ---- logits and running max (thread owns keys j = j0 + tid + k*256)
-    float mloc[kMaxGroup];
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) mloc[g] = -INFINITY;
-    for (int j = j0 + tid; j < j1; j += kAttnThreads) {
-        const T *row = (j < n) ? K + row_of(c, b, h, j) * D : kn;
-        float acc[kMaxGroup];
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
-        for (int d = 0; d < D; ++d) {
-            const float kv = Elem<T>::get(row, d);
-#pragma unroll
-            for (int g = 0; g < kMaxGroup; ++g)
-                if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
-        }
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g)
-            if (g < G) {
-                const float z = acc[g] * a.scale;
-                lg[g * ld + j] = z;
-                mloc[g] = fmaxf(mloc[g], z);
-            }
-    }
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) {
-        const float w = wave_max(mloc[g]);
-        if (lane == 0) red[wv][g] = w;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float m = red[0][tid];
-        for (int w = 1; w < kAttnThreads / 64; ++w) m = fmaxf(m, red[w][tid]);
-        st_m[tid] = m;
-    }
-    __syncthreads();
-
-    // ---- unnormalised weights w = exp(z - m), row sums
-    float lloc[kMaxGroup];
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) lloc[g] = 0.f;
-    for (int j = j0 + tid; j < j1; j += kAttnThreads) {
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g)
-            if (g < G) {
-                const float w = __expf(lg[g * ld + j] - st_m[g]);
-                lg[g * ld + j] = w;
-                lloc[g] += w;
-            }
-    }
-#pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) {
-        const float w = wave_sum(lloc[g]);
-        if (lane == 0) red[wv][g] = w;
-    }
-    __syncthreads();
-    if (tid < G) {
-        float l = 0.f;
-        for (int w = 0; w < kAttnThreads / 64; ++w) l += red[w][tid];
-        st_l[tid] = l;
-    }
-    __syncthreads();
-
-    // ---- P.V: thread owns one dimension d and every kParts-th key
-    {
-        const int d = tid % D, part = tid / D;
-        float acc[kMaxGroup];
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
-        for (int j = j0 + part; j < j1; j += kParts) {
-            const T *row = (j < n) ? V + row_of(c, b, h, j) * D : vn;
-            const float vv = Elem<T>::get(row, d);
-#pragma unroll
-            for (int g = 0; g < kMaxGroup; ++g)
-                if (g < G) acc[g] = fmaf(lg[g * ld + j], vv, acc[g]);
-        }
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g) pv[part][g][d] = acc[g];
-    }
-    __syncthreads();
-
-    if (a.nsplit == 1) {
-        if (tid < D) {
-            for (int g = 0; g < G; ++g) {
-                float o = 0.f;
-                for (int p = 0; p < kParts; ++p) o += pv[p][g][tid];
-                a.out[((size_t)b * c.Hq + (size_t)h * G + g) * D + tid] = o / st_l[g];
-            }
-        }
-        if (a.scores) {
-            float *sc = a.scores + (size_t)u * c.cap;
-            for (int j = j0 + tid; j < j1; j += kAttnThreads) {
-                float ps = 0.f;
-                for (int g = 0; g < G; ++g) ps += lg[g * ld + j] / st_l[g];
-                if (j < n) sc[j] += ps;
-                else if (can_store) sc[n] = ps;
-            }
-        }
-    } else {
-        float *pp = a.part + ((size_t)u * a.nsplit + s) * G * (D + 2);
-        if (tid < D) {
-            for (int g = 0; g < G; ++g) {
-                float o = 0.f;
-                for (int p = 0; p < kParts; ++p) o += pv[p][g][tid];
-                pp[g * (D + 2) + tid] = o;
-            }
-        }
-        if (tid < G) {
-            pp[tid * (D + 2) + D] = st_m[tid];
-            pp[tid * (D + 2) + D + 1] = st_l[tid];
-        }
-    }
-
-    // ---- append the new token (the workgroup whose range holds index n)
-    if (can_store && j0 <= n && n < j1) {
-        T *Kw = (T *)c.k;
-        T *Vw = (T *)c.v;
-        const size_t r = row_of(c, b, h, n) * D;
-        for (int e = tid; e < D; e += kAttnThreads) {
-            Kw[r + e] = kn[e];
-            Vw[r + e] = vn[e];
-        }
-        if (tid == 0) c.pos[(size_t)u * c.cap + n] = a.new_pos[b];
-    }
-    if (a.nsplit == 1 && tid == 0 && can_store) c.n_slots[u] = n + 1;
+    __shared__ AttnLds<D> L;
+    attn_unit_generic<T, D>(a, blockIdx.x / a.nsplit, blockIdx.x % a.nsplit, L);
 }
 
 // Combine the splits of one unit: rescale partial sums to the global max,

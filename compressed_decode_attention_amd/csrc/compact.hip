@@ -11,97 +11,14 @@
 // position -- the regular [kv_heads, prompt_len + n_keep, head_dim] layout of
 // the eviction-in-practice blog's reference hook (per-head gather, ascending
 // order kept for paged kernels and prefix caching).
-#include "kvc_internal.h"
+#include "generic.h"
 
 namespace kvc {
 
-constexpr int kCompThreads = 256;
-constexpr int kOrderedMax = 8192;
-
-template <typename T, int D>
-__device__ inline void copy_row(T *dst, const T *src) {
-    static_assert((D * sizeof(T)) % 16 == 0, "row must be a multiple of 16 bytes");
-    const uint4 *s = reinterpret_cast<const uint4 *>(src);
-    uint4 *d = reinterpret_cast<uint4 *>(dst);
-#pragma unroll
-    for (int i = 0; i < (int)(D * sizeof(T) / 16); ++i) d[i] = s[i];
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kCompThreads) void compact_kernel(CompactArgs a) {
-    const CacheDev &c = a.c;
-    const int u = blockIdx.x, b = u / c.Hkv, h = u % c.Hkv;
-    const int tid = threadIdx.x;
-    __shared__ uint32_t kept_bits[kMaxCapacity / 32];
-    __shared__ int red[kCompThreads / 64];
-
-    const int n = load_count(c, u, tid == 0);
-    int m = a.n_out[u];
-    if (m < 0 || m > n) {
-        if (tid == 0) raise_flag(c, KVC_FLAG_BAD_COUNT);
-        m = m < 0 ? 0 : n;
-    }
-    const int32_t *ks = a.keep_slots + (size_t)u * c.cap;
-    const int words = (m + 31) / 32;
-    // kept slots below m form a prefix of the ascending list; mark them
-    for (int w = tid; w < words; w += kCompThreads) kept_bits[w] = 0;
-    __syncthreads();
-    int below = 0;
-    for (int i = tid; i < m; i += kCompThreads) {
-        const int j = ks[i];
-        if (j >= 0 && j < m) {
-            atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
-            ++below;
-        }
-    }
-    int cnt;
-    (void)block_excl_scan(below, red, &cnt);
-    below = cnt;   // sources are ks[below .. m)
-    __syncthreads();
-
-    T *K = (T *)c.k;
-    T *V = (T *)c.v;
-    int32_t *P = c.pos + (size_t)u * c.cap;
-    float *S = a.scores ? a.scores + (size_t)u * c.cap : nullptr;
-    int base = 0;
-    for (int j0 = 0; j0 < m; j0 += kCompThreads) {
-        const int j = j0 + tid;
-        const int hole = (j < m) && !((kept_bits[j >> 5] >> (j & 31)) & 1u);
-        int t;
-        const int r = block_excl_scan(hole, red, &t);
-        const int idx = below + base + r;
-        if (hole && idx < m) {
-            const int src = ks[idx];
-            if (src >= m && src < n) {
-                copy_row<T, D>(K + row_of(c, b, h, j) * D, K + row_of(c, b, h, src) * D);
-                copy_row<T, D>(V + row_of(c, b, h, j) * D, V + row_of(c, b, h, src) * D);
-                P[j] = P[src];
-                if (S) S[j] = S[src];
-            }
-        }
-        base += t;
-    }
-    if (tid == 0) c.n_slots[u] = m;
-}
-
-// bitonic sort of 64-bit keys in LDS, ascending (len a power of two)
-__device__ inline void bitonic_sort(uint64_t *x, int len) {
-    for (int k = 2; k <= len; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < len; i += blockDim.x) {
-                const int p = i ^ j;
-                if (p > i) {
-                    const bool up = (i & k) == 0;
-                    const uint64_t xi = x[i], xp = x[p];
-                    if ((xi > xp) == up) {
-                        x[i] = xp;
-                        x[p] = xi;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
+    __shared__ CompLds CL;
+    compact_unit<T, D>(a, blockIdx.x, CL);
 }
 
 template <typename T, int D>

@@ -1,0 +1,502 @@
+// fused.hip -- one whole decode step per unit (sequence b, kv head h) in one
+// workgroup, on the matrix cores of gfx950.
+//
+// What a step computes (KV cache compression guide, section 16, "prefill,
+// decode, TP" and "the 4 methods"; eviction-in-practice blog, "reference
+// implementation"; online compaction study, section 4.2):
+//   z_gj = scale * q_g . k_j over the n cached slots and the new token,
+//   p = softmax_j(z), o_g = sum_j p_gj v_j,
+//   H2O: s_j += sum_g p_gj (exact probabilities, final normaliser),
+//   then the policy's kept set, then hole-fill compaction.
+//
+// Layout of the work (bf16 K/V, head_dim 128, G <= 16 query heads):
+//  * QK^T runs as v_mfma_f32_16x16x32_bf16 with the group's queries as the A
+//    operand (rows = query heads, padded to 16) and 16 keys as the B operand:
+//    every lane loads 16 contiguous bytes of one key row straight from HBM
+//    into its operand registers; bf16 x bf16 products are exact in fp32.
+//  * the logits of the whole unit stay in LDS ([G][n+1] fp32), so the softmax
+//    is exact (no online rescaling) and the H2O update uses the final
+//    normaliser without a second pass over K.
+//  * P.V runs as v_mfma_f32_16x16x4_f32 with fp32 probabilities (no bf16
+//    rounding of P): each lane loads 16 contiguous bytes of a V row (4 rows x
+//    256 B per wave instruction, fully coalesced) and feeds its 8 values to 8
+//    MFMAs whose output columns are dims 8c+t.
+//  * selection runs on the LDS copies of pos / scores / random keys; the
+//    common steady-state case (exactly one eviction) is an arg-min, the
+//    general case an 8-bit radix select over 64-bit (key, position) words.
+//  * compaction pairs evicted slots below n_out with kept slots at or above
+//    n_out; the new token is written straight into its final slot.
+// Units longer than the launch's LDS capacity (or a full cache) take the
+// generic per-unit routines inside the same workgroup, so results never
+// depend on the length hint.
+#include "generic.h"
+
+namespace kvc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kFThreads = 256;
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kHD = 128;   // head_dim of the fast path
+
+struct FusedSmall {
+    float m[kMaxGroup];
+    float l[kMaxGroup];
+    float wred[kFWaves][kMaxGroup];
+    int hist[256];
+    int red[kFWaves * 2];
+    uint32_t mn_hi[kFWaves], mn_lo[kFWaves];
+    int sh[8];
+};
+
+__device__ inline bf16x8_t as_bf16x8(u16x8_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+__device__ inline void load_q(u16x8_t (&qa)[4], const uint16_t *qp, bool valid, int r) {
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+        if (valid) qa[c4] = *reinterpret_cast<const u16x8_t *>(qp + 32 * c4 + 8 * r);
+        else qa[c4] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+}
+
+__device__ inline void load_k(u16x8_t (&kb)[4], const uint16_t *kp, int r) {
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) kb[c4] = *reinterpret_cast<const u16x8_t *>(kp + 32 * c4 + 8 * r);
+}
+
+// 64-bit ranking word: larger = better (kept first); unique inside a unit
+__device__ inline uint64_t rank_word(uint32_t primary, int32_t pos) {
+    return ((uint64_t)primary << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
+}
+
+template <int MODE>
+__device__ void fused_generic(const FusedArgs &fa, int u, unsigned char *smem) {
+    attn_unit_generic<uint16_t, kHD>(fa.attn, u, 0, *reinterpret_cast<AttnLds<kHD> *>(smem));
+    if (MODE == kModeAttn) return;
+    __syncthreads();
+    select_unit<1>(fa.sel, u, *reinterpret_cast<SelLds<1> *>(smem));
+    __syncthreads();
+    compact_unit<uint16_t, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs fa) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const AttnArgs &a = fa.attn;
+    const CacheDev &c = a.c;
+    const int u = blockIdx.x;
+    const int b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane >> 4, col = lane & 15;
+    const int G = c.G;
+
+    const int n = load_count(c, u, tid == 0);
+    const int T = n + 1;
+    if (T > fa.tcap || n >= c.cap) {
+        fused_generic<MODE>(fa, u, smem);
+        return;
+    }
+
+    const int LD = fa.ld, TC = fa.tcap;
+    float *lg = reinterpret_cast<float *>(smem);
+    int32_t *pos_s = reinterpret_cast<int32_t *>(lg + G * LD);
+    float *sc_s = reinterpret_cast<float *>(pos_s + TC);
+    uint32_t *key_s = reinterpret_cast<uint32_t *>(sc_s + TC);
+    uint8_t *flg_s = reinterpret_cast<uint8_t *>(key_s + TC);
+    FusedSmall &sm = *reinterpret_cast<FusedSmall *>(flg_s + TC);
+
+    const uint16_t *K = static_cast<const uint16_t *>(c.k);
+    const uint16_t *V = static_cast<const uint16_t *>(c.v);
+    const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (size_t)u * kHD;
+    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (size_t)u * kHD;
+    int32_t *P = c.pos + (size_t)u * c.cap;
+    float *S = a.scores ? a.scores + (size_t)u * c.cap : nullptr;
+    const bool h2o = S != nullptr;
+    const int32_t npos = a.new_pos[b];
+
+    for (int j = tid; j < T; j += kFThreads) {
+        pos_s[j] = (j < n) ? P[j] : npos;
+        sc_s[j] = (h2o && j < n) ? S[j] : 0.f;
+    }
+
+    // ---------------- logits: MFMA 16x16x32 bf16, A = queries, B = 16 keys
+    u16x8_t qa[4];
+    load_q(qa, static_cast<const uint16_t *>(a.q) + ((size_t)b * c.Hq + (size_t)h * G + col) * kHD,
+           col < G, r);
+    const int ntiles = (T + 15) >> 4;
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    {
+        int t = w;
+        u16x8_t kb[4];
+        if (t < ntiles) {
+            const int j = 16 * t + col;
+            load_k(kb, (j < n) ? K + row_of(c, b, h, j) * kHD : kn, r);
+        }
+        while (t < ntiles) {
+            const int tn = t + kFWaves;
+            u16x8_t nb[4];
+            if (tn < ntiles) {
+                const int jn = 16 * tn + col;
+                load_k(nb, (jn < n) ? K + row_of(c, b, h, jn) * kHD : kn, r);
+            }
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kb[c4]),
+                                                              acc, 0, 0, 0);
+            const int j = 16 * t + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int g = 4 * r + i;
+                const float z = (j < T) ? acc[i] * a.scale : -INFINITY;
+                if (g < G) lg[g * LD + j] = z;
+                mx[i] = fmaxf(mx[i], z);
+            }
+            if (tn < ntiles) {
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) kb[c4] = nb[c4];
+            }
+            t = tn;
+        }
+    }
+    // row maxima: 16-lane groups share a query head set, then across waves
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float m = mx[i];
+        m = fmaxf(m, __shfl_xor(m, 8, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        if (col == 0 && 4 * r + i < G) sm.wred[w][4 * r + i] = m;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float m = sm.wred[0][tid];
+        for (int v = 1; v < kFWaves; ++v) m = fmaxf(m, sm.wred[v][tid]);
+        sm.m[tid] = m;
+    }
+    __syncthreads();
+
+    // ---------------- exact softmax weights w = exp(z - m) and row sums l
+    {
+        float ls[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) ls[g] = 0.f;
+        for (int j = tid; j < T; j += kFThreads) {
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) {
+                    const float e = __expf(lg[g * LD + j] - sm.m[g]);
+                    lg[g * LD + j] = e;
+                    ls[g] += e;
+                }
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) {
+            const float v = wave_sum(ls[g]);
+            if (lane == 0 && g < G) sm.wred[w][g] = v;
+        }
+    }
+    __syncthreads();
+    if (tid < G) {
+        float l = 0.f;
+        for (int v = 0; v < kFWaves; ++v) l += sm.wred[v][tid];
+        sm.l[tid] = l;
+    }
+    __syncthreads();
+
+    // ---------------- H2O: accumulated attention with the final normaliser
+    if (h2o) {
+        for (int j = tid; j < T; j += kFThreads) {
+            float ps = 0.f;
+            for (int g = 0; g < G; ++g) ps += lg[g * LD + j] / sm.l[g];
+            sc_s[j] = (j < n) ? sc_s[j] + ps : ps;
+        }
+    }
+
+    // ---------------- P.V: MFMA 16x16x4 f32, A = probabilities, B = 4 V rows
+    f32x4_t oacc[8];
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) oacc[t8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+        const int ngroups = (T + 3) >> 2;
+        int q4 = w;
+        u16x8_t vv;
+        if (q4 < ngroups) {
+            const int j = 4 * q4 + r;
+            vv = *reinterpret_cast<const u16x8_t *>(((j < n) ? V + row_of(c, b, h, j) * kHD : vn) +
+                                                    8 * col);
+        }
+        while (q4 < ngroups) {
+            const int qn = q4 + kFWaves;
+            u16x8_t nv;
+            if (qn < ngroups) {
+                const int jn = 4 * qn + r;
+                nv = *reinterpret_cast<const u16x8_t *>(
+                    ((jn < n) ? V + row_of(c, b, h, jn) * kHD : vn) + 8 * col);
+            }
+            const int j = 4 * q4 + r;
+            const float p = (col < G && j < T) ? lg[col * LD + j] : 0.f;
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8)
+                oacc[t8] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, bf16_to_f32(vv[t8]), oacc[t8], 0,
+                                                                 0, 0);
+            if (qn < ngroups) vv = nv;
+            q4 = qn;
+        }
+    }
+    __syncthreads();   // every wave is done with the weights in lg
+
+    // ---------------- output: sum the four waves' partial P.V, normalise
+    {
+        float *opart = lg;   // [kFWaves][G][128], fits: LD >= 512 + 4
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = 4 * r + i;
+            if (g < G) {
+                float *dst = opart + ((size_t)w * G + g) * kHD + 8 * col;
+#pragma unroll
+                for (int t8 = 0; t8 < 8; ++t8) dst[t8] = oacc[t8][i];
+            }
+        }
+        __syncthreads();
+        float *outp = a.out + ((size_t)b * c.Hq + (size_t)h * G) * kHD;
+        for (int e = tid; e < G * kHD; e += kFThreads) {
+            const int g = e / kHD;
+            float o = opart[e];
+            for (int v = 1; v < kFWaves; ++v) o += opart[(size_t)v * G * kHD + e];
+            outp[e] = o / sm.l[g];
+        }
+    }
+
+    uint16_t *Kw = static_cast<uint16_t *>(c.k);
+    uint16_t *Vw = static_cast<uint16_t *>(c.v);
+
+    if (MODE == kModeAttn) {
+        // append the new token at slot n, write every score back
+        if (h2o)
+            for (int j = tid; j < T; j += kFThreads) S[j] = sc_s[j];
+        if (tid < 16) {
+            const size_t rw = row_of(c, b, h, n) * kHD;
+            reinterpret_cast<uint4 *>(Kw + rw)[tid] = reinterpret_cast<const uint4 *>(kn)[tid];
+            reinterpret_cast<uint4 *>(Vw + rw)[tid] = reinterpret_cast<const uint4 *>(vn)[tid];
+        }
+        if (tid == 0) {
+            P[n] = npos;
+            c.n_slots[u] = n + 1;
+        }
+        return;
+    }
+
+    // ================= selection on the LDS copies =================
+    const SelectArgs &sa = fa.sel;
+    __syncthreads();
+    int mxp = -1;
+    for (int j = tid; j < T; j += kFThreads) mxp = max(mxp, pos_s[j]);
+    const int L = block_max_i(mxp, sm.red) + 1;
+
+    int ncand = 0;
+    for (int j = tid; j < T; j += kFThreads) {
+        const int32_t p = pos_s[j];
+        uint8_t k = kKeep;
+        if (sa.kind == KVC_POLICY_STREAMING)
+            k = (p < sa.n_sink || (int64_t)p >= (int64_t)L - sa.n_recent) ? kKeep : kDrop;
+        else if (sa.kind == KVC_POLICY_H2O)
+            k = ((int64_t)p >= (int64_t)L - sa.n_recent) ? kKeep : kCand;
+        else if (sa.kind == KVC_POLICY_RANDOM)
+            k = (p < sa.prompt_len) ? kKeep : kCand;
+        if (k == kCand) {
+            key_s[j] = (sa.kind == KVC_POLICY_H2O)
+                           ? float_order_bits(sc_s[j])
+                           : ~philox_word0((uint32_t)p, sa.step, (uint32_t)h, (uint32_t)b,
+                                           (uint32_t)(sa.seed & 0xFFFFFFFFu),
+                                           (uint32_t)(sa.seed >> 32));
+            ++ncand;
+        }
+        flg_s[j] = k;
+    }
+    int tot;
+    (void)block_excl_scan(ncand, sm.red, &tot);
+    ncand = tot;
+    const int want = (sa.kind == KVC_POLICY_H2O) ? sa.n_heavy : sa.n_keep;
+    if (ncand > want) {
+        if (want <= 0) {
+            for (int j = tid; j < T; j += kFThreads)
+                if (flg_s[j] == kCand) flg_s[j] = kDrop;
+        } else if (ncand - want == 1) {
+            // exactly one eviction: the candidate with the smallest ranking word
+            uint64_t best = ~0ull;
+            int arg = -1;
+            for (int j = tid; j < T; j += kFThreads)
+                if (flg_s[j] == kCand) {
+                    const uint64_t wd = rank_word(key_s[j], pos_s[j]);
+                    if (wd < best) {
+                        best = wd;
+                        arg = j;
+                    }
+                }
+            for (int o = 32; o > 0; o >>= 1) {
+                const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
+                const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
+                const int oa = __shfl_xor(arg, o, 64);
+                const uint64_t ob = ((uint64_t)hi << 32) | lo;
+                if (ob < best) {
+                    best = ob;
+                    arg = oa;
+                }
+            }
+            if (lane == 0) {
+                sm.mn_hi[w] = (uint32_t)(best >> 32);
+                sm.mn_lo[w] = (uint32_t)best;
+                sm.sh[w] = arg;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                uint64_t bb = ~0ull;
+                int aa = -1;
+                for (int v = 0; v < kFWaves; ++v) {
+                    const uint64_t ob = ((uint64_t)sm.mn_hi[v] << 32) | sm.mn_lo[v];
+                    if (sm.sh[v] >= 0 && ob < bb) {
+                        bb = ob;
+                        aa = sm.sh[v];
+                    }
+                }
+                sm.sh[kFWaves] = aa;
+            }
+            __syncthreads();
+            const int ev = sm.sh[kFWaves];
+            for (int j = tid; j < T; j += kFThreads)
+                if (flg_s[j] == kCand) flg_s[j] = (j == ev) ? kDrop : kKeep;
+        } else {
+            // radix select of the 'want' largest ranking words among candidates
+            uint64_t prefix = 0, mask = 0;
+            int krem = want;
+            for (int shift = 56; shift >= 0; shift -= 8) {
+                sm.hist[tid] = 0;   // kFThreads == 256 bins
+                __syncthreads();
+                for (int j = tid; j < T; j += kFThreads)
+                    if (flg_s[j] == kCand) {
+                        const uint64_t wd = rank_word(key_s[j], pos_s[j]);
+                        if ((wd & mask) == prefix) atomicAdd(&sm.hist[(wd >> shift) & 255], 1);
+                    }
+                __syncthreads();
+                if (tid == 0) {
+                    int cum = 0, dsel = 0;
+                    for (int d = 255; d >= 0; --d) {
+                        if (cum + sm.hist[d] >= krem) {
+                            dsel = d;
+                            break;
+                        }
+                        cum += sm.hist[d];
+                    }
+                    sm.sh[0] = dsel;
+                    sm.sh[1] = krem - cum;
+                    sm.sh[2] = (sm.hist[dsel] == krem - cum);
+                }
+                __syncthreads();
+                krem = sm.sh[1];
+                prefix |= (uint64_t)sm.sh[0] << shift;
+                mask |= (uint64_t)255 << shift;
+                const int done = sm.sh[2];
+                __syncthreads();
+                if (done) break;
+            }
+            for (int j = tid; j < T; j += kFThreads)
+                if (flg_s[j] == kCand)
+                    flg_s[j] = ((rank_word(key_s[j], pos_s[j]) & mask) >= prefix) ? kKeep : kDrop;
+        }
+    } else {
+        for (int j = tid; j < T; j += kFThreads)
+            if (flg_s[j] == kCand) flg_s[j] = kKeep;
+    }
+    __syncthreads();
+
+    // ================= compaction =================
+    // n_out kept; holes = dropped slots below n_out, sources = kept slots at or
+    // above n_out (slot n is the new token), paired in ascending order.
+    int kc = 0;
+    for (int j = tid; j < T; j += kFThreads) kc += (flg_s[j] == kKeep);
+    (void)block_excl_scan(kc, sm.red, &tot);
+    const int n_out = tot;
+    int32_t *hole = reinterpret_cast<int32_t *>(key_s);   // reuse: ranks are final
+    int32_t *srcl = reinterpret_cast<int32_t *>(lg);
+    int nh = 0, ns = 0;
+    for (int j0 = 0; j0 < T; j0 += kFThreads) {
+        const int j = j0 + tid;
+        const int isHole = (j < n_out) && flg_s[j] != kKeep;
+        const int isSrc = (j >= n_out) && (j < T) && flg_s[j] == kKeep;
+        int th, ts;
+        const int rh = block_excl_scan(isHole, sm.red, &th);
+        const int rs = block_excl_scan(isSrc, sm.red + kFWaves, &ts);
+        if (isHole) hole[nh + rh] = j;
+        if (isSrc) srcl[ns + rs] = j;
+        nh += th;
+        ns += ts;
+    }
+    __syncthreads();
+    const int moves = min(nh, ns);
+    for (int e = tid; e < moves * 16; e += kFThreads) {
+        const int i = e >> 4, part = e & 15;
+        const int d = hole[i], s = srcl[i];
+        const size_t rd = row_of(c, b, h, d) * kHD;
+        const uint4 *ks = reinterpret_cast<const uint4 *>((s == n) ? kn : K + row_of(c, b, h, s) * kHD);
+        const uint4 *vs = reinterpret_cast<const uint4 *>((s == n) ? vn : V + row_of(c, b, h, s) * kHD);
+        reinterpret_cast<uint4 *>(Kw + rd)[part] = ks[part];
+        reinterpret_cast<uint4 *>(Vw + rd)[part] = vs[part];
+    }
+    for (int i = tid; i < moves; i += kFThreads) {
+        const int d = hole[i], s = srcl[i];
+        P[d] = pos_s[s];
+        if (h2o) S[d] = sc_s[s];
+    }
+    // kept slots that stay: new scores; the new token kept in place (no eviction)
+    for (int j = tid; j < n_out; j += kFThreads)
+        if (flg_s[j] == kKeep) {
+            if (h2o) S[j] = sc_s[j];
+            if (j == n) P[n] = npos;
+        }
+    if (n < n_out && tid < 16) {
+        const size_t rw = row_of(c, b, h, n) * kHD;
+        reinterpret_cast<uint4 *>(Kw + rw)[tid] = reinterpret_cast<const uint4 *>(kn)[tid];
+        reinterpret_cast<uint4 *>(Vw + rw)[tid] = reinterpret_cast<const uint4 *>(vn)[tid];
+    }
+    if (tid == 0) c.n_slots[u] = n_out;
+}
+
+size_t fused_smem_bytes(int G, int tcap) {
+    const size_t ld = (size_t)tcap + 4;
+    size_t fast = (size_t)G * ld * 4 + (size_t)tcap * (4 + 4 + 4 + 1) + sizeof(FusedSmall) + 16;
+    size_t gen = sizeof(AttnLds<kHD>);
+    if (sizeof(SelLds<1>) > gen) gen = sizeof(SelLds<1>);
+    if (sizeof(CompLds) > gen) gen = sizeof(CompLds);
+    return fast > gen ? fast : gen;
+}
+
+static hipError_t allow_large_lds() {
+    static hipError_t once = [] {
+        const int most = (int)fused_smem_bytes(kMaxGroup, kFusedMaxT);
+        hipError_t e = hipFuncSetAttribute((const void *)fused_kernel<kModeAttn>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)fused_kernel<kModeStep>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        return e;
+    }();
+    return once;
+}
+
+hipError_t launch_fused(const FusedArgs &fa, int mode, hipStream_t s) {
+    const hipError_t e = allow_large_lds();
+    if (e != hipSuccess) return e;
+    const int units = fa.attn.c.B * fa.attn.c.Hkv;
+    const size_t smem = fused_smem_bytes(fa.attn.c.G, fa.tcap);
+    if (mode == kModeAttn)
+        hipLaunchKernelGGL((fused_kernel<kModeAttn>), dim3(units), dim3(kFThreads), smem, s, fa);
+    else
+        hipLaunchKernelGGL((fused_kernel<kModeStep>), dim3(units), dim3(kFThreads), smem, s, fa);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,461 @@
+// generic.h -- per-unit device routines of libkvc that work for any unit
+// length, dtype and head_dim: attention with logits in a global scratch row,
+// radix selection, hole-fill and ordered compaction.  The standalone kernels
+// wrap them one unit per workgroup; the fused step kernel falls back to them
+// for units that do not fit its LDS-resident fast path.
+#pragma once
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+constexpr int kAttnThreads = 256;
+constexpr int kMaxSplit = 64;
+
+template <int D>
+struct AttnLds {
+    float q_s[kMaxGroup * D];
+    float st_m[kMaxGroup], st_l[kMaxGroup];
+    float red[kAttnThreads / 64][kMaxGroup];
+    float pv[kAttnThreads / D][kMaxGroup][D];
+};
+
+// ===========================================================================
+// decode attention (see attn.hip for the method and citations)
+// ===========================================================================
+template <typename T, int D>
+__device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLds<D> &L) {
+    const CacheDev &c = a.c;
+    const int G = c.G;
+    const int b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    constexpr int kParts = kAttnThreads / D;
+
+    float *q_s = L.q_s;
+    float *st_m = L.st_m, *st_l = L.st_l;
+    auto &red = L.red;
+    auto &pv = L.pv;
+
+    const int n = load_count(c, u, s == 0 && tid == 0);
+    const bool can_store = n < c.cap;
+    if (!can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
+    const int T_len = n + 1;
+    const int chunk = (T_len + a.nsplit - 1) / a.nsplit;
+    const int j0 = min(s * chunk, T_len), j1 = min(T_len, j0 + chunk);
+
+    const T *qp = (const T *)a.q + ((size_t)b * c.Hq + (size_t)h * G) * D;
+    for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<T>::get(qp, e);
+    __syncthreads();
+
+    const T *K = (const T *)c.k;
+    const T *V = (const T *)c.v;
+    const T *kn = (const T *)a.k_new + ((size_t)b * c.Hkv + h) * D;
+    const T *vn = (const T *)a.v_new + ((size_t)b * c.Hkv + h) * D;
+    const size_t ld = (size_t)c.cap + 1;
+    float *lg = a.logits + (size_t)u * G * ld;
+
+    // ---- logits and running max (thread owns keys j = j0 + tid + k*256)
+    float mloc[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) mloc[g] = -INFINITY;
+    for (int j = j0 + tid; j < j1; j += kAttnThreads) {
+        const T *row = (j < n) ? K + row_of(c, b, h, j) * D : kn;
+        float acc[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
+        for (int d = 0; d < D; ++d) {
+            const float kv = Elem<T>::get(row, d);
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g)
+            if (g < G) {
+                const float z = acc[g] * a.scale;
+                lg[g * ld + j] = z;
+                mloc[g] = fmaxf(mloc[g], z);
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+        const float w = wave_max(mloc[g]);
+        if (lane == 0) red[wv][g] = w;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float m = red[0][tid];
+        for (int w = 1; w < kAttnThreads / 64; ++w) m = fmaxf(m, red[w][tid]);
+        st_m[tid] = m;
+    }
+    __syncthreads();
+
+    // ---- unnormalised weights w = exp(z - m), row sums
+    float lloc[kMaxGroup];
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) lloc[g] = 0.f;
+    for (int j = j0 + tid; j < j1; j += kAttnThreads) {
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g)
+            if (g < G) {
+                const float w = __expf(lg[g * ld + j] - st_m[g]);
+                lg[g * ld + j] = w;
+                lloc[g] += w;
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxGroup; ++g) {
+        const float w = wave_sum(lloc[g]);
+        if (lane == 0) red[wv][g] = w;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float l = 0.f;
+        for (int w = 0; w < kAttnThreads / 64; ++w) l += red[w][tid];
+        st_l[tid] = l;
+    }
+    __syncthreads();
+
+    // ---- P.V: thread owns one dimension d and every kParts-th key
+    {
+        const int d = tid % D, part = tid / D;
+        float acc[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
+        for (int j = j0 + part; j < j1; j += kParts) {
+            const T *row = (j < n) ? V + row_of(c, b, h, j) * D : vn;
+            const float vv = Elem<T>::get(row, d);
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G) acc[g] = fmaf(lg[g * ld + j], vv, acc[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) pv[part][g][d] = acc[g];
+    }
+    __syncthreads();
+
+    if (a.nsplit == 1) {
+        if (tid < D) {
+            for (int g = 0; g < G; ++g) {
+                float o = 0.f;
+                for (int p = 0; p < kParts; ++p) o += pv[p][g][tid];
+                a.out[((size_t)b * c.Hq + (size_t)h * G + g) * D + tid] = o / st_l[g];
+            }
+        }
+        if (a.scores) {
+            float *sc = a.scores + (size_t)u * c.cap;
+            for (int j = j0 + tid; j < j1; j += kAttnThreads) {
+                float ps = 0.f;
+                for (int g = 0; g < G; ++g) ps += lg[g * ld + j] / st_l[g];
+                if (j < n) sc[j] += ps;
+                else if (can_store) sc[n] = ps;
+            }
+        }
+    } else {
+        float *pp = a.part + ((size_t)u * a.nsplit + s) * G * (D + 2);
+        if (tid < D) {
+            for (int g = 0; g < G; ++g) {
+                float o = 0.f;
+                for (int p = 0; p < kParts; ++p) o += pv[p][g][tid];
+                pp[g * (D + 2) + tid] = o;
+            }
+        }
+        if (tid < G) {
+            pp[tid * (D + 2) + D] = st_m[tid];
+            pp[tid * (D + 2) + D + 1] = st_l[tid];
+        }
+    }
+
+    // ---- append the new token (the workgroup whose range holds index n)
+    if (can_store && j0 <= n && n < j1) {
+        T *Kw = (T *)c.k;
+        T *Vw = (T *)c.v;
+        const size_t r = row_of(c, b, h, n) * D;
+        for (int e = tid; e < D; e += kAttnThreads) {
+            Kw[r + e] = kn[e];
+            Vw[r + e] = vn[e];
+        }
+        if (tid == 0) c.pos[(size_t)u * c.cap + n] = a.new_pos[b];
+    }
+    if (a.nsplit == 1 && tid == 0 && can_store) c.n_slots[u] = n + 1;
+}
+
+// ===========================================================================
+// selection (see select.hip for the policies and citations)
+// ===========================================================================
+enum : uint8_t { kDrop = 0, kKeep = 1, kCand = 2 };
+
+constexpr int kSelThreads = 256;
+
+struct SelView {
+    int kind, n_sink, n_recent, prompt_len;
+    uint32_t step, seed_lo, seed_hi;
+    int u, b, h, n, L;
+    const int32_t *P;
+    const float *S;
+};
+
+// class and 64-bit ranking key of slot j
+__device__ inline uint8_t sel_class(const SelView &v, int j, int32_t p) {
+    switch (v.kind) {
+        case KVC_POLICY_STREAMING:
+            return (p < v.n_sink || (int64_t)p >= (int64_t)v.L - v.n_recent) ? kKeep : kDrop;
+        case KVC_POLICY_H2O:
+            return ((int64_t)p >= (int64_t)v.L - v.n_recent) ? kKeep : kCand;
+        case KVC_POLICY_RANDOM:
+            return (p < v.prompt_len) ? kKeep : kCand;
+        default:
+            return kKeep;
+    }
+}
+
+__device__ inline uint32_t sel_primary(const SelView &v, int j, int32_t p) {
+    if (v.kind == KVC_POLICY_H2O) return float_order_bits(v.S[j]);
+    // random: smaller Philox word = better -> invert
+    const uint32_t w = philox_word0((uint32_t)p, v.step, (uint32_t)v.h, (uint32_t)v.b,
+                                    v.seed_lo, v.seed_hi);
+    return ~w;
+}
+
+template <int kSelLds>
+struct SelLds {
+    uint32_t prim_s[kSelLds];
+    int32_t pos_s[kSelLds];
+    uint8_t cls_s[kSelLds];
+    int hist[256];
+    int red[kSelThreads / 64];
+    int sh_digit, sh_krem, sh_done;
+};
+
+// Units of up to kSelLds slots keep their ranking keys in LDS; longer units
+// recompute them from global memory on every pass.
+template <int kSelLds>
+__device__ inline void select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S) {
+    const CacheDev &c = a.c;
+    const int tid = threadIdx.x;
+    uint32_t *prim_s = S.prim_s;
+    int32_t *pos_s = S.pos_s;
+    uint8_t *cls_s = S.cls_s;
+    int *hist = S.hist;
+    int *red = S.red;
+    int &sh_digit = S.sh_digit, &sh_krem = S.sh_krem, &sh_done = S.sh_done;
+
+    SelView v;
+    v.kind = a.kind;
+    v.n_sink = a.n_sink;
+    v.n_recent = a.n_recent;
+    v.prompt_len = a.prompt_len;
+    v.step = a.step;
+    v.seed_lo = (uint32_t)(a.seed & 0xFFFFFFFFu);
+    v.seed_hi = (uint32_t)(a.seed >> 32);
+    v.u = u;
+    v.b = u / c.Hkv;
+    v.h = u % c.Hkv;
+    v.n = load_count(c, u, tid == 0);
+    v.P = c.pos + (size_t)u * c.cap;
+    v.S = a.scores ? a.scores + (size_t)u * c.cap : nullptr;
+    const int n = v.n;
+    const bool in_lds = n <= kSelLds;
+
+    int mx = -1;
+    for (int j = tid; j < n; j += kSelThreads) mx = max(mx, v.P[j]);
+    v.L = block_max_i(mx, red) + 1;
+
+    // classify, count candidates, cache keys
+    int ncand = 0;
+    for (int j = tid; j < n; j += kSelThreads) {
+        const int32_t p = v.P[j];
+        const uint8_t k = sel_class(v, j, p);
+        if (in_lds) {
+            cls_s[j] = k;
+            pos_s[j] = p;
+            if (k == kCand) prim_s[j] = sel_primary(v, j, p);
+        }
+        ncand += (k == kCand);
+    }
+    int tot;
+    (void)block_excl_scan(ncand, red, &tot);
+    ncand = tot;
+    const int want = (a.kind == KVC_POLICY_H2O) ? a.n_heavy : a.n_keep;
+
+    // radix select of the 'want' largest composite keys among candidates
+    uint64_t prefix = 0, mask = 0;
+    const bool rank = ncand > want;          // otherwise every candidate stays
+    const bool keep_none = rank && want <= 0;
+    if (rank && want > 0) {
+        int krem = want;
+        for (int shift = 56; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+            __syncthreads();
+            for (int j = tid; j < n; j += kSelThreads) {
+                int32_t p;
+                uint8_t k;
+                if (in_lds) {
+                    k = cls_s[j];
+                    p = pos_s[j];
+                } else {
+                    p = v.P[j];
+                    k = sel_class(v, j, p);
+                }
+                if (k != kCand) continue;
+                const uint32_t pr = in_lds ? prim_s[j] : sel_primary(v, j, p);
+                const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                // digit holding the krem-th largest matching key
+                int cum = 0, dsel = 0;
+                for (int d = 255; d >= 0; --d) {
+                    if (cum + hist[d] >= krem) {
+                        dsel = d;
+                        break;
+                    }
+                    cum += hist[d];
+                }
+                sh_digit = dsel;
+                sh_krem = krem - cum;
+                sh_done = (hist[dsel] == krem - cum);
+            }
+            __syncthreads();
+            krem = sh_krem;
+            prefix |= (uint64_t)sh_digit << shift;
+            mask |= (uint64_t)255 << shift;
+            const int done = sh_done;
+            __syncthreads();
+            if (done) break;   // every key of the selected bin is kept
+        }
+    }
+
+    // keep flags -> ascending slot list
+    int32_t *ks = a.keep_slots + (size_t)u * c.cap;
+    int base = 0;
+    for (int j0 = 0; j0 < n; j0 += kSelThreads) {
+        const int j = j0 + tid;
+        int keep = 0;
+        if (j < n) {
+            int32_t p;
+            uint8_t k;
+            if (in_lds) {
+                k = cls_s[j];
+                p = pos_s[j];
+            } else {
+                p = v.P[j];
+                k = sel_class(v, j, p);
+            }
+            if (k == kKeep) keep = 1;
+            else if (k == kCand) {
+                if (!rank) keep = 1;
+                else if (!keep_none) {
+                    const uint32_t pr = in_lds ? prim_s[j] : sel_primary(v, j, p);
+                    const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+                    keep = (key & mask) >= prefix;
+                }
+            }
+        }
+        int t;
+        const int off = block_excl_scan(keep, red, &t);
+        if (keep) ks[base + off] = j;
+        base += t;
+    }
+    if (tid == 0) a.n_out[u] = base;
+}
+
+// ===========================================================================
+// compaction (see compact.hip)
+// ===========================================================================
+constexpr int kCompThreads = 256;
+constexpr int kOrderedMax = 8192;
+
+template <typename T, int D>
+__device__ inline void copy_row(T *dst, const T *src) {
+    static_assert((D * sizeof(T)) % 16 == 0, "row must be a multiple of 16 bytes");
+    const uint4 *s = reinterpret_cast<const uint4 *>(src);
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int i = 0; i < (int)(D * sizeof(T) / 16); ++i) d[i] = s[i];
+}
+
+struct CompLds {
+    uint32_t kept_bits[kMaxCapacity / 32];
+    int red[kCompThreads / 64];
+};
+
+template <typename T, int D>
+__device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
+    const CacheDev &c = a.c;
+    const int b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x;
+    uint32_t *kept_bits = CL.kept_bits;
+    int *red = CL.red;
+
+    const int n = load_count(c, u, tid == 0);
+    int m = a.n_out[u];
+    if (m < 0 || m > n) {
+        if (tid == 0) raise_flag(c, KVC_FLAG_BAD_COUNT);
+        m = m < 0 ? 0 : n;
+    }
+    const int32_t *ks = a.keep_slots + (size_t)u * c.cap;
+    const int words = (m + 31) / 32;
+    // kept slots below m form a prefix of the ascending list; mark them
+    for (int w = tid; w < words; w += kCompThreads) kept_bits[w] = 0;
+    __syncthreads();
+    int below = 0;
+    for (int i = tid; i < m; i += kCompThreads) {
+        const int j = ks[i];
+        if (j >= 0 && j < m) {
+            atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
+            ++below;
+        }
+    }
+    int cnt;
+    (void)block_excl_scan(below, red, &cnt);
+    below = cnt;   // sources are ks[below .. m)
+    __syncthreads();
+
+    T *K = (T *)c.k;
+    T *V = (T *)c.v;
+    int32_t *P = c.pos + (size_t)u * c.cap;
+    float *S = a.scores ? a.scores + (size_t)u * c.cap : nullptr;
+    int base = 0;
+    for (int j0 = 0; j0 < m; j0 += kCompThreads) {
+        const int j = j0 + tid;
+        const int hole = (j < m) && !((kept_bits[j >> 5] >> (j & 31)) & 1u);
+        int t;
+        const int r = block_excl_scan(hole, red, &t);
+        const int idx = below + base + r;
+        if (hole && idx < m) {
+            const int src = ks[idx];
+            if (src >= m && src < n) {
+                copy_row<T, D>(K + row_of(c, b, h, j) * D, K + row_of(c, b, h, src) * D);
+                copy_row<T, D>(V + row_of(c, b, h, j) * D, V + row_of(c, b, h, src) * D);
+                P[j] = P[src];
+                if (S) S[j] = S[src];
+            }
+        }
+        base += t;
+    }
+    if (tid == 0) c.n_slots[u] = m;
+}
+
+// bitonic sort of 64-bit keys in LDS, ascending (len a power of two)
+__device__ inline void bitonic_sort(uint64_t *x, int len) {
+    for (int k = 2; k <= len; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < len; i += blockDim.x) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const bool up = (i & k) == 0;
+                    const uint64_t xi = x[i], xp = x[p];
+                    if ((xi > xp) == up) {
+                        x[i] = xp;
+                        x[p] = xi;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace kvc

@@ -88,6 +88,16 @@ int choose_nsplit(const kvc_cache *c, int hint) {
     return ns;
 }
 
+// Attended length the caller promises (n_slots + 1 <= hint); <= 0 means the
+// capacity bound.
+int effective_len(const kvc_cache *c, int hint) {
+    return (hint <= 0 || hint > c->capacity + 1) ? c->capacity + 1 : hint;
+}
+
+bool use_fused(const kvc_cache *c, int hint) {
+    return c->dtype == KVC_BF16 && c->head_dim == 128 && effective_len(c, hint) <= kvc::kFusedMaxT;
+}
+
 struct Workspace {
     size_t part_off, part_bytes;
     size_t logit_off, logit_bytes;
@@ -176,6 +186,22 @@ kvc::AttnArgs attn_args(const kvc_cache *c, const int32_t *new_pos, const void *
     return a;
 }
 
+// Arguments of the one-workgroup-per-unit kernel; its fallback routines use
+// the same workspace regions as the split path (logits, keep lists).
+kvc::FusedArgs fused_args(const kvc_cache *c, const kvc::AttnArgs &a, int hint) {
+    kvc::FusedArgs fa;
+    fa.attn = a;
+    fa.attn.nsplit = 1;
+    fa.attn.part = nullptr;
+    int tcap = (effective_len(c, hint) + 63) / 64 * 64;
+    if (tcap < 512) tcap = 512;
+    fa.tcap = tcap;
+    fa.ld = tcap + 4;
+    fa.sel = kvc::SelectArgs();
+    fa.comp = kvc::CompactArgs();
+    return fa;
+}
+
 kvc_status check_attn_args(const kvc_cache *c, const int32_t *new_pos, const void *q,
                            const void *k_new, const void *v_new, const float *out, float scale,
                            const char *what) {
@@ -254,6 +280,10 @@ KVC_EXPORT kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos
     const Workspace w = layout(c, max_len_hint);
     if ((s = check_ws(w, workspace, workspace_bytes, what)) != KVC_OK) return s;
     kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, h2o_scores, scale, w, workspace);
+    if (use_fused(c, max_len_hint)) {
+        kvc::FusedArgs fa = fused_args(c, a, max_len_hint);
+        return hip_status(kvc::launch_fused(fa, kvc::kModeAttn, (hipStream_t)stream), what);
+    }
     return hip_status(kvc::launch_attn(a, c->dtype, (hipStream_t)stream), what);
 }
 
@@ -364,12 +394,23 @@ KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *poli
     hipStream_t st = (hipStream_t)stream;
     float *scores = policy->kind == KVC_POLICY_H2O ? h2o_scores : nullptr;
     kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, scores, scale, w, workspace);
-    hipError_t e = kvc::launch_attn(a, c->dtype, st);
-    if (e != hipSuccess) return hip_status(e, what);
-    if (policy->kind == KVC_POLICY_FULL) return ok();
     int32_t *keep = (int32_t *)((char *)workspace + w.keep_off);
     int32_t *nout = (int32_t *)((char *)workspace + w.nout_off);
     kvc::SelectArgs sa = select_args(c, *policy, step, scores, keep, nout);
+    if (use_fused(c, max_len_hint)) {
+        kvc::FusedArgs fa = fused_args(c, a, max_len_hint);
+        fa.sel = sa;
+        fa.comp.c = kvc::make_dev(*c);
+        fa.comp.keep_slots = keep;
+        fa.comp.n_out = nout;
+        fa.comp.scores = scores;
+        fa.comp.ordered = false;
+        fa.comp.dst = fa.comp.c;
+        return hip_status(kvc::launch_fused(fa, kvc::kModeStep, st), what);
+    }
+    hipError_t e = kvc::launch_attn(a, c->dtype, st);
+    if (e != hipSuccess) return hip_status(e, what);
+    if (policy->kind == KVC_POLICY_FULL) return ok();
     e = kvc::launch_select(sa, st);
     if (e != hipSuccess) return hip_status(e, what);
     kvc::CompactArgs ca;

@@ -20,7 +20,26 @@ from kvc_harness import (OUT_ATOL, Snapshot, assert_scores_close, dev, make_cach
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, lengths, capacity, with_scores=True, hint=0, paged=0, step=1, q_zero=False):
+def _path(path, lengths, capacity):
+    """(capacity, hint) that route a bf16 / head_dim 128 call to a given path:
+    'fused' = one workgroup per unit with LDS-resident logits, 'split' = the
+    generic split kernels (attended length above the fused limit of 1024),
+    'fallback' = fused launch whose hint is too small for some units."""
+    if path == "fused":
+        return capacity, max(lengths) + 1
+    if path == "split":
+        cap = max(capacity, 1104)   # a multiple of the paged block size
+        return cap, cap + 1
+    if path == "fallback":
+        assert max(lengths) + 1 > 512
+        return capacity, 1
+    return capacity, 0
+
+
+def _run(w, lengths, capacity, with_scores=True, hint=0, paged=0, step=1, q_zero=False,
+         path=None):
+    if path is not None:
+        capacity, hint = _path(path, lengths, capacity)
     B = len(lengths)
     G, D = w.group, w.head_dim
     cache = make_cache(w, lengths, capacity, paged=paged)
@@ -72,36 +91,54 @@ W_G8 = synth.workload("heavy_load_b512_l2048")
 W_F32 = synth.workload("tiny_mha_streaming_f32")
 
 
-@pytest.mark.parametrize("hint", [0, 1, 600])
+PATHS = ["fused", "split"]
+
+
+@pytest.mark.parametrize("hint", [0, 1, 600, 2000])
 def test_ragged_lengths_every_split_mode(hint):
     # lengths span several tiles and a ragged tail, plus an empty unit
-    _run(W_GQA, [0, 37, 300, 511], capacity=512, hint=hint)
+    _run(W_GQA, [0, 37, 300, 511], capacity=512 if hint < 1024 else 1500, hint=hint)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("w", [W_HEAVY, W_G5, W_G8, W_F32], ids=lambda w: w.name)
-def test_group_sizes_dtypes_and_heavy_hitters(w):
-    _run(w, [129, 700, 2], capacity=1024)
+def test_group_sizes_dtypes_and_heavy_hitters(w, path):
+    _run(w, [129, 700, 2], capacity=1000, path=path)
 
 
-def test_without_scores():
-    _run(W_G8, [513, 64], capacity=520, with_scores=False)
+@pytest.mark.parametrize("path", PATHS)
+def test_without_scores(path):
+    _run(W_G8, [513, 64], capacity=520, with_scores=False, path=path)
 
 
-def test_zero_query_spreads_probability_uniformly():
-    _run(W_GQA, [100, 255], capacity=300, q_zero=True)
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_query_spreads_probability_uniformly(path):
+    _run(W_GQA, [100, 255], capacity=300, q_zero=True, path=path)
 
 
 def test_long_units_split_across_workgroups():
     _run(W_G5, [5120, 3000], capacity=5121, hint=5121)
 
 
-def test_paged_layout_matches_contiguous_results():
-    _run(W_GQA, [17, 100, 300], capacity=320, paged=16)
+def test_fused_launch_with_too_small_hint_falls_back_exactly():
+    _run(W_G8, [900, 40, 513, 1000], capacity=1001, path="fallback")
 
 
-def test_empty_cache_returns_the_new_value():
+def test_group_of_sixteen_query_heads():
+    w = synth.workload("heavy_load_b512_l2048", q_heads=128)
+    for path in PATHS:
+        _run(w, [300, 17], capacity=400, path=path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_paged_layout_matches_contiguous_results(path):
+    _run(W_GQA, [17, 100, 300], capacity=320, paged=16, path=path)
+
+
+@pytest.mark.parametrize("capacity", [4, 1100])
+def test_empty_cache_returns_the_new_value(capacity):
     w = W_GQA
-    cache = make_cache(w, [0, 0], capacity=4)
+    cache = make_cache(w, [0, 0], capacity=capacity)
     q, kn, vn = synth.batch_step_inputs(w, 1, 2)
     out = torch.empty((2, w.q_heads, w.head_dim), device="cuda")
     kvc.decode_attn(cache, torch.zeros(2, dtype=torch.int32, device="cuda"), dev(q, w.dtype),
@@ -113,18 +150,19 @@ def test_empty_cache_returns_the_new_value():
             np.testing.assert_array_equal(o[b, i], vf[b, i // w.group])
 
 
-def test_full_cache_sets_flag_and_does_not_store():
+@pytest.mark.parametrize("capacity", [8, 1100])
+def test_full_cache_sets_flag_and_does_not_store(capacity):
     w = W_GQA
-    cache = make_cache(w, [8, 3], capacity=8)
+    cache = make_cache(w, [capacity, 3], capacity=capacity)
     q, kn, vn = synth.batch_step_inputs(w, 1, 2)
     out = torch.empty((2, w.q_heads, w.head_dim), device="cuda")
     before = cache.k.clone()
-    kvc.decode_attn(cache, torch.tensor([8, 3], dtype=torch.int32, device="cuda"),
+    kvc.decode_attn(cache, torch.tensor([capacity, 3], dtype=torch.int32, device="cuda"),
                     dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype), out, None,
                     workspace=cache.workspace())
     torch.cuda.synchronize()
     assert int(cache.flags.item()) & kvc.FLAG_FULL
-    assert cache.n_slots[0].tolist() == [8] * w.kv_heads
+    assert cache.n_slots[0].tolist() == [capacity] * w.kv_heads
     assert cache.n_slots[1].tolist() == [4] * w.kv_heads
     assert torch.equal(cache.k[0], before[0])
     assert torch.isfinite(out).all()

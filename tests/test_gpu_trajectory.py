@@ -36,8 +36,12 @@ def _policy_pair(w):
     return kvc.policy_full(), oracle.Policy.full()
 
 
-def _trajectory(w, lengths, capacity, steps, fused=True, paged=0):
-    """Oracle trajectory vs GPU trajectory, kept sets and outputs every step."""
+def _trajectory(w, lengths, capacity, steps, fused=True, paged=0, hint=None):
+    """Oracle trajectory vs GPU trajectory, kept sets and outputs every step.
+
+    hint None = the capacity bound: up to 1024 attended entries that is the
+    one-workgroup fused kernel (bf16, head_dim 128), above it the split path."""
+    hint = capacity + 1 if hint is None else hint
     B = len(lengths)
     cache = make_cache(w, lengths, capacity, paged=paged)
     orc = oracle.Oracle(w.q_heads, w.kv_heads, w.head_dim, w.dtype)
@@ -45,7 +49,7 @@ def _trajectory(w, lengths, capacity, steps, fused=True, paged=0):
         k, v = synth.prefill_kv(w, b, L)
         orc.load(b, k, v)
     pol_gpu, pol_orc = _policy_pair(w)
-    ws = cache.workspace(capacity)
+    ws = cache.workspace(hint)
     out = torch.empty((B, w.q_heads, w.head_dim), device="cuda")
     scores = torch.zeros((B, w.kv_heads, capacity), device="cuda") if w.policy == "h2o" else None
     seen = list(lengths)
@@ -55,9 +59,9 @@ def _trajectory(w, lengths, capacity, steps, fused=True, paged=0):
         qd, knd, vnd = dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype)
         if fused:
             kvc.decode_step(cache, pol_gpu, t, new_pos, qd, knd, vnd, out, scores,
-                            max_len_hint=capacity, workspace=ws)
+                            max_len_hint=hint, workspace=ws)
         else:
-            _three_calls(cache, w, pol_gpu, t, new_pos, qd, knd, vnd, out, scores, ws, capacity)
+            _three_calls(cache, w, pol_gpu, t, new_pos, qd, knd, vnd, out, scores, ws, hint)
         snap = Snapshot(cache, w.dtype)
         o = out.cpu().numpy()
         for b in range(B):
@@ -100,10 +104,11 @@ def test_tiny_streaming_three_call_path():
     _trajectory(w, [w.prompt_len], capacity=w.prompt_len + 1, steps=4, fused=False)
 
 
-def test_random_eviction_trajectory_reaches_steady_state():
+@pytest.mark.parametrize("capacity", [200, 1100])
+def test_random_eviction_trajectory_reaches_steady_state(capacity):
     # reasoning-trace shape, shortened: pinned prompt 64, 96 kept generated
     w = synth.workload("reasoning_random_b32", pinned=64, n_keep=96)
-    _trajectory(w, [150, 170, 64], capacity=200, steps=24)
+    _trajectory(w, [150, 170, 64], capacity=capacity, steps=24)
 
 
 def test_random_eviction_three_call_path():
@@ -111,17 +116,37 @@ def test_random_eviction_three_call_path():
     _trajectory(w, [150, 170], capacity=200, steps=6, fused=False)
 
 
-def test_streaming_on_paged_cache():
+def test_random_eviction_long_prompt_steady_state():
+    # reasoning shape at its real budget: 1,024 pinned + 4,096 kept generated,
+    # starting one token over budget so that every step evicts one per head
+    w = synth.workload("reasoning_random_b32")
+    _trajectory(w, [5120, 5000], capacity=5121, steps=3)
+
+
+@pytest.mark.parametrize("capacity", [208, 1104])
+def test_streaming_on_paged_cache(capacity):
     w = synth.workload("mixed_paged_h2o_b128", policy="streaming", n_sink=8, n_recent=40)
-    _trajectory(w, [30, 47, 80, 200], capacity=208, steps=8, paged=16)
+    _trajectory(w, [30, 47, 80, 200], capacity=capacity, steps=8, paged=16)
 
 
-def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None):
+def test_streaming_heavy_load_shape_fused():
+    # the heavy-load layer shape (G = 8) with its 64 + 448 budget, reduced batch
+    w = synth.workload("heavy_load_b512_l2048", policy="streaming")
+    _trajectory(w, [600, 512, 511, 900], capacity=901, steps=3, hint=901)
+
+
+def test_undersized_hint_falls_back_inside_the_step_kernel():
+    w = synth.workload("heavy_load_b512_l2048", policy="streaming")
+    _trajectory(w, [900, 40, 700], capacity=901, steps=3, hint=2)
+
+
+def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None, hint=None):
+    hint = capacity + 1 if hint is None else hint
     B = len(lengths)
     G = w.group
     cache = make_cache(w, lengths, capacity, paged=paged)
     scores = torch.zeros((B, w.kv_heads, capacity), device="cuda")
-    ws = cache.workspace(capacity)
+    ws = cache.workspace(hint)
     out = torch.empty((B, w.q_heads, w.head_dim), device="cuda")
     keep = torch.empty((B, w.kv_heads, capacity), dtype=torch.int32, device="cuda")
     nout = torch.empty((B, w.kv_heads), dtype=torch.int32, device="cuda")
@@ -133,7 +158,7 @@ def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None):
         pre = Snapshot(cache, w.dtype, scores, units)
         kvc.decode_attn(cache, torch.tensor(seen, dtype=torch.int32, device="cuda"),
                         dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype), out, scores,
-                        max_len_hint=capacity, workspace=ws)
+                        max_len_hint=hint, workspace=ws)
         mid = Snapshot(cache, w.dtype, scores, units)
         kvc.evict_h2o(cache, scores, w.n_heavy, w.n_recent, keep, nout)
         kk, mm = keep.cpu().numpy(), nout.cpu().numpy()
@@ -169,9 +194,10 @@ def test_h2o_state_synchronised_with_heavy_hitters():
     _h2o_sync(w, [2048, 2048, 700], capacity=2049, steps=4)
 
 
-def test_h2o_small_budget_many_steps():
+@pytest.mark.parametrize("capacity", [48, 1100])
+def test_h2o_small_budget_many_steps(capacity):
     w = synth.workload("llama3_8b_h2o_b64", n_heavy=6, n_recent=20)
-    _h2o_sync(w, [40, 26, 3], capacity=48, steps=30)
+    _h2o_sync(w, [40, 26, 3], capacity=capacity, steps=30)
 
 
 def test_h2o_on_paged_mixed_lengths():
@@ -179,44 +205,58 @@ def test_h2o_on_paged_mixed_lengths():
     _h2o_sync(w, [600, 64, 1000, 17], capacity=1008, steps=5, paged=16)
 
 
+def test_h2o_heavy_load_shape_fused_steady_state():
+    # heavy-load layer (G = 8), 64 + 448, units starting at and below budget
+    w = synth.workload("heavy_load_b512_l2048")
+    _h2o_sync(w, [512, 512, 300, 700], capacity=701, steps=3)
+
+
 def _state(cache, scores, dn):
     s = Snapshot(cache, dn, scores)
     return {k: rows_by_pos(v) for k, v in s.units.items()}, s
 
 
+def _live_equal(c0, c1, s0=None, s1=None):
+    """Same live state: slot counts, and per unit the live slots' K, V, pos
+    (and scores) bit for bit.  Slots at or above n_slots are not state."""
+    assert torch.equal(c0.n_slots, c1.n_slots)
+    n = c0.n_slots.cpu()
+    for b in range(c0.batch):
+        for h in range(c0.kv_heads):
+            m = int(n[b, h])
+            assert torch.equal(c0.pos[b, h, :m], c1.pos[b, h, :m])
+            k0, v0 = c0.rows(b, h, range(m))
+            k1, v1 = c1.rows(b, h, range(m))
+            assert torch.equal(k0, k1) and torch.equal(v0, v1)
+            if s0 is not None:
+                assert torch.equal(s0[b, h, :m], s1[b, h, :m])
+
+
+@pytest.mark.parametrize("cap", [160, 1100])
 @pytest.mark.parametrize("policy", ["h2o", "streaming", "random", "full"])
-def test_fused_step_equals_three_calls(policy):
+def test_fused_step_equals_three_calls(policy, cap):
     w = synth.workload("llama3_8b_h2o_b64", policy=policy, n_heavy=8, n_recent=40,
                        n_sink=4, pinned=50, n_keep=30) if policy != "h2o" else \
         synth.workload("llama3_8b_h2o_b64", n_heavy=8, n_recent=40)
-    lengths, cap = [120, 60, 49, 0], 160
+    lengths = [120, 60, 49, 0]
     caches = [make_cache(w, lengths, cap), make_cache(w, lengths, cap)]
     B = len(lengths)
     scs = [torch.zeros((B, w.kv_heads, cap), device="cuda") for _ in range(2)]
     outs = [torch.empty((B, w.q_heads, w.head_dim), device="cuda") for _ in range(2)]
     pol, _ = _policy_pair(w)
-    wss = [c.workspace(cap) for c in caches]
+    wss = [c.workspace(cap + 1) for c in caches]
     for t in range(1, 7):
         q, kn, vn = synth.batch_step_inputs(w, t, B)
         new_pos = torch.tensor([L + t - 1 for L in lengths], dtype=torch.int32, device="cuda")
         args = (new_pos, dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype))
         sc0 = scs[0] if policy == "h2o" else None
         sc1 = scs[1] if policy == "h2o" else None
-        kvc.decode_step(caches[0], pol, t, *args, outs[0], sc0, max_len_hint=cap,
+        kvc.decode_step(caches[0], pol, t, *args, outs[0], sc0, max_len_hint=cap + 1,
                         workspace=wss[0])
-        _three_calls(caches[1], w, pol, t, *args, outs[1], sc1, wss[1], cap)
+        _three_calls(caches[1], w, pol, t, *args, outs[1], sc1, wss[1], cap + 1)
         torch.cuda.synchronize()
         assert torch.equal(outs[0], outs[1])
-        assert torch.equal(caches[0].n_slots, caches[1].n_slots)
-        assert torch.equal(caches[0].pos, caches[1].pos)
-        assert torch.equal(caches[0].k, caches[1].k)
-        assert torch.equal(caches[0].v, caches[1].v)
-        if policy == "h2o":
-            n = caches[0].n_slots.cpu()
-            for b in range(B):
-                for h in range(w.kv_heads):
-                    m = int(n[b, h])
-                    assert torch.equal(scs[0][b, h, :m], scs[1][b, h, :m])
+        _live_equal(caches[0], caches[1], sc0, sc1)
 
 
 def test_paged_and_contiguous_give_identical_results():
@@ -238,7 +278,4 @@ def test_paged_and_contiguous_give_identical_results():
         kvc.decode_step(p, pol, t, *args, op, sp, max_len_hint=cap, workspace=p.workspace(cap))
         torch.cuda.synchronize()
         assert torch.equal(oa, op)
-        assert torch.equal(a.pos, p.pos) and torch.equal(a.n_slots, p.n_slots)
-        sta, _ = _state(a, sa, "bf16")
-        stp, _ = _state(p, sp, "bf16")
-        assert sta == stp
+        _live_equal(a, p, sa, sp)
