@@ -87,6 +87,24 @@ def cpu_baseline(w, n_cached: int, budget_s: float = 12.0):
     }
 
 
+def copy_probe(torch, mib: int, reps: int = 5):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counter readings calibrate the counters against exact byte counts."""
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_probe_bytes": n, "reps": reps, "ms_per_copy": ms,
+                      "copy_gbs_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +114,8 @@ def main():
     ap.add_argument("--policy", default="h2o", choices=["h2o", "streaming", "full"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -105,6 +125,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe_mb:
+        copy_probe(torch, args.copy_probe_mb)
+        return
 
     import compressed_decode_attention_amd as kvc
     import synth

@@ -40,6 +40,18 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kHD = 128;   // head_dim of the fast path
+#ifndef KVC_DK
+#define KVC_DK 3
+#endif
+#ifndef KVC_DV
+#define KVC_DV 8
+#endif
+constexpr int kDK = KVC_DK;   // K tiles (16 keys x 256 B) in flight per wave
+constexpr int kDV = KVC_DV;   // V groups (4 keys x 256 B) in flight per wave
+#ifndef KVC_WAVES_PER_EU
+#define KVC_WAVES_PER_EU 4
+#endif
+constexpr int kWavesPerEU = KVC_WAVES_PER_EU;   // 4 workgroups of 4 waves per CU
 
 struct FusedSmall {
     float m[kMaxGroup];
@@ -66,6 +78,45 @@ __device__ inline void load_k(u16x8_t (&kb)[4], const uint16_t *kp, int r) {
     for (int c4 = 0; c4 < 4; ++c4) kb[c4] = *reinterpret_cast<const u16x8_t *>(kp + 32 * c4 + 8 * r);
 }
 
+// Row (in head_dim units) of slot j in the fast path, without branches: a
+// block id outside the pool is redirected to block 0 and remembered in 'bad'
+// (reported once after the loops).  Paged block sizes are powers of two.
+template <bool PAGED>
+struct FastRows {
+    size_t ubase;          // contiguous: first row of the unit
+    const int32_t *bt;     // paged: block-table row of the sequence
+    int stride, hoff, shift, mask, nblk;
+
+    __device__ inline FastRows(const CacheDev &c, int b, int h) {
+        ubase = ((size_t)b * c.Hkv + h) * (size_t)c.cap;
+        bt = c.bt ? c.bt + (size_t)b * c.max_blocks : nullptr;
+        stride = c.Hkv * c.bs;
+        hoff = h * c.bs;
+        shift = PAGED ? __ffs(c.bs) - 1 : 0;
+        mask = c.bs - 1;
+        nblk = c.num_blocks;
+    }
+    __device__ inline size_t row(int j, bool &bad) const {
+        if constexpr (!PAGED) {
+            return ubase + (size_t)j;
+        } else {
+            int blk = bt[j >> shift];
+            const bool bb = (unsigned)blk >= (unsigned)nblk;
+            bad |= bb;
+            blk = bb ? 0 : blk;
+            return (size_t)blk * stride + hoff + (j & mask);
+        }
+    }
+};
+
+// Bytes of the per-wave K staging tiles, or of the selection keys and flags
+// that reuse them, whichever is larger.
+constexpr size_t kStageBytes = 16 * 256;   // 16 rows x 256 B per wave
+__host__ __device__ constexpr size_t stage_region_bytes(int tc) {
+    return (size_t)kFWaves * kStageBytes > (size_t)tc * 5 ? (size_t)kFWaves * kStageBytes
+                                                          : ((size_t)tc * 5 + 15) / 16 * 16;
+}
+
 // 64-bit ranking word: larger = better (kept first); unique inside a unit
 __device__ inline uint64_t rank_word(uint32_t primary, int32_t pos) {
     return ((uint64_t)primary << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
@@ -81,8 +132,13 @@ __device__ void fused_generic(const FusedArgs &fa, int u, unsigned char *smem) {
     compact_unit<uint16_t, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs fa) {
+template <int MODE, bool PAGED, int TC>
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
+void fused_kernel(FusedArgs fa) {
+    // most K tiles / V groups one wave handles: fixed trip counts let the
+    // loops unroll into straight-line code with exact load/wait pairing
+    constexpr int kNTW = (TC / 16 + kFWaves - 1) / kFWaves;
+    constexpr int kNGW = (TC / 4 + kFWaves - 1) / kFWaves;
     extern __shared__ __align__(16) unsigned char smem[];
     const AttnArgs &a = fa.attn;
     const CacheDev &c = a.c;
@@ -94,18 +150,22 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs fa) {
 
     const int n = load_count(c, u, tid == 0);
     const int T = n + 1;
-    if (T > fa.tcap || n >= c.cap) {
+    if (T > TC || n >= c.cap) {
         fused_generic<MODE>(fa, u, smem);
         return;
     }
 
-    const int LD = fa.ld, TC = fa.tcap;
+    constexpr int LD = TC + 4;
     float *lg = reinterpret_cast<float *>(smem);
     int32_t *pos_s = reinterpret_cast<int32_t *>(lg + G * LD);
     float *sc_s = reinterpret_cast<float *>(pos_s + TC);
-    uint32_t *key_s = reinterpret_cast<uint32_t *>(sc_s + TC);
+    // K staging (one 16-row tile per wave) while keys stream; the selection
+    // keys and flags reuse the same bytes afterwards
+    unsigned char *stage_all = reinterpret_cast<unsigned char *>(sc_s + TC);
+    unsigned char *stage = stage_all + w * kStageBytes;
+    uint32_t *key_s = reinterpret_cast<uint32_t *>(stage_all);
     uint8_t *flg_s = reinterpret_cast<uint8_t *>(key_s + TC);
-    FusedSmall &sm = *reinterpret_cast<FusedSmall *>(flg_s + TC);
+    FusedSmall &sm = *reinterpret_cast<FusedSmall *>(stage_all + stage_region_bytes(TC));
 
     const uint16_t *K = static_cast<const uint16_t *>(c.k);
     const uint16_t *V = static_cast<const uint16_t *>(c.v);
@@ -127,40 +187,69 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs fa) {
            col < G, r);
     const int ntiles = (T + 15) >> 4;
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    const FastRows<PAGED> rows(c, b, h);
+    bool bad = false;
+    // every tile index is loadable: slots at or past n read the new token's
+    // row, so the loads need no branch (the results are masked by j < T)
+    // K tile t = slots 16t .. 16t+15.  Loads are coalesced: instruction k of a
+    // lane reads 16 B (chunk 'col') of row 4k + r, so one wave instruction
+    // covers 4 whole rows.  The tile then goes through the wave's LDS staging
+    // buffer, chunk c of row q stored at slot c ^ q (conflict-free on both
+    // sides), and comes back in the MFMA B layout: key = col, 8 dims per
+    // 16-lane group.
+    auto krow = [&](int t, int k) -> const u16x8_t * {
+        const int j = 16 * t + 4 * k + r;
+        const size_t rr = rows.row(j < n ? j : 0, bad);
+        return reinterpret_cast<const u16x8_t *>(((j < n) ? K + rr * kHD : kn) + 8 * col);
+    };
     {
-        int t = w;
-        u16x8_t kb[4];
-        if (t < ntiles) {
-            const int j = 16 * t + col;
-            load_k(kb, (j < n) ? K + row_of(c, b, h, j) * kHD : kn, r);
-        }
-        while (t < ntiles) {
-            const int tn = t + kFWaves;
-            u16x8_t nb[4];
-            if (tn < ntiles) {
-                const int jn = 16 * tn + col;
-                load_k(nb, (jn < n) ? K + row_of(c, b, h, jn) * kHD : kn, r);
+        u16x8_t kb[kDK][4];
+#pragma unroll
+        for (int d = 0; d < kDK; ++d)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) kb[d][k] = *krow(w + kFWaves * d, k);
+#pragma unroll
+        for (int i = 0; i < kNTW; ++i) {
+            const int t = w + kFWaves * i;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int q = 4 * k + r;
+                *reinterpret_cast<u16x8_t *>(stage + q * 256 + ((col ^ q) << 4)) = kb[i % kDK][k];
             }
+            if (i + kDK < kNTW)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) kb[i % kDK][k] = *krow(t + kFWaves * kDK, k);
+            u16x8_t kop[4];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                kop[c4] = *reinterpret_cast<const u16x8_t *>(stage + col * 256 +
+                                                             (((4 * c4 + r) ^ col) << 4));
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kb[c4]),
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kop[c4]),
                                                               acc, 0, 0, 0);
             const int j = 16 * t + col;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int g = 4 * r + i;
-                const float z = (j < T) ? acc[i] * a.scale : -INFINITY;
-                if (g < G) lg[g * LD + j] = z;
-                mx[i] = fmaxf(mx[i], z);
+            for (int ii = 0; ii < 4; ++ii) {
+                const int g = 4 * r + ii;
+                const float z = (j < T) ? acc[ii] * a.scale : -INFINITY;
+                if (g < G && j < T) lg[g * LD + j] = z;
+                mx[ii] = fmaxf(mx[ii], z);
             }
-            if (tn < ntiles) {
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) kb[c4] = nb[c4];
-            }
-            t = tn;
         }
     }
+    // V rows do not depend on the softmax: start streaming them now
+    const int ngroups = (T + 3) >> 2;
+    auto vptr = [&](int q4) -> const u16x8_t * {
+        const int j = 4 * q4 + r;
+        const size_t rr = rows.row(j < n ? j : 0, bad);
+        return reinterpret_cast<const u16x8_t *>(((j < n) ? V + rr * kHD : vn) + 8 * col);
+    };
+    u16x8_t vb[kDV];
+#pragma unroll
+    for (int d = 0; d < kDV; ++d) vb[d] = *vptr(w + kFWaves * d);
+    (void)ngroups;
     // row maxima: 16-lane groups share a query head set, then across waves
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -220,33 +309,20 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs fa) {
     f32x4_t oacc[8];
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8) oacc[t8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-        const int ngroups = (T + 3) >> 2;
-        int q4 = w;
-        u16x8_t vv;
-        if (q4 < ngroups) {
-            const int j = 4 * q4 + r;
-            vv = *reinterpret_cast<const u16x8_t *>(((j < n) ? V + row_of(c, b, h, j) * kHD : vn) +
-                                                    8 * col);
-        }
-        while (q4 < ngroups) {
-            const int qn = q4 + kFWaves;
-            u16x8_t nv;
-            if (qn < ngroups) {
-                const int jn = 4 * qn + r;
-                nv = *reinterpret_cast<const u16x8_t *>(
-                    ((jn < n) ? V + row_of(c, b, h, jn) * kHD : vn) + 8 * col);
-            }
-            const int j = 4 * q4 + r;
-            const float p = (col < G && j < T) ? lg[col * LD + j] : 0.f;
 #pragma unroll
-            for (int t8 = 0; t8 < 8; ++t8)
-                oacc[t8] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, bf16_to_f32(vv[t8]), oacc[t8], 0,
-                                                                 0, 0);
-            if (qn < ngroups) vv = nv;
-            q4 = qn;
-        }
+    for (int i = 0; i < kNGW; ++i) {
+        const int q4 = w + kFWaves * i;
+        const int j = 4 * q4 + r;
+        // groups past the end carry p = 0 and read valid rows
+        const float p = (col < G && j < T) ? lg[col * LD + j] : 0.f;
+        const u16x8_t cur = vb[i % kDV];
+        if (i + kDV < kNGW) vb[i % kDV] = *vptr(q4 + kFWaves * kDV);
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8)
+            oacc[t8] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, bf16_to_f32(cur[t8]), oacc[t8], 0,
+                                                             0, 0);
     }
+    if (bad) raise_flag(c, KVC_FLAG_BAD_BLOCK);
     __syncthreads();   // every wave is done with the weights in lg
 
     // ---------------- output: sum the four waves' partial P.V, normalise
@@ -467,36 +543,52 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(FusedArgs fa) {
 
 size_t fused_smem_bytes(int G, int tcap) {
     const size_t ld = (size_t)tcap + 4;
-    size_t fast = (size_t)G * ld * 4 + (size_t)tcap * (4 + 4 + 4 + 1) + sizeof(FusedSmall) + 16;
+    size_t fast = (size_t)G * ld * 4 + (size_t)tcap * (4 + 4) + stage_region_bytes(tcap) +
+                  sizeof(FusedSmall) + 16;
     size_t gen = sizeof(AttnLds<kHD>);
     if (sizeof(SelLds<1>) > gen) gen = sizeof(SelLds<1>);
     if (sizeof(CompLds) > gen) gen = sizeof(CompLds);
     return fast > gen ? fast : gen;
 }
 
-static hipError_t allow_large_lds() {
-    static hipError_t once = [] {
-        const int most = (int)fused_smem_bytes(kMaxGroup, kFusedMaxT);
-        hipError_t e = hipFuncSetAttribute((const void *)fused_kernel<kModeAttn>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, most);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)fused_kernel<kModeStep>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, most);
+template <int TC>
+static hipError_t launch_tc(const FusedArgs &fa, int mode, size_t smem, hipStream_t s) {
+    const int units = fa.attn.c.B * fa.attn.c.Hkv;
+    const bool paged = fa.attn.c.bs > 0;
+    static hipError_t attr = [smem] {
+        (void)smem;
+        const int most = (int)fused_smem_bytes(kMaxGroup, TC);
+        const void *fns[4] = {(const void *)fused_kernel<kModeAttn, false, TC>,
+                              (const void *)fused_kernel<kModeStep, false, TC>,
+                              (const void *)fused_kernel<kModeAttn, true, TC>,
+                              (const void *)fused_kernel<kModeStep, true, TC>};
+        hipError_t e = hipSuccess;
+        for (const void *f : fns)
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, most);
         return e;
     }();
-    return once;
+    if (attr != hipSuccess) return attr;
+    if (mode == kModeAttn && !paged)
+        hipLaunchKernelGGL((fused_kernel<kModeAttn, false, TC>), dim3(units), dim3(kFThreads), smem,
+                           s, fa);
+    else if (mode == kModeAttn)
+        hipLaunchKernelGGL((fused_kernel<kModeAttn, true, TC>), dim3(units), dim3(kFThreads), smem,
+                           s, fa);
+    else if (!paged)
+        hipLaunchKernelGGL((fused_kernel<kModeStep, false, TC>), dim3(units), dim3(kFThreads), smem,
+                           s, fa);
+    else
+        hipLaunchKernelGGL((fused_kernel<kModeStep, true, TC>), dim3(units), dim3(kFThreads), smem,
+                           s, fa);
+    return hipGetLastError();
 }
 
 hipError_t launch_fused(const FusedArgs &fa, int mode, hipStream_t s) {
-    const hipError_t e = allow_large_lds();
-    if (e != hipSuccess) return e;
-    const int units = fa.attn.c.B * fa.attn.c.Hkv;
     const size_t smem = fused_smem_bytes(fa.attn.c.G, fa.tcap);
-    if (mode == kModeAttn)
-        hipLaunchKernelGGL((fused_kernel<kModeAttn>), dim3(units), dim3(kFThreads), smem, s, fa);
-    else
-        hipLaunchKernelGGL((fused_kernel<kModeStep>), dim3(units), dim3(kFThreads), smem, s, fa);
-    return hipGetLastError();
+    if (fa.tcap == kFusedSmallT) return launch_tc<kFusedSmallT>(fa, mode, smem, s);
+    if (fa.tcap == kFusedMaxT) return launch_tc<kFusedMaxT>(fa, mode, smem, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kvc

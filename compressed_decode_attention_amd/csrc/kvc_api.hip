@@ -95,7 +95,9 @@ int effective_len(const kvc_cache *c, int hint) {
 }
 
 bool use_fused(const kvc_cache *c, int hint) {
-    return c->dtype == KVC_BF16 && c->head_dim == 128 && effective_len(c, hint) <= kvc::kFusedMaxT;
+    const bool pow2_blocks = c->block_size == 0 || (c->block_size & (c->block_size - 1)) == 0;
+    return c->dtype == KVC_BF16 && c->head_dim == 128 && pow2_blocks &&
+           effective_len(c, hint) <= kvc::kFusedMaxT;
 }
 
 struct Workspace {
@@ -193,10 +195,7 @@ kvc::FusedArgs fused_args(const kvc_cache *c, const kvc::AttnArgs &a, int hint) 
     fa.attn = a;
     fa.attn.nsplit = 1;
     fa.attn.part = nullptr;
-    int tcap = (effective_len(c, hint) + 63) / 64 * 64;
-    if (tcap < 512) tcap = 512;
-    fa.tcap = tcap;
-    fa.ld = tcap + 4;
+    fa.tcap = effective_len(c, hint) <= kvc::kFusedSmallT ? kvc::kFusedSmallT : kvc::kFusedMaxT;
     fa.sel = kvc::SelectArgs();
     fa.comp = kvc::CompactArgs();
     return fa;

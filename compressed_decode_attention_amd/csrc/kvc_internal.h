@@ -219,13 +219,13 @@ hipError_t launch_compact(const CompactArgs &a, int dtype, hipStream_t s);
 // (decode_attn) or the whole step (decode_step)
 enum { kModeAttn = 0, kModeStep = 1 };
 constexpr int kFusedMaxT = 1024;   // largest attended length of the LDS fast path
+constexpr int kFusedSmallT = 576;  // LDS capacity used up to 576 (a 512 budget + 1)
 
 struct FusedArgs {
     AttnArgs attn;      // nsplit must be 1; logits = global scratch of the fallback
     SelectArgs sel;     // step mode: policy, keep_slots / n_out scratch
     CompactArgs comp;   // step mode: in-place compaction of the fallback
-    int tcap;           // attended entries held in LDS (multiple of 64, >= 512)
-    int ld;             // LDS row stride of the logits (tcap + 4)
+    int tcap;           // attended entries held in LDS: kFusedSmallT or kFusedMaxT
 };
 size_t fused_smem_bytes(int G, int tcap);
 hipError_t launch_fused(const FusedArgs &fa, int mode, hipStream_t s);
