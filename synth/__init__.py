@@ -192,3 +192,29 @@ def block_permutation(n_blocks: int, *parts: int) -> np.ndarray:
 def workload(name: str, **overrides) -> Workload:
     """A registered workload, optionally with fields replaced (smaller test cases)."""
     return dataclasses.replace(WORKLOADS[name], **overrides)
+
+
+# ----------------------------------------------------------------------------
+# device-side draws for full-size workloads (torch's own generator, seeded from
+# the same SeedSequence parts); the numbers differ from the numpy streams but
+# follow the same recipe: N(0,1) float32 rounded to bf16 (round to nearest even)
+# ----------------------------------------------------------------------------
+
+def device_seed(*parts: int) -> int:
+    return int(np.random.SeedSequence([int(p) for p in parts]).generate_state(1, np.uint64)[0]
+               & np.uint64(0x7FFFFFFFFFFFFFFF))
+
+
+def device_normal(shape, *parts: int, device="cuda", dtype=None, scale_rows_frac: float = 0.0,
+                  scale: float = 8.0):
+    """N(0,1) draws on the device, rounded to `dtype` (bf16 by default); with
+    scale_rows_frac > 0 a Bernoulli fraction of the rows (last axis) is scaled."""
+    import torch
+    dtype = torch.bfloat16 if dtype is None else dtype
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(*parts))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if scale_rows_frac > 0.0:
+        m = torch.rand(shape[:-1], generator=g, device=device) < scale_rows_frac
+        x = torch.where(m[..., None], x * scale, x)
+    return x.to(dtype)
