@@ -54,11 +54,15 @@ constexpr int kDV = KVC_DV;   // V groups (4 keys x 256 B) in flight per wave
 constexpr int kWavesPerEU = KVC_WAVES_PER_EU;   // 4 workgroups of 4 waves per CU
 
 struct FusedSmall {
-    float m[kMaxGroup];
-    float l[kMaxGroup];
+    float m[kMaxGroup];      // row maxima of the logits
+    float l[kMaxGroup];      // softmax normalisers
+    float il[kMaxGroup];     // 1 / l
     float wred[kFWaves][kMaxGroup];
     int hist[256];
     int red[kFWaves * 2];
+    int pmax[kFWaves];       // newest position seen by each wave
+    int posmax;
+    int r_nc[kFWaves], r_nd[kFWaves], r_ds[kFWaves], r_arg[kFWaves];
     uint32_t mn_hi[kFWaves], mn_lo[kFWaves];
     int sh[8];
 };
@@ -176,8 +180,11 @@ void fused_kernel(FusedArgs fa) {
     const bool h2o = S != nullptr;
     const int32_t npos = a.new_pos[b];
 
+    int pmax = -1;
     for (int j = tid; j < T; j += kFThreads) {
-        pos_s[j] = (j < n) ? P[j] : npos;
+        const int32_t pj = (j < n) ? P[j] : npos;
+        pos_s[j] = pj;
+        pmax = max(pmax, pj);
         sc_s[j] = (h2o && j < n) ? S[j] : 0.f;
     }
 
@@ -250,7 +257,8 @@ void fused_kernel(FusedArgs fa) {
 #pragma unroll
     for (int d = 0; d < kDV; ++d) vb[d] = *vptr(w + kFWaves * d);
     (void)ngroups;
-    // row maxima: 16-lane groups share a query head set, then across waves
+    // row maxima (16-lane groups share a query head set, then across waves),
+    // and the newest position of the unit
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float m = mx[i];
@@ -260,61 +268,40 @@ void fused_kernel(FusedArgs fa) {
         m = fmaxf(m, __shfl_xor(m, 1, 64));
         if (col == 0 && 4 * r + i < G) sm.wred[w][4 * r + i] = m;
     }
+    pmax = wave_max_i(pmax);
+    if (lane == 0) sm.pmax[w] = pmax;
     __syncthreads();
     if (tid < G) {
         float m = sm.wred[0][tid];
         for (int v = 1; v < kFWaves; ++v) m = fmaxf(m, sm.wred[v][tid]);
         sm.m[tid] = m;
     }
-    __syncthreads();
-
-    // ---------------- exact softmax weights w = exp(z - m) and row sums l
-    {
-        float ls[kMaxGroup];
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g) ls[g] = 0.f;
-        for (int j = tid; j < T; j += kFThreads) {
-#pragma unroll
-            for (int g = 0; g < kMaxGroup; ++g)
-                if (g < G) {
-                    const float e = __expf(lg[g * LD + j] - sm.m[g]);
-                    lg[g * LD + j] = e;
-                    ls[g] += e;
-                }
-        }
-#pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g) {
-            const float v = wave_sum(ls[g]);
-            if (lane == 0 && g < G) sm.wred[w][g] = v;
-        }
-    }
-    __syncthreads();
-    if (tid < G) {
-        float l = 0.f;
-        for (int v = 0; v < kFWaves; ++v) l += sm.wred[v][tid];
-        sm.l[tid] = l;
+    if (tid == 64) {
+        int pm = sm.pmax[0];
+        for (int v = 1; v < kFWaves; ++v) pm = max(pm, sm.pmax[v]);
+        sm.posmax = pm;
     }
     __syncthreads();
 
-    // ---------------- H2O: accumulated attention with the final normaliser
-    if (h2o) {
-        for (int j = tid; j < T; j += kFThreads) {
-            float ps = 0.f;
-            for (int g = 0; g < G; ++g) ps += lg[g * LD + j] / sm.l[g];
-            sc_s[j] = (j < n) ? sc_s[j] + ps : ps;
-        }
-    }
-
-    // ---------------- P.V: MFMA 16x16x4 f32, A = probabilities, B = 4 V rows
+    // ---------------- P.V: MFMA 16x16x4 f32, A = probabilities, B = 4 V rows.
+    // The lane that feeds weight (g = col, key j) to the MFMA computes it:
+    // w = exp(z - m_g), stored back for the H2O update, summed for l_g.
     f32x4_t oacc[8];
 #pragma unroll
     for (int t8 = 0; t8 < 8; ++t8) oacc[t8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    const float mcol = (col < G) ? sm.m[col] : 0.f;
 #pragma unroll
     for (int i = 0; i < kNGW; ++i) {
         const int q4 = w + kFWaves * i;
         const int j = 4 * q4 + r;
         // groups past the end carry p = 0 and read valid rows
-        const float p = (col < G && j < T) ? lg[col * LD + j] : 0.f;
+        float p = 0.f;
+        if (col < G && j < T) {
+            p = __expf(lg[col * LD + j] - mcol);
+            lg[col * LD + j] = p;
+        }
+        lsum += p;
         const u16x8_t cur = vb[i % kDV];
         if (i + kDV < kNGW) vb[i % kDV] = *vptr(q4 + kFWaves * kDV);
 #pragma unroll
@@ -323,11 +310,35 @@ void fused_kernel(FusedArgs fa) {
                                                              0, 0);
     }
     if (bad) raise_flag(c, KVC_FLAG_BAD_BLOCK);
-    __syncthreads();   // every wave is done with the weights in lg
+    // lanes col, col+16, col+32, col+48 hold partial sums of query head col
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (lane < G) sm.wred[w][lane] = lsum;
+    __syncthreads();   // weights in lg are final, partial row sums written
+    if (tid < G) {
+        float l = 0.f;
+        for (int v = 0; v < kFWaves; ++v) l += sm.wred[v][tid];
+        sm.l[tid] = l;
+        sm.il[tid] = 1.f / l;
+    }
+    __syncthreads();
 
-    // ---------------- output: sum the four waves' partial P.V, normalise
+    // ---------------- H2O: accumulated attention with the final normaliser
+    if (h2o) {
+        for (int j = tid; j < T; j += kFThreads) {
+            float ps = 0.f;
+            for (int g = 0; g < G; ++g) ps += lg[g * LD + j] * sm.il[g];
+            sc_s[j] = (j < n) ? sc_s[j] + ps : ps;
+        }
+    }
+
+    // ---------------- output: sum the four waves' partial P.V, normalise.
+    // The partials go to the staging bytes when they fit (G <= 8), else to
+    // the weights' bytes once the H2O pass is done with them.
     {
-        float *opart = lg;   // [kFWaves][G][128], fits: LD >= 512 + 4
+        const bool in_stage = G * kHD * kFWaves * 4 <= (int)(kFWaves * kStageBytes);
+        float *opart = in_stage ? reinterpret_cast<float *>(stage_all) : lg;
+        if (!in_stage) __syncthreads();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int g = 4 * r + i;
@@ -367,13 +378,13 @@ void fused_kernel(FusedArgs fa) {
     }
 
     // ================= selection on the LDS copies =================
+    // One pass classifies every entry, draws the candidates' ranking keys and
+    // finds the worst candidate (smallest ranking word) and a dropped entry.
     const SelectArgs &sa = fa.sel;
-    __syncthreads();
-    int mxp = -1;
-    for (int j = tid; j < T; j += kFThreads) mxp = max(mxp, pos_s[j]);
-    const int L = block_max_i(mxp, sm.red) + 1;
-
-    int ncand = 0;
+    __syncthreads();   // the output pass is done with the staging bytes
+    const int L = sm.posmax + 1;
+    int ncand = 0, ndrop = 0, dslot = -1, barg = -1;
+    uint64_t best = ~0ull;
     for (int j = tid; j < T; j += kFThreads) {
         const int32_t p = pos_s[j];
         uint8_t k = kKeep;
@@ -384,67 +395,94 @@ void fused_kernel(FusedArgs fa) {
         else if (sa.kind == KVC_POLICY_RANDOM)
             k = (p < sa.prompt_len) ? kKeep : kCand;
         if (k == kCand) {
-            key_s[j] = (sa.kind == KVC_POLICY_H2O)
-                           ? float_order_bits(sc_s[j])
-                           : ~philox_word0((uint32_t)p, sa.step, (uint32_t)h, (uint32_t)b,
-                                           (uint32_t)(sa.seed & 0xFFFFFFFFu),
-                                           (uint32_t)(sa.seed >> 32));
+            const uint32_t key = (sa.kind == KVC_POLICY_H2O)
+                                     ? float_order_bits(sc_s[j])
+                                     : ~philox_word0((uint32_t)p, sa.step, (uint32_t)h, (uint32_t)b,
+                                                     (uint32_t)(sa.seed & 0xFFFFFFFFu),
+                                                     (uint32_t)(sa.seed >> 32));
+            key_s[j] = key;
             ++ncand;
+            const uint64_t wd = rank_word(key, p);
+            if (wd < best) {
+                best = wd;
+                barg = j;
+            }
+        } else if (k == kDrop) {
+            ++ndrop;
+            dslot = max(dslot, j);
         }
         flg_s[j] = k;
     }
-    int tot;
-    (void)block_excl_scan(ncand, sm.red, &tot);
-    ncand = tot;
+    ncand = wave_sum_i(ncand);
+    ndrop = wave_sum_i(ndrop);
+    dslot = wave_max_i(dslot);
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
+        const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
+        const int oa = __shfl_xor(barg, o, 64);
+        const uint64_t ob = ((uint64_t)hi << 32) | lo;
+        if (ob < best) {
+            best = ob;
+            barg = oa;
+        }
+    }
+    if (lane == 0) {
+        sm.r_nc[w] = ncand;
+        sm.r_nd[w] = ndrop;
+        sm.r_ds[w] = dslot;
+        sm.r_arg[w] = barg;
+        sm.mn_hi[w] = (uint32_t)(best >> 32);
+        sm.mn_lo[w] = (uint32_t)best;
+    }
+    __syncthreads();
+    ncand = 0;
+    ndrop = 0;
+    dslot = -1;
+    barg = -1;
+    best = ~0ull;
+    for (int v = 0; v < kFWaves; ++v) {
+        ncand += sm.r_nc[v];
+        ndrop += sm.r_nd[v];
+        dslot = max(dslot, sm.r_ds[v]);
+        const uint64_t ob = ((uint64_t)sm.mn_hi[v] << 32) | sm.mn_lo[v];
+        if (sm.r_arg[v] >= 0 && ob < best) {
+            best = ob;
+            barg = sm.r_arg[v];
+        }
+    }
     const int want = (sa.kind == KVC_POLICY_H2O) ? sa.n_heavy : sa.n_keep;
-    if (ncand > want) {
+    const int extra = (ncand > want) ? (want <= 0 ? ncand : ncand - want) : 0;
+
+    if (ndrop + extra <= 1) {
+        // ---- at most one eviction (the steady state): no scans.  With one
+        // evicted slot e, n_out = n and the new token fills e when e < n
+        // (the hole-fill pairing of a single hole with source slot n).
+        const int e = (extra == 1) ? barg : (ndrop == 1 ? dslot : -1);
+        const int n_out = (e < 0) ? T : n;
+        const int dst_new = (e < 0) ? n : (e < n ? e : -1);
+        if (dst_new >= 0 && tid < 16) {
+            const size_t rw = row_of(c, b, h, dst_new) * kHD;
+            reinterpret_cast<uint4 *>(Kw + rw)[tid] = reinterpret_cast<const uint4 *>(kn)[tid];
+            reinterpret_cast<uint4 *>(Vw + rw)[tid] = reinterpret_cast<const uint4 *>(vn)[tid];
+        }
+        if (h2o)
+            for (int j = tid; j < n; j += kFThreads)
+                if (j != e) S[j] = sc_s[j];
+        if (tid == 0) {
+            if (dst_new >= 0) {
+                P[dst_new] = npos;
+                if (h2o) S[dst_new] = sc_s[n];
+            }
+            c.n_slots[u] = n_out;
+        }
+        return;
+    }
+
+    // ---- general case: finish the candidates' flags, then hole-fill
+    if (extra > 0) {
         if (want <= 0) {
             for (int j = tid; j < T; j += kFThreads)
                 if (flg_s[j] == kCand) flg_s[j] = kDrop;
-        } else if (ncand - want == 1) {
-            // exactly one eviction: the candidate with the smallest ranking word
-            uint64_t best = ~0ull;
-            int arg = -1;
-            for (int j = tid; j < T; j += kFThreads)
-                if (flg_s[j] == kCand) {
-                    const uint64_t wd = rank_word(key_s[j], pos_s[j]);
-                    if (wd < best) {
-                        best = wd;
-                        arg = j;
-                    }
-                }
-            for (int o = 32; o > 0; o >>= 1) {
-                const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
-                const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
-                const int oa = __shfl_xor(arg, o, 64);
-                const uint64_t ob = ((uint64_t)hi << 32) | lo;
-                if (ob < best) {
-                    best = ob;
-                    arg = oa;
-                }
-            }
-            if (lane == 0) {
-                sm.mn_hi[w] = (uint32_t)(best >> 32);
-                sm.mn_lo[w] = (uint32_t)best;
-                sm.sh[w] = arg;
-            }
-            __syncthreads();
-            if (tid == 0) {
-                uint64_t bb = ~0ull;
-                int aa = -1;
-                for (int v = 0; v < kFWaves; ++v) {
-                    const uint64_t ob = ((uint64_t)sm.mn_hi[v] << 32) | sm.mn_lo[v];
-                    if (sm.sh[v] >= 0 && ob < bb) {
-                        bb = ob;
-                        aa = sm.sh[v];
-                    }
-                }
-                sm.sh[kFWaves] = aa;
-            }
-            __syncthreads();
-            const int ev = sm.sh[kFWaves];
-            for (int j = tid; j < T; j += kFThreads)
-                if (flg_s[j] == kCand) flg_s[j] = (j == ev) ? kDrop : kKeep;
         } else {
             // radix select of the 'want' largest ranking words among candidates
             uint64_t prefix = 0, mask = 0;
@@ -493,6 +531,7 @@ void fused_kernel(FusedArgs fa) {
     // n_out kept; holes = dropped slots below n_out, sources = kept slots at or
     // above n_out (slot n is the new token), paired in ascending order.
     int kc = 0;
+    int tot;
     for (int j = tid; j < T; j += kFThreads) kc += (flg_s[j] == kKeep);
     (void)block_excl_scan(kc, sm.red, &tot);
     const int n_out = tot;

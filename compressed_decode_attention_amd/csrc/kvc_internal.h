@@ -219,7 +219,10 @@ hipError_t launch_compact(const CompactArgs &a, int dtype, hipStream_t s);
 // (decode_attn) or the whole step (decode_step)
 enum { kModeAttn = 0, kModeStep = 1 };
 constexpr int kFusedMaxT = 1024;   // largest attended length of the LDS fast path
-constexpr int kFusedSmallT = 576;  // LDS capacity used up to 576 (a 512 budget + 1)
+#ifndef KVC_FUSED_SMALL_T
+#define KVC_FUSED_SMALL_T 528
+#endif
+constexpr int kFusedSmallT = KVC_FUSED_SMALL_T;  // LDS capacity used up to a 512 budget + 1
 
 struct FusedArgs {
     AttnArgs attn;      // nsplit must be 1; logits = global scratch of the fallback
