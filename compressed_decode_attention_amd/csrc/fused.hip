@@ -12,15 +12,21 @@
 // Layout of the work (bf16 K/V, head_dim 128, G <= 16 query heads):
 //  * QK^T runs as v_mfma_f32_16x16x32_bf16 with the group's queries as the A
 //    operand (rows = query heads, padded to 16) and 16 keys as the B operand:
-//    every lane loads 16 contiguous bytes of one key row straight from HBM
-//    into its operand registers; bf16 x bf16 products are exact in fp32.
+//    K rows are loaded coalesced (4 rows x 256 B per wave instruction) and
+//    turned into the B layout through a small swizzled LDS tile per wave;
+//    bf16 x bf16 products are exact in fp32.
 //  * the logits of the whole unit stay in LDS ([G][n+1] fp32), so the softmax
 //    is exact (no online rescaling) and the H2O update uses the final
 //    normaliser without a second pass over K.
-//  * P.V runs as v_mfma_f32_16x16x4_f32 with fp32 probabilities (no bf16
-//    rounding of P): each lane loads 16 contiguous bytes of a V row (4 rows x
-//    256 B per wave instruction, fully coalesced) and feeds its 8 values to 8
-//    MFMAs whose output columns are dims 8c+t.
+//  * P.V runs as v_mfma_f32_16x16x16_bf16 over 16-key tiles.  V rows are
+//    loaded coalesced (4 rows x 256 B per wave instruction): lane (r, c)
+//    holds dims 8c..8c+7 of keys 4e + r, e = 0..3.  Taking MFMA k-index 4r + e
+//    as key 4e + r and output column c of MFMA m as dim 8c + m, the B operand
+//    of MFMA m is element m of the lane's four rows: a repack in registers.
+//    P enters as a bf16 pair: rows 0..7 carry bf16(p), rows 8..15 the bf16
+//    rounding of the remainder (G <= 8; two MFMAs per tile above that), so
+//    their sum carries p to about 2^-17 relative and every product is exact
+//    in the fp32 accumulator.
 //  * selection runs on the LDS copies of pos / scores / random keys; the
 //    common steady-state case (exactly one eviction) is an arg-min, the
 //    general case an 8-bit radix select over 64-bit (key, position) words.
@@ -36,6 +42,7 @@ namespace kvc {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
@@ -44,10 +51,10 @@ constexpr int kHD = 128;   // head_dim of the fast path
 #define KVC_DK 3
 #endif
 #ifndef KVC_DV
-#define KVC_DV 8
+#define KVC_DV 2
 #endif
 constexpr int kDK = KVC_DK;   // K tiles (16 keys x 256 B) in flight per wave
-constexpr int kDV = KVC_DV;   // V groups (4 keys x 256 B) in flight per wave
+constexpr int kDV = KVC_DV;   // V tiles (16 keys x 256 B) in flight per wave
 #ifndef KVC_WAVES_PER_EU
 #define KVC_WAVES_PER_EU 4
 #endif
@@ -65,9 +72,20 @@ struct FusedSmall {
     int r_nc[kFWaves], r_nd[kFWaves], r_ds[kFWaves], r_arg[kFWaves];
     uint32_t mn_hi[kFWaves], mn_lo[kFWaves];
     int sh[8];
+    int blk[kFusedMaxT / 16 + 1];   // paged: block ids of the attended slots
+    u16x8_t knew[kHD / 8];          // the new token's key row
 };
 
 __device__ inline bf16x8_t as_bf16x8(u16x8_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+// LDS column of key j in a logit row. Inside each 16-key tile, key 4e + r sits
+// at column 4r + e, so that the four probabilities one lane feeds to the P.V
+// MFMA (keys r, r+4, r+8, r+12 of the tile) are contiguous.
+__device__ inline int lg_col(int j) { return (j & ~15) | ((j & 3) << 2) | ((j >> 2) & 3); }
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ inline short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
+__device__ inline float bf16_value(short b) { return __uint_as_float((uint32_t)(uint16_t)b << 16); }
 
 __device__ inline void load_q(u16x8_t (&qa)[4], const uint16_t *qp, bool valid, int r) {
 #pragma unroll
@@ -82,33 +100,54 @@ __device__ inline void load_k(u16x8_t (&kb)[4], const uint16_t *kp, int r) {
     for (int c4 = 0; c4 < 4; ++c4) kb[c4] = *reinterpret_cast<const u16x8_t *>(kp + 32 * c4 + 8 * r);
 }
 
-// Row (in head_dim units) of slot j in the fast path, without branches: a
-// block id outside the pool is redirected to block 0 and remembered in 'bad'
-// (reported once after the loops).  Paged block sizes are powers of two.
-template <bool PAGED>
-struct FastRows {
-    size_t ubase;          // contiguous: first row of the unit
-    const int32_t *bt;     // paged: block-table row of the sequence
-    int stride, hoff, shift, mask, nblk;
+// Where the fast path reads K and V: buffer resources whose range ends at the
+// unit's n-th row, so that rows at or past n (the new token's slot and the
+// padding of the last tile) read as zeros, with no branch and no clamp, and
+// every load address is one per-lane offset plus an immediate.  Contiguous
+// caches take one resource per unit; paged caches one per 16-slot tile (block
+// sizes are powers of two of at least 16, so a tile never straddles a block).
+constexpr int kRsrcWord3 = 0x00020000;   // buffer resource dword 3 on gfx9-family parts
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+__device__ inline u16x8_t buffer_row(__amdgpu_buffer_rsrc_t rs, int voff) {
+    return __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+}
 
-    __device__ inline FastRows(const CacheDev &c, int b, int h) {
-        ubase = ((size_t)b * c.Hkv + h) * (size_t)c.cap;
-        bt = c.bt ? c.bt + (size_t)b * c.max_blocks : nullptr;
-        stride = c.Hkv * c.bs;
-        hoff = h * c.bs;
+template <bool PAGED>
+struct TileSrc {
+    const unsigned char *k0, *v0;   // contiguous: the unit's slot 0; paged: pool + head offset
+    const int *blk_s;               // paged: the sequence's block ids, staged in LDS
+    uint32_t nbytes;                // contiguous: the unit's n rows
+    uint32_t blk_bytes;             // paged: bytes of one block (all kv heads)
+    int n, shift, mask;
+
+    __device__ inline TileSrc(const CacheDev &c, int b, int h, int n_, const int *blk) {
+        n = n_;
+        blk_s = blk;
         shift = PAGED ? __ffs(c.bs) - 1 : 0;
-        mask = c.bs - 1;
-        nblk = c.num_blocks;
+        mask = PAGED ? c.bs - 1 : 0;
+        const size_t first = PAGED ? (size_t)h * c.bs : ((size_t)b * c.Hkv + h) * (size_t)c.cap;
+        k0 = static_cast<const unsigned char *>(c.k) + first * (2 * kHD);
+        v0 = static_cast<const unsigned char *>(c.v) + first * (2 * kHD);
+        nbytes = (uint32_t)n * (2 * kHD);
+        blk_bytes = PAGED ? (uint32_t)(c.Hkv * c.bs * 2 * kHD) : 0u;
     }
-    __device__ inline size_t row(int j, bool &bad) const {
+    // resource holding tile t (K or V) and the tile's byte offset inside it
+    __device__ inline void tile(int t, bool v, __amdgpu_buffer_rsrc_t &rs, int &toff) const {
         if constexpr (!PAGED) {
-            return ubase + (size_t)j;
+            rs = make_rsrc(v ? v0 : k0, nbytes);
+            toff = 16 * 2 * kHD * t;
         } else {
-            int blk = bt[j >> shift];
-            const bool bb = (unsigned)blk >= (unsigned)nblk;
-            bad |= bb;
-            blk = bb ? 0 : blk;
-            return (size_t)blk * stride + hoff + (j & mask);
+            const int j0 = 16 * t;
+            const int rows = min(max(n - j0, 0), 16);
+            const int last = n > 0 ? n - 1 : 0;
+            int blk = __builtin_amdgcn_readfirstlane(blk_s[(j0 < last ? j0 : last) >> shift]);
+            blk = rows > 0 ? blk : 0;
+            const size_t off = (size_t)blk * blk_bytes + (size_t)(j0 & mask) * (2 * kHD);
+            rs = make_rsrc((v ? v0 : k0) + off, (uint32_t)rows * (2 * kHD));
+            toff = 0;
         }
     }
 };
@@ -136,23 +175,25 @@ __device__ void fused_generic(const FusedArgs &fa, int u, unsigned char *smem) {
     compact_unit<uint16_t, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
 }
 
-template <int MODE, bool PAGED, int TC>
+// PACK2: G <= 8, so one P.V MFMA carries both bf16 parts of p (rows 0..7 and
+// 8..15); otherwise each tile takes two MFMAs per dim block.
+template <int MODE, bool PAGED, int TC, bool PACK2>
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void fused_kernel(FusedArgs fa) {
     // most K tiles / V groups one wave handles: fixed trip counts let the
     // loops unroll into straight-line code with exact load/wait pairing
     constexpr int kNTW = (TC / 16 + kFWaves - 1) / kFWaves;
-    constexpr int kNGW = (TC / 4 + kFWaves - 1) / kFWaves;
     extern __shared__ __align__(16) unsigned char smem[];
     const AttnArgs &a = fa.attn;
     const CacheDev &c = a.c;
     const int u = blockIdx.x;
     const int b = u / c.Hkv, h = u % c.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane >> 4, col = lane & 15;
     const int G = c.G;
 
-    const int n = load_count(c, u, tid == 0);
+    const int n = __builtin_amdgcn_readfirstlane(load_count(c, u, tid == 0));
     const int T = n + 1;
     if (T > TC || n >= c.cap) {
         fused_generic<MODE>(fa, u, smem);
@@ -187,6 +228,22 @@ void fused_kernel(FusedArgs fa) {
         pmax = max(pmax, pj);
         sc_s[j] = (h2o && j < n) ? S[j] : 0.f;
     }
+    if (tid < kHD / 8) sm.knew[tid] = reinterpret_cast<const u16x8_t *>(kn)[tid];
+    if constexpr (PAGED) {
+        // the sequence's block ids, checked once; an id outside the pool is
+        // reported and replaced by block 0
+        const int nb = (n + c.bs - 1) / c.bs;
+        const int32_t *bt = c.bt + (size_t)b * c.max_blocks;
+        for (int i = tid; i < nb; i += kFThreads) {
+            int blk = bt[i];
+            if ((unsigned)blk >= (unsigned)c.num_blocks) {
+                raise_flag(c, KVC_FLAG_BAD_BLOCK);
+                blk = 0;
+            }
+            sm.blk[i] = blk;
+        }
+        __syncthreads();
+    }
 
     // ---------------- logits: MFMA 16x16x32 bf16, A = queries, B = 16 keys
     u16x8_t qa[4];
@@ -194,27 +251,29 @@ void fused_kernel(FusedArgs fa) {
            col < G, r);
     const int ntiles = (T + 15) >> 4;
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    const FastRows<PAGED> rows(c, b, h);
-    bool bad = false;
-    // every tile index is loadable: slots at or past n read the new token's
-    // row, so the loads need no branch (the results are masked by j < T)
+    const TileSrc<PAGED> src(c, b, h, n, sm.blk);
     // K tile t = slots 16t .. 16t+15.  Loads are coalesced: instruction k of a
     // lane reads 16 B (chunk 'col') of row 4k + r, so one wave instruction
-    // covers 4 whole rows.  The tile then goes through the wave's LDS staging
-    // buffer, chunk c of row q stored at slot c ^ q (conflict-free on both
-    // sides), and comes back in the MFMA B layout: key = col, 8 dims per
-    // 16-lane group.
-    auto krow = [&](int t, int k) -> const u16x8_t * {
-        const int j = 16 * t + 4 * k + r;
-        const size_t rr = rows.row(j < n ? j : 0, bad);
-        return reinterpret_cast<const u16x8_t *>(((j < n) ? K + rr * kHD : kn) + 8 * col);
+    // covers 4 whole rows; rows at or past n come back as zeros, and the lane
+    // that holds row n takes the new token's chunk instead.  The tile then goes
+    // through the wave's LDS staging buffer, chunk c of row q stored at slot
+    // c ^ q (conflict-free on both sides), and comes back in the MFMA B
+    // layout: key = col, 8 dims per 16-lane group.
+    const int lane_off = r * (2 * kHD) + 16 * col;
+    auto kload = [&](int t, int k) -> u16x8_t {
+        __amdgpu_buffer_rsrc_t rs;
+        int toff;
+        src.tile(t, false, rs, toff);
+        return buffer_row(rs, lane_off + toff + 4 * (2 * kHD) * k);
     };
+    const int tn = n >> 4, qn = n & 15;   // tile and row of the new token
+    __syncthreads();                      // the new key row is in LDS
     {
         u16x8_t kb[kDK][4];
 #pragma unroll
         for (int d = 0; d < kDK; ++d)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) kb[d][k] = *krow(w + kFWaves * d, k);
+            for (int k = 0; k < 4; ++k) kb[d][k] = kload(w + kFWaves * d, k);
 #pragma unroll
         for (int i = 0; i < kNTW; ++i) {
             const int t = w + kFWaves * i;
@@ -223,9 +282,11 @@ void fused_kernel(FusedArgs fa) {
                 const int q = 4 * k + r;
                 *reinterpret_cast<u16x8_t *>(stage + q * 256 + ((col ^ q) << 4)) = kb[i % kDK][k];
             }
+            if (t == tn && lane < 16)   // row n read as zeros: put the new key there
+                *reinterpret_cast<u16x8_t *>(stage + qn * 256 + ((lane ^ qn) << 4)) = sm.knew[lane];
             if (i + kDK < kNTW)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) kb[i % kDK][k] = *krow(t + kFWaves * kDK, k);
+                for (int k = 0; k < 4; ++k) kb[i % kDK][k] = kload(t + kFWaves * kDK, k);
             u16x8_t kop[4];
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4)
@@ -237,26 +298,31 @@ void fused_kernel(FusedArgs fa) {
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kop[c4]),
                                                               acc, 0, 0, 0);
             const int j = 16 * t + col;
+            const int jc = 16 * t + (((col & 3) << 2) | (col >> 2));   // lg_col(j)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int g = 4 * r + ii;
                 const float z = (j < T) ? acc[ii] * a.scale : -INFINITY;
-                if (g < G && j < T) lg[g * LD + j] = z;
+                if (g < G && j < T) lg[g * LD + jc] = z;
                 mx[ii] = fmaxf(mx[ii], z);
             }
         }
     }
-    // V rows do not depend on the softmax: start streaming them now
-    const int ngroups = (T + 3) >> 2;
-    auto vptr = [&](int q4) -> const u16x8_t * {
-        const int j = 4 * q4 + r;
-        const size_t rr = rows.row(j < n ? j : 0, bad);
-        return reinterpret_cast<const u16x8_t *>(((j < n) ? V + rr * kHD : vn) + 8 * col);
+    // V rows do not depend on the softmax: start streaming them now.  Wave w
+    // takes the same tiles as for K; instruction k of a lane reads chunk col
+    // of row 16t + 4k + r (zeros at or past n; row n is the new token's).
+    auto vload = [&](int t, int k) -> u16x8_t {
+        __amdgpu_buffer_rsrc_t rs;
+        int toff;
+        src.tile(t, true, rs, toff);
+        return buffer_row(rs, lane_off + toff + 4 * (2 * kHD) * k);
     };
-    u16x8_t vb[kDV];
+    const u16x8_t vnc = *reinterpret_cast<const u16x8_t *>(vn + 8 * col);
+    u16x8_t vb[kDV][4];
 #pragma unroll
-    for (int d = 0; d < kDV; ++d) vb[d] = *vptr(w + kFWaves * d);
-    (void)ngroups;
+    for (int d = 0; d < kDV; ++d)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) vb[d][k] = vload(w + kFWaves * d, k);
     // row maxima (16-lane groups share a query head set, then across waves),
     // and the newest position of the unit
 #pragma unroll
@@ -283,34 +349,65 @@ void fused_kernel(FusedArgs fa) {
     }
     __syncthreads();
 
-    // ---------------- P.V: MFMA 16x16x4 f32, A = probabilities, B = 4 V rows.
-    // The lane that feeds weight (g = col, key j) to the MFMA computes it:
-    // w = exp(z - m_g), stored back for the H2O update, summed for l_g.
+    // ---------------- P.V: MFMA 16x16x16 bf16 per 16-key tile.
+    // A row (lane col) = query head ga; with G <= 8 rows 8..15 repeat heads
+    // 0..7 and carry the low bf16 part of p.  The lane computes the weights
+    // it feeds, w = exp(z - m_g) for keys 16t + 4e + r, stores them back for
+    // the H2O update (high-part lanes only) and sums them for l_g.
     f32x4_t oacc[8];
 #pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) oacc[t8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int m8 = 0; m8 < 8; ++m8) oacc[m8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
-    const float mcol = (col < G) ? sm.m[col] : 0.f;
+    constexpr bool pack2 = PACK2;
+    const int ga = pack2 ? (col & 7) : col;
+    const bool arow = ga < G;
+    const bool hi_lane = !pack2 || col < 8;
+    const float mrow = arow ? sm.m[ga] : 0.f;
+    float *lrow = lg + (arow ? ga : 0) * LD;
 #pragma unroll
-    for (int i = 0; i < kNGW; ++i) {
-        const int q4 = w + kFWaves * i;
-        const int j = 4 * q4 + r;
-        // groups past the end carry p = 0 and read valid rows
-        float p = 0.f;
-        if (col < G && j < T) {
-            p = __expf(lg[col * LD + j] - mcol);
-            lg[col * LD + j] = p;
+    for (int i = 0; i < kNTW; ++i) {
+        const int t = w + kFWaves * i;
+        const int c0 = 16 * t + 4 * r;         // lg_col of key 16t + r
+        const f32x4_t z = *reinterpret_cast<const f32x4_t *>(lrow + (c0 < LD - 3 ? c0 : 0));
+        f32x4_t p;
+        s16x4_t ahi, alo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool live = arow && (16 * t + 4 * e + r) < T;
+            p[e] = live ? __expf(z[e] - mrow) : 0.f;
+            ahi[e] = bf16_bits(p[e]);
+            alo[e] = bf16_bits(p[e] - bf16_value(ahi[e]));
         }
-        lsum += p;
-        const u16x8_t cur = vb[i % kDV];
-        if (i + kDV < kNGW) vb[i % kDV] = *vptr(q4 + kFWaves * kDV);
+        if (hi_lane) {
+            lsum += (p[0] + p[1]) + (p[2] + p[3]);
+            if (arow && t < ntiles) *reinterpret_cast<f32x4_t *>(lrow + c0) = p;
+        }
+        const s16x4_t a0 = (pack2 && !hi_lane) ? alo : ahi;
+        // B operand of MFMA m: element m of the four rows this lane loaded
+        u16x8_t vr[4];
 #pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8)
-            oacc[t8] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, bf16_to_f32(cur[t8]), oacc[t8], 0,
-                                                             0, 0);
+        for (int e = 0; e < 4; ++e) vr[e] = (16 * t + 4 * e + r == n) ? vnc : vb[i % kDV][e];
+        s16x4_t bop[8];
+#pragma unroll
+        for (int m8 = 0; m8 < 8; ++m8)
+            bop[m8] = s16x4_t{(short)vr[0][m8], (short)vr[1][m8], (short)vr[2][m8], (short)vr[3][m8]};
+        if (i + kDV < kNTW)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vb[i % kDV][k] = vload(t + kFWaves * kDV, k);
+#pragma unroll
+        for (int m8 = 0; m8 < 8; ++m8)
+            oacc[m8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, bop[m8], oacc[m8], 0, 0, 0);
+        if (!pack2)
+#pragma unroll
+            for (int m8 = 0; m8 < 8; ++m8)
+                oacc[m8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, bop[m8], oacc[m8], 0, 0, 0);
     }
-    if (bad) raise_flag(c, KVC_FLAG_BAD_BLOCK);
-    // lanes col, col+16, col+32, col+48 hold partial sums of query head col
+    if (pack2)   // rows 8..15 (lanes 32..63) hold the low parts of rows 0..7
+#pragma unroll
+        for (int m8 = 0; m8 < 8; ++m8)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) oacc[m8][ii] += __shfl_xor(oacc[m8][ii], 32, 64);
+    // lanes col, col+16, col+32, col+48 hold partial sums of A row col
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
     if (lane < G) sm.wred[w][lane] = lsum;
@@ -327,7 +424,8 @@ void fused_kernel(FusedArgs fa) {
     if (h2o) {
         for (int j = tid; j < T; j += kFThreads) {
             float ps = 0.f;
-            for (int g = 0; g < G; ++g) ps += lg[g * LD + j] * sm.il[g];
+            const int jc = lg_col(j);
+            for (int g = 0; g < G; ++g) ps += lg[g * LD + jc] * sm.il[g];
             sc_s[j] = (j < n) ? sc_s[j] + ps : ps;
         }
     }
@@ -342,10 +440,10 @@ void fused_kernel(FusedArgs fa) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int g = 4 * r + i;
-            if (g < G) {
+            if (g < G && (!pack2 || r < 2)) {
                 float *dst = opart + ((size_t)w * G + g) * kHD + 8 * col;
 #pragma unroll
-                for (int t8 = 0; t8 < 8; ++t8) dst[t8] = oacc[t8][i];
+                for (int m8 = 0; m8 < 8; ++m8) dst[m8] = oacc[m8][i];
             }
         }
         __syncthreads();
@@ -590,17 +688,29 @@ size_t fused_smem_bytes(int G, int tcap) {
     return fast > gen ? fast : gen;
 }
 
+template <int MODE, bool PAGED, int TC>
+static void launch_pk(const FusedArgs &fa, bool pack2, size_t smem, hipStream_t s) {
+    const dim3 grid(fa.attn.c.B * fa.attn.c.Hkv), block(kFThreads);
+    if (pack2)
+        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, true>), grid, block, smem, s, fa);
+    else
+        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, false>), grid, block, smem, s, fa);
+}
+
 template <int TC>
 static hipError_t launch_tc(const FusedArgs &fa, int mode, size_t smem, hipStream_t s) {
-    const int units = fa.attn.c.B * fa.attn.c.Hkv;
     const bool paged = fa.attn.c.bs > 0;
     static hipError_t attr = [smem] {
         (void)smem;
         const int most = (int)fused_smem_bytes(kMaxGroup, TC);
-        const void *fns[4] = {(const void *)fused_kernel<kModeAttn, false, TC>,
-                              (const void *)fused_kernel<kModeStep, false, TC>,
-                              (const void *)fused_kernel<kModeAttn, true, TC>,
-                              (const void *)fused_kernel<kModeStep, true, TC>};
+        const void *fns[8] = {(const void *)fused_kernel<kModeAttn, false, TC, true>,
+                              (const void *)fused_kernel<kModeStep, false, TC, true>,
+                              (const void *)fused_kernel<kModeAttn, true, TC, true>,
+                              (const void *)fused_kernel<kModeStep, true, TC, true>,
+                              (const void *)fused_kernel<kModeAttn, false, TC, false>,
+                              (const void *)fused_kernel<kModeStep, false, TC, false>,
+                              (const void *)fused_kernel<kModeAttn, true, TC, false>,
+                              (const void *)fused_kernel<kModeStep, true, TC, false>};
         hipError_t e = hipSuccess;
         for (const void *f : fns)
             if (e == hipSuccess)
@@ -608,18 +718,13 @@ static hipError_t launch_tc(const FusedArgs &fa, int mode, size_t smem, hipStrea
         return e;
     }();
     if (attr != hipSuccess) return attr;
-    if (mode == kModeAttn && !paged)
-        hipLaunchKernelGGL((fused_kernel<kModeAttn, false, TC>), dim3(units), dim3(kFThreads), smem,
-                           s, fa);
-    else if (mode == kModeAttn)
-        hipLaunchKernelGGL((fused_kernel<kModeAttn, true, TC>), dim3(units), dim3(kFThreads), smem,
-                           s, fa);
-    else if (!paged)
-        hipLaunchKernelGGL((fused_kernel<kModeStep, false, TC>), dim3(units), dim3(kFThreads), smem,
-                           s, fa);
+    const bool pack2 = fa.attn.c.G <= 8;
+    if (mode == kModeAttn)
+        paged ? launch_pk<kModeAttn, true, TC>(fa, pack2, smem, s)
+              : launch_pk<kModeAttn, false, TC>(fa, pack2, smem, s);
     else
-        hipLaunchKernelGGL((fused_kernel<kModeStep, true, TC>), dim3(units), dim3(kFThreads), smem,
-                           s, fa);
+        paged ? launch_pk<kModeStep, true, TC>(fa, pack2, smem, s)
+              : launch_pk<kModeStep, false, TC>(fa, pack2, smem, s);
     return hipGetLastError();
 }
 

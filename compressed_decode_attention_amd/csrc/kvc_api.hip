@@ -95,8 +95,10 @@ int effective_len(const kvc_cache *c, int hint) {
 }
 
 bool use_fused(const kvc_cache *c, int hint) {
-    const bool pow2_blocks = c->block_size == 0 || (c->block_size & (c->block_size - 1)) == 0;
-    return c->dtype == KVC_BF16 && c->head_dim == 128 && pow2_blocks &&
+    // paged: power-of-two blocks of at least one 16-slot tile
+    const bool tile_blocks = c->block_size == 0 ||
+                             (c->block_size >= 16 && (c->block_size & (c->block_size - 1)) == 0);
+    return c->dtype == KVC_BF16 && c->head_dim == 128 && tile_blocks &&
            effective_len(c, hint) <= kvc::kFusedMaxT;
 }
 
