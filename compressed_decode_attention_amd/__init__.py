@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libkvc.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libkvc.so not found at {LIB_PATH}; build it with "
-        "`python -m compressed_decode_attention_amd.build`")
+        "`python compressed_decode_attention_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -36,7 +36,7 @@ POLICY_FULL, POLICY_STREAMING, POLICY_H2O, POLICY_RANDOM = range(4)
 EXPORTED = (
     "kvc_bytes_per_token", "kvc_n_keep", "kvc_status_string", "kvc_last_error",
     "kvc_workspace_bytes", "kvc_decode_attn", "kvc_h2o_accumulate", "kvc_evict_streaming",
-    "kvc_evict_h2o", "kvc_evict_random", "kvc_compact", "kvc_decode_step",
+    "kvc_evict_h2o", "kvc_evict_random", "kvc_compact", "kvc_decode_step", "kvc_stream_read",
 )
 
 
@@ -89,6 +89,8 @@ _lib.kvc_decode_step.restype = ctypes.c_int
 _lib.kvc_decode_step.argtypes = [_CP, ctypes.POINTER(kvc_policy), ctypes.c_uint32, _P, _P, _P,
                                  _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
                                  ctypes.c_size_t, _P]
+_lib.kvc_stream_read.restype = ctypes.c_int
+_lib.kvc_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
 
 
 class KvcError(RuntimeError):
@@ -292,3 +294,11 @@ def decode_step(cache: KvCache, policy: kvc_policy, step: int, new_pos, q, k_new
                                 _ptr(new_pos), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
                                 _ptr(scores), _scale(cache, scale), max_len_hint, wp, wn,
                                 _stream(stream)))
+
+
+def stream_read(buf, sink, nbytes: Optional[int] = None, stream=None):
+    """Read `nbytes` (default: all) of device tensor `buf` once with the
+    library's streaming kernel; `sink` is a one-element int32/uint32 device
+    tensor that is written only for an impossible data pattern."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(_lib.kvc_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)))

@@ -1,6 +1,8 @@
 """Build libkvc.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-    python -m compressed_decode_attention_amd.build
+    python compressed_decode_attention_amd/build.py
+
+(run as a script: importing the package would load the library it builds)
 """
 from __future__ import annotations
 
@@ -16,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "kvc")
 LIB = os.path.join(PKG, "libkvc.so")
 
-SOURCES = ["kvc_api.hip", "attn.hip", "select.hip", "compact.hip", "fused.hip"]
+SOURCES = ["kvc_api.hip", "attn.hip", "select.hip", "compact.hip", "fused.hip", "stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

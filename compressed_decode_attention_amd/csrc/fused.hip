@@ -193,6 +193,10 @@ void fused_kernel(FusedArgs fa) {
     const int r = lane >> 4, col = lane & 15;
     const int G = c.G;
 
+    // the queries do not depend on the slot count: their loads go first
+    u16x8_t qa[4];
+    load_q(qa, static_cast<const uint16_t *>(a.q) + ((size_t)b * c.Hq + (size_t)h * G + col) * kHD,
+           col < G, r);
     const int n = __builtin_amdgcn_readfirstlane(load_count(c, u, tid == 0));
     const int T = n + 1;
     if (T > TC || n >= c.cap) {
@@ -221,17 +225,25 @@ void fused_kernel(FusedArgs fa) {
     const bool h2o = S != nullptr;
     const int32_t npos = a.new_pos[b];
 
-    int pmax = -1;
-    for (int j = tid; j < T; j += kFThreads) {
-        const int32_t pj = (j < n) ? P[j] : npos;
-        pos_s[j] = pj;
-        pmax = max(pmax, pj);
-        sc_s[j] = (h2o && j < n) ? S[j] : 0.f;
+    // positions, old scores and the new key row are requested together, before
+    // any of them is waited for and ahead of the first K tiles (fixed trip
+    // count, in-bounds indexes; without scores the positions are read twice
+    // and the copy is ignored, which keeps every load unconditional)
+    constexpr int kNS = (TC + kFThreads - 1) / kFThreads;
+    const float *Ssrc = h2o ? S : reinterpret_cast<const float *>(P);
+    int32_t pst[kNS];
+    float sst[kNS];
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) {
+        const int j = tid + kFThreads * i;
+        const int jj = j < n ? j : 0;   // cap >= 1
+        pst[i] = P[jj];
+        sst[i] = Ssrc[jj];
     }
-    if (tid < kHD / 8) sm.knew[tid] = reinterpret_cast<const u16x8_t *>(kn)[tid];
+    const u16x8_t knr = reinterpret_cast<const u16x8_t *>(kn)[lane & 15];
     if constexpr (PAGED) {
-        // the sequence's block ids, checked once; an id outside the pool is
-        // reported and replaced by block 0
+        // the sequence's block ids, checked once (an id outside the pool is
+        // reported and replaced by block 0); every K load needs them
         const int nb = (n + c.bs - 1) / c.bs;
         const int32_t *bt = c.bt + (size_t)b * c.max_blocks;
         for (int i = tid; i < nb; i += kFThreads) {
@@ -244,11 +256,9 @@ void fused_kernel(FusedArgs fa) {
         }
         __syncthreads();
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---------------- logits: MFMA 16x16x32 bf16, A = queries, B = 16 keys
-    u16x8_t qa[4];
-    load_q(qa, static_cast<const uint16_t *>(a.q) + ((size_t)b * c.Hq + (size_t)h * G + col) * kHD,
-           col < G, r);
     const int ntiles = (T + 15) >> 4;
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     const TileSrc<PAGED> src(c, b, h, n, sm.blk);
@@ -267,13 +277,28 @@ void fused_kernel(FusedArgs fa) {
         return buffer_row(rs, lane_off + toff + 4 * (2 * kHD) * k);
     };
     const int tn = n >> 4, qn = n & 15;   // tile and row of the new token
-    __syncthreads();                      // the new key row is in LDS
+    int pmax = -1;
     {
         u16x8_t kb[kDK][4];
 #pragma unroll
         for (int d = 0; d < kDK; ++d)
 #pragma unroll
             for (int k = 0; k < 4; ++k) kb[d][k] = kload(w + kFWaves * d, k);
+        // the staged values land in LDS while the first K tiles are in flight.
+        // No branch: every index at or past n writes slot n with the new
+        // token's position and a zero score, the values slot n takes anyway.
+#pragma unroll
+        for (int i = 0; i < kNS; ++i) {
+            const int j = tid + kFThreads * i;
+            const bool old_slot = j < n;
+            const int jw = old_slot ? j : n;
+            const int32_t pj = old_slot ? pst[i] : npos;
+            pos_s[jw] = pj;
+            pmax = max(pmax, pj);
+            sc_s[jw] = (h2o && old_slot) ? sst[i] : 0.f;
+        }
+        if (tid < kHD / 8) sm.knew[tid] = knr;
+        __syncthreads();   // the new key row is in LDS
 #pragma unroll
         for (int i = 0; i < kNTW; ++i) {
             const int t = w + kFWaves * i;

@@ -423,3 +423,13 @@ KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *poli
     ca.dst = ca.c;
     return hip_status(kvc::launch_compact(ca, c->dtype, st), what);
 }
+
+KVC_EXPORT kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink,
+                                      void *stream) {
+    const char *what = "kvc_stream_read";
+    if (!src || !sink) return fail(KVC_ERR_INVALID_ARG, "%s: src and sink must not be NULL", what);
+    if ((uintptr_t)src % 16 || bytes == 0 || bytes % 16)
+        return fail(KVC_ERR_INVALID_ARG,
+                    "%s: src must be 16-byte aligned and bytes a positive multiple of 16", what);
+    return hip_status(kvc::launch_stream_read(src, bytes, sink, (hipStream_t)stream), what);
+}

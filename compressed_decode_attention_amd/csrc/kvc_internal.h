@@ -233,4 +233,6 @@ struct FusedArgs {
 size_t fused_smem_bytes(int G, int tcap);
 hipError_t launch_fused(const FusedArgs &fa, int mode, hipStream_t s);
 
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
+
 }  // namespace kvc

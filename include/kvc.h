@@ -268,6 +268,18 @@ kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *policy,
                            int32_t max_len_hint, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * Measurement helper, not part of a decode step: reads `bytes` bytes of
+ * device memory at `src` once, with fully coalesced 16-byte loads spread over
+ * the whole GPU, and writes `sink` (one uint32_t of device memory) only if the
+ * data hold a pattern that the caller's buffer does not.  Its duration gives
+ * the read-only streaming rate this GPU reaches in practice, the figure a
+ * decode step's achieved HBM rate is compared with next to the nominal peak.
+ * `src` must be 16-byte aligned and `bytes` a positive multiple of 16;
+ * nothing is enqueued otherwise (KVC_ERR_INVALID_ARG).
+ */
+kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -145,3 +145,14 @@ def test_workspace_grows_with_the_split():
     big = lib.kvc_workspace_bytes(ctypes.byref(_fake_cache(batch=2, capacity=8192)), 8192)
     assert small > 0 and big > 0
     assert lib.kvc_workspace_bytes(None, 0) == 0
+
+
+@no_gpu
+def test_stream_read_argument_errors():
+    lib = kvc.library()
+    assert lib.kvc_stream_read(None, 1024, 0x20000, None) == kvc.ERR_INVALID_ARG
+    assert lib.kvc_stream_read(0x10000, 1024, None, None) == kvc.ERR_INVALID_ARG
+    assert lib.kvc_stream_read(0x10008, 1024, 0x20000, None) == kvc.ERR_INVALID_ARG  # misaligned
+    assert lib.kvc_stream_read(0x10000, 1000, 0x20000, None) == kvc.ERR_INVALID_ARG  # not x16
+    assert lib.kvc_stream_read(0x10000, 0, 0x20000, None) == kvc.ERR_INVALID_ARG
+    assert b"16-byte aligned" in lib.kvc_last_error()
