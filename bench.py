@@ -80,19 +80,19 @@ def per_unit_bytes(n: int, G: int, D: int, b: int, policy: str) -> int:
     kv = 2 * n * D * b
     new = 4 * D * b
     qo = G * D * (b + 4)
-    sc = 8 * (n + 1) if policy == "h2o" else 0
+    sc = 8 * (n + 1) if policy.startswith("h2o") else 0
     pos = 4 * n if policy != "full" else 0
     return kv + new + qo + sc + pos + 4
 
 
-def cpu_baseline(w, n_cached: int, budget_s: float = 12.0):
+def cpu_baseline(w, n_cached: int, budget_s: float = 12.0, decay: float = 0.0):
     """The oracle (single thread) stepping the whole batch at the same shape
     from a steady state of n_cached entries per unit, whole decode steps until
     about budget_s seconds of work have been timed."""
     import oracle
     import synth
     orc = oracle.Oracle(w.q_heads, w.kv_heads, w.head_dim, w.dtype)
-    pol = oracle.Policy.h2o(w.n_heavy, w.n_recent)
+    pol = oracle.Policy.h2o(w.n_heavy, w.n_recent, decay=decay)
     import numpy as np
     # steady state: the first n_sink/n_heavy positions plus the recent window
     keep = n_cached - w.n_recent
@@ -168,7 +168,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="heavy_load_b512_l2048")
-    ap.add_argument("--policy", default="h2o", choices=["h2o", "streaming", "full"])
+    ap.add_argument("--policy", default="h2o", choices=["h2o", "h2o_decay", "streaming", "full"],
+                    help="h2o_decay: H2O with a decayed attention activity (decay 0.99)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -209,7 +210,7 @@ def main():
                                          dtype=torch.float32).to(torch.bfloat16)
     cache.pos[:, :, :P] = torch.arange(P, dtype=torch.int32, device=dev)
     cache.n_slots.fill_(P)
-    scores = torch.zeros((B, Hkv, cap), device=dev) if policy == "h2o" else None
+    scores = torch.zeros((B, Hkv, cap), device=dev) if policy.startswith("h2o") else None
     n_pool = 4
     pool = [(torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16),
              torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16),
@@ -221,6 +222,8 @@ def main():
     out = torch.empty((B, Hq, D), device=dev)
     if policy == "h2o":
         pol = kvc.policy_h2o(w.n_heavy, w.n_recent)
+    elif policy == "h2o_decay":
+        pol = kvc.policy_h2o(w.n_heavy, w.n_recent, decay=0.99)
     elif policy == "streaming":
         pol = kvc.policy_streaming(w.n_sink, w.n_recent)
     else:
@@ -327,7 +330,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(w, n_cached if policy != "full" else P,
-                                              args.cpu_budget)
+                                              args.cpu_budget, decay=0.99 if policy == "h2o_decay" else 0.0)
     print(json.dumps(result), flush=True)
 
 

@@ -55,7 +55,7 @@ class kvc_policy(ctypes.Structure):
     _fields_ = [
         ("kind", ctypes.c_int32), ("n_sink", ctypes.c_int32), ("n_heavy", ctypes.c_int32),
         ("n_recent", ctypes.c_int32), ("prompt_len", ctypes.c_int32), ("n_keep", ctypes.c_int32),
-        ("seed", ctypes.c_uint64),
+        ("seed", ctypes.c_uint64), ("decay", ctypes.c_float),
     ]
 
 
@@ -72,8 +72,8 @@ _lib.kvc_last_error.argtypes = []
 _lib.kvc_workspace_bytes.restype = ctypes.c_size_t
 _lib.kvc_workspace_bytes.argtypes = [_CP, ctypes.c_int32]
 _lib.kvc_decode_attn.restype = ctypes.c_int
-_lib.kvc_decode_attn.argtypes = [_CP, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32,
-                                 _P, ctypes.c_size_t, _P]
+_lib.kvc_decode_attn.argtypes = [_CP, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float,
+                                 ctypes.c_int32, _P, ctypes.c_size_t, _P]
 _lib.kvc_h2o_accumulate.restype = ctypes.c_int
 _lib.kvc_h2o_accumulate.argtypes = [_CP, _P, ctypes.c_int32, _P, _P, ctypes.c_float, _P]
 _lib.kvc_evict_streaming.restype = ctypes.c_int
@@ -212,10 +212,11 @@ class KvCache:
         return torch.empty((max(n, 1),), dtype=torch.uint8, device=self.k.device)
 
 
-def _policy(kind: int, n_sink=0, n_heavy=0, n_recent=0, prompt_len=0, n_keep=0, seed=0):
+def _policy(kind: int, n_sink=0, n_heavy=0, n_recent=0, prompt_len=0, n_keep=0, seed=0,
+            decay=0.0):
     p = kvc_policy()
     p.kind, p.n_sink, p.n_heavy, p.n_recent = kind, n_sink, n_heavy, n_recent
-    p.prompt_len, p.n_keep, p.seed = prompt_len, n_keep, seed
+    p.prompt_len, p.n_keep, p.seed, p.decay = prompt_len, n_keep, seed, decay
     return p
 
 
@@ -227,8 +228,10 @@ def policy_streaming(n_sink=64, n_recent=448):
     return _policy(POLICY_STREAMING, n_sink=n_sink, n_recent=n_recent)
 
 
-def policy_h2o(n_heavy=64, n_recent=448):
-    return _policy(POLICY_H2O, n_heavy=n_heavy, n_recent=n_recent)
+def policy_h2o(n_heavy=64, n_recent=448, decay=0.0):
+    """H2O: recent window + heavy hitters by score; decay 0 sums the attention,
+    0 < decay < 1 keeps a decayed attention activity instead."""
+    return _policy(POLICY_H2O, n_heavy=n_heavy, n_recent=n_recent, decay=decay)
 
 
 def policy_random(prompt_len, n_keep, seed=0):
@@ -250,11 +253,11 @@ def _ws(workspace):
 # ---------------------------------------------------------------------------
 
 def decode_attn(cache: KvCache, new_pos, q, k_new, v_new, out, scores=None, scale=None,
-                max_len_hint: int = 0, workspace=None, stream=None):
+                max_len_hint: int = 0, workspace=None, stream=None, score_decay: float = 0.0):
     wp, wn = _ws(workspace)
     _check(_lib.kvc_decode_attn(ctypes.byref(cache.c()), _ptr(new_pos), _ptr(q), _ptr(k_new),
                                 _ptr(v_new), _ptr(out), _ptr(scores), _scale(cache, scale),
-                                max_len_hint, wp, wn, _stream(stream)))
+                                score_decay, max_len_hint, wp, wn, _stream(stream)))
 
 
 def h2o_accumulate(cache: KvCache, q_rows, m_rows: int, scores, q_pos=None, scale=None,

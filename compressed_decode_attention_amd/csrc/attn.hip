@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
             const int s = j / chunk;
             float ps = 0.f;
             for (int g = 0; g < G; ++g) ps += lg[g * ld + j] * fac[s][g];
-            if (j < n) sc[j] += ps;
-            else if (can_store) sc[n] = ps;
+            if (j < n) sc[j] = score_update(sc[j], ps, a.decay);
+            else if (can_store) sc[n] = score_update(0.f, ps, a.decay);
         }
     }
     if (tid == 0 && can_store) c.n_slots[u] = n + 1;

@@ -451,7 +451,7 @@ void fused_kernel(FusedArgs fa) {
             float ps = 0.f;
             const int jc = lg_col(j);
             for (int g = 0; g < G; ++g) ps += lg[g * LD + jc] * sm.il[g];
-            sc_s[j] = (j < n) ? sc_s[j] + ps : ps;
+            sc_s[j] = score_update((j < n) ? sc_s[j] : 0.f, ps, a.decay);
         }
     }
 

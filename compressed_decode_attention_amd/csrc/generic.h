@@ -147,8 +147,8 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
             for (int j = j0 + tid; j < j1; j += kAttnThreads) {
                 float ps = 0.f;
                 for (int g = 0; g < G; ++g) ps += lg[g * ld + j] / st_l[g];
-                if (j < n) sc[j] += ps;
-                else if (can_store) sc[n] = ps;
+                if (j < n) sc[j] = score_update(sc[j], ps, a.decay);
+                else if (can_store) sc[n] = score_update(0.f, ps, a.decay);
             }
         }
     } else {

@@ -162,6 +162,8 @@ kvc_status check_policy(const kvc_policy *p, const float *scores, const char *wh
             if (p->n_heavy < 0 || p->n_recent < 0)
                 return fail(KVC_ERR_INVALID_ARG, "%s: n_heavy and n_recent must be >= 0", what);
             if (!scores) return fail(KVC_ERR_INVALID_ARG, "%s: H2O needs h2o_scores", what);
+            if (!(p->decay >= 0.f && p->decay < 1.f))
+                return fail(KVC_ERR_INVALID_ARG, "%s: decay must be 0 or in (0, 1)", what);
             return KVC_OK;
         case KVC_POLICY_RANDOM:
             if (p->prompt_len < 0 || p->n_keep < 0)
@@ -174,9 +176,10 @@ kvc_status check_policy(const kvc_policy *p, const float *scores, const char *wh
 
 kvc::AttnArgs attn_args(const kvc_cache *c, const int32_t *new_pos, const void *q,
                         const void *k_new, const void *v_new, float *out, float *scores,
-                        float scale, const Workspace &w, void *ws) {
+                        float scale, float decay, const Workspace &w, void *ws) {
     kvc::AttnArgs a;
     a.c = kvc::make_dev(*c);
+    a.decay = decay;
     a.new_pos = new_pos;
     a.q = q;
     a.k_new = k_new;
@@ -273,14 +276,18 @@ KVC_EXPORT size_t kvc_workspace_bytes(const kvc_cache *c, int32_t max_len_hint) 
 
 KVC_EXPORT kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos, const void *q,
                                       const void *k_new, const void *v_new, float *out,
-                                      float *h2o_scores, float scale, int32_t max_len_hint,
-                                      void *workspace, size_t workspace_bytes, void *stream) {
+                                      float *h2o_scores, float scale, float score_decay,
+                                      int32_t max_len_hint, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
     const char *what = "kvc_decode_attn";
     kvc_status s = check_attn_args(c, new_pos, q, k_new, v_new, out, scale, what);
     if (s != KVC_OK) return s;
+    if (!(score_decay >= 0.f && score_decay < 1.f))
+        return fail(KVC_ERR_INVALID_ARG, "%s: score_decay must be 0 or in (0, 1)", what);
     const Workspace w = layout(c, max_len_hint);
     if ((s = check_ws(w, workspace, workspace_bytes, what)) != KVC_OK) return s;
-    kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, h2o_scores, scale, w, workspace);
+    kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, h2o_scores, scale,
+                                h2o_scores ? score_decay : 0.f, w, workspace);
     if (use_fused(c, max_len_hint)) {
         kvc::FusedArgs fa = fused_args(c, a, max_len_hint);
         return hip_status(kvc::launch_fused(fa, kvc::kModeAttn, (hipStream_t)stream), what);
@@ -394,7 +401,8 @@ KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *poli
     if ((s = check_ws(w, workspace, workspace_bytes, what)) != KVC_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     float *scores = policy->kind == KVC_POLICY_H2O ? h2o_scores : nullptr;
-    kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, scores, scale, w, workspace);
+    kvc::AttnArgs a = attn_args(c, new_pos, q, k_new, v_new, out, scores, scale,
+                                scores ? policy->decay : 0.f, w, workspace);
     int32_t *keep = (int32_t *)((char *)workspace + w.keep_off);
     int32_t *nout = (int32_t *)((char *)workspace + w.nout_off);
     kvc::SelectArgs sa = select_args(c, *policy, step, scores, keep, nout);

@@ -178,12 +178,20 @@ struct AttnArgs {
     float *out;
     float *scores;        // may be null
     float scale;
+    float decay;          // 0: scores += p; in (0, 1): scores = decay*scores + (1-decay)*p
     int nsplit;
     float *part;          // [units][nsplit][G][D+2] when nsplit > 1
     float *logits;        // [units][G][cap+1] scratch (scores and/or nsplit > 1)
 };
 
 hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s);
+
+// New H2O score of a slot from its old score s and the group-summed
+// probability w of this step: a plain sum, or a decayed attention activity
+// d*s + (1-d)*w (online compaction study, sections 3.1 and 4.1).
+__device__ inline float score_update(float s, float w, float d) {
+    return d == 0.f ? s + w : d * s + (1.f - d) * w;
+}
 
 struct AccumArgs {
     CacheDev c;

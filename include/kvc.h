@@ -118,6 +118,13 @@ typedef struct kvc_policy {
     int32_t prompt_len;
     int32_t n_keep;
     uint64_t seed;
+    /* KVC_POLICY_H2O only.  0: scores accumulate the group-summed
+     * probabilities (plain H2O).  0 < decay < 1: they are a decayed attention
+     * activity, s <- decay * s + (1 - decay) * sum_i p_i, a new slot starting
+     * from 0 [EMP 3.1: accumulation with a decay coefficient on earlier
+     * attention; EMP 4.1: the incremental update, decay e.g. 0.99].  The
+     * kept set is chosen from these scores exactly as for plain H2O. */
+    float decay;
 } kvc_policy;
 
 /* ------------------------------------------------------------------------
@@ -174,6 +181,10 @@ size_t kvc_workspace_bytes(const kvc_cache *c, int32_t max_len_hint);
  *   q        [batch, q_heads, head_dim]  dtype
  *   k_new,v_new [batch, kv_heads, head_dim] dtype
  *   out      [batch, q_heads, head_dim] fp32
+ *   score_decay  0 for the sums above; 0 < score_decay < 1 updates each score
+ *            as s <- score_decay * s + (1 - score_decay) * sum_i p_i instead
+ *            (decayed attention activity, see kvc_policy.decay); other values
+ *            are rejected.  Ignored when h2o_scores is NULL.
  *   max_len_hint  upper bound on n_slots + 1 over the batch (<= capacity+1);
  *            sizes the split of long units over workgroups.  A unit longer
  *            than the hint is still computed exactly (less parallel).
@@ -183,8 +194,8 @@ size_t kvc_workspace_bytes(const kvc_cache *c, int32_t max_len_hint);
 kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos,
                            const void *q, const void *k_new, const void *v_new,
                            float *out, float *h2o_scores, float scale,
-                           int32_t max_len_hint, void *workspace,
-                           size_t workspace_bytes, void *stream);
+                           float score_decay, int32_t max_len_hint,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Unfused H2O score pass: adds the group-summed softmax probabilities of

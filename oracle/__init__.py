@@ -171,8 +171,10 @@ class Policy(dict):
         return Policy(kind="streaming", n_sink=n_sink, n_recent=n_recent)
 
     @staticmethod
-    def h2o(n_heavy=64, n_recent=448):
-        return Policy(kind="h2o", n_heavy=n_heavy, n_recent=n_recent)
+    def h2o(n_heavy=64, n_recent=448, decay=0.0):
+        """decay 0: accumulated attention; 0 < decay < 1: decayed attention
+        activity (online compaction study, sections 3.1 and 4.1)."""
+        return Policy(kind="h2o", n_heavy=n_heavy, n_recent=n_recent, decay=decay)
 
     @staticmethod
     def random(prompt_len, n_keep, seed=0):
@@ -244,7 +246,14 @@ class Oracle:
             o, p = attend(q[h * self.G:(h + 1) * self.G], u.k, u.v, self.scale, want_p=True)
             out[h * self.G:(h + 1) * self.G] = o
             if policy["kind"] == "h2o":
-                u.s = u.s + p.sum(axis=0)
+                # this step's attention weight of every entry, summed over the
+                # group; the new entry's score starts at 0 (appended above)
+                w_step = p.sum(axis=0)
+                lam = policy.get("decay", 0.0)
+                if lam == 0.0:
+                    u.s = u.s + w_step           # H2O: accumulated attention
+                else:
+                    u.s = lam * u.s + (1.0 - lam) * w_step   # A <- lam*A + (1-lam)*w
             post.append((u.pos.copy(), u.s.copy()))
         self.seen[b] = p_new + 1
         L = self.seen[b]

@@ -70,12 +70,12 @@ def _fake_cache(**kw):
 
 def _attn(c, ws=None, nbytes=0, **kw):
     args = dict(new_pos=0x1000, q=0x2000, k_new=0x3000, v_new=0x4000, out=0x5000, scores=None,
-                scale=0.088)
+                scale=0.088, decay=0.0)
     args.update(kw)
     return kvc.library().kvc_decode_attn(ctypes.byref(c) if c is not None else None,
                                          args["new_pos"], args["q"], args["k_new"],
                                          args["v_new"], args["out"], args["scores"],
-                                         args["scale"], 0, ws, nbytes, None)
+                                         args["scale"], args["decay"], 0, ws, nbytes, None)
 
 
 @no_gpu
@@ -101,6 +101,9 @@ def test_attention_argument_errors():
     assert _attn(None) == kvc.ERR_INVALID_ARG
     assert _attn(_fake_cache(), q=None) == kvc.ERR_INVALID_ARG
     assert _attn(_fake_cache(), scale=float("inf")) == kvc.ERR_INVALID_ARG
+    for bad in (1.0, -0.5, float("nan"), 2.0):
+        assert _attn(_fake_cache(), decay=bad) == kvc.ERR_INVALID_ARG
+    assert b"score_decay" in kvc.library().kvc_last_error()
     # workspace required but missing / too small
     assert _attn(_fake_cache()) == kvc.ERR_WORKSPACE
     need = kvc.library().kvc_workspace_bytes(ctypes.byref(_fake_cache()), 0)
@@ -134,6 +137,12 @@ def test_policy_and_selection_errors():
     bad = kvc._policy(9)
     assert lib.kvc_decode_step(ctypes.byref(c), ctypes.byref(bad), 1, 0x1, 0x2000, 0x3000, 0x4000,
                                0x5000, None, 0.1, 0, ws, need, None) == kvc.ERR_INVALID_ARG
+    for decay in (1.0, -0.1, float("nan")):
+        pd = kvc.policy_h2o(decay=decay)
+        assert lib.kvc_decode_step(ctypes.byref(c), ctypes.byref(pd), 1, 0x1, 0x2000, 0x3000,
+                                   0x4000, 0x5000, 0x6000, 0.1, 0, ws, need, None) == \
+            kvc.ERR_INVALID_ARG
+        assert b"decay" in lib.kvc_last_error()
     assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1000, -1, None, 0x2000, 0.1, None) == \
         kvc.ERR_INVALID_ARG
     assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1000, 0, None, 0x2000, 0.1, None) == kvc.OK

@@ -78,7 +78,8 @@ def _trajectory(w, lengths, capacity, steps, fused=True, paged=0, hint=None):
 
 
 def _three_calls(cache, w, pol, t, new_pos, q, kn, vn, out, scores, ws, hint):
-    kvc.decode_attn(cache, new_pos, q, kn, vn, out, scores, max_len_hint=hint, workspace=ws)
+    kvc.decode_attn(cache, new_pos, q, kn, vn, out, scores, max_len_hint=hint, workspace=ws,
+                    score_decay=pol.decay if pol.kind == kvc.POLICY_H2O else 0.0)
     keep = torch.empty((cache.batch, cache.kv_heads, cache.capacity), dtype=torch.int32,
                        device="cuda")
     nout = torch.empty((cache.batch, cache.kv_heads), dtype=torch.int32, device="cuda")
@@ -140,7 +141,7 @@ def test_undersized_hint_falls_back_inside_the_step_kernel():
     _trajectory(w, [900, 40, 700], capacity=901, steps=3, hint=2)
 
 
-def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None, hint=None):
+def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None, hint=None, decay=0.0):
     hint = capacity + 1 if hint is None else hint
     B = len(lengths)
     G = w.group
@@ -158,7 +159,7 @@ def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None, hint=None)
         pre = Snapshot(cache, w.dtype, scores, units)
         kvc.decode_attn(cache, torch.tensor(seen, dtype=torch.int32, device="cuda"),
                         dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype), out, scores,
-                        max_len_hint=hint, workspace=ws)
+                        max_len_hint=hint, workspace=ws, score_decay=decay)
         mid = Snapshot(cache, w.dtype, scores, units)
         kvc.evict_h2o(cache, scores, w.n_heavy, w.n_recent, keep, nout)
         kk, mm = keep.cpu().numpy(), nout.cpu().numpy()
@@ -171,8 +172,12 @@ def _h2o_sync(w, lengths, capacity, steps, paged=0, check_units=None, hint=None)
                                            vn[b, h], scale)
             assert np.abs(o[b, h * G:(h + 1) * G] - ref).max() <= OUT_ATOL
             n = u0["n"]
-            assert_scores_close(u1["s"][:n], u0["s"] + psum[:n])
-            assert_scores_close(u1["s"][n:n + 1], psum[n:])
+            if decay == 0.0:
+                assert_scores_close(u1["s"][:n], u0["s"] + psum[:n])
+                assert_scores_close(u1["s"][n:n + 1], psum[n:])
+            else:   # decayed activity: old score fades, this step's weight enters
+                assert_scores_close(u1["s"][:n], decay * u0["s"] + (1 - decay) * psum[:n])
+                assert_scores_close(u1["s"][n:n + 1], (1 - decay) * psum[n:])
             # oracle selection on the GPU's own post-attention scores
             L = seen[b] + 1
             want = oracle.select_h2o(u1["pos"], u1["s"].astype(np.float64), L, w.n_heavy,
@@ -205,6 +210,19 @@ def test_h2o_on_paged_mixed_lengths():
     _h2o_sync(w, [600, 64, 1000, 17], capacity=1008, steps=5, paged=16)
 
 
+@pytest.mark.parametrize("decay", [0.5, 0.99])
+@pytest.mark.parametrize("capacity", [48, 1100])
+def test_h2o_decayed_activity_small_budget(decay, capacity):
+    # both paths (one-workgroup step kernel at 48, split kernels at 1,100)
+    w = synth.workload("llama3_8b_h2o_b64", n_heavy=6, n_recent=20)
+    _h2o_sync(w, [40, 26, 3], capacity=capacity, steps=20, decay=decay)
+
+
+def test_h2o_decayed_activity_heavy_load_shape():
+    w = synth.workload("heavy_load_b512_l2048")
+    _h2o_sync(w, [512, 512, 300, 700], capacity=701, steps=3, decay=0.99)
+
+
 def test_h2o_heavy_load_shape_fused_steady_state():
     # heavy-load layer (G = 8), 64 + 448, units starting at and below budget
     w = synth.workload("heavy_load_b512_l2048")
@@ -233,10 +251,10 @@ def _live_equal(c0, c1, s0=None, s1=None):
 
 
 @pytest.mark.parametrize("cap", [160, 1100])
-@pytest.mark.parametrize("policy", ["h2o", "streaming", "random", "full"])
+@pytest.mark.parametrize("policy", ["h2o", "h2o_decay", "streaming", "random", "full"])
 def test_fused_step_equals_three_calls(policy, cap):
     w = synth.workload("llama3_8b_h2o_b64", policy=policy, n_heavy=8, n_recent=40,
-                       n_sink=4, pinned=50, n_keep=30) if policy != "h2o" else \
+                       n_sink=4, pinned=50, n_keep=30) if not policy.startswith("h2o") else \
         synth.workload("llama3_8b_h2o_b64", n_heavy=8, n_recent=40)
     lengths = [120, 60, 49, 0]
     caches = [make_cache(w, lengths, cap), make_cache(w, lengths, cap)]
@@ -244,13 +262,15 @@ def test_fused_step_equals_three_calls(policy, cap):
     scs = [torch.zeros((B, w.kv_heads, cap), device="cuda") for _ in range(2)]
     outs = [torch.empty((B, w.q_heads, w.head_dim), device="cuda") for _ in range(2)]
     pol, _ = _policy_pair(w)
+    if policy == "h2o_decay":
+        pol = kvc.policy_h2o(w.n_heavy, w.n_recent, decay=0.99)
     wss = [c.workspace(cap + 1) for c in caches]
     for t in range(1, 7):
         q, kn, vn = synth.batch_step_inputs(w, t, B)
         new_pos = torch.tensor([L + t - 1 for L in lengths], dtype=torch.int32, device="cuda")
         args = (new_pos, dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype))
-        sc0 = scs[0] if policy == "h2o" else None
-        sc1 = scs[1] if policy == "h2o" else None
+        sc0 = scs[0] if policy.startswith("h2o") else None
+        sc1 = scs[1] if policy.startswith("h2o") else None
         kvc.decode_step(caches[0], pol, t, *args, outs[0], sc0, max_len_hint=cap + 1,
                         workspace=wss[0])
         _three_calls(caches[1], w, pol, t, *args, outs[1], sc1, wss[1], cap + 1)

@@ -214,6 +214,44 @@ def test_h2o_zero_query_spreads_mass_uniformly():
         np.testing.assert_allclose(post[h][1], G / 10, rtol=1e-14)
 
 
+@pytest.mark.parametrize("lam", [0.5, 0.9, 0.99])
+def test_decayed_activity_matches_the_geometric_closed_form(lam):
+    # Zero queries attend uniformly: every entry's step weight is exactly G/T_k
+    # (T_k entries attended at step k).  An entry appended at step s then holds
+    # A = sum_{k=s..t} (1-lam) lam^(t-k) G/T_k -- the unrolled decayed update of
+    # the online compaction study (sections 3.1, 4.1) -- and the n0 prompt
+    # entries, present from the start with A = 0, the same sum from k = 1.
+    G, n0, steps = 3, 9, 7
+    orc, rng = _small_h2o_oracle(G=G, n=n0)
+    pol = oracle.Policy.h2o(n_heavy=100, n_recent=100, decay=lam)  # no eviction
+    q = np.zeros((2 * G, 16), np.float32)
+    for t in range(1, steps + 1):
+        kn = rng.standard_normal((2, 16)).astype(np.float32)
+        _, post = orc.step(0, q, kn, kn, pol, step=t)
+    T = [n0 + k for k in range(1, steps + 1)]        # attended count at step k
+    def closed(first):
+        return sum((1 - lam) * lam ** (steps - k) * G / T[k - 1] for k in range(first, steps + 1))
+    for h in range(2):
+        pos, score = post[h]
+        assert pos.size == n0 + steps
+        for i, p in enumerate(pos):
+            first = 1 if p < n0 else p - n0 + 1      # the step that appended position p
+            assert abs(score[i] - closed(first)) < 1e-14, (lam, p)
+
+
+def test_decay_zero_is_plain_accumulation():
+    G = 2
+    a, rng = _small_h2o_oracle(G=G)
+    b, _ = _small_h2o_oracle(G=G)
+    for t in range(1, 5):
+        q = rng.standard_normal((2 * G, 16)).astype(np.float32)
+        kn = rng.standard_normal((2, 16)).astype(np.float32)
+        _, pa = a.step(0, q, kn, kn, oracle.Policy.h2o(100, 100), step=t)
+        _, pb = b.step(0, q, kn, kn, oracle.Policy.h2o(100, 100, decay=0.0), step=t)
+        for h in range(2):
+            np.testing.assert_array_equal(pa[h][1], pb[h][1])
+
+
 # ---------------------------------------------------------------------------
 # H2O selection: brute force over all subsets on tiny inputs
 # ---------------------------------------------------------------------------
