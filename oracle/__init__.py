@@ -137,6 +137,35 @@ def select_streaming(pos, L: int, n_sink: int, n_recent: int) -> np.ndarray:
     return keep.astype(bool)
 
 
+def prompt_scores(q_rows: np.ndarray, K: np.ndarray, pos: np.ndarray,
+                  q_pos: Optional[np.ndarray], scale: Optional[float] = None) -> np.ndarray:
+    """H2O scores that a block of query rows leaves on one kv head's cache.
+
+    q_rows [m, G, D] (the m query rows of the G query heads of this kv head),
+    K [n, D], pos [n] slot positions, q_pos [m] row positions or None.  Row r
+    of head g attends the slots with pos <= q_pos[r] (every slot when q_pos is
+    None): p = softmax(scale q K^T) over them, and each slot's score receives
+    the sum over rows and heads of its probability.  A row that sees no slot
+    adds nothing.  This is how H2O accumulates attention scores over the
+    prompt's own causal attention before eviction starts (guide, sections 2
+    and 16, "the 4 methods" and "prefill, decode, TP").  float64.
+    """
+    q_rows = np.asarray(q_rows, np.float64)
+    K = np.asarray(K, np.float64)
+    pos = np.asarray(pos, np.int64)
+    m, G, D = q_rows.shape
+    s = np.zeros(K.shape[0])
+    for r in range(m):
+        vis = np.ones(pos.size, bool) if q_pos is None else pos <= int(q_pos[r])
+        if not vis.any():
+            continue
+        idx = np.flatnonzero(vis)
+        Kv = K[idx]
+        _, p = attend(q_rows[r], Kv, Kv, scale, want_p=True)   # V unused: only p matters
+        s[idx] += p[:, :idx.size].sum(axis=0)
+    return s
+
+
 def select_h2o(pos, score, L: int, n_heavy: int, n_recent: int) -> np.ndarray:
     pos = np.ascontiguousarray(pos, np.int32)
     score = np.ascontiguousarray(score, np.float64)

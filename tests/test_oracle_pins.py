@@ -461,3 +461,55 @@ def test_budget_above_length_equals_full_attention():
         ob, _ = b.step(0, q, kn, vn, oracle.Policy.full(), step=t)
         np.testing.assert_array_equal(oa, ob)
     assert a.units[0][0].pos.tolist() == list(range(35))
+
+
+# ---------------------------------------------------------------------------
+# prompt scoring (H2O scores from the prompt's own causal attention)
+# ---------------------------------------------------------------------------
+
+def test_prompt_scores_zero_queries_give_the_harmonic_tail():
+    # uniform causal attention: row r spreads G over r + 1 slots, so slot j
+    # collects G * sum_{r >= j} 1 / (r + 1) = G * (H_m - H_j)
+    m, G, D = 37, 3, 16
+    K = np.random.default_rng(1).standard_normal((m, D))
+    s = oracle.prompt_scores(np.zeros((m, G, D)), K, np.arange(m), np.arange(m))
+    harmonic = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, m + 1))])
+    np.testing.assert_allclose(s, G * (harmonic[m] - harmonic[:m]), rtol=1e-13)
+
+
+def test_prompt_scores_mass_is_group_size_per_row_that_sees_a_slot():
+    rng = np.random.default_rng(2)
+    m, n, G, D = 20, 30, 4, 16
+    pos = rng.permutation(100)[:n]
+    q_pos = rng.integers(-5, 100, m)
+    s = oracle.prompt_scores(rng.standard_normal((m, G, D)), rng.standard_normal((n, D)), pos,
+                             q_pos)
+    rows_seeing = sum(int((pos <= qp).any()) for qp in q_pos)
+    assert abs(s.sum() - G * rows_seeing) < 1e-12 * G * m
+    assert (s[pos > q_pos.max()] == 0).all()
+
+
+def test_prompt_scores_two_key_logistic_closed_form():
+    q = np.array([[[0.5, -1.0, 2.0, 0.25]]])          # one row, one head
+    K = np.array([[1.0, 0.0, -1.0, 2.0], [0.0, 1.0, 0.5, -1.0]])
+    scale = 0.5
+    dz = scale * (q[0, 0] @ (K[1] - K[0]))
+    p0 = 1.0 / (1.0 + math.exp(dz))
+    s = oracle.prompt_scores(q, K, np.array([3, 7]), None, scale)
+    np.testing.assert_allclose(s, [p0, 1.0 - p0], rtol=1e-14)
+    # the row at position 5 sees only the slot at position 3
+    s = oracle.prompt_scores(q, K, np.array([3, 7]), np.array([5]), scale)
+    np.testing.assert_array_equal(s, [1.0, 0.0])
+
+
+def test_prompt_scores_follow_a_permutation_of_the_slots():
+    rng = np.random.default_rng(3)
+    m, n, G, D = 12, 25, 2, 16
+    q = rng.standard_normal((m, G, D))
+    K = rng.standard_normal((n, D))
+    pos = np.arange(n)
+    q_pos = np.sort(rng.integers(0, n, m))
+    perm = rng.permutation(n)
+    a = oracle.prompt_scores(q, K, pos, q_pos)
+    b = oracle.prompt_scores(q, K[perm], pos[perm], q_pos)
+    np.testing.assert_allclose(b, a[perm], rtol=1e-13)
