@@ -37,6 +37,7 @@ EXPORTED = (
     "kvc_bytes_per_token", "kvc_n_keep", "kvc_status_string", "kvc_last_error",
     "kvc_workspace_bytes", "kvc_decode_attn", "kvc_h2o_accumulate", "kvc_evict_streaming",
     "kvc_evict_h2o", "kvc_evict_random", "kvc_compact", "kvc_decode_step", "kvc_stream_read",
+    "kvc_h2o_accumulate_workspace_bytes",
 )
 
 
@@ -75,7 +76,10 @@ _lib.kvc_decode_attn.restype = ctypes.c_int
 _lib.kvc_decode_attn.argtypes = [_CP, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float,
                                  ctypes.c_int32, _P, ctypes.c_size_t, _P]
 _lib.kvc_h2o_accumulate.restype = ctypes.c_int
-_lib.kvc_h2o_accumulate.argtypes = [_CP, _P, ctypes.c_int32, _P, _P, ctypes.c_float, _P]
+_lib.kvc_h2o_accumulate.argtypes = [_CP, _P, ctypes.c_int32, _P, _P, ctypes.c_float, _P,
+                                    ctypes.c_size_t, _P]
+_lib.kvc_h2o_accumulate_workspace_bytes.restype = ctypes.c_size_t
+_lib.kvc_h2o_accumulate_workspace_bytes.argtypes = [_CP, ctypes.c_int32]
 _lib.kvc_evict_streaming.restype = ctypes.c_int
 _lib.kvc_evict_streaming.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
 _lib.kvc_evict_h2o.restype = ctypes.c_int
@@ -211,6 +215,11 @@ class KvCache:
         n = self.workspace_bytes(max_len_hint)
         return torch.empty((max(n, 1),), dtype=torch.uint8, device=self.k.device)
 
+    def prompt_workspace(self, m_rows: int) -> torch.Tensor:
+        """Workspace of kvc_h2o_accumulate for m_rows query rows per sequence."""
+        n = int(_lib.kvc_h2o_accumulate_workspace_bytes(ctypes.byref(self.c()), m_rows))
+        return torch.empty((max(n, 1),), dtype=torch.uint8, device=self.k.device)
+
 
 def _policy(kind: int, n_sink=0, n_heavy=0, n_recent=0, prompt_len=0, n_keep=0, seed=0,
             decay=0.0):
@@ -261,9 +270,15 @@ def decode_attn(cache: KvCache, new_pos, q, k_new, v_new, out, scores=None, scal
 
 
 def h2o_accumulate(cache: KvCache, q_rows, m_rows: int, scores, q_pos=None, scale=None,
-                   stream=None):
+                   stream=None, workspace=None):
+    """Add the group-summed softmax probabilities of m_rows query rows per
+    sequence (causal when q_pos is given) to the scores.  The workspace holds
+    one fp32 log-sum-exp per row and head; it is allocated here if not given."""
+    if workspace is None:
+        workspace = cache.prompt_workspace(m_rows)
+    wp, wn = _ws(workspace)
     _check(_lib.kvc_h2o_accumulate(ctypes.byref(cache.c()), _ptr(q_rows), m_rows, _ptr(q_pos),
-                                   _ptr(scores), _scale(cache, scale), _stream(stream)))
+                                   _ptr(scores), _scale(cache, scale), wp, wn, _stream(stream)))
 
 
 def evict_streaming(cache: KvCache, n_sink: int, n_recent: int, keep_slots, n_out, stream=None):

@@ -295,8 +295,21 @@ KVC_EXPORT kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos
     return hip_status(kvc::launch_attn(a, c->dtype, (hipStream_t)stream), what);
 }
 
+// the matrix-core prompt scoring: bf16 K, head_dim 128
+static bool use_prompt_mfma(const kvc_cache *c) {
+    return c->dtype == KVC_BF16 && c->head_dim == 128;
+}
+
+KVC_EXPORT size_t kvc_h2o_accumulate_workspace_bytes(const kvc_cache *c, int32_t m_rows) {
+    if (check_cache(c, "kvc_h2o_accumulate_workspace_bytes") != KVC_OK || m_rows <= 0) return 0;
+    if (!use_prompt_mfma(c)) return 0;
+    return align_up(kvc::prompt_workspace_bytes(c->batch * c->kv_heads, m_rows,
+                                                c->q_heads / c->kv_heads));
+}
+
 KVC_EXPORT kvc_status kvc_h2o_accumulate(const kvc_cache *c, const void *q_rows, int32_t m_rows,
                                          const int32_t *q_pos, float *h2o_scores, float scale,
+                                         void *workspace, size_t workspace_bytes,
                                          void *stream) {
     const char *what = "kvc_h2o_accumulate";
     kvc_status s = check_cache(c, what);
@@ -306,6 +319,22 @@ KVC_EXPORT kvc_status kvc_h2o_accumulate(const kvc_cache *c, const void *q_rows,
     if (!q_rows || !h2o_scores)
         return fail(KVC_ERR_INVALID_ARG, "%s: q_rows and h2o_scores must not be NULL", what);
     if (!isfinite(scale)) return fail(KVC_ERR_INVALID_ARG, "%s: scale is not finite", what);
+    if (use_prompt_mfma(c)) {
+        if ((uintptr_t)q_rows % 16)
+            return fail(KVC_ERR_INVALID_ARG, "%s: q_rows must be 16-byte aligned", what);
+        Workspace w{};
+        w.total = kvc_h2o_accumulate_workspace_bytes(c, m_rows);
+        if ((s = check_ws(w, workspace, workspace_bytes, what)) != KVC_OK) return s;
+        kvc::PromptArgs p;
+        p.c = kvc::make_dev(*c);
+        p.q_rows = q_rows;
+        p.m_rows = m_rows;
+        p.q_pos = q_pos;
+        p.scores = h2o_scores;
+        p.scale = scale;
+        p.lse = static_cast<float *>(workspace);
+        return hip_status(kvc::launch_prompt_scores(p, (hipStream_t)stream), what);
+    }
     kvc::AccumArgs a;
     a.c = kvc::make_dev(*c);
     a.q_rows = q_rows;

@@ -101,6 +101,10 @@ __device__ inline int wave_max_i(int x) {
     for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
     return x;
 }
+__device__ inline int wave_min_i(int x) {
+    for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, kWave));
+    return x;
+}
 
 // Block-wide max of an int (blockDim.x a multiple of 64, <= 1024).
 __device__ inline int block_max_i(int x, int *red) {
@@ -202,6 +206,21 @@ struct AccumArgs {
     float scale;
 };
 hipError_t launch_accumulate(const AccumArgs &a, int dtype, hipStream_t s);
+
+// Scores from a block of causal query rows on the matrix cores (bf16, head
+// dim 128): pass 1 writes every row's log-sum-exp to lse, pass 2 adds the
+// probabilities to the scores.
+struct PromptArgs {
+    CacheDev c;
+    const void *q_rows;   // [batch, m_rows, q_heads, head_dim] bf16
+    int m_rows;
+    const int32_t *q_pos; // [batch, m_rows] or null (every slot visible)
+    float *scores;
+    float scale;
+    float *lse;           // workspace [units][m_rows * G]
+};
+size_t prompt_workspace_bytes(int units, int m_rows, int G);
+hipError_t launch_prompt_scores(const PromptArgs &a, hipStream_t s);
 
 struct SelectArgs {
     CacheDev c;

@@ -204,13 +204,23 @@ kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos,
  * <= q_pos[b*m_rows + r] when q_pos is not NULL (causal prompt scoring), all
  * slots otherwise.  This is the "extra traversal" that maintaining H2O scores
  * costs when attention does not expose its probabilities [GUIDE 16 "limits"],
- * and the prefill scoring of H2O [GUIDE 16 "prefill, decode, TP"].
+ * and the prefill scoring of H2O [GUIDE 16 "prefill, decode, TP"]: with the
+ * prompt's queries as the rows and q_pos their positions, the scores are the
+ * attention the prompt's own causal attention gave each cached token.
  *   q_rows [batch, m_rows, q_heads, head_dim] dtype;  q_pos NULL or
  *   [batch, m_rows] int32.
+ *   workspace  kvc_h2o_accumulate_workspace_bytes(c, m_rows) device bytes
+ *            (bf16, head_dim 128: one fp32 log-sum-exp per query row and head;
+ *            0 bytes and NULL allowed otherwise).
+ * bf16 caches with head_dim 128 run on the matrix cores (two exact passes:
+ * the rows' softmax statistics, then every slot's probability sum in fp64,
+ * a fixed summation order); other shapes use a VALU pass.
  */
+size_t kvc_h2o_accumulate_workspace_bytes(const kvc_cache *c, int32_t m_rows);
 kvc_status kvc_h2o_accumulate(const kvc_cache *c, const void *q_rows,
                               int32_t m_rows, const int32_t *q_pos,
-                              float *h2o_scores, float scale, void *stream);
+                              float *h2o_scores, float scale, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * Selection ("mark" of mark-then-compact [EMP 4.2]).  Reads each unit's

@@ -143,9 +143,19 @@ def test_policy_and_selection_errors():
                                    0x4000, 0x5000, 0x6000, 0.1, 0, ws, need, None) == \
             kvc.ERR_INVALID_ARG
         assert b"decay" in lib.kvc_last_error()
-    assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1000, -1, None, 0x2000, 0.1, None) == \
-        kvc.ERR_INVALID_ARG
-    assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1000, 0, None, 0x2000, 0.1, None) == kvc.OK
+    assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1000, -1, None, 0x2000, 0.1, None, 0,
+                                  None) == kvc.ERR_INVALID_ARG
+    assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1000, 0, None, 0x2000, 0.1, None, 0,
+                                  None) == kvc.OK
+    # bf16 / head_dim 128 runs on the matrix cores and needs one fp32 per row and head
+    need = lib.kvc_h2o_accumulate_workspace_bytes(ctypes.byref(c), 10)
+    assert need >= c.batch * c.kv_heads * 10 * (c.q_heads // c.kv_heads) * 4
+    assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1000, 10, None, 0x2000, 0.1, None, 0,
+                                  None) == kvc.ERR_WORKSPACE
+    assert lib.kvc_h2o_accumulate(ctypes.byref(c), 0x1008, 10, None, 0x2000, 0.1, 0x100000,
+                                  need, None) == kvc.ERR_INVALID_ARG   # q_rows misaligned
+    assert lib.kvc_h2o_accumulate_workspace_bytes(ctypes.byref(_fake_cache(dtype=kvc.F32)),
+                                                  10) == 0
 
 
 def test_workspace_grows_with_the_split():
