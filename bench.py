@@ -162,6 +162,63 @@ def attainable_read_gbs(torch, kvc, mib: int = 2048, reps: int = 10) -> dict:
     return {"gbs": gbs, "how": f"kvc_stream_read over {mib} MiB, mean of {reps} launches"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prompt_scoring(torch, kvc, synth, args):
+    """H2O prompt scoring: every query row of the causal prompt (position r,
+    each of the G heads of a kv head) adds its softmax probabilities over
+    positions 0..r to the scores.  Algorithmic work: one QK^T over the
+    visible (row, slot) pairs, 2 * D flop each (G * P * (P + 1) / 2 pairs per
+    unit); the kernel's two exact passes compute the logits twice."""
+    w = synth.workload(args.workload)
+    B, Hq, Hkv, D, P = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.prompt_len
+    G = Hq // Hkv
+    dev = torch.device("cuda", 0)
+    cache = kvc.KvCache(B, Hq, Hkv, D, P, kvc.BF16, device=dev)
+    cache.k.copy_(synth.device_normal(cache.k.shape, w.seed, w.wid, 1,
+                                      scale_rows_frac=w.heavy_frac))
+    cache.pos.copy_(torch.arange(P, dtype=torch.int32, device=dev).expand(B, Hkv, P))
+    cache.n_slots.fill_(P)
+    q = synth.device_normal((B, P, Hq, D), w.seed, w.wid, 3)
+    qp = torch.arange(P, dtype=torch.int32, device=dev).repeat(B, 1)
+    scores = torch.zeros((B, Hkv, P), device=dev)
+    ws = cache.prompt_workspace(P)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        kvc.h2o_accumulate(cache, q, P, scores, q_pos=qp, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    pairs = B * Hkv * G * P * (P + 1) // 2
+    flops = 2 * D * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"prompt scoring {w.name}: {ms:.3f} ms per call, {tflops:.0f} TFLOP/s algorithmic")
+    print(json.dumps({
+        "metric": "H2O prompt scoring (causal prompt attention summed into the scores)",
+        "value": 1e3 / ms, "unit": "calls/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "prompt": P, "causal": True},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prompt_stats_kernel + prompt_scores_kernel",
+                     "flop_per_call": flops,
+                     "note": "algorithmic = one QK^T over the visible pairs; "
+                             "the two exact passes compute it twice"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +229,9 @@ def main():
                     help="h2o_decay: H2O with a decayed attention activity (decay 0.99)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--prompt-scoring", action="store_true",
+                    help="time H2O prompt scoring (kvc_h2o_accumulate over the causal prompt) "
+                         "instead of the decode step")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -190,6 +250,10 @@ def main():
 
     import compressed_decode_attention_amd as kvc
     import synth
+
+    if args.prompt_scoring:
+        prompt_scoring(torch, kvc, synth, args)
+        return
 
     w = synth.workload(args.workload)
     policy = args.policy

@@ -218,6 +218,7 @@ struct PromptArgs {
     float *scores;
     float scale;
     float *lse;           // workspace [units][m_rows * G]
+    int row_tiles_lds;    // pass 2: row tiles tracked in LDS (0: none, every tile visited)
 };
 size_t prompt_workspace_bytes(int units, int m_rows, int G);
 hipError_t launch_prompt_scores(const PromptArgs &a, hipStream_t s);

@@ -23,7 +23,11 @@
 //     sums (a fixed order: the scores are deterministic), and one lane per
 //     slot adds the total to the score.
 // Tiles that no row of a block can see (from the positions alone) are
-// skipped, which halves the work of a causal prompt.  All blocks of one unit
+// skipped, which halves the work of a causal prompt; tiles that every row sees
+// whole (most of a causal triangle) run without the per-element mask.  The
+// softmax runs in base 2 (scale * log2(e) folded into one factor, the row
+// statistic a base-2 log-sum-exp), so an element costs one multiply-add and
+// one v_exp_f32.  All blocks of one unit
 // run on one XCD (workgroups are dealt round-robin over the eight XCDs), so
 // the K (pass 1) or Q (pass 2) rows they share are read from that XCD's L2.
 #include "kvc_internal.h"
@@ -43,6 +47,7 @@ constexpr int kPD = 128;          // head_dim of this path
 constexpr int kStatRows = 128;    // rows per workgroup, pass 1 (32 per wave)
 constexpr int kScoreSlots = 128;  // slots per workgroup, pass 2 (32 per wave)
 constexpr int kTile = 64;         // slots (pass 1) or rows (pass 2) staged per step
+constexpr int kMaxRowTilesLds = 4096;   // pass 2: row tiles whose largest position fits in LDS
 
 __device__ inline bf16x8_p as_bf(u16x8_p x) { return __builtin_bit_cast(bf16x8_p, x); }
 
@@ -89,15 +94,24 @@ __device__ inline int row_pos(const PromptArgs &a, int b, int R) {
     return a.q_pos ? a.q_pos[(size_t)b * a.m_rows + R / a.c.G] : INT_MAX;
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }   // v_exp_f32
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // pass 1: log-sum-exp of every row over the slots it sees
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kPThreads) void prompt_stats_kernel(PromptArgs a) {
-    __shared__ __align__(16) unsigned char ktile[kTile * 256];
-    __shared__ int kpos[kTile];
+// Software pipeline over the 64-slot tiles that some row of the block sees
+// (found up front from each tile's smallest position): while the MFMAs run on
+// one LDS buffer, the next active tile's K rows are already in registers on
+// their way; one barrier per tile.
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void prompt_stats_kernel(PromptArgs a) {
+    __shared__ __align__(16) unsigned char ktile[2][kTile * 256];
+    __shared__ int kpos[2][kTile];
     __shared__ int red[kPThreads / 64];
+    extern __shared__ int tile_pos[];   // [2][tiles of the capacity]: min, max position
     const CacheDev &c = a.c;
     const int nrows = a.m_rows * c.G;
     const int nblk = (nrows + kStatRows - 1) / kStatRows;
@@ -109,6 +123,8 @@ __global__ __launch_bounds__(kPThreads) void prompt_stats_kernel(PromptArgs a) {
     const int n = load_count(c, u, tid == 0);
     const uint16_t *K = static_cast<const uint16_t *>(c.k);
     const int32_t *P = c.pos + (size_t)u * c.cap;
+    const int ntile = (n + kTile - 1) / kTile;
+    int *tmin_s = tile_pos, *tmax_s = tile_pos + (c.cap + kTile - 1) / kTile;
 
     // B operands: two 16-row tiles per wave; lane (col, r) holds dims
     // 32c + 8r .. 32c + 8r + 7 of row col
@@ -128,28 +144,71 @@ __global__ __launch_bounds__(kPThreads) void prompt_stats_kernel(PromptArgs a) {
         qp[t] = ok ? row_pos(a, b, R) : INT_MIN;
         qmax = max(qmax, qp[t]);
     }
-    qmax = block_max(qmax, red);
-
-    float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};
-    const int ntile = (n + kTile - 1) / kTile;
-    for (int kt = 0; kt < ntile; ++kt) {
+    // smallest and largest position of every slot tile
+    for (int i = tid; i < ntile; i += kPThreads) {
+        tmin_s[i] = INT_MAX;
+        tmax_s[i] = INT_MIN;
+    }
+    qmax = block_max(qmax, red);   // (its barriers also publish the initial values)
+    for (int j = tid; j < n; j += kPThreads) {
+        const int p = P[j];
+        atomicMin(&tmin_s[j / kTile], p);
+        atomicMax(&tmax_s[j / kTile], p);
+    }
+    __syncthreads();
+    // smallest position of each 16-row tile of the wave, and whether the tile
+    // holds no padding row (only such tiles may skip the mask)
+    int qmin[2];
+    bool rows_full[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        qmin[t] = __builtin_amdgcn_readfirstlane(wave_min_i(qp[t]));
+        rows_full[t] = blk * kStatRows + 32 * w + 16 * t + 15 < nrows;
+    }
+    const float c2 = a.scale * kLog2e;
+    // next tile (from kt on) that some row of the block sees (uniform)
+    auto next_active = [&](int kt) {
+        while (kt < ntile && tmin_s[kt] > qmax) ++kt;
+        return kt;
+    };
+    // the tile's K rows and positions into registers; rows past n read row
+    // n - 1 (every load unconditional, in bounds; such slots are masked)
+    u16x8_p pre[kTile / 16];
+    int ppos = 0;
+    auto fetch = [&](int kt) {
         const int j0 = kt * kTile;
-        if (tid < kTile) kpos[tid] = (j0 + tid < n) ? P[j0 + tid] : INT_MAX;
-        __syncthreads();
-        // no row of this block sees a slot of the tile: skip it (uniform)
-        const int kmin = wave_min_i(kpos[lane]);
-        if (kmin > qmax) {
-            __syncthreads();
-            continue;
-        }
 #pragma unroll
         for (int pass = 0; pass < kTile / 16; ++pass) {
-            const int q = 16 * pass + (tid >> 4), ch = tid & 15, j = j0 + q;
-            u16x8_p v = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (j < n) v = *reinterpret_cast<const u16x8_p *>(K + row_of(c, b, h, j) * kPD + 8 * ch);
-            *reinterpret_cast<u16x8_p *>(ktile + tile_off(q, ch)) = v;
+            const int j = min(j0 + 16 * pass + (tid >> 4), n - 1);
+            pre[pass] = *reinterpret_cast<const u16x8_p *>(K + row_of(c, b, h, j) * kPD +
+                                                           8 * (tid & 15));
         }
+        const int jp = min(j0 + (tid & (kTile - 1)), n - 1);
+        const int p = P[jp];
+        ppos = (j0 + (tid & (kTile - 1)) < n) ? p : INT_MAX;
+    };
+
+    float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};
+    int cur = next_active(0);
+    if (cur < ntile) fetch(cur);
+    int buf = 0;
+    while (cur < ntile) {
+        const int j0 = cur * kTile;
+#pragma unroll
+        for (int pass = 0; pass < kTile / 16; ++pass)
+            *reinterpret_cast<u16x8_p *>(ktile[buf] + tile_off(16 * pass + (tid >> 4), tid & 15)) =
+                pre[pass];
+        if (tid < kTile) kpos[buf][tid] = ppos;
         __syncthreads();
+        const int nxt = next_active(cur + 1);
+        if (nxt < ntile) fetch(nxt);   // lands while this tile computes
+        // every row of a 16-row tile sees every slot of a filled 64-slot tile:
+        // no mask (positions alone cannot tell padding, so fullness is checked)
+        const bool slots_full = j0 + kTile <= n;
+        const int kmax = tmax_s[cur];
+        bool inner[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) inner[t] = slots_full && rows_full[t] && kmax <= qmin[t];
 #pragma unroll
         for (int s = 0; s < kTile / 16; ++s) {
             // A operand: lane (col, r) holds dims 32c + 8r.. of slot 16s + col
@@ -157,13 +216,13 @@ __global__ __launch_bounds__(kPThreads) void prompt_stats_kernel(PromptArgs a) {
             u16x8_p ka[4];
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4)
-                ka[c4] = *reinterpret_cast<const u16x8_p *>(ktile + tile_off(q, 4 * c4 + r));
+                ka[c4] = *reinterpret_cast<const u16x8_p *>(ktile[buf] + tile_off(q, 4 * c4 + r));
             // C[slot 4r + i][row col]
             int kp[4];
             bool kv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                kp[i] = kpos[16 * s + 4 * r + i];
+                kp[i] = kpos[buf][16 * s + 4 * r + i];
                 kv[i] = j0 + 16 * s + 4 * r + i < n;
             }
 #pragma unroll
@@ -173,23 +232,28 @@ __global__ __launch_bounds__(kPThreads) void prompt_stats_kernel(PromptArgs a) {
                 for (int c4 = 0; c4 < 4; ++c4)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ka[c4]), as_bf(qb[t][c4]), acc,
                                                                   0, 0, 0);
-                float z[4], zmax = -INFINITY;
+                // base-2 logits (scale * log2 e folded in)
+                float z[4];
+                if (inner[t]) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    z[i] = (kv[i] && kp[i] <= qp[t]) ? acc[i] * a.scale : -INFINITY;
-                    zmax = fmaxf(zmax, z[i]);
+                    for (int i = 0; i < 4; ++i) z[i] = acc[i] * c2;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        z[i] = (kv[i] && kp[i] <= qp[t]) ? acc[i] * c2 : -INFINITY;
                 }
+                const float zmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
                 const float mnew = fmaxf(mm[t], zmax);
                 if (mnew != -INFINITY) {
-                    float sum = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sum += __expf(z[i] - mnew);
-                    ll[t] = ll[t] * __expf(mm[t] - mnew) + sum;
+                    const float sum = (exp2_hw(z[0] - mnew) + exp2_hw(z[1] - mnew)) +
+                                      (exp2_hw(z[2] - mnew) + exp2_hw(z[3] - mnew));
+                    ll[t] = ll[t] * exp2_hw(mm[t] - mnew) + sum;
                     mm[t] = mnew;
                 }
             }
         }
-        __syncthreads();
+        buf ^= 1;
+        cur = nxt;
     }
     // merge the four lanes of each row, then log-sum-exp
 #pragma unroll
@@ -200,23 +264,30 @@ __global__ __launch_bounds__(kPThreads) void prompt_stats_kernel(PromptArgs a) {
             const float mo = __shfl_xor(m, off, 64), lo = __shfl_xor(l, off, 64);
             const float mn = fmaxf(m, mo);
             if (mn != -INFINITY) {
-                l = l * __expf(m - mn) + lo * __expf(mo - mn);
+                l = l * exp2_hw(m - mn) + lo * exp2_hw(mo - mn);
                 m = mn;
             }
         }
+        // base-2 log-sum-exp of the row
         if (r == 0 && Rw[t] < nrows)
-            a.lse[(size_t)u * nrows + Rw[t]] = (l > 0.f) ? m + logf(l) : -INFINITY;
+            a.lse[(size_t)u * nrows + Rw[t]] = (l > 0.f) ? m + log2f(l) : -INFINITY;
     }
 }
 
 // ---------------------------------------------------------------------------
 // pass 2: every slot's score receives the probabilities of all rows
 // ---------------------------------------------------------------------------
+// Software pipeline over the 64-row query tiles that see some slot of the
+// block (from each row tile's largest position, found up front when the
+// number of row tiles fits the LDS table; otherwise every tile is visited and
+// the masks alone decide): the next active tile's rows load into registers
+// while the MFMAs run on the current LDS buffer.
 __global__ __launch_bounds__(kPThreads) void prompt_scores_kernel(PromptArgs a) {
-    __shared__ __align__(16) unsigned char qtile[kTile * 256];
-    __shared__ int rpos[kTile];
-    __shared__ float rlse[kTile];
+    __shared__ __align__(16) unsigned char qtile[2][kTile * 256];
+    __shared__ int rpos[2][kTile];
+    __shared__ float rlse[2][kTile];
     __shared__ int red[kPThreads / 64];
+    extern __shared__ int rtile_max[];   // [row tiles] largest position, when tracked
     const CacheDev &c = a.c;
     const int nrows = a.m_rows * c.G;
     const int nblk = (c.cap + kScoreSlots - 1) / kScoreSlots;
@@ -229,6 +300,8 @@ __global__ __launch_bounds__(kPThreads) void prompt_scores_kernel(PromptArgs a) 
     if (blk * kScoreSlots >= n) return;   // the whole block is past the filled slots
     const uint16_t *K = static_cast<const uint16_t *>(c.k);
     const int32_t *P = c.pos + (size_t)u * c.cap;
+    const int nrt = (nrows + kTile - 1) / kTile;
+    const bool track = nrt <= a.row_tiles_lds;
 
     // B operands: two 16-slot tiles per wave; lane (col, r) holds dims
     // 32c + 8r .. of slot col
@@ -249,33 +322,76 @@ __global__ __launch_bounds__(kPThreads) void prompt_scores_kernel(PromptArgs a) 
         kp[t] = kv[t] ? P[j] : INT_MAX;
         kmin = min(kmin, kp[t]);
     }
-    kmin = block_min(kmin, red);
-
-    double cs[2] = {0.0, 0.0};
-    const int ntile = (nrows + kTile - 1) / kTile;
-    for (int rt = 0; rt < ntile; ++rt) {
-        const int R0 = rt * kTile;
-        if (tid < kTile) {
-            const int R = R0 + tid;
-            const bool ok = R < nrows;
-            rpos[tid] = ok ? row_pos(a, b, R) : INT_MIN;
-            rlse[tid] = ok ? a.lse[(size_t)u * nrows + R] : -INFINITY;
+    if (track)
+        for (int i = tid; i < nrt; i += kPThreads) rtile_max[i] = INT_MIN;
+    kmin = block_min(kmin, red);   // (its barriers also publish the initial values)
+    if (track) {
+        for (int rr = tid; rr < a.m_rows; rr += kPThreads) {
+            const int p = a.q_pos ? a.q_pos[(size_t)b * a.m_rows + rr] : INT_MAX;
+            const int t0 = rr * c.G / kTile, t1 = (rr * c.G + c.G - 1) / kTile;
+            atomicMax(&rtile_max[t0], p);
+            if (t1 != t0) atomicMax(&rtile_max[t1], p);
         }
         __syncthreads();
-        // no row of the tile sees a slot of this block: skip it (uniform)
-        const int tmax = wave_max_i(rpos[lane]);
-        if (tmax < kmin) {
-            __syncthreads();
-            continue;
-        }
+    }
+    // largest position of each 16-slot tile of the wave, and whether all its
+    // slots are filled (only such tiles may skip the mask)
+    int kmaxw[2];
+    bool slots_full[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        kmaxw[t] = __builtin_amdgcn_readfirstlane(wave_max_i(kp[t]));
+        slots_full[t] = blk * kScoreSlots + 32 * w + 16 * t + 15 < n;
+    }
+    const float c2 = a.scale * kLog2e;
+    auto next_active = [&](int rt) {
+        if (track)
+            while (rt < nrt && rtile_max[rt] < kmin) ++rt;
+        return rt;
+    };
+    // the tile's query rows, positions and base-2 log-sum-exps into registers;
+    // rows past the last read the last one (unconditional, in bounds; such
+    // rows are masked)
+    u16x8_p pre[kTile / 16];
+    int ppos = 0;
+    float plse = 0.f;
+    auto fetch = [&](int rt) {
+        const int R0 = rt * kTile;
 #pragma unroll
         for (int pass = 0; pass < kTile / 16; ++pass) {
-            const int q = 16 * pass + (tid >> 4), ch = tid & 15, R = R0 + q;
-            u16x8_p v = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (R < nrows) v = *reinterpret_cast<const u16x8_p *>(q_row(a, b, h, R) + 8 * ch);
-            *reinterpret_cast<u16x8_p *>(qtile + tile_off(q, ch)) = v;
+            const int R = min(R0 + 16 * pass + (tid >> 4), nrows - 1);
+            pre[pass] = *reinterpret_cast<const u16x8_p *>(q_row(a, b, h, R) + 8 * (tid & 15));
+        }
+        const int R = R0 + (tid & (kTile - 1)), Rc = min(R, nrows - 1);
+        const int p = row_pos(a, b, Rc);
+        const float l = a.lse[(size_t)u * nrows + Rc];
+        ppos = R < nrows ? p : INT_MIN;
+        plse = R < nrows ? l : -INFINITY;
+    };
+
+    double cs[2] = {0.0, 0.0};
+    int cur = next_active(0);
+    if (cur < nrt) fetch(cur);
+    int buf = 0;
+    while (cur < nrt) {
+        const int R0 = cur * kTile;
+#pragma unroll
+        for (int pass = 0; pass < kTile / 16; ++pass)
+            *reinterpret_cast<u16x8_p *>(qtile[buf] + tile_off(16 * pass + (tid >> 4), tid & 15)) =
+                pre[pass];
+        if (tid < kTile) {
+            rpos[buf][tid] = ppos;
+            rlse[buf][tid] = plse;
         }
         __syncthreads();
+        const int nxt = next_active(cur + 1);
+        if (nxt < nrt) fetch(nxt);   // lands while this tile computes
+        // every row of a filled 64-row tile sees the wave's whole 16-slot tile
+        const int tmin = __builtin_amdgcn_readfirstlane(wave_min_i(rpos[buf][lane]));
+        const bool rows_full = R0 + kTile <= nrows;
+        bool inner[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) inner[t] = slots_full[t] && rows_full && kmaxw[t] <= tmin;
 #pragma unroll
         for (int s = 0; s < kTile / 16; ++s) {
             // A operand: lane (col, r) holds dims 32c + 8r.. of row 16s + col
@@ -283,14 +399,14 @@ __global__ __launch_bounds__(kPThreads) void prompt_scores_kernel(PromptArgs a) 
             u16x8_p qa[4];
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4)
-                qa[c4] = *reinterpret_cast<const u16x8_p *>(qtile + tile_off(q, 4 * c4 + r));
+                qa[c4] = *reinterpret_cast<const u16x8_p *>(qtile[buf] + tile_off(q, 4 * c4 + r));
             // C[row 4r + i][slot col]
             int rp[4];
             float rl[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                rp[i] = rpos[16 * s + 4 * r + i];
-                rl[i] = rlse[16 * s + 4 * r + i];
+                rp[i] = rpos[buf][16 * s + 4 * r + i];
+                rl[i] = rlse[buf][16 * s + 4 * r + i];   // base 2
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -299,14 +415,20 @@ __global__ __launch_bounds__(kPThreads) void prompt_scores_kernel(PromptArgs a) 
                 for (int c4 = 0; c4 < 4; ++c4)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(qa[c4]), as_bf(kb[t][c4]), acc,
                                                                   0, 0, 0);
-                float part = 0.f;
+                float e[4];
+                if (inner[t]) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    part += (kv[t] && kp[t] <= rp[i]) ? __expf(acc[i] * a.scale - rl[i]) : 0.f;
-                cs[t] += (double)part;
+                    for (int i = 0; i < 4; ++i) e[i] = exp2_hw(fmaf(acc[i], c2, -rl[i]));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        e[i] = (kv[t] && kp[t] <= rp[i]) ? exp2_hw(fmaf(acc[i], c2, -rl[i])) : 0.f;
+                }
+                cs[t] += (double)((e[0] + e[1]) + (e[2] + e[3]));
             }
         }
-        __syncthreads();
+        buf ^= 1;
+        cur = nxt;
     }
     // the four lanes of a slot hold different rows: add them, then the score
 #pragma unroll
@@ -329,8 +451,15 @@ hipError_t launch_prompt_scores(const PromptArgs &a, hipStream_t s) {
     if (nrows == 0) return hipSuccess;
     const int nb1 = (nrows + kStatRows - 1) / kStatRows;
     const int nb2 = (a.c.cap + kScoreSlots - 1) / kScoreSlots;
-    hipLaunchKernelGGL(prompt_stats_kernel, dim3(groups * 8 * nb1), dim3(kPThreads), 0, s, a);
-    hipLaunchKernelGGL(prompt_scores_kernel, dim3(groups * 8 * nb2), dim3(kPThreads), 0, s, a);
+    const size_t tile_bytes = 2 * (size_t)((a.c.cap + kTile - 1) / kTile) * sizeof(int);
+    hipLaunchKernelGGL(prompt_stats_kernel, dim3(groups * 8 * nb1), dim3(kPThreads), tile_bytes, s,
+                       a);
+    // row tiles whose largest position is tracked in LDS (up to 16 KB)
+    PromptArgs a2 = a;
+    const int nrt = (nrows + kTile - 1) / kTile;
+    a2.row_tiles_lds = nrt <= kMaxRowTilesLds ? nrt : 0;
+    hipLaunchKernelGGL(prompt_scores_kernel, dim3(groups * 8 * nb2), dim3(kPThreads),
+                       (size_t)a2.row_tiles_lds * sizeof(int), s, a2);
     return hipGetLastError();
 }
 
