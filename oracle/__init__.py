@@ -50,6 +50,10 @@ def lib():
         L.orc_bytes_per_token.argtypes = [ctypes.c_int64] * 4
         L.orc_bf16_to_f64.restype = None
         L.orc_bf16_to_f64.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16), c_dp]
+        L.orc_e5m2_to_f64.restype = None
+        L.orc_e5m2_to_f64.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_uint8), c_dp]
+        L.orc_f64_to_e5m2.restype = None
+        L.orc_f64_to_e5m2.argtypes = [ctypes.c_int64, c_dp, ctypes.POINTER(ctypes.c_uint8)]
         L.orc_philox4x32_10.restype = None
         L.orc_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32)] * 3
         L.orc_random_key.restype = ctypes.c_uint32
@@ -87,13 +91,32 @@ def bytes_per_token(layers: int, kv_heads: int, head_dim: int, dtype_bytes: int)
 
 
 def decode(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage array (bf16 bit patterns or float32) -> float64, exactly."""
+    """Storage array (bf16 bit patterns, E5M2 codes or float32) -> float64, exactly."""
     if dtype == "f32":
         return np.asarray(x, np.float32).astype(np.float64)
+    if dtype == "e5m2":
+        codes = np.ascontiguousarray(x, dtype=np.uint8)
+        out = np.empty(codes.shape, np.float64)
+        lib().orc_e5m2_to_f64(codes.size, _p(codes, ctypes.c_uint8), _p(out, ctypes.c_double))
+        return out
     bits = np.ascontiguousarray(x, dtype=np.uint16)
     out = np.empty(bits.shape, np.float64)
     lib().orc_bf16_to_f64(bits.size, _p(bits, ctypes.c_uint16), _p(out, ctypes.c_double))
     return out
+
+
+def encode_e5m2(x: np.ndarray) -> np.ndarray:
+    """float64 -> nearest E5M2 codes (ties to even, saturating at +-57344)."""
+    v = np.ascontiguousarray(x, np.float64)
+    out = np.empty(v.shape, np.uint8)
+    lib().orc_f64_to_e5m2(v.size, _p(v, ctypes.c_double), _p(out, ctypes.c_uint8))
+    return out
+
+
+def act_dtype(dtype: str) -> str:
+    """Storage dtype of q, k_new and v_new for a cache of this dtype: an E5M2
+    cache is fed bf16 activations."""
+    return "bf16" if dtype == "e5m2" else dtype
 
 
 def philox4x32_10(ctr, key) -> np.ndarray:
@@ -261,9 +284,14 @@ class Oracle:
         Returns out [Hq, D] float64 and the per-head post-attention scores
         (before eviction, keyed by position) for H2O.
         """
-        q = decode(q_store, self.dtype).reshape(self.Hq, self.D)
-        kn = decode(knew_store, self.dtype).reshape(self.Hkv, self.D)
-        vn = decode(vnew_store, self.dtype).reshape(self.Hkv, self.D)
+        act = act_dtype(self.dtype)
+        q = decode(q_store, act).reshape(self.Hq, self.D)
+        kn = decode(knew_store, act).reshape(self.Hkv, self.D)
+        vn = decode(vnew_store, act).reshape(self.Hkv, self.D)
+        if self.dtype == "e5m2":
+            # the new token is stored, and therefore attended, as E5M2
+            kn = decode(encode_e5m2(kn), "e5m2")
+            vn = decode(encode_e5m2(vn), "e5m2")
         p_new = self.seen[b]
         out = np.empty((self.Hq, self.D))
         post = []

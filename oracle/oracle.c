@@ -19,6 +19,8 @@
  *       "reference implementation".
  *  [R123] J. Salmon, M. Moraes, R. Dror, D. Shaw, "Parallel random numbers: as
  *       easy as 1, 2, 3", SC'11 -- the Philox4x32-10 counter-based generator.
+ *  [OCP8] "OCP 8-bit Floating Point Specification (OFP8)", Open Compute
+ *       Project -- the E5M2 format.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *  - scale 1/sqrt(D); no position encoding applied here (keys already carry it,
@@ -65,6 +67,56 @@ ORC_API void orc_bf16_to_f64(int64_t n, const uint16_t *bits, double *out)
         float f;
         memcpy(&f, &w, sizeof f);
         out[i] = (double)f;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit floating point E5M2 [OCP8]: the fp8 KV-cache dtype of the serving
+ * command on [P2] ("fp8_e5m2").  1 sign bit, 5 exponent bits (bias 15), 2
+ * mantissa bits; exponent field 0 holds zero and the subnormals m * 2^-16,
+ * field 31 holds infinity (m = 0) and NaN (m != 0).  Exact in double. */
+static double e5m2_value(unsigned c)
+{
+    const unsigned s = c >> 7, e = (c >> 2) & 31u, m = c & 3u;
+    double v;
+    if (e == 31u) v = (m == 0u) ? INFINITY : NAN;
+    else if (e == 0u) v = ldexp((double)m, -16);
+    else v = ldexp((double)(4u + m), (int)e - 17);   /* (1 + m/4) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+ORC_API void orc_e5m2_to_f64(int64_t n, const uint8_t *codes, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = e5m2_value(codes[i]);
+}
+
+/* The E5M2 code nearest to x, by plain search over the 124 non-negative
+ * finite codes: ties go to the even code (round to nearest even);
+ * magnitudes at or beyond the largest finite value, 57344, become +-57344
+ * (saturation, as a fp8 cache write does); NaN becomes the NaN code 0x7F
+ * with x's sign. */
+ORC_API void orc_f64_to_e5m2(int64_t n, const double *x, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const double v = x[i];
+        const unsigned sign = signbit(v) ? 0x80u : 0u;
+        if (isnan(v)) {
+            out[i] = (uint8_t)(sign | 0x7Fu);
+            continue;
+        }
+        const double a = fabs(v);
+        unsigned best = 0x7Bu;
+        if (a < 57344.0) {
+            double bestd = INFINITY;
+            for (unsigned c = 0; c <= 0x7Bu; ++c) {
+                const double d = fabs(e5m2_value(c) - a);
+                if (d < bestd || (d == bestd && (c & 1u) == 0u)) {
+                    bestd = d;
+                    best = c;
+                }
+            }
+        }
+        out[i] = (uint8_t)(sign | best);
     }
 }
 

@@ -16,7 +16,10 @@ Recipe (every workload):
     head, position) key row is multiplied by 8 with probability 0.02 before the
     rounding, for prompt keys and for decode keys alike;
   * mixed-length batch: ``L_b = floor(exp(U(ln 512, ln 32768)))`` and a seeded
-    permutation of the physical block ids.
+    permutation of the physical block ids;
+  * E5M2 (fp8) caches: the cached K / V are the same float32 draws truncated to
+    E5M2 codes (sign, exponent, the top two mantissa bits; magnitudes below
+    2^-14 become zero), and q, k_new, v_new stay bf16 activations.
 
 The workloads mirror the shapes the source pages talk about (a heavy-load
 batch of 512 sequences with 2,048-token prompts, a 512-token budget of 64 + 448,
@@ -45,7 +48,7 @@ class Workload:
     q_heads: int
     kv_heads: int
     head_dim: int
-    dtype: str               # "bf16" or "f32"
+    dtype: str               # "bf16", "f32" or "e5m2" (cache; activations bf16)
     prompt_len: int          # cached tokens before the first decode step
     steps: int               # decode steps
     policy: str              # "streaming" | "h2o" | "random" | "full"
@@ -67,7 +70,12 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return {"bf16": 2, "f32": 4, "e5m2": 1}[self.dtype]
+
+    @property
+    def act_dtype(self) -> str:
+        """Storage of q, k_new and v_new."""
+        return "bf16" if self.dtype == "e5m2" else self.dtype
 
 
 WORKLOADS = {
@@ -113,12 +121,27 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
             << np.uint32(16)).view(np.float32)
 
 
+def e5m2_truncated(x: np.ndarray) -> np.ndarray:
+    """float32 -> E5M2 codes by dropping the low mantissa bits (round toward
+    zero; |x| < 2^-14 -> signed zero).  Only used to draw cache contents;
+    draws here never reach the E5M2 overflow range (|x| >= 2^16)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    sign = ((u >> np.uint32(31)) << np.uint32(7)).astype(np.uint8)
+    e = ((u >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64)
+    m = ((u >> np.uint32(21)) & np.uint32(3)).astype(np.int64)
+    assert (e < 143).all(), "draw beyond the E5M2 range"
+    code = np.where(e < 113, 0, ((e - 112) << 2) | m)
+    return (sign | code.astype(np.uint8)).astype(np.uint8)
+
+
 def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Canonical storage form: uint16 bf16 patterns, or float32."""
+    """Canonical storage form: uint16 bf16 patterns, uint8 E5M2 codes, or float32."""
     if dtype == "bf16":
         return bf16_bits(x)
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "e5m2":
+        return e5m2_truncated(x)
     raise ValueError(f"unknown dtype {dtype}")
 
 
@@ -166,7 +189,8 @@ def step_inputs(w: Workload, b: int, step: int):
     kn = normal((w.kv_heads, w.head_dim), w.seed, w.wid, T_KNEW, b, step)
     kn = _heavy_rows(w, kn, T_HEAVY_NEW, b, step)
     vn = normal((w.kv_heads, w.head_dim), w.seed, w.wid, T_VNEW, b, step)
-    return to_storage(q, w.dtype), to_storage(kn, w.dtype), to_storage(vn, w.dtype)
+    act = w.act_dtype
+    return to_storage(q, act), to_storage(kn, act), to_storage(vn, act)
 
 
 def batch_step_inputs(w: Workload, step: int, batch: Optional[int] = None):

@@ -513,3 +513,50 @@ def test_prompt_scores_follow_a_permutation_of_the_slots():
     a = oracle.prompt_scores(q, K, pos, q_pos)
     b = oracle.prompt_scores(q, K[perm], pos[perm], q_pos)
     np.testing.assert_allclose(b, a[perm], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# E5M2 (fp8 KV cache): values from the OCP 8-bit floating point specification
+# ---------------------------------------------------------------------------
+
+E5M2_TABLE = {   # code -> value (sign, 5-bit exponent with bias 15, 2-bit mantissa)
+    0x00: 0.0, 0x01: 2.0 ** -16, 0x02: 2.0 ** -15, 0x03: 3 * 2.0 ** -16, 0x04: 2.0 ** -14,
+    0x3C: 1.0, 0x3D: 1.25, 0x3E: 1.5, 0x3F: 1.75, 0x40: 2.0, 0x7B: 57344.0,
+    0xBC: -1.0, 0xFB: -57344.0, 0x7C: math.inf, 0xFC: -math.inf,
+}
+
+
+def test_e5m2_decodes_the_specification_values():
+    codes = np.array(list(E5M2_TABLE), np.uint8)
+    np.testing.assert_array_equal(oracle.decode(codes, "e5m2"), list(E5M2_TABLE.values()))
+    nan = oracle.decode(np.array([0x7D, 0x7E, 0x7F, 0xFF], np.uint8), "e5m2")
+    assert np.isnan(nan).all()
+    neg0 = oracle.decode(np.array([0x80], np.uint8), "e5m2")[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0
+
+
+def test_e5m2_every_finite_code_round_trips():
+    codes = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], np.uint8)
+    np.testing.assert_array_equal(oracle.encode_e5m2(oracle.decode(codes, "e5m2")), codes)
+
+
+@pytest.mark.parametrize("x,code", [
+    (1.125, 0x3C), (1.375, 0x3E), (1.625, 0x3E), (1.875, 0x40),   # ties to the even code
+    (1.1, 0x3C), (1.2, 0x3D),                                        # nearest
+    (2.0 ** -17, 0x00), (3 * 2.0 ** -17, 0x02), (5 * 2.0 ** -17, 0x02),   # subnormal ties
+    (57344.0, 0x7B), (60000.0, 0x7B), (1e9, 0x7B), (-1e9, 0xFB), (math.inf, 0x7B),  # saturation
+    (-1.0, 0xBC), (-0.0, 0x80),
+])
+def test_e5m2_rounding_and_saturation(x, code):
+    assert int(oracle.encode_e5m2(np.array([x]))[0]) == code
+
+
+def test_e5m2_encoding_is_monotone_and_within_half_a_step():
+    x = np.linspace(-70000, 70000, 200001)
+    c = oracle.encode_e5m2(x)
+    v = oracle.decode(c, "e5m2")
+    assert (np.diff(v) >= 0).all()
+    inside = np.abs(x) <= 57344
+    # relative error of the nearest code: at most 2^-3 of the value (2 mantissa bits)
+    err = np.abs(v[inside] - x[inside])
+    assert (err <= np.maximum(np.abs(x[inside]) * 2.0 ** -3, 2.0 ** -17)).all()
