@@ -29,7 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 # C types
 # ---------------------------------------------------------------------------
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_SHAPE, ERR_WORKSPACE, ERR_HIP = range(6)
-BF16, F32 = 0, 1
+BF16, F32, FP8_E5M2 = 0, 1, 2
 FLAG_FULL, FLAG_BAD_COUNT, FLAG_BAD_BLOCK = 1, 2, 4
 POLICY_FULL, POLICY_STREAMING, POLICY_H2O, POLICY_RANDOM = range(4)
 
@@ -132,7 +132,10 @@ def n_keep(n_candidates: int, keep_ratio: float) -> int:
 # ---------------------------------------------------------------------------
 # tensors -> pointers
 # ---------------------------------------------------------------------------
-_TORCH_DTYPE = {BF16: torch.bfloat16, F32: torch.float32}
+# cache storage per dtype (an E5M2 cache holds its codes as bytes)
+_TORCH_DTYPE = {BF16: torch.bfloat16, F32: torch.float32, FP8_E5M2: torch.uint8}
+# storage of q, k_new and v_new for a cache of each dtype
+ACT_TORCH_DTYPE = {BF16: torch.bfloat16, F32: torch.float32, FP8_E5M2: torch.bfloat16}
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

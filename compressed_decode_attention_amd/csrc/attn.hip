@@ -92,6 +92,9 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
     if (dtype == KVC_BF16) {
         if (a.c.D == 128) return launch_typed<uint16_t, 128>(a, s);
         if (a.c.D == 64) return launch_typed<uint16_t, 64>(a, s);
+    } else if (dtype == KVC_FP8_E5M2) {
+        if (a.c.D == 128) return launch_typed<e5m2_t, 128>(a, s);
+        if (a.c.D == 64) return launch_typed<e5m2_t, 64>(a, s);
     } else {
         if (a.c.D == 128) return launch_typed<float, 128>(a, s);
         if (a.c.D == 64) return launch_typed<float, 64>(a, s);
@@ -106,8 +109,9 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
 // normalised probabilities.  The thread that owns a slot is the only writer of
 // its score, so the accumulation order is fixed.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename TK, int D>
 __global__ __launch_bounds__(kAttnThreads) void accumulate_kernel(AccumArgs a) {
+    using TA = typename ActOf<TK>::type;
     const CacheDev &c = a.c;
     const int G = c.G;
     const int u = blockIdx.x, b = u / c.Hkv, h = u % c.Hkv;
@@ -117,16 +121,16 @@ __global__ __launch_bounds__(kAttnThreads) void accumulate_kernel(AccumArgs a) {
     __shared__ float red[kAttnThreads / 64][kMaxGroup];
 
     const int n = load_count(c, u, tid == 0);
-    const T *K = (const T *)c.k;
+    const TK *K = (const TK *)c.k;
     const int32_t *P = c.pos + (size_t)u * c.cap;
     float *sc = a.scores + (size_t)u * c.cap;
 
     for (int r = 0; r < a.m_rows; ++r) {
-        const T *qp = (const T *)a.q_rows +
+        const TA *qp = (const TA *)a.q_rows +
                       (((size_t)b * a.m_rows + r) * c.Hq + (size_t)h * G) * D;
         const int limit = a.q_pos ? a.q_pos[(size_t)b * a.m_rows + r] : 0x7FFFFFFF;
         __syncthreads();
-        for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<T>::get(qp, e);
+        for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<TA>::get(qp, e);
         __syncthreads();
         float mloc[kMaxGroup], lloc[kMaxGroup];
 #pragma unroll
@@ -137,12 +141,12 @@ __global__ __launch_bounds__(kAttnThreads) void accumulate_kernel(AccumArgs a) {
         // online max / sum over the thread's keys
         for (int j = tid; j < n; j += kAttnThreads) {
             if (P[j] > limit) continue;
-            const T *row = K + row_of(c, b, h, j) * D;
+            const TK *row = K + row_of(c, b, h, j) * D;
             float acc[kMaxGroup];
 #pragma unroll
             for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
             for (int d = 0; d < D; ++d) {
-                const float kv = Elem<T>::get(row, d);
+                const float kv = Elem<TK>::get(row, d);
 #pragma unroll
                 for (int g = 0; g < kMaxGroup; ++g)
                     if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
@@ -187,12 +191,12 @@ __global__ __launch_bounds__(kAttnThreads) void accumulate_kernel(AccumArgs a) {
         // add normalised probabilities
         for (int j = tid; j < n; j += kAttnThreads) {
             if (P[j] > limit) continue;
-            const T *row = K + row_of(c, b, h, j) * D;
+            const TK *row = K + row_of(c, b, h, j) * D;
             float acc[kMaxGroup];
 #pragma unroll
             for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
             for (int d = 0; d < D; ++d) {
-                const float kv = Elem<T>::get(row, d);
+                const float kv = Elem<TK>::get(row, d);
 #pragma unroll
                 for (int g = 0; g < kMaxGroup; ++g)
                     if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
@@ -214,6 +218,11 @@ hipError_t launch_accumulate(const AccumArgs &a, int dtype, hipStream_t s) {
             hipLaunchKernelGGL((accumulate_kernel<uint16_t, 128>), dim3(units), dim3(kAttnThreads), 0, s, a);
         else
             hipLaunchKernelGGL((accumulate_kernel<uint16_t, 64>), dim3(units), dim3(kAttnThreads), 0, s, a);
+    } else if (dtype == KVC_FP8_E5M2) {
+        if (a.c.D == 128)
+            hipLaunchKernelGGL((accumulate_kernel<e5m2_t, 128>), dim3(units), dim3(kAttnThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((accumulate_kernel<e5m2_t, 64>), dim3(units), dim3(kAttnThreads), 0, s, a);
     } else {
         if (a.c.D == 128)
             hipLaunchKernelGGL((accumulate_kernel<float, 128>), dim3(units), dim3(kAttnThreads), 0, s, a);

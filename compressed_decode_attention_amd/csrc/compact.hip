@@ -76,6 +76,10 @@ static hipError_t launch_compact_typed(const CompactArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_compact(const CompactArgs &a, int dtype, hipStream_t s) {
+    if (dtype == KVC_FP8_E5M2) {
+        if (a.c.D == 128) return launch_compact_typed<e5m2_t, 128>(a, s);
+        if (a.c.D == 64) return launch_compact_typed<e5m2_t, 64>(a, s);
+    }
     if (dtype == KVC_BF16) {
         if (a.c.D == 128) return launch_compact_typed<uint16_t, 128>(a, s);
         if (a.c.D == 64) return launch_compact_typed<uint16_t, 64>(a, s);

@@ -23,8 +23,10 @@ struct AttnLds {
 // ===========================================================================
 // decode attention (see attn.hip for the method and citations)
 // ===========================================================================
-template <typename T, int D>
+// TK: cache element; its activations (q, k_new, v_new) are ActOf<TK>.
+template <typename TK, int D>
 __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLds<D> &L) {
+    using TA = typename ActOf<TK>::type;
     const CacheDev &c = a.c;
     const int G = c.G;
     const int b = u / c.Hkv, h = u % c.Hkv;
@@ -43,14 +45,25 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
     const int chunk = (T_len + a.nsplit - 1) / a.nsplit;
     const int j0 = min(s * chunk, T_len), j1 = min(T_len, j0 + chunk);
 
-    const T *qp = (const T *)a.q + ((size_t)b * c.Hq + (size_t)h * G) * D;
-    for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<T>::get(qp, e);
+    const TA *qp = (const TA *)a.q + ((size_t)b * c.Hq + (size_t)h * G) * D;
+    for (int e = tid; e < G * D; e += kAttnThreads) q_s[e] = Elem<TA>::get(qp, e);
     __syncthreads();
 
-    const T *K = (const T *)c.k;
-    const T *V = (const T *)c.v;
-    const T *kn = (const T *)a.k_new + ((size_t)b * c.Hkv + h) * D;
-    const T *vn = (const T *)a.v_new + ((size_t)b * c.Hkv + h) * D;
+    const TK *K = (const TK *)c.k;
+    const TK *V = (const TK *)c.v;
+    const TA *kn = (const TA *)a.k_new + ((size_t)b * c.Hkv + h) * D;
+    const TA *vn = (const TA *)a.v_new + ((size_t)b * c.Hkv + h) * D;
+    // the new token as the cache holds it (an E5M2 cache rounds it)
+    auto knew = [&](int d) {
+        const float x = Elem<TA>::get(kn, d);
+        if constexpr (kIsE5M2<TK>) return e5m2_round(x);
+        else return x;
+    };
+    auto vnew = [&](int d) {
+        const float x = Elem<TA>::get(vn, d);
+        if constexpr (kIsE5M2<TK>) return e5m2_round(x);
+        else return x;
+    };
     const size_t ld = (size_t)c.cap + 1;
     float *lg = a.logits + (size_t)u * G * ld;
 
@@ -59,12 +72,12 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
 #pragma unroll
     for (int g = 0; g < kMaxGroup; ++g) mloc[g] = -INFINITY;
     for (int j = j0 + tid; j < j1; j += kAttnThreads) {
-        const T *row = (j < n) ? K + row_of(c, b, h, j) * D : kn;
+        const TK *row = (j < n) ? K + row_of(c, b, h, j) * D : nullptr;
         float acc[kMaxGroup];
 #pragma unroll
         for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
         for (int d = 0; d < D; ++d) {
-            const float kv = Elem<T>::get(row, d);
+            const float kv = (j < n) ? Elem<TK>::get(row, d) : knew(d);
 #pragma unroll
             for (int g = 0; g < kMaxGroup; ++g)
                 if (g < G) acc[g] = fmaf(q_s[g * D + d], kv, acc[g]);
@@ -123,8 +136,7 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
 #pragma unroll
         for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
         for (int j = j0 + part; j < j1; j += kParts) {
-            const T *row = (j < n) ? V + row_of(c, b, h, j) * D : vn;
-            const float vv = Elem<T>::get(row, d);
+            const float vv = (j < n) ? Elem<TK>::get(V + row_of(c, b, h, j) * D, d) : vnew(d);
 #pragma unroll
             for (int g = 0; g < kMaxGroup; ++g)
                 if (g < G) acc[g] = fmaf(lg[g * ld + j], vv, acc[g]);
@@ -168,12 +180,17 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
 
     // ---- append the new token (the workgroup whose range holds index n)
     if (can_store && j0 <= n && n < j1) {
-        T *Kw = (T *)c.k;
-        T *Vw = (T *)c.v;
+        TK *Kw = (TK *)c.k;
+        TK *Vw = (TK *)c.v;
         const size_t r = row_of(c, b, h, n) * D;
         for (int e = tid; e < D; e += kAttnThreads) {
-            Kw[r + e] = kn[e];
-            Vw[r + e] = vn[e];
+            if constexpr (kIsE5M2<TK>) {
+                Kw[r + e].v = e5m2_encode(Elem<TA>::get(kn, e));
+                Vw[r + e].v = e5m2_encode(Elem<TA>::get(vn, e));
+            } else {
+                Kw[r + e] = kn[e];
+                Vw[r + e] = vn[e];
+            }
         }
         if (tid == 0) c.pos[(size_t)u * c.cap + n] = a.new_pos[b];
     }

@@ -45,7 +45,7 @@ kvc_status check_cache(const kvc_cache *c, const char *what) {
                     c->q_heads / c->kv_heads, kvc::kMaxGroup);
     if (c->head_dim != 64 && c->head_dim != 128)
         return fail(KVC_ERR_UNSUPPORTED, "%s: head_dim %d (built: 64, 128)", what, c->head_dim);
-    if (c->dtype != KVC_BF16 && c->dtype != KVC_F32)
+    if (c->dtype != KVC_BF16 && c->dtype != KVC_F32 && c->dtype != KVC_FP8_E5M2)
         return fail(KVC_ERR_UNSUPPORTED, "%s: dtype %d", what, c->dtype);
     if (c->capacity > kvc::kMaxCapacity)
         return fail(KVC_ERR_UNSUPPORTED, "%s: capacity %d > %d", what, c->capacity,

@@ -82,6 +82,45 @@ template <> struct Elem<float> {
     __device__ static inline float get(const float *p, size_t i) { return p[i]; }
 };
 
+// E5M2 (OCP 8-bit float: sign, 5 exponent bits with bias 15, 2 mantissa
+// bits) cache element.  Decoding uses the hardware conversion (exact); the
+// activations of an E5M2 cache are bf16.
+struct e5m2_t {
+    uint8_t v;
+};
+template <> struct Elem<e5m2_t> {
+    __device__ static inline float get(const e5m2_t *p, size_t i) {
+        return __builtin_amdgcn_cvt_f32_bf8((int)p[i].v, 0);
+    }
+};
+template <typename T> struct ActOf { using type = T; };
+template <> struct ActOf<e5m2_t> { using type = uint16_t; };
+template <typename T> struct IsE5M2 { static constexpr bool value = false; };
+template <> struct IsE5M2<e5m2_t> { static constexpr bool value = true; };
+template <typename T> inline constexpr bool kIsE5M2 = IsE5M2<T>::value;
+
+// Nearest E5M2 code of x: round to nearest, ties to the even code;
+// magnitudes at or beyond the largest finite value 57344 saturate to it; NaN
+// stays NaN.  Integer arithmetic on the binary32 pattern.
+__device__ inline uint8_t e5m2_encode(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return (uint8_t)(sign | 0x7Fu);            // NaN
+    if (a >= 0x47600000u) return (uint8_t)(sign | 0x7Bu);           // >= 57344: saturate
+    if (a < 0x38800000u) {                                           // < 2^-14: m * 2^-16
+        const float m = rintf(__uint_as_float(a) * 65536.0f);        // exact scaling; ties to even
+        return (uint8_t)(sign | (uint32_t)m);                        // m == 4 is the code of 2^-14
+    }
+    // keep 2 of the 23 mantissa bits, ties to even, then re-bias 127 -> 15
+    const uint32_t r = (a + 0x000FFFFFu + ((a >> 21) & 1u)) >> 21;
+    uint32_t code = r - (112u << 2);
+    if (code > 0x7Bu) code = 0x7Bu;
+    return (uint8_t)(sign | code);
+}
+__device__ inline float e5m2_round(float x) {   // the value an E5M2 cache stores for x
+    return __builtin_amdgcn_cvt_f32_bf8((int)e5m2_encode(x), 0);
+}
+
 // ---------------------------------------------------------------------------
 // wave / block reductions
 // ---------------------------------------------------------------------------

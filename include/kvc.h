@@ -57,8 +57,17 @@ typedef enum kvc_status {
 } kvc_status;
 
 typedef enum kvc_dtype {
-    KVC_BF16 = 0, /* K, V, q, k_new, v_new stored as bfloat16 */
-    KVC_F32 = 1   /* ... as float32 */
+    KVC_BF16 = 0,     /* K, V, q, k_new, v_new stored as bfloat16 */
+    KVC_F32 = 1,      /* ... as float32 */
+    /* K, V stored as 8-bit floats E5M2 (OCP 8-bit floating point: sign, 5
+     * exponent bits with bias 15, 2 mantissa bits; no scale), the fp8
+     * KV-cache dtype of the serving command in [BLOG] "reference
+     * implementation"; q, k_new, v_new are bfloat16.  A new token is stored
+     * as the nearest E5M2 value (ties to even, magnitudes beyond 57344
+     * saturate) and attended as stored.  [BLOG] advises measuring the cache
+     * dtype apart from eviction: a KVC_BF16 cache of the same shape is that
+     * reference. */
+    KVC_FP8_E5M2 = 2
 } kvc_dtype;
 
 /* bits OR-ed into *kvc_cache.flags by kernels */

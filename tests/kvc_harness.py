@@ -13,7 +13,7 @@ import compressed_decode_attention_amd as kvc
 import oracle
 import synth
 
-DT = {"bf16": kvc.BF16, "f32": kvc.F32}
+DT = {"bf16": kvc.BF16, "f32": kvc.F32, "e5m2": kvc.FP8_E5M2}
 
 # tolerances (outputs: bf16 inputs, fp32 accumulation vs fp64; scores: relative)
 OUT_ATOL = 2e-3
@@ -25,6 +25,8 @@ def dev(x: np.ndarray, dtype: str) -> torch.Tensor:
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(x, np.uint16).view(np.int16)).view(
             torch.bfloat16).cuda()
+    if dtype == "e5m2":
+        return torch.from_numpy(np.ascontiguousarray(x, np.uint8)).cuda()
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
 
 
@@ -32,6 +34,8 @@ def host(t: torch.Tensor, dtype: str) -> np.ndarray:
     """Device tensor -> storage array (bf16 bit patterns or float32)."""
     if dtype == "bf16":
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    if dtype == "e5m2":
+        return t.contiguous().cpu().numpy().astype(np.uint8)
     return t.contiguous().cpu().numpy()
 
 
@@ -103,14 +107,19 @@ def oracle_unit_attend(dtype: str, q_store: np.ndarray, pre: dict, knew: np.ndar
                        vnew: np.ndarray, scale: float):
     """Oracle attention of one unit over its pre-step entries plus the new token.
 
-    q_store [G, D], knew / vnew [D] (storage).  Returns out [G, D], p-sum over
-    the group for the n cached slots (slot order) and the new token.
+    q_store [G, D], knew / vnew [D] (activation storage; an E5M2 cache takes
+    bf16 activations and holds, hence attends, the new token rounded to
+    E5M2).  Returns out [G, D], p-sum over the group for the n cached slots
+    (slot order) and the new token.
     """
-    K = np.vstack([oracle.decode(pre["k"], dtype).reshape(-1, q_store.shape[1]),
-                   oracle.decode(knew, dtype)[None]])
-    V = np.vstack([oracle.decode(pre["v"], dtype).reshape(-1, q_store.shape[1]),
-                   oracle.decode(vnew, dtype)[None]])
-    out, p = oracle.attend(oracle.decode(q_store, dtype), K, V, scale, want_p=True)
+    act = oracle.act_dtype(dtype)
+    kn, vn = oracle.decode(knew, act), oracle.decode(vnew, act)
+    if dtype == "e5m2":
+        kn = oracle.decode(oracle.encode_e5m2(kn), "e5m2")
+        vn = oracle.decode(oracle.encode_e5m2(vn), "e5m2")
+    K = np.vstack([oracle.decode(pre["k"], dtype).reshape(-1, q_store.shape[1]), kn[None]])
+    V = np.vstack([oracle.decode(pre["v"], dtype).reshape(-1, q_store.shape[1]), vn[None]])
+    out, p = oracle.attend(oracle.decode(q_store, act), K, V, scale, want_p=True)
     return out, p.sum(axis=0)
 
 
