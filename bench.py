@@ -68,18 +68,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def per_unit_bytes(n: int, G: int, D: int, b: int, policy: str) -> int:
+def per_unit_bytes(n: int, G: int, D: int, b: int, policy: str, act_b: int = 0) -> int:
     """Algorithmic HBM bytes of one unit (sequence x kv head) in one steady step.
 
-    n = cached slots before the step.  K and V of the n cached slots are read
-    once; the new token's k, v are read once and written once; the group's q
-    is read and its fp32 output written; H2O reads and writes one fp32 score
-    per attended slot; every policy but 'full' reads one int32 position per
-    cached slot (the selection), and the new slot's position is written.
+    n = cached slots before the step, b = bytes of a cached K / V element,
+    act_b = bytes of an activation element (q, k_new, v_new; default b).  K and
+    V of the n cached slots are read once; the new token's k, v are read once
+    (activations) and written once (cache elements); the group's q is read
+    and its fp32 output written; H2O reads and writes one fp32 score per
+    attended slot; every policy but 'full' reads one int32 position per cached
+    slot (the selection), and the new slot's position is written.
     """
+    act_b = act_b or b
     kv = 2 * n * D * b
-    new = 4 * D * b
-    qo = G * D * (b + 4)
+    new = 2 * D * act_b + 2 * D * b
+    qo = G * D * (act_b + 4)
     sc = 8 * (n + 1) if policy.startswith("h2o") else 0
     pos = 4 * n if policy != "full" else 0
     return kv + new + qo + sc + pos + 4
@@ -227,6 +230,8 @@ def main():
     ap.add_argument("--workload", default="heavy_load_b512_l2048")
     ap.add_argument("--policy", default="h2o", choices=["h2o", "h2o_decay", "streaming", "full"],
                     help="h2o_decay: H2O with a decayed attention activity (decay 0.99)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="fp8: K / V cached as E5M2 codes (activations stay bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--prompt-scoring", action="store_true",
@@ -255,23 +260,37 @@ def main():
         prompt_scoring(torch, kvc, synth, args)
         return
 
-    w = synth.workload(args.workload)
+    f8 = args.kv_dtype == "fp8"
+    w = synth.workload(args.workload, dtype="e5m2" if f8 else "bf16")
     policy = args.policy
     B, Hq, Hkv, D, P = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.prompt_len
     G = Hq // Hkv
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cap = P + 1 if policy != "full" else P + 2 + args.warmup + 2 * args.steps
-    log(f"workload {w.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} prompt={P} policy={policy} cap={cap}")
+    log(f"workload {w.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} prompt={P} policy={policy} cap={cap} "
+        f"kv={w.dtype}")
 
     gen = torch.Generator(device=dev).manual_seed(w.seed)
-    cache = kvc.KvCache(B, Hq, Hkv, D, cap, kvc.BF16, device=dev)
+    cache = kvc.KvCache(B, Hq, Hkv, D, cap, kvc.FP8_E5M2 if f8 else kvc.BF16, device=dev)
+
+    def stored(x):
+        """normal draws -> cache storage (E5M2: the draw's sign, exponent and
+        top two mantissa bits; |x| < 2^-14 -> zero)"""
+        if not f8:
+            return x.to(torch.bfloat16)
+        u = x.view(torch.int32)
+        sign = (u >> 24) & 0x80
+        e = (u >> 23) & 0xFF
+        code = torch.where(e < 113, torch.zeros_like(u), ((e - 112) << 2) | ((u >> 21) & 3))
+        return (sign | code).to(torch.uint8)
+
     for b0 in range(0, B, 64):
         sl = slice(b0, min(B, b0 + 64))
-        cache.k[sl, :, :P] = torch.randn(cache.k[sl, :, :P].shape, generator=gen, device=dev,
-                                         dtype=torch.float32).to(torch.bfloat16)
-        cache.v[sl, :, :P] = torch.randn(cache.v[sl, :, :P].shape, generator=gen, device=dev,
-                                         dtype=torch.float32).to(torch.bfloat16)
+        cache.k[sl, :, :P] = stored(torch.randn(cache.k[sl, :, :P].shape, generator=gen,
+                                                device=dev, dtype=torch.float32))
+        cache.v[sl, :, :P] = stored(torch.randn(cache.v[sl, :, :P].shape, generator=gen,
+                                                device=dev, dtype=torch.float32))
     cache.pos[:, :, :P] = torch.arange(P, dtype=torch.int32, device=dev)
     cache.n_slots.fill_(P)
     scores = torch.zeros((B, Hkv, cap), device=dev) if policy.startswith("h2o") else None
@@ -356,11 +375,11 @@ def main():
     log(f"attainable read-only stream: {attain['gbs']:.0f} GB/s")
 
     n_cached = n_after if policy != "full" else P + 1 + args.warmup + args.steps
-    unit_bytes = per_unit_bytes(n_cached, G, D, 2, policy)
+    unit_bytes = per_unit_bytes(n_cached, G, D, 1 if f8 else 2, policy, act_b=2)
     step_bytes = unit_bytes * B * Hkv
     achieved = step_bytes / (launch_ms * 1e-3) / 1e9
     steps_per_s = 1e3 / ms_per_step
-    traffic = profiled_traffic(w.name, policy)
+    traffic = None if f8 else profiled_traffic(w.name, policy)
 
     result = {
         "metric": "decode steps/s and achieved HBM GB/s (% of peak), attn+evict, B=512 L=2048",
@@ -378,7 +397,8 @@ def main():
         "config": {
             "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
             "prompt": P, "policy": policy, "budget": "64+448" if policy != "full" else "none",
-            "cached_per_unit": n_cached, "kv_dtype": "bf16", "accumulate": "fp32",
+            "cached_per_unit": n_cached, "kv_dtype": "e5m2" if f8 else "bf16",
+            "accumulate": "fp32",
             "tokens_per_s": steps_per_s * B, "trim_step_ms": trim_ms,
         },
         "roofline": {

@@ -32,6 +32,12 @@
 //    general case an 8-bit radix select over 64-bit (key, position) words.
 //  * compaction pairs evicted slots below n_out with kept slots at or above
 //    n_out; the new token is written straight into its final slot.
+// E5M2 caches (8-bit codes, bf16 activations) run the same kernel: a lane
+// loads 8 codes (8 B) where it loads 8 bf16 values (16 B) for bf16, which
+// keeps every lane's share of a row the same, and widens them to bf16 with
+// the hardware conversion (exact: every E5M2 value is a bf16 value) before
+// the staging and the repack.  The new token is rounded to E5M2 once, and
+// that rounded row is what is attended and stored.
 // Units longer than the launch's LDS capacity (or a full cache) take the
 // generic per-unit routines inside the same workgroup, so results never
 // depend on the length hint.
@@ -43,6 +49,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
@@ -53,8 +61,16 @@ constexpr int kHD = 128;   // head_dim of the fast path
 #ifndef KVC_DV
 #define KVC_DV 2
 #endif
+#ifndef KVC_DK8
+#define KVC_DK8 4
+#endif
+#ifndef KVC_DV8
+#define KVC_DV8 3
+#endif
 constexpr int kDK = KVC_DK;   // K tiles (16 keys x 256 B) in flight per wave
 constexpr int kDV = KVC_DV;   // V tiles (16 keys x 256 B) in flight per wave
+constexpr int kDK8 = KVC_DK8;   // the same for E5M2 rows (16 keys x 128 B)
+constexpr int kDV8 = KVC_DV8;
 #ifndef KVC_WAVES_PER_EU
 #define KVC_WAVES_PER_EU 4
 #endif
@@ -73,7 +89,9 @@ struct FusedSmall {
     uint32_t mn_hi[kFWaves], mn_lo[kFWaves];
     int sh[8];
     int blk[kFusedMaxT / 16 + 1];   // paged: block ids of the attended slots
-    u16x8_t knew[kHD / 8];          // the new token's key row
+    u16x8_t knew[kHD / 8];          // the new token's key row (as attended)
+    alignas(16) u32x2_t kenc[kHD / 8];   // E5M2: the new token's stored K row
+    alignas(16) u32x2_t venc[kHD / 8];   // ... and V row
 };
 
 __device__ inline bf16x8_t as_bf16x8(u16x8_t x) { return __builtin_bit_cast(bf16x8_t, x); }
@@ -86,6 +104,34 @@ __device__ inline int lg_col(int j) { return (j & ~15) | ((j & 3) << 2) | ((j >>
 // float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ inline short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
 __device__ inline float bf16_value(short b) { return __uint_as_float((uint32_t)(uint16_t)b << 16); }
+
+// E5M2 codes of one lane's 8 dims -> bf16 (v_cvt_scalef32_pk_bf16_bf8 with
+// scale 1 widens two codes; exact for all 256 codes incl. inf / NaN)
+__device__ inline u16x8_t e5m2x8_to_bf16(u32x2_t x) {
+    uint4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x[0], 1.f, false));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x[0], 1.f, true));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x[1], 1.f, false));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)x[1], 1.f, true));
+    return __builtin_bit_cast(u16x8_t, o);
+}
+__device__ inline u16x8_t as_bf16_row(u16x8_t x) { return x; }
+__device__ inline u16x8_t as_bf16_row(u32x2_t x) { return e5m2x8_to_bf16(x); }
+
+// 8 bf16 values -> their nearest E5M2 codes (the cache's rounding of a new token)
+__device__ inline u32x2_t e5m2x8_encode(u16x8_t x) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo |= (uint32_t)e5m2_encode(__uint_as_float((uint32_t)x[e] << 16)) << (8 * e);
+        hi |= (uint32_t)e5m2_encode(__uint_as_float((uint32_t)x[4 + e] << 16)) << (8 * e);
+    }
+    return u32x2_t{lo, hi};
+}
+
+// one lane's 8 dims of a K or V row as loaded: 8 bf16 (16 B) or 8 E5M2 codes (8 B)
+template <bool F8> struct KvRow { using type = u16x8_t; static constexpr int kBytes = 16; };
+template <> struct KvRow<true> { using type = u32x2_t; static constexpr int kBytes = 8; };
 
 __device__ inline void load_q(u16x8_t (&qa)[4], const uint16_t *qp, bool valid, int r) {
 #pragma unroll
@@ -111,11 +157,16 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              kRsrcWord3);
 }
-__device__ inline u16x8_t buffer_row(__amdgpu_buffer_rsrc_t rs, int voff) {
-    return __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+template <bool F8>
+__device__ inline typename KvRow<F8>::type buffer_row(__amdgpu_buffer_rsrc_t rs, int voff) {
+    if constexpr (F8)
+        return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0));
+    else
+        return __builtin_bit_cast(u16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
 }
 
-template <bool PAGED>
+// RB = bytes of one K or V row (256 for bf16, 128 for E5M2)
+template <bool PAGED, int RB>
 struct TileSrc {
     const unsigned char *k0, *v0;   // contiguous: the unit's slot 0; paged: pool + head offset
     const int *blk_s;               // paged: the sequence's block ids, staged in LDS
@@ -129,24 +180,24 @@ struct TileSrc {
         shift = PAGED ? __ffs(c.bs) - 1 : 0;
         mask = PAGED ? c.bs - 1 : 0;
         const size_t first = PAGED ? (size_t)h * c.bs : ((size_t)b * c.Hkv + h) * (size_t)c.cap;
-        k0 = static_cast<const unsigned char *>(c.k) + first * (2 * kHD);
-        v0 = static_cast<const unsigned char *>(c.v) + first * (2 * kHD);
-        nbytes = (uint32_t)n * (2 * kHD);
-        blk_bytes = PAGED ? (uint32_t)(c.Hkv * c.bs * 2 * kHD) : 0u;
+        k0 = static_cast<const unsigned char *>(c.k) + first * RB;
+        v0 = static_cast<const unsigned char *>(c.v) + first * RB;
+        nbytes = (uint32_t)n * RB;
+        blk_bytes = PAGED ? (uint32_t)(c.Hkv * c.bs * RB) : 0u;
     }
     // resource holding tile t (K or V) and the tile's byte offset inside it
     __device__ inline void tile(int t, bool v, __amdgpu_buffer_rsrc_t &rs, int &toff) const {
         if constexpr (!PAGED) {
             rs = make_rsrc(v ? v0 : k0, nbytes);
-            toff = 16 * 2 * kHD * t;
+            toff = 16 * RB * t;
         } else {
             const int j0 = 16 * t;
             const int rows = min(max(n - j0, 0), 16);
             const int last = n > 0 ? n - 1 : 0;
             int blk = __builtin_amdgcn_readfirstlane(blk_s[(j0 < last ? j0 : last) >> shift]);
             blk = rows > 0 ? blk : 0;
-            const size_t off = (size_t)blk * blk_bytes + (size_t)(j0 & mask) * (2 * kHD);
-            rs = make_rsrc((v ? v0 : k0) + off, (uint32_t)rows * (2 * kHD));
+            const size_t off = (size_t)blk * blk_bytes + (size_t)(j0 & mask) * RB;
+            rs = make_rsrc((v ? v0 : k0) + off, (uint32_t)rows * RB);
             toff = 0;
         }
     }
@@ -165,21 +216,27 @@ __device__ inline uint64_t rank_word(uint32_t primary, int32_t pos) {
     return ((uint64_t)primary << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
 }
 
-template <int MODE>
+template <int MODE, bool F8>
 __device__ void fused_generic(const FusedArgs &fa, int u, unsigned char *smem) {
-    attn_unit_generic<uint16_t, kHD>(fa.attn, u, 0, *reinterpret_cast<AttnLds<kHD> *>(smem));
+    using TK = typename std::conditional<F8, e5m2_t, uint16_t>::type;
+    attn_unit_generic<TK, kHD>(fa.attn, u, 0, *reinterpret_cast<AttnLds<kHD> *>(smem));
     if (MODE == kModeAttn) return;
     __syncthreads();
     select_unit<1>(fa.sel, u, *reinterpret_cast<SelLds<1> *>(smem));
     __syncthreads();
-    compact_unit<uint16_t, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
+    compact_unit<TK, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
 }
 
 // PACK2: G <= 8, so one P.V MFMA carries both bf16 parts of p (rows 0..7 and
-// 8..15); otherwise each tile takes two MFMAs per dim block.
-template <int MODE, bool PAGED, int TC, bool PACK2>
+// 8..15); otherwise each tile takes two MFMAs per dim block.  F8: E5M2 cache.
+template <int MODE, bool PAGED, int TC, bool PACK2, bool F8>
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void fused_kernel(FusedArgs fa) {
+    using Row = typename KvRow<F8>::type;
+    constexpr int RB = F8 ? kHD : 2 * kHD;   // bytes of one cached K or V row
+    constexpr int NP = RB / 16;                // its 16-byte parts
+    constexpr int DK = F8 ? kDK8 : kDK;
+    constexpr int DV = F8 ? kDV8 : kDV;
     // most K tiles / V groups one wave handles: fixed trip counts let the
     // loops unroll into straight-line code with exact load/wait pairing
     constexpr int kNTW = (TC / 16 + kFWaves - 1) / kFWaves;
@@ -200,7 +257,7 @@ void fused_kernel(FusedArgs fa) {
     const int n = __builtin_amdgcn_readfirstlane(load_count(c, u, tid == 0));
     const int T = n + 1;
     if (T > TC || n >= c.cap) {
-        fused_generic<MODE>(fa, u, smem);
+        fused_generic<MODE, F8>(fa, u, smem);
         return;
     }
 
@@ -216,8 +273,8 @@ void fused_kernel(FusedArgs fa) {
     uint8_t *flg_s = reinterpret_cast<uint8_t *>(key_s + TC);
     FusedSmall &sm = *reinterpret_cast<FusedSmall *>(stage_all + stage_region_bytes(TC));
 
-    const uint16_t *K = static_cast<const uint16_t *>(c.k);
-    const uint16_t *V = static_cast<const uint16_t *>(c.v);
+    const unsigned char *K = static_cast<const unsigned char *>(c.k);
+    const unsigned char *V = static_cast<const unsigned char *>(c.v);
     const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (size_t)u * kHD;
     const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (size_t)u * kHD;
     int32_t *P = c.pos + (size_t)u * c.cap;
@@ -261,7 +318,7 @@ void fused_kernel(FusedArgs fa) {
     // ---------------- logits: MFMA 16x16x32 bf16, A = queries, B = 16 keys
     const int ntiles = (T + 15) >> 4;
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    const TileSrc<PAGED> src(c, b, h, n, sm.blk);
+    const TileSrc<PAGED, RB> src(c, b, h, n, sm.blk);
     // K tile t = slots 16t .. 16t+15.  Loads are coalesced: instruction k of a
     // lane reads 16 B (chunk 'col') of row 4k + r, so one wave instruction
     // covers 4 whole rows; rows at or past n come back as zeros, and the lane
@@ -269,19 +326,19 @@ void fused_kernel(FusedArgs fa) {
     // through the wave's LDS staging buffer, chunk c of row q stored at slot
     // c ^ q (conflict-free on both sides), and comes back in the MFMA B
     // layout: key = col, 8 dims per 16-lane group.
-    const int lane_off = r * (2 * kHD) + 16 * col;
-    auto kload = [&](int t, int k) -> u16x8_t {
+    const int lane_off = r * RB + KvRow<F8>::kBytes * col;
+    auto kload = [&](int t, int k) -> Row {
         __amdgpu_buffer_rsrc_t rs;
         int toff;
         src.tile(t, false, rs, toff);
-        return buffer_row(rs, lane_off + toff + 4 * (2 * kHD) * k);
+        return buffer_row<F8>(rs, lane_off + toff + 4 * RB * k);
     };
     const int tn = n >> 4, qn = n & 15;   // tile and row of the new token
     int pmax = -1;
     {
-        u16x8_t kb[kDK][4];
+        Row kb[DK][4];
 #pragma unroll
-        for (int d = 0; d < kDK; ++d)
+        for (int d = 0; d < DK; ++d)
 #pragma unroll
             for (int k = 0; k < 4; ++k) kb[d][k] = kload(w + kFWaves * d, k);
         // the staged values land in LDS while the first K tiles are in flight.
@@ -297,7 +354,15 @@ void fused_kernel(FusedArgs fa) {
             pmax = max(pmax, pj);
             sc_s[jw] = (h2o && old_slot) ? sst[i] : 0.f;
         }
-        if (tid < kHD / 8) sm.knew[tid] = knr;
+        if (tid < kHD / 8) {
+            if constexpr (F8) {
+                const u32x2_t ke = e5m2x8_encode(knr);
+                sm.kenc[tid] = ke;
+                sm.knew[tid] = e5m2x8_to_bf16(ke);
+            } else {
+                sm.knew[tid] = knr;
+            }
+        }
         __syncthreads();   // the new key row is in LDS
 #pragma unroll
         for (int i = 0; i < kNTW; ++i) {
@@ -305,13 +370,14 @@ void fused_kernel(FusedArgs fa) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int q = 4 * k + r;
-                *reinterpret_cast<u16x8_t *>(stage + q * 256 + ((col ^ q) << 4)) = kb[i % kDK][k];
+                *reinterpret_cast<u16x8_t *>(stage + q * 256 + ((col ^ q) << 4)) =
+                    as_bf16_row(kb[i % DK][k]);
             }
             if (t == tn && lane < 16)   // row n read as zeros: put the new key there
                 *reinterpret_cast<u16x8_t *>(stage + qn * 256 + ((lane ^ qn) << 4)) = sm.knew[lane];
-            if (i + kDK < kNTW)
+            if (i + DK < kNTW)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) kb[i % kDK][k] = kload(t + kFWaves * kDK, k);
+                for (int k = 0; k < 4; ++k) kb[i % DK][k] = kload(t + kFWaves * DK, k);
             u16x8_t kop[4];
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4)
@@ -336,16 +402,21 @@ void fused_kernel(FusedArgs fa) {
     // V rows do not depend on the softmax: start streaming them now.  Wave w
     // takes the same tiles as for K; instruction k of a lane reads chunk col
     // of row 16t + 4k + r (zeros at or past n; row n is the new token's).
-    auto vload = [&](int t, int k) -> u16x8_t {
+    auto vload = [&](int t, int k) -> Row {
         __amdgpu_buffer_rsrc_t rs;
         int toff;
         src.tile(t, true, rs, toff);
-        return buffer_row(rs, lane_off + toff + 4 * (2 * kHD) * k);
+        return buffer_row<F8>(rs, lane_off + toff + 4 * RB * k);
     };
-    const u16x8_t vnc = *reinterpret_cast<const u16x8_t *>(vn + 8 * col);
-    u16x8_t vb[kDV][4];
+    u16x8_t vnc = *reinterpret_cast<const u16x8_t *>(vn + 8 * col);
+    if constexpr (F8) {
+        const u32x2_t ve = e5m2x8_encode(vnc);
+        if (tid < kHD / 8) sm.venc[tid] = ve;   // lanes 0..15: col = tid
+        vnc = e5m2x8_to_bf16(ve);
+    }
+    Row vb[DV][4];
 #pragma unroll
-    for (int d = 0; d < kDV; ++d)
+    for (int d = 0; d < DV; ++d)
 #pragma unroll
         for (int k = 0; k < 4; ++k) vb[d][k] = vload(w + kFWaves * d, k);
     // row maxima (16-lane groups share a query head set, then across waves),
@@ -411,14 +482,15 @@ void fused_kernel(FusedArgs fa) {
         // B operand of MFMA m: element m of the four rows this lane loaded
         u16x8_t vr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[e] = (16 * t + 4 * e + r == n) ? vnc : vb[i % kDV][e];
+        for (int e = 0; e < 4; ++e)
+            vr[e] = (16 * t + 4 * e + r == n) ? vnc : as_bf16_row(vb[i % DV][e]);
         s16x4_t bop[8];
 #pragma unroll
         for (int m8 = 0; m8 < 8; ++m8)
             bop[m8] = s16x4_t{(short)vr[0][m8], (short)vr[1][m8], (short)vr[2][m8], (short)vr[3][m8]};
-        if (i + kDV < kNTW)
+        if (i + DV < kNTW)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) vb[i % kDV][k] = vload(t + kFWaves * kDV, k);
+            for (int k = 0; k < 4; ++k) vb[i % DV][k] = vload(t + kFWaves * DV, k);
 #pragma unroll
         for (int m8 = 0; m8 < 8; ++m8)
             oacc[m8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, bop[m8], oacc[m8], 0, 0, 0);
@@ -481,18 +553,28 @@ void fused_kernel(FusedArgs fa) {
         }
     }
 
-    uint16_t *Kw = static_cast<uint16_t *>(c.k);
-    uint16_t *Vw = static_cast<uint16_t *>(c.v);
+    unsigned char *Kw = static_cast<unsigned char *>(c.k);
+    unsigned char *Vw = static_cast<unsigned char *>(c.v);
+    // 16-byte part p of the new token's stored K / V row
+    auto knew_part = [&](int p) -> uint4 {
+        if constexpr (F8) return reinterpret_cast<const uint4 *>(sm.kenc)[p];
+        else return reinterpret_cast<const uint4 *>(kn)[p];
+    };
+    auto vnew_part = [&](int p) -> uint4 {
+        if constexpr (F8) return reinterpret_cast<const uint4 *>(sm.venc)[p];
+        else return reinterpret_cast<const uint4 *>(vn)[p];
+    };
+    auto store_new = [&](int slot) {   // lanes 0..NP-1
+        const size_t rw = row_of(c, b, h, slot) * RB;
+        reinterpret_cast<uint4 *>(Kw + rw)[tid] = knew_part(tid);
+        reinterpret_cast<uint4 *>(Vw + rw)[tid] = vnew_part(tid);
+    };
 
     if (MODE == kModeAttn) {
         // append the new token at slot n, write every score back
         if (h2o)
             for (int j = tid; j < T; j += kFThreads) S[j] = sc_s[j];
-        if (tid < 16) {
-            const size_t rw = row_of(c, b, h, n) * kHD;
-            reinterpret_cast<uint4 *>(Kw + rw)[tid] = reinterpret_cast<const uint4 *>(kn)[tid];
-            reinterpret_cast<uint4 *>(Vw + rw)[tid] = reinterpret_cast<const uint4 *>(vn)[tid];
-        }
+        if (tid < NP) store_new(n);
         if (tid == 0) {
             P[n] = npos;
             c.n_slots[u] = n + 1;
@@ -583,11 +665,7 @@ void fused_kernel(FusedArgs fa) {
         const int e = (extra == 1) ? barg : (ndrop == 1 ? dslot : -1);
         const int n_out = (e < 0) ? T : n;
         const int dst_new = (e < 0) ? n : (e < n ? e : -1);
-        if (dst_new >= 0 && tid < 16) {
-            const size_t rw = row_of(c, b, h, dst_new) * kHD;
-            reinterpret_cast<uint4 *>(Kw + rw)[tid] = reinterpret_cast<const uint4 *>(kn)[tid];
-            reinterpret_cast<uint4 *>(Vw + rw)[tid] = reinterpret_cast<const uint4 *>(vn)[tid];
-        }
+        if (dst_new >= 0 && tid < NP) store_new(dst_new);
         if (h2o)
             for (int j = tid; j < n; j += kFThreads)
                 if (j != e) S[j] = sc_s[j];
@@ -675,14 +753,15 @@ void fused_kernel(FusedArgs fa) {
     }
     __syncthreads();
     const int moves = min(nh, ns);
-    for (int e = tid; e < moves * 16; e += kFThreads) {
-        const int i = e >> 4, part = e & 15;
+    for (int e = tid; e < moves * NP; e += kFThreads) {
+        const int i = e / NP, part = e % NP;
         const int d = hole[i], s = srcl[i];
-        const size_t rd = row_of(c, b, h, d) * kHD;
-        const uint4 *ks = reinterpret_cast<const uint4 *>((s == n) ? kn : K + row_of(c, b, h, s) * kHD);
-        const uint4 *vs = reinterpret_cast<const uint4 *>((s == n) ? vn : V + row_of(c, b, h, s) * kHD);
-        reinterpret_cast<uint4 *>(Kw + rd)[part] = ks[part];
-        reinterpret_cast<uint4 *>(Vw + rd)[part] = vs[part];
+        const size_t rd = row_of(c, b, h, d) * RB;
+        const size_t rs = row_of(c, b, h, s) * RB;
+        reinterpret_cast<uint4 *>(Kw + rd)[part] =
+            (s == n) ? knew_part(part) : reinterpret_cast<const uint4 *>(K + rs)[part];
+        reinterpret_cast<uint4 *>(Vw + rd)[part] =
+            (s == n) ? vnew_part(part) : reinterpret_cast<const uint4 *>(V + rs)[part];
     }
     for (int i = tid; i < moves; i += kFThreads) {
         const int d = hole[i], s = srcl[i];
@@ -695,11 +774,7 @@ void fused_kernel(FusedArgs fa) {
             if (h2o) S[j] = sc_s[j];
             if (j == n) P[n] = npos;
         }
-    if (n < n_out && tid < 16) {
-        const size_t rw = row_of(c, b, h, n) * kHD;
-        reinterpret_cast<uint4 *>(Kw + rw)[tid] = reinterpret_cast<const uint4 *>(kn)[tid];
-        reinterpret_cast<uint4 *>(Vw + rw)[tid] = reinterpret_cast<const uint4 *>(vn)[tid];
-    }
+    if (n < n_out && tid < NP) store_new(n);
     if (tid == 0) c.n_slots[u] = n_out;
 }
 
@@ -713,43 +788,56 @@ size_t fused_smem_bytes(int G, int tcap) {
     return fast > gen ? fast : gen;
 }
 
-template <int MODE, bool PAGED, int TC>
+template <int MODE, bool PAGED, int TC, bool F8>
 static void launch_pk(const FusedArgs &fa, bool pack2, size_t smem, hipStream_t s) {
     const dim3 grid(fa.attn.c.B * fa.attn.c.Hkv), block(kFThreads);
     if (pack2)
-        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, true>), grid, block, smem, s, fa);
+        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, true, F8>), grid, block, smem, s, fa);
     else
-        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, false>), grid, block, smem, s, fa);
+        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, false, F8>), grid, block, smem, s, fa);
+}
+
+// every instantiation of one LDS capacity may use its largest LDS size
+template <int TC, bool F8>
+static hipError_t allow_smem(int most) {
+    const void *fns[8] = {(const void *)fused_kernel<kModeAttn, false, TC, true, F8>,
+                          (const void *)fused_kernel<kModeStep, false, TC, true, F8>,
+                          (const void *)fused_kernel<kModeAttn, true, TC, true, F8>,
+                          (const void *)fused_kernel<kModeStep, true, TC, true, F8>,
+                          (const void *)fused_kernel<kModeAttn, false, TC, false, F8>,
+                          (const void *)fused_kernel<kModeStep, false, TC, false, F8>,
+                          (const void *)fused_kernel<kModeAttn, true, TC, false, F8>,
+                          (const void *)fused_kernel<kModeStep, true, TC, false, F8>};
+    hipError_t e = hipSuccess;
+    for (const void *f : fns)
+        if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, most);
+    return e;
+}
+
+template <int TC, bool F8>
+static void launch_mode(const FusedArgs &fa, int mode, bool pack2, size_t smem, hipStream_t s) {
+    const bool paged = fa.attn.c.bs > 0;
+    if (mode == kModeAttn)
+        paged ? launch_pk<kModeAttn, true, TC, F8>(fa, pack2, smem, s)
+              : launch_pk<kModeAttn, false, TC, F8>(fa, pack2, smem, s);
+    else
+        paged ? launch_pk<kModeStep, true, TC, F8>(fa, pack2, smem, s)
+              : launch_pk<kModeStep, false, TC, F8>(fa, pack2, smem, s);
 }
 
 template <int TC>
 static hipError_t launch_tc(const FusedArgs &fa, int mode, size_t smem, hipStream_t s) {
-    const bool paged = fa.attn.c.bs > 0;
-    static hipError_t attr = [smem] {
-        (void)smem;
+    static hipError_t attr = [] {
         const int most = (int)fused_smem_bytes(kMaxGroup, TC);
-        const void *fns[8] = {(const void *)fused_kernel<kModeAttn, false, TC, true>,
-                              (const void *)fused_kernel<kModeStep, false, TC, true>,
-                              (const void *)fused_kernel<kModeAttn, true, TC, true>,
-                              (const void *)fused_kernel<kModeStep, true, TC, true>,
-                              (const void *)fused_kernel<kModeAttn, false, TC, false>,
-                              (const void *)fused_kernel<kModeStep, false, TC, false>,
-                              (const void *)fused_kernel<kModeAttn, true, TC, false>,
-                              (const void *)fused_kernel<kModeStep, true, TC, false>};
-        hipError_t e = hipSuccess;
-        for (const void *f : fns)
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, most);
-        return e;
+        hipError_t e = allow_smem<TC, false>(most);
+        return e == hipSuccess ? allow_smem<TC, true>(most) : e;
     }();
     if (attr != hipSuccess) return attr;
     const bool pack2 = fa.attn.c.G <= 8;
-    if (mode == kModeAttn)
-        paged ? launch_pk<kModeAttn, true, TC>(fa, pack2, smem, s)
-              : launch_pk<kModeAttn, false, TC>(fa, pack2, smem, s);
+    if (fa.e5m2)
+        launch_mode<TC, true>(fa, mode, pack2, smem, s);
     else
-        paged ? launch_pk<kModeStep, true, TC>(fa, pack2, smem, s)
-              : launch_pk<kModeStep, false, TC>(fa, pack2, smem, s);
+        launch_mode<TC, false>(fa, mode, pack2, smem, s);
     return hipGetLastError();
 }
 

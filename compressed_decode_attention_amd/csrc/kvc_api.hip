@@ -98,7 +98,7 @@ bool use_fused(const kvc_cache *c, int hint) {
     // paged: power-of-two blocks of at least one 16-slot tile
     const bool tile_blocks = c->block_size == 0 ||
                              (c->block_size >= 16 && (c->block_size & (c->block_size - 1)) == 0);
-    return c->dtype == KVC_BF16 && c->head_dim == 128 && tile_blocks &&
+    return (c->dtype == KVC_BF16 || c->dtype == KVC_FP8_E5M2) && c->head_dim == 128 && tile_blocks &&
            effective_len(c, hint) <= kvc::kFusedMaxT;
 }
 
@@ -203,6 +203,7 @@ kvc::FusedArgs fused_args(const kvc_cache *c, const kvc::AttnArgs &a, int hint) 
     fa.tcap = effective_len(c, hint) <= kvc::kFusedSmallT ? kvc::kFusedSmallT : kvc::kFusedMaxT;
     fa.sel = kvc::SelectArgs();
     fa.comp = kvc::CompactArgs();
+    fa.e5m2 = c->dtype == KVC_FP8_E5M2;
     return fa;
 }
 

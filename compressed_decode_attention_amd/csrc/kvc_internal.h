@@ -282,7 +282,7 @@ struct CompactArgs {
 };
 hipError_t launch_compact(const CompactArgs &a, int dtype, hipStream_t s);
 
-// one-workgroup-per-unit fast path (bf16, head_dim 128): attention only
+// one-workgroup-per-unit fast path (bf16 or E5M2, head_dim 128): attention only
 // (decode_attn) or the whole step (decode_step)
 enum { kModeAttn = 0, kModeStep = 1 };
 constexpr int kFusedMaxT = 1024;   // largest attended length of the LDS fast path
@@ -296,6 +296,7 @@ struct FusedArgs {
     SelectArgs sel;     // step mode: policy, keep_slots / n_out scratch
     CompactArgs comp;   // step mode: in-place compaction of the fallback
     int tcap;           // attended entries held in LDS: kFusedSmallT or kFusedMaxT
+    bool e5m2;          // K / V held as E5M2 codes (else bf16)
 };
 size_t fused_smem_bytes(int G, int tcap);
 hipError_t launch_fused(const FusedArgs &fa, int mode, hipStream_t s);
