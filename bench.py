@@ -88,21 +88,32 @@ def per_unit_bytes(n: int, G: int, D: int, b: int, policy: str, act_b: int = 0) 
     return kv + new + qo + sc + pos + 4
 
 
-def cpu_baseline(w, n_cached: int, budget_s: float = 12.0, decay: float = 0.0):
+def cpu_baseline(w, n_cached: int, budget_s: float = 12.0, decay: float = 0.0,
+                 policy: str = "h2o"):
     """The oracle (single thread) stepping the whole batch at the same shape
     from a steady state of n_cached entries per unit, whole decode steps until
     about budget_s seconds of work have been timed."""
     import oracle
     import synth
-    orc = oracle.Oracle(w.q_heads, w.kv_heads, w.head_dim, w.dtype)
-    pol = oracle.Policy.h2o(w.n_heavy, w.n_recent, decay=decay)
     import numpy as np
-    # steady state: the first n_sink/n_heavy positions plus the recent window
-    keep = n_cached - w.n_recent
-    pos = np.concatenate([np.arange(keep), np.arange(w.prompt_len - w.n_recent, w.prompt_len)])
+    orc = oracle.Oracle(w.q_heads, w.kv_heads, w.head_dim, w.dtype)
+    if policy == "random":
+        pol = oracle.Policy.random(w.pinned, w.n_keep, w.seed)
+        pos, seen = np.arange(n_cached), n_cached
+    else:
+        if policy == "streaming":
+            pol = oracle.Policy.streaming(w.n_sink, w.n_recent)
+        elif policy == "full":
+            pol = oracle.Policy.full()
+        else:
+            pol = oracle.Policy.h2o(w.n_heavy, w.n_recent, decay=decay)
+        # steady state: the first n_sink/n_heavy positions plus the recent window
+        keep = n_cached - w.n_recent
+        pos = np.concatenate([np.arange(keep), np.arange(w.prompt_len - w.n_recent, w.prompt_len)])
+        seen = w.prompt_len
     for b in range(w.batch):
         k, v = synth.prefill_kv(w, b, n_cached)
-        orc.load(b, k, v, seen=w.prompt_len, pos=[pos] * w.kv_heads)
+        orc.load(b, k, v, seen=seen, pos=[pos] * w.kv_heads)
     t_work = 0.0
     steps = 0
     while t_work < budget_s and steps < 64:
@@ -117,7 +128,7 @@ def cpu_baseline(w, n_cached: int, budget_s: float = 12.0, decay: float = 0.0):
         "unit": "steps/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{steps} whole-batch H2O steps ({w.batch} sequences x {w.kv_heads} kv heads, "
+        "sample": (f"{steps} whole-batch {policy} steps ({w.batch} sequences x {w.kv_heads} kv heads, "
                    f"{n_cached} cached + 1 new per unit, fp64, one thread), "
                    f"{t_work:.1f} s of timed work"),
         "host_cpu": platform.processor() or platform.machine(),
@@ -222,14 +233,114 @@ def prompt_scoring(torch, kvc, synth, args):
     }), flush=True)
 
 
+# (batch, prompt length) points of the sweep: batch at a 2,048-token prompt, then
+# length at batch 64; heavy-load heads (64 q / 8 kv, head_dim 128, bf16)
+SWEEP_POINTS = [(64, 2048), (128, 2048), (256, 2048), (512, 2048),
+                (64, 512), (64, 1024), (64, 4096), (64, 8192)]
+
+
+def sweep_point(torch, kvc, synth, B: int, P: int, policy: str, steps: int, warmup: int,
+                unfused: bool = False) -> dict:
+    """Steady decode steps of one (batch, prompt, policy) point.  'full' keeps
+    every token (the cache grows by one per step); the others trim to 512 at
+    step 1 (not timed) and then hold 512 + 1.  unfused (H2O only): attention
+    without scores, then kvc_h2o_accumulate with the step's query as one row
+    (a second traversal of K), then selection and compaction: the extra pass
+    that a FlashAttention without exposed probabilities costs."""
+    Hq, Hkv, D = 64, 8, 128
+    G = Hq // Hkv
+    dev = torch.device("cuda", 0)
+    full = policy == "full"
+    cap = P + 2 + warmup + steps if full else P + 1
+    cache = kvc.KvCache(B, Hq, Hkv, D, cap, kvc.BF16, device=dev)
+    for b0 in range(0, B, 64):
+        sl = slice(b0, min(B, b0 + 64))
+        shape = cache.k[sl, :, :P].shape
+        cache.k[sl, :, :P] = synth.device_normal(shape, 0, 900 + P, 1, b0)
+        cache.v[sl, :, :P] = synth.device_normal(shape, 0, 900 + P, 2, b0)
+    cache.pos[:, :, :P] = torch.arange(P, dtype=torch.int32, device=dev)
+    cache.n_slots.fill_(P)
+    h2o = policy == "h2o"
+    scores = torch.zeros((B, Hkv, cap), device=dev) if h2o else None
+    pool = [(synth.device_normal((B, Hq, D), 0, 901, 3, i),
+             synth.device_normal((B, Hkv, D), 0, 901, 4, i),
+             synth.device_normal((B, Hkv, D), 0, 901, 5, i)) for i in range(4)]
+    total = 1 + warmup + steps
+    new_pos = (P + torch.arange(total, dtype=torch.int32, device=dev)).view(-1, 1).expand(
+        total, B).contiguous()
+    out = torch.empty((B, Hq, D), device=dev)
+    pol = {"h2o": kvc.policy_h2o(64, 448), "streaming": kvc.policy_streaming(64, 448),
+           "full": kvc.policy_full()}[policy]
+    ws = cache.workspace(cap)
+    pws = cache.prompt_workspace(1)
+    keep = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
+    nout = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    hint = [cap]
+
+    def step(t):
+        q, kn, vn = pool[t % 4]
+        if unfused and t > 1:
+            kvc.decode_attn(cache, new_pos[t - 1], q, kn, vn, out, None, max_len_hint=hint[0],
+                            workspace=ws, stream=stream)
+            kvc.h2o_accumulate(cache, q, 1, scores, workspace=pws, stream=stream)
+            kvc.evict_h2o(cache, scores, 64, 448, keep, nout, stream=stream)
+            kvc.compact(cache, keep, nout, scores, stream=stream)
+        else:
+            kvc.decode_step(cache, pol, t, new_pos[t - 1], q, kn, vn, out, scores,
+                            max_len_hint=hint[0], workspace=ws, stream=stream)
+
+    step(1)
+    torch.cuda.synchronize()
+    if not full:
+        hint[0] = int(cache.n_slots[0, 0].item()) + 1
+    for t in range(2, 2 + warmup):
+        step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(2 + warmup, 2 + warmup + steps):
+        step(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert int(cache.flags.item()) == 0
+    if full:   # mean cached length over the timed steps
+        n = P + 1 + warmup + (steps - 1) / 2.0
+        unit = per_unit_bytes(0, G, D, 2, "full") + 2 * n * D * 2
+    else:
+        unit = per_unit_bytes(512, G, D, 2, policy)
+    gbs = unit * B * Hkv / (ms * 1e-3) / 1e9
+    del cache, scores, ws, keep
+    return {"batch": B, "prompt": P, "policy": policy + ("_unfused" if unfused else ""),
+            "us_per_step": ms * 1e3, "steps_per_s": 1e3 / ms, "tokens_per_s": B * 1e3 / ms,
+            "algorithmic_gbs": gbs, "frac_of_8tbs": gbs / HBM_PEAK_GBS}
+
+
+def sweep(torch, kvc, synth, args):
+    """Where eviction pays: full vs StreamingLLM-512 vs H2O-512 (and H2O with an
+    unfused score pass) over batch and prompt length.  One JSON line per point."""
+    for B, P in SWEEP_POINTS:
+        for policy, unfused in (("full", False), ("streaming", False), ("h2o", False),
+                                ("h2o", True)):
+            r = sweep_point(torch, kvc, synth, B, P, policy, args.steps, args.warmup, unfused)
+            log(f"B={B} P={P} {r['policy']}: {r['us_per_step']:.1f} us/step, "
+                f"{r['algorithmic_gbs']:.0f} GB/s")
+            print(json.dumps(r), flush=True)
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="heavy_load_b512_l2048")
-    ap.add_argument("--policy", default="h2o", choices=["h2o", "h2o_decay", "streaming", "full"],
-                    help="h2o_decay: H2O with a decayed attention activity (decay 0.99)")
+    ap.add_argument("--policy", default="h2o",
+                    choices=["h2o", "h2o_decay", "streaming", "full", "random"],
+                    help="h2o_decay: H2O with a decayed attention activity (decay 0.99); "
+                         "random: per-head random eviction from a cache filled to its budget "
+                         "(pinned prompt + n_keep, e.g. --workload reasoning_random_b32)")
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: K / V cached as E5M2 codes (activations stay bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -237,6 +348,9 @@ def main():
     ap.add_argument("--prompt-scoring", action="store_true",
                     help="time H2O prompt scoring (kvc_h2o_accumulate over the causal prompt) "
                          "instead of the decode step")
+    ap.add_argument("--sweep", action="store_true",
+                    help="full / StreamingLLM / H2O (fused and unfused) over batch and prompt "
+                         "length; one JSON line per point")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -259,11 +373,16 @@ def main():
     if args.prompt_scoring:
         prompt_scoring(torch, kvc, synth, args)
         return
+    if args.sweep:
+        sweep(torch, kvc, synth, args)
+        return
 
     f8 = args.kv_dtype == "fp8"
     w = synth.workload(args.workload, dtype="e5m2" if f8 else "bf16")
     policy = args.policy
     B, Hq, Hkv, D, P = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.prompt_len
+    if policy == "random":   # filled to the budget: every step evicts one per head
+        P = w.pinned + w.n_keep
     G = Hq // Hkv
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -309,6 +428,8 @@ def main():
         pol = kvc.policy_h2o(w.n_heavy, w.n_recent, decay=0.99)
     elif policy == "streaming":
         pol = kvc.policy_streaming(w.n_sink, w.n_recent)
+    elif policy == "random":
+        pol = kvc.policy_random(w.pinned, w.n_keep, w.seed)
     else:
         pol = kvc.policy_full()
     # workspace sized for the longest attended length (the first step)
@@ -382,7 +503,7 @@ def main():
     traffic = None if f8 else profiled_traffic(w.name, policy)
 
     result = {
-        "metric": "decode steps/s and achieved HBM GB/s (% of peak), attn+evict, B=512 L=2048",
+        "metric": f"decode steps/s and achieved HBM GB/s (% of peak), attn+evict, B={B} L={P}",
         "value": steps_per_s,
         "unit": "steps/s",
         "n_gpus": 1,
@@ -396,7 +517,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
-            "prompt": P, "policy": policy, "budget": "64+448" if policy != "full" else "none",
+            "prompt": P, "policy": policy,
+            "budget": {"full": "none", "random": f"{w.pinned} pinned + {w.n_keep}"}.get(policy,
+                                                                                    "64+448"),
             "cached_per_unit": n_cached, "kv_dtype": "e5m2" if f8 else "bf16",
             "accumulate": "fp32",
             "tokens_per_s": steps_per_s * B, "trim_step_ms": trim_ms,
@@ -413,8 +536,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, n_cached if policy != "full" else P,
-                                              args.cpu_budget, decay=0.99 if policy == "h2o_decay" else 0.0)
+        result["cpu_baseline"] = cpu_baseline(
+            w, n_cached if policy != "full" else P, args.cpu_budget,
+            decay=0.99 if policy == "h2o_decay" else 0.0,
+            policy="h2o" if policy.startswith("h2o") else policy)
     print(json.dumps(result), flush=True)
 
 

@@ -18,8 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "kvc")
 LIB = os.path.join(PKG, "libkvc.so")
 
-SOURCES = ["kvc_api.hip", "attn.hip", "select.hip", "compact.hip", "fused.hip", "stream.hip",
-           "prompt.hip"]
+SOURCES = ["kvc_api.hip", "attn.hip", "select.hip", "compact.hip", "fused.hip", "split.hip",
+           "stream.hip", "prompt.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

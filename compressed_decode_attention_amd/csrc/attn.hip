@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
     const int n = load_count(c, u, false);
     const bool can_store = n < c.cap;
     const int T_len = n + 1;
-    const int chunk = (T_len + ns - 1) / ns;
+    const int chunk = split_chunk(T_len, ns);
     const float *pp = a.part + (size_t)u * ns * G * (D + 2);
 
     if (tid < G) {
@@ -89,6 +89,13 @@ static hipError_t launch_typed(const AttnArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
+    if (a.nsplit > 1 && mfma_tiles_ok(dtype, a.c.D, a.c.bs)) {
+        const hipError_t e = launch_split(a, dtype == KVC_FP8_E5M2, a.max_len, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0,
+                           s, a);
+        return hipGetLastError();
+    }
     if (dtype == KVC_BF16) {
         if (a.c.D == 128) return launch_typed<uint16_t, 128>(a, s);
         if (a.c.D == 64) return launch_typed<uint16_t, 64>(a, s);

@@ -76,6 +76,16 @@ int units_of(const kvc_cache *c) { return c->batch * c->kv_heads; }
 int choose_nsplit(const kvc_cache *c, int hint) {
     const int T = (hint <= 0 || hint > c->capacity + 1) ? c->capacity + 1 : hint;
     const int units = units_of(c);
+    if (kvc::mfma_tiles_ok(c->dtype, c->head_dim, c->block_size) && T > kvc::kFusedMaxT) {
+        // matrix-core splits: chunks of at most 512 slots (the 528-entry LDS
+        // instance, four workgroups per CU) and about 4,096 workgroups in
+        // all, but no chunk under 128 slots; at most 64 splits
+        int ns = (T + 511) / 512;
+        const int fill = (4096 + units - 1) / units, by_len = (T + 127) / 128;
+        const int want = fill < by_len ? fill : by_len;
+        ns = ns > want ? ns : want;
+        return ns > 64 ? 64 : ns;
+    }
     int ns = (T + 1023) / 1024;
     if (units < 2048) {
         int fill = (2048 + units - 1) / units;
@@ -109,6 +119,7 @@ struct Workspace {
     size_t nout_off, nout_bytes;
     size_t total;
     int nsplit;
+    int max_len;   // attended length bound of every unit
 };
 
 Workspace layout(const kvc_cache *c, int hint) {
@@ -116,6 +127,7 @@ Workspace layout(const kvc_cache *c, int hint) {
     const size_t units = (size_t)units_of(c);
     const size_t G = (size_t)(c->q_heads / c->kv_heads);
     w.nsplit = choose_nsplit(c, hint);
+    w.max_len = effective_len(c, hint);
     w.part_bytes = w.nsplit > 1 ? units * w.nsplit * G * (c->head_dim + 2) * sizeof(float) : 0;
     w.logit_bytes = units * G * ((size_t)c->capacity + 1) * sizeof(float);
     w.keep_bytes = units * (size_t)c->capacity * sizeof(int32_t);
@@ -188,6 +200,7 @@ kvc::AttnArgs attn_args(const kvc_cache *c, const int32_t *new_pos, const void *
     a.scores = scores;
     a.scale = scale;
     a.nsplit = w.nsplit;
+    a.max_len = w.max_len;
     a.part = w.part_bytes ? (float *)((char *)ws + w.part_off) : nullptr;
     a.logits = (float *)((char *)ws + w.logit_off);
     return a;

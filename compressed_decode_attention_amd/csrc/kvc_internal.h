@@ -223,11 +223,25 @@ struct AttnArgs {
     float scale;
     float decay;          // 0: scores += p; in (0, 1): scores = decay*scores + (1-decay)*p
     int nsplit;
+    int max_len;          // attended length bound of every unit (n_slots + 1)
     float *part;          // [units][nsplit][G][D+2] when nsplit > 1
     float *logits;        // [units][G][cap+1] scratch (scores and/or nsplit > 1)
 };
 
 hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s);
+
+// Slots per split of a unit attending T entries over ns splits: equal shares
+// rounded up to whole 16-slot tiles (split s covers [s*chunk, (s+1)*chunk) of
+// the attended entries, clipped to T; trailing splits may be empty).
+__host__ __device__ inline int split_chunk(int T, int ns) { return ((T + ns - 1) / ns + 15) & ~15; }
+
+// Matrix-core split kernels (split.hip): bf16 or E5M2, head_dim 128, block
+// sizes 0 or a power of two >= 16; ns >= 2 splits of at most kFusedMaxT slots.
+inline bool mfma_tiles_ok(int dtype, int head_dim, int block_size) {
+    return (dtype == KVC_BF16 || dtype == KVC_FP8_E5M2) && head_dim == 128 &&
+           (block_size == 0 || (block_size >= 16 && (block_size & (block_size - 1)) == 0));
+}
+hipError_t launch_split(const AttnArgs &a, bool e5m2, int max_len, hipStream_t s);
 
 // New H2O score of a slot from its old score s and the group-summed
 // probability w of this step: a plain sum, or a decayed attention activity

@@ -124,6 +124,13 @@ def test_fused_launch_with_too_small_hint_falls_back_exactly():
     _run(W_G8, [900, 40, 513, 1000], capacity=1001, path="fallback")
 
 
+def test_split_launch_with_too_small_hint_falls_back_exactly():
+    # a length bound of 1,100 sizes the split launch for chunks of at most 144
+    # slots; the one unit of 4,401 entries needs 560 per split and must take
+    # the generic routine inside the same launch, the short units the fast one
+    _run(W_GQA, [4400] + [3] * 63, capacity=4401, hint=1100)
+
+
 def test_group_of_sixteen_query_heads():
     w = synth.workload("heavy_load_b512_l2048", q_heads=128)
     for path in PATHS:
