@@ -23,16 +23,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
     attn_unit_generic<T, D>(a, blockIdx.x / a.nsplit, blockIdx.x % a.nsplit, L);
 }
 
+struct CombLds {
+    float fac[kMaxSplit][kMaxGroup];   // exp(m_s - M) / L
+    float ms[kMaxSplit][kMaxGroup], ls[kMaxSplit][kMaxGroup];   // the splits' m, l
+    float Mg[kMaxGroup], Lg[kMaxGroup];
+};
+
 // Combine the splits of one unit: rescale partial sums to the global max,
 // normalise, update scores and the slot count.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
+__device__ inline void combine_unit(const AttnArgs &a, int u, CombLds &CB) {
     const CacheDev &c = a.c;
     const int G = c.G, ns = a.nsplit;
-    const int u = blockIdx.x, b = u / c.Hkv, h = u % c.Hkv;
+    const int b = u / c.Hkv, h = u % c.Hkv;
     const int tid = threadIdx.x;
-    __shared__ float fac[kMaxSplit][kMaxGroup];   // exp(m_s - M) / L
-    __shared__ float Mg[kMaxGroup], Lg[kMaxGroup];
+    auto &fac = CB.fac;
+    float *Mg = CB.Mg, *Lg = CB.Lg;
 
     const int n = load_count(c, u, false);
     const bool can_store = n < c.cap;
@@ -40,19 +46,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
     const int chunk = split_chunk(T_len, ns);
     const float *pp = a.part + (size_t)u * ns * G * (D + 2);
 
+    // the splits' (m, l), one load per thread, then the global max and sum
+    for (int i = tid; i < ns * G; i += kAttnThreads) {
+        const int s = i / G, g = i % G;
+        CB.ms[s][g] = pp[(s * G + g) * (D + 2) + D];
+        CB.ls[s][g] = pp[(s * G + g) * (D + 2) + D + 1];
+    }
+    __syncthreads();
     if (tid < G) {
         float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, pp[(s * G + tid) * (D + 2) + D]);
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, CB.ms[s][tid]);
         float L = 0.f;
         for (int s = 0; s < ns; ++s) {
-            const float ms = pp[(s * G + tid) * (D + 2) + D];
-            const float ls = pp[(s * G + tid) * (D + 2) + D + 1];
-            L += (ms == -INFINITY) ? 0.f : ls * __expf(ms - M);
+            const float ms = CB.ms[s][tid];
+            L += (ms == -INFINITY) ? 0.f : CB.ls[s][tid] * __expf(ms - M);
         }
         Mg[tid] = M;
         Lg[tid] = L;
         for (int s = 0; s < ns; ++s) {
-            const float ms = pp[(s * G + tid) * (D + 2) + D];
+            const float ms = CB.ms[s][tid];
             fac[s][tid] = (ms == -INFINITY) ? 0.f : __expf(ms - M) / L;
         }
     }
@@ -60,6 +72,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
     for (int e = tid; e < G * D; e += kAttnThreads) {
         const int g = e / D, d = e % D;
         float o = 0.f;
+#pragma unroll 8
         for (int s = 0; s < ns; ++s) o += pp[(s * G + g) * (D + 2) + d] * fac[s][g];
         a.out[((size_t)b * c.Hq + (size_t)h * G + g) * D + d] = o;
     }
@@ -67,6 +80,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
         const size_t ld = (size_t)c.cap + 1;
         const float *lg = a.logits + (size_t)u * G * ld;
         float *sc = a.scores + (size_t)u * c.cap;
+#pragma unroll 2
         for (int j = tid; j < T_len; j += kAttnThreads) {
             const int s = j / chunk;
             float ps = 0.f;
@@ -78,35 +92,94 @@ __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) 
     if (tid == 0 && can_store) c.n_slots[u] = n + 1;
 }
 
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
+    __shared__ CombLds CB;
+    combine_unit<D>(a, blockIdx.x, CB);
+}
+
+// The rest of a decode step after the split kernels, one workgroup per unit:
+// combine (output, scores, the appended slot), then selection, then
+// compaction, each phase reading what the previous one wrote.
+union FinishLds {
+    CombLds comb;
+    SelLds<kSelLdsSlots> sel;
+    CompLds comp;
+};
+
 template <typename T, int D>
-static hipError_t launch_typed(const AttnArgs &a, hipStream_t s) {
+__global__ __launch_bounds__(kAttnThreads) void finish_kernel(AttnArgs a, SelectArgs sa,
+                                                            CompactArgs ca) {
+    __shared__ FinishLds F;
+    const int u = blockIdx.x;
+    if (a.nsplit > 1) {
+        combine_unit<D>(a, u, F.comb);
+        __syncthreads();
+    }
+    const int e = select_unit<kSelLdsSlots>(sa, u, F.sel);
+    __syncthreads();
+    if (e >= -1) compact_one<T, D>(ca, u, e);
+    else compact_unit<T, D>(ca, u, F.comp);
+}
+
+template <typename T, int D>
+static hipError_t launch_typed(const AttnArgs &a, bool combine, hipStream_t s) {
     const int units = a.c.B * a.c.Hkv;
     hipLaunchKernelGGL((attn_valu_kernel<T, D>), dim3(units * a.nsplit), dim3(kAttnThreads), 0, s,
                        a);
-    if (a.nsplit > 1)
+    if (a.nsplit > 1 && combine)
         hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(units), dim3(kAttnThreads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
+// combine = false leaves the split partials for finish_kernel
+static hipError_t launch_attn_impl(const AttnArgs &a, int dtype, bool combine, hipStream_t s) {
     if (a.nsplit > 1 && mfma_tiles_ok(dtype, a.c.D, a.c.bs)) {
         const hipError_t e = launch_split(a, dtype == KVC_FP8_E5M2, a.max_len, s);
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess || !combine) return e;
         hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0,
                            s, a);
         return hipGetLastError();
     }
     if (dtype == KVC_BF16) {
-        if (a.c.D == 128) return launch_typed<uint16_t, 128>(a, s);
-        if (a.c.D == 64) return launch_typed<uint16_t, 64>(a, s);
+        if (a.c.D == 128) return launch_typed<uint16_t, 128>(a, combine, s);
+        if (a.c.D == 64) return launch_typed<uint16_t, 64>(a, combine, s);
     } else if (dtype == KVC_FP8_E5M2) {
-        if (a.c.D == 128) return launch_typed<e5m2_t, 128>(a, s);
-        if (a.c.D == 64) return launch_typed<e5m2_t, 64>(a, s);
+        if (a.c.D == 128) return launch_typed<e5m2_t, 128>(a, combine, s);
+        if (a.c.D == 64) return launch_typed<e5m2_t, 64>(a, combine, s);
     } else {
-        if (a.c.D == 128) return launch_typed<float, 128>(a, s);
-        if (a.c.D == 64) return launch_typed<float, 64>(a, s);
+        if (a.c.D == 128) return launch_typed<float, 128>(a, combine, s);
+        if (a.c.D == 64) return launch_typed<float, 64>(a, combine, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
+    return launch_attn_impl(a, dtype, true, s);
+}
+
+template <typename T, int D>
+static void launch_finish_typed(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,
+                                hipStream_t s) {
+    hipLaunchKernelGGL((finish_kernel<T, D>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0, s, a,
+                       sa, ca);
+}
+
+hipError_t launch_step_split(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,
+                             int dtype, hipStream_t s) {
+    hipError_t e = launch_attn_impl(a, dtype, false, s);
+    if (e != hipSuccess) return e;
+    if (dtype == KVC_BF16) {
+        if (a.c.D == 128) launch_finish_typed<uint16_t, 128>(a, sa, ca, s);
+        else launch_finish_typed<uint16_t, 64>(a, sa, ca, s);
+    } else if (dtype == KVC_FP8_E5M2) {
+        if (a.c.D == 128) launch_finish_typed<e5m2_t, 128>(a, sa, ca, s);
+        else launch_finish_typed<e5m2_t, 64>(a, sa, ca, s);
+    } else {
+        if (a.c.D == 128) launch_finish_typed<float, 128>(a, sa, ca, s);
+        else launch_finish_typed<float, 64>(a, sa, ca, s);
+    }
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

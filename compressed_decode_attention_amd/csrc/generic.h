@@ -234,6 +234,8 @@ __device__ inline uint32_t sel_primary(const SelView &v, int j, int32_t p) {
     return ~w;
 }
 
+constexpr int kSelLdsSlots = 8192;   // units up to this many slots keep keys in LDS
+
 template <int kSelLds>
 struct SelLds {
     uint32_t prim_s[kSelLds];
@@ -241,13 +243,15 @@ struct SelLds {
     uint8_t cls_s[kSelLds];
     int hist[256];
     int red[kSelThreads / 64];
+    uint32_t red3[3 * (kSelThreads / 64)];
     int sh_digit, sh_krem, sh_done;
 };
 
 // Units of up to kSelLds slots keep their ranking keys in LDS; longer units
-// recompute them from global memory on every pass.
+// recompute them from global memory on every pass.  Returns the evicted slot
+// when at most one slot leaves (-1: none leaves), else -2.
 template <int kSelLds>
-__device__ inline void select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S) {
+__device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S) {
     const CacheDev &c = a.c;
     const int tid = threadIdx.x;
     uint32_t *prim_s = S.prim_s;
@@ -274,26 +278,67 @@ __device__ inline void select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &
     const int n = v.n;
     const bool in_lds = n <= kSelLds;
 
+    // one pass over global memory: positions (and H2O score keys) go to LDS
+    // when they fit, and the newest position gives L; the loads of a thread
+    // are independent, so the unrolled loop keeps several in flight
+    const bool h2o_keys = in_lds && a.kind == KVC_POLICY_H2O;
     int mx = -1;
-    for (int j = tid; j < n; j += kSelThreads) mx = max(mx, v.P[j]);
-    v.L = block_max_i(mx, red) + 1;
-
-    // classify, count candidates, cache keys
-    int ncand = 0;
-    for (int j = tid; j < n; j += kSelThreads) {
-        const int32_t p = v.P[j];
-        const uint8_t k = sel_class(v, j, p);
-        if (in_lds) {
-            cls_s[j] = k;
+    if (in_lds) {
+#pragma unroll 4
+        for (int j = tid; j < n; j += kSelThreads) {
+            const int32_t p = v.P[j];
             pos_s[j] = p;
-            if (k == kCand) prim_s[j] = sel_primary(v, j, p);
+            if (h2o_keys) prim_s[j] = float_order_bits(v.S[j]);
+            mx = max(mx, p);
         }
-        ncand += (k == kCand);
+    } else {
+#pragma unroll 4
+        for (int j = tid; j < n; j += kSelThreads) mx = max(mx, v.P[j]);
+    }
+    v.L = block_max_i(mx, red) + 1;   // (its barriers publish the LDS copies)
+
+    // classify, count candidates and drops, cache keys; the smallest
+    // candidate key and the last dropped slot serve the one-eviction case
+    int ncand = 0, ndrop = 0, dslot = -1, barg = -1;
+    uint64_t best = ~0ull;
+    for (int j = tid; j < n; j += kSelThreads) {
+        const int32_t p = in_lds ? pos_s[j] : v.P[j];
+        const uint8_t k = sel_class(v, j, p);
+        if (in_lds) cls_s[j] = k;
+        if (k == kCand) {
+            const uint32_t pr = h2o_keys ? prim_s[j] : sel_primary(v, j, p);
+            if (in_lds) prim_s[j] = pr;
+            const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+            if (key < best) {
+                best = key;
+                barg = j;
+            }
+            ++ncand;
+        } else if (k == kDrop) {
+            ++ndrop;
+            dslot = j;
+        }
     }
     int tot;
     (void)block_excl_scan(ncand, red, &tot);
     ncand = tot;
+    (void)block_excl_scan(ndrop, red, &tot);
+    ndrop = tot;
     const int want = (a.kind == KVC_POLICY_H2O) ? a.n_heavy : a.n_keep;
+    const int extra = (ncand > want) ? (want <= 0 ? ncand : ncand - want) : 0;
+    if (ndrop + extra <= 1) {
+        // at most one slot leaves (the steady state): it is the smallest
+        // candidate key or the one dropped slot, and the keep list is every
+        // other slot in order, with no ranking passes
+        block_min_u64(best, barg, S.red3);
+        dslot = block_max_i(dslot, red);
+        const int e = (extra == 1) ? barg : (ndrop == 1 ? dslot : -1);
+        int32_t *ks = a.keep_slots + (size_t)u * c.cap;
+        for (int j = tid; j < n; j += kSelThreads)
+            if (j != e) ks[(e >= 0 && j > e) ? j - 1 : j] = j;
+        if (tid == 0) a.n_out[u] = (e >= 0) ? n - 1 : n;
+        return e;
+    }
 
     // radix select of the 'want' largest composite keys among candidates
     uint64_t prefix = 0, mask = 0;
@@ -376,6 +421,7 @@ __device__ inline void select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &
         base += t;
     }
     if (tid == 0) a.n_out[u] = base;
+    return -2;
 }
 
 // ===========================================================================
@@ -397,6 +443,33 @@ struct CompLds {
     uint32_t kept_bits[kMaxCapacity / 32];
     int red[kCompThreads / 64];
 };
+
+// Compaction when slot e alone leaves a unit of n slots (e < 0: none): the
+// last slot fills the hole, the hole-fill pairing of one hole with one source.
+template <typename T, int D>
+__device__ inline void compact_one(const CompactArgs &a, int u, int e) {
+    const CacheDev &c = a.c;
+    const int b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x;
+    const int n = load_count(c, u, false);
+    if (e < 0 || e >= n) return;
+    const int src = n - 1;
+    constexpr int kParts = (int)(D * sizeof(T) / 16);
+    if (e < src) {
+        if (tid < 2 * kParts) {
+            T *X = (tid < kParts) ? (T *)c.k : (T *)c.v;
+            const int part = tid % kParts;
+            reinterpret_cast<uint4 *>(X + row_of(c, b, h, e) * D)[part] =
+                reinterpret_cast<const uint4 *>(X + row_of(c, b, h, src) * D)[part];
+        }
+        if (tid == 0) {
+            int32_t *P = c.pos + (size_t)u * c.cap;
+            P[e] = P[src];
+            if (a.scores) a.scores[(size_t)u * c.cap + e] = a.scores[(size_t)u * c.cap + src];
+        }
+    }
+    if (tid == 0) c.n_slots[u] = src;
+}
 
 template <typename T, int D>
 __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {

@@ -460,11 +460,8 @@ KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *poli
         fa.comp.dst = fa.comp.c;
         return hip_status(kvc::launch_fused(fa, kvc::kModeStep, st), what);
     }
-    hipError_t e = kvc::launch_attn(a, c->dtype, st);
-    if (e != hipSuccess) return hip_status(e, what);
-    if (policy->kind == KVC_POLICY_FULL) return ok();
-    e = kvc::launch_select(sa, st);
-    if (e != hipSuccess) return hip_status(e, what);
+    if (policy->kind == KVC_POLICY_FULL)
+        return hip_status(kvc::launch_attn(a, c->dtype, st), what);
     kvc::CompactArgs ca;
     ca.c = kvc::make_dev(*c);
     ca.keep_slots = keep;
@@ -472,7 +469,7 @@ KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *poli
     ca.scores = scores;
     ca.ordered = false;
     ca.dst = ca.c;
-    return hip_status(kvc::launch_compact(ca, c->dtype, st), what);
+    return hip_status(kvc::launch_step_split(a, sa, ca, c->dtype, st), what);
 }
 
 KVC_EXPORT kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink,

@@ -158,6 +158,37 @@ __device__ inline int block_max_i(int x, int *red) {
     return r;
 }
 
+// Block-wide minimum of 64-bit keys with the argument that holds it (the
+// keys are unique, so the argument is too); red needs 3 words per wave.
+__device__ inline void block_min_u64(uint64_t &key, int &arg, uint32_t *red) {
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t hi = __shfl_xor((uint32_t)(key >> 32), o, kWave);
+        const uint32_t lo = __shfl_xor((uint32_t)key, o, kWave);
+        const int oa = __shfl_xor(arg, o, kWave);
+        const uint64_t ok = ((uint64_t)hi << 32) | lo;
+        if (ok < key) {
+            key = ok;
+            arg = oa;
+        }
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+        red[3 * w] = (uint32_t)(key >> 32);
+        red[3 * w + 1] = (uint32_t)key;
+        red[3 * w + 2] = (uint32_t)arg;
+    }
+    __syncthreads();
+    for (int i = 0; i < nw; ++i) {
+        const uint64_t ok = ((uint64_t)red[3 * i] << 32) | red[3 * i + 1];
+        if (ok < key) {
+            key = ok;
+            arg = (int)red[3 * i + 2];
+        }
+    }
+    __syncthreads();
+}
+
 // Block-wide exclusive prefix sum of small ints; returns the exclusive prefix
 // of the calling thread and writes the block total to *total.
 __device__ inline int block_excl_scan(int x, int *red, int *total) {
@@ -295,6 +326,12 @@ struct CompactArgs {
     CacheDev dst;         // ordered destination
 };
 hipError_t launch_compact(const CompactArgs &a, int dtype, hipStream_t s);
+
+// A whole decode step through the split kernels (attended lengths above the
+// one-workgroup kernel's): attention partials, then one workgroup per unit
+// for combine + selection + compaction.
+hipError_t launch_step_split(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,
+                             int dtype, hipStream_t s);
 
 // one-workgroup-per-unit fast path (bf16 or E5M2, head_dim 128): attention only
 // (decode_attn) or the whole step (decode_step)

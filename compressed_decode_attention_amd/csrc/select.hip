@@ -17,8 +17,6 @@
 
 namespace kvc {
 
-constexpr int kSelLdsSlots = 8192;   // units up to this many slots keep keys in LDS
-
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     __shared__ SelLds<kSelLdsSlots> S;
     select_unit<kSelLdsSlots>(a, blockIdx.x, S);
