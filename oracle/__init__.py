@@ -74,6 +74,13 @@ def lib():
                                         ctypes.c_uint32, c_u8p]
         L.orc_n_keep.restype = ctypes.c_int64
         L.orc_n_keep.argtypes = [ctypes.c_int64, ctypes.c_double]
+        c_fp = ctypes.POINTER(ctypes.c_float)
+        L.orc_quantize_groups.restype = None
+        L.orc_quantize_groups.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, c_fp,
+                                          c_u8p, c_fp, c_fp]
+        L.orc_dequantize_groups.restype = None
+        L.orc_dequantize_groups.argtypes = [ctypes.c_int64, ctypes.c_int32, c_u8p, c_fp, c_fp,
+                                            c_dp]
         _lib = L
     return _lib
 
@@ -335,3 +342,155 @@ class Oracle:
 
     def kept_positions(self, b: int) -> List[np.ndarray]:
         return [u.pos.copy() for u in self.units[b]]
+
+
+# ----------------------------------------------------------------------------
+# KIVI-style quantized cache (guide page, sections "2. cost structure of the 4
+# baselines", "16. -- KV cache capacity formula", "16. -- the 4 methods step
+# by step" and "16. -- limits and conclusion"; see oracle.c)
+# ----------------------------------------------------------------------------
+
+def quantize_groups(x: np.ndarray, bits: int):
+    """Each row of x [n_groups, len] (float32 values) on its own min/max grid
+    of 2^bits levels: codes uint8 [n_groups, len], scale and lo float32
+    [n_groups].  Code decisions in binary32, as orc_quantize_groups states."""
+    v = np.ascontiguousarray(x, np.float32)
+    n, ln = v.shape
+    codes = np.empty((n, ln), np.uint8)
+    scale = np.empty(n, np.float32)
+    lo = np.empty(n, np.float32)
+    lib().orc_quantize_groups(n, ln, bits, _p(v, ctypes.c_float), _p(codes, ctypes.c_uint8),
+                              _p(scale, ctypes.c_float), _p(lo, ctypes.c_float))
+    return codes, scale, lo
+
+
+def dequantize_groups(codes: np.ndarray, scale: np.ndarray, lo: np.ndarray) -> np.ndarray:
+    """codes [n_groups, len] -> code * scale + lo in float64 (exact)."""
+    c = np.ascontiguousarray(codes, np.uint8)
+    sc = np.ascontiguousarray(scale, np.float32)
+    lw = np.ascontiguousarray(lo, np.float32)
+    n, ln = c.shape
+    out = np.empty((n, ln), np.float64)
+    lib().orc_dequantize_groups(n, ln, _p(c, ctypes.c_uint8), _p(sc, ctypes.c_float),
+                                _p(lw, ctypes.c_float), _p(out, ctypes.c_double))
+    return out
+
+
+def kivi_split(n_tokens: int, group: int = 32, residual: int = 128):
+    """(quantized, residual) token counts of a cache holding n_tokens: the
+    residual keeps at most `residual` of the newest tokens and the quantized
+    part is whole groups, as few as that allows."""
+    over = max(n_tokens - residual, 0)
+    q = group * ((over + group - 1) // group)
+    return q, n_tokens - q
+
+
+class KiviGroup:
+    """One quantized group of `group` consecutive tokens of one kv head.
+
+    K is quantized per channel: channel d of the group's tokens is one grid
+    (k_scale[d], k_lo[d]).  V is quantized per token: each token's channels
+    32c .. 32c + 31 form one grid (v_scale[t, c], v_lo[t, c]).
+    k_codes, v_codes: [group tokens, D] uint8."""
+
+    def __init__(self, K: np.ndarray, V: np.ndarray, bits: int, cgroup: int):
+        t, D = K.shape
+        kc, ks, kl = quantize_groups(K.T, bits)                       # D grids of t values
+        self.k_codes, self.k_scale, self.k_lo = kc.T.copy(), ks, kl
+        vc, vs, vl = quantize_groups(V.reshape(t * (D // cgroup), cgroup), bits)
+        self.v_codes = vc.reshape(t, D)
+        self.v_scale = vs.reshape(t, D // cgroup)
+        self.v_lo = vl.reshape(t, D // cgroup)
+        self.cgroup = cgroup
+
+    def keys(self) -> np.ndarray:
+        return dequantize_groups(self.k_codes.T, self.k_scale, self.k_lo).T
+
+    def values(self) -> np.ndarray:
+        t, D = self.v_codes.shape
+        c = self.cgroup
+        return dequantize_groups(self.v_codes.reshape(t * (D // c), c), self.v_scale.reshape(-1),
+                                 self.v_lo.reshape(-1)).reshape(t, D)
+
+
+class KiviUnit:
+    def __init__(self):
+        self.groups: List[KiviGroup] = []
+        self.res_k = None   # [r, D] float64 (bf16 values)
+        self.res_v = None
+
+    @property
+    def n_quant(self) -> int:
+        return sum(g.k_codes.shape[0] for g in self.groups)
+
+    @property
+    def n_res(self) -> int:
+        return self.res_k.shape[0]
+
+
+class Kivi:
+    """KIVI-style cache of one attention layer: per (sequence, kv head) whole
+    groups of `group` quantized tokens, oldest first, then a residual of at
+    most `residual` newest tokens kept as given (bf16).
+
+    A decode step attends the G query heads of each kv head over the
+    dequantized tokens, the residual and the new token (attention first, as
+    for eviction); then, when the residual already holds `residual` tokens,
+    its `group` oldest are quantized as the next group, and the new token
+    joins the residual.  That keeps the residual between residual - group + 1
+    and residual tokens once the cache is longer than the residual: the
+    conversion the guide describes as periodic work when the residual fills.
+    """
+
+    def __init__(self, q_heads: int, kv_heads: int, head_dim: int, bits: int = 4,
+                 group: int = 32, residual: int = 128, cgroup: int = 32,
+                 scale: Optional[float] = None):
+        self.Hq, self.Hkv, self.D = q_heads, kv_heads, head_dim
+        self.G = q_heads // kv_heads
+        self.bits, self.group, self.residual, self.cgroup = bits, group, residual, cgroup
+        self.scale = 1.0 / math.sqrt(head_dim) if scale is None else scale
+        self.units: Dict[int, List[KiviUnit]] = {}
+
+    def load(self, b: int, k_store: np.ndarray, v_store: np.ndarray):
+        """Prefill of sequence b: bf16 storage [kv_heads, L, D]."""
+        K = decode(k_store, "bf16")
+        V = decode(v_store, "bf16")
+        L = K.shape[1]
+        q, _ = kivi_split(L, self.group, self.residual)
+        units = []
+        for h in range(self.Hkv):
+            u = KiviUnit()
+            for g0 in range(0, q, self.group):
+                u.groups.append(KiviGroup(K[h, g0:g0 + self.group], V[h, g0:g0 + self.group],
+                                          self.bits, self.cgroup))
+            u.res_k, u.res_v = K[h, q:].copy(), V[h, q:].copy()
+            units.append(u)
+        self.units[b] = units
+
+    def entries(self, b: int, h: int):
+        """(K, V) float64 of every cached token of (b, h), oldest first."""
+        u = self.units[b][h]
+        ks = [g.keys() for g in u.groups] + [u.res_k]
+        vs = [g.values() for g in u.groups] + [u.res_v]
+        return np.vstack(ks), np.vstack(vs)
+
+    def step(self, b: int, q_store, knew_store, vnew_store) -> np.ndarray:
+        """One decode step of sequence b (bf16 storage: q [Hq, D], k_new / v_new
+        [Hkv, D]); returns out [Hq, D] float64."""
+        q = decode(q_store, "bf16").reshape(self.Hq, self.D)
+        kn = decode(knew_store, "bf16").reshape(self.Hkv, self.D)
+        vn = decode(vnew_store, "bf16").reshape(self.Hkv, self.D)
+        out = np.empty((self.Hq, self.D))
+        for h, u in enumerate(self.units[b]):
+            K, V = self.entries(b, h)
+            K = np.vstack([K, kn[h][None]])
+            V = np.vstack([V, vn[h][None]])
+            out[h * self.G:(h + 1) * self.G] = attend(q[h * self.G:(h + 1) * self.G], K, V,
+                                                      self.scale)
+            if u.n_res == self.residual:
+                g = self.group
+                u.groups.append(KiviGroup(u.res_k[:g], u.res_v[:g], self.bits, self.cgroup))
+                u.res_k, u.res_v = u.res_k[g:], u.res_v[g:]
+            u.res_k = np.vstack([u.res_k, kn[h][None]])
+            u.res_v = np.vstack([u.res_v, vn[h][None]])
+        return out

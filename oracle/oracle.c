@@ -21,6 +21,12 @@
  *       easy as 1, 2, 3", SC'11 -- the Philox4x32-10 counter-based generator.
  *  [OCP8] "OCP 8-bit Floating Point Specification (OFP8)", Open Compute
  *       Project -- the E5M2 format.
+ *  [P1 KIVI] the guide page's KIVI passages: "2. cost structure of the 4
+ *       baselines" (group 32, residual 128), "16. -- KV cache capacity
+ *       formula" (keep every token, fewer bits, a full-precision recent
+ *       residual), "16. -- the 4 methods step by step" (K quantized along
+ *       channels, V along tokens) and "16. -- limits and conclusion" (scale
+ *       granularity, periodic conversion when the residual fills).
  *
  * Readings where the pages are silent (each listed in the design notes):
  *  - scale 1/sqrt(D); no position encoding applied here (keys already carry it,
@@ -323,4 +329,58 @@ ORC_API int64_t orc_n_keep(int64_t N, double keep_ratio)
     if (k > N)
         k = N;
     return k;
+}
+
+/* ------------------------------------------------------------------------ */
+/* KIVI-style quantization of groups of values [P1 KIVI].  Each group gets
+ * its own asymmetric uniform grid of 2^bits levels between its minimum and
+ * maximum:
+ *     lo = min, scale = (max - lo) / (2^bits - 1),
+ *     code = round-half-to-even((x - lo) / scale) clamped to [0, 2^bits - 1]
+ *     (every code 0 when scale is 0),     value = code * scale + lo.
+ * The pages fix neither the grid nor the precision of its parameters; the
+ * reading taken is the plain min/max grid with lo and scale kept in binary32.
+ * The code decisions are taken in binary32 arithmetic -- every operation
+ * rounded to float, as the device kernel that must reproduce the codes bit
+ * for bit takes them -- while the values are formed exactly in double.
+ * x: n_groups consecutive groups of len values. */
+ORC_API void orc_quantize_groups(int64_t n_groups, int32_t len, int32_t bits, const float *x,
+                                 uint8_t *codes, float *scale, float *lo)
+{
+    const float top = (float)((1 << bits) - 1);
+    for (int64_t g = 0; g < n_groups; ++g) {
+        const float *xg = x + g * len;
+        float mn = xg[0], mx = xg[0];
+        for (int32_t i = 1; i < len; ++i) {
+            if (xg[i] < mn)
+                mn = xg[i];
+            if (xg[i] > mx)
+                mx = xg[i];
+        }
+        const float s = (mx - mn) / top;
+        scale[g] = s;
+        lo[g] = mn;
+        for (int32_t i = 0; i < len; ++i) {
+            float c = 0.0f;
+            if (s > 0.0f) {
+                const float t = (xg[i] - mn) / s;
+                c = rintf(t);
+                if (c < 0.0f)
+                    c = 0.0f;
+                if (c > top)
+                    c = top;
+            }
+            codes[g * len + i] = (uint8_t)c;
+        }
+    }
+}
+
+/* value of each code: code * scale + lo in double, element i using
+ * scale[i / len] and lo[i / len] */
+ORC_API void orc_dequantize_groups(int64_t n_groups, int32_t len, const uint8_t *codes,
+                                   const float *scale, const float *lo, double *out)
+{
+    for (int64_t g = 0; g < n_groups; ++g)
+        for (int32_t i = 0; i < len; ++i)
+            out[g * len + i] = (double)codes[g * len + i] * (double)scale[g] + (double)lo[g];
 }

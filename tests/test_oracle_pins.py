@@ -560,3 +560,146 @@ def test_e5m2_encoding_is_monotone_and_within_half_a_step():
     # relative error of the nearest code: at most 2^-3 of the value (2 mantissa bits)
     err = np.abs(v[inside] - x[inside])
     assert (err <= np.maximum(np.abs(x[inside]) * 2.0 ** -3, 2.0 ** -17)).all()
+
+
+# ---------------------------------------------------------------------------
+# KIVI-style quantized cache (guide page: "2. cost structure of the 4
+# baselines", group 32 and residual 128; "16. -- the 4 methods step by step",
+# K along channels and V along tokens; "16. -- limits and conclusion",
+# periodic conversion when the residual fills)
+# ---------------------------------------------------------------------------
+
+def test_quantizer_reproduces_values_on_an_exact_grid():
+    # values lo + k * s with s a power of two and both ends present: the grid
+    # is exactly those values, so the codes are k and the values come back
+    rng = np.random.default_rng(0)
+    for bits in (2, 4):
+        top = (1 << bits) - 1
+        k = rng.integers(0, top + 1, size=(50, 32))
+        k[:, 0], k[:, 1] = 0, top
+        lo = rng.integers(-64, 64, size=(50, 1)) * 0.125
+        s = 2.0 ** rng.integers(-6, 2, size=(50, 1))
+        x = (lo + k * s).astype(np.float32)
+        c, sc, l = oracle.quantize_groups(x, bits)
+        np.testing.assert_array_equal(c, k)
+        np.testing.assert_array_equal(sc, s[:, 0].astype(np.float32))
+        np.testing.assert_array_equal(oracle.dequantize_groups(c, sc, l), x)
+
+
+def test_quantizer_ties_go_to_the_even_code():
+    # grid 0, 1, .., 15 (scale 1): a value half-way between two levels takes
+    # the even one
+    base = np.arange(16, dtype=np.float32)
+    x = np.concatenate([base, np.array([0.5, 1.5, 2.5, 3.5, 12.5, 13.5, 14.5, 7.25], np.float32),
+                        np.zeros(8, np.float32)])[None]
+    c, sc, _ = oracle.quantize_groups(x, 4)
+    assert sc[0] == 1.0
+    np.testing.assert_array_equal(c[0, 16:24], [0, 2, 2, 4, 12, 14, 14, 7])
+
+
+def test_quantizer_constant_group_and_error_bound():
+    c, sc, lo = oracle.quantize_groups(np.full((1, 32), 3.5, np.float32), 4)
+    assert sc[0] == 0 and lo[0] == 3.5 and (c == 0).all()
+    assert (oracle.dequantize_groups(c, sc, lo) == 3.5).all()
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((400, 32)) * rng.uniform(0.01, 100, (400, 1))).astype(np.float32)
+    for bits in (2, 4):
+        c, sc, lo = oracle.quantize_groups(x, bits)
+        v = oracle.dequantize_groups(c, sc, lo)
+        # every value within half a grid step; the ends land on the ends
+        assert (np.abs(v - x) <= 0.5 * sc[:, None].astype(np.float64) * (1 + 1e-6)).all()
+        assert (c.max(axis=1) == (1 << bits) - 1).all() and (c.min(axis=1) == 0).all()
+        np.testing.assert_array_equal(c[np.arange(400), x.argmin(axis=1)], 0)
+        # order is kept
+        order = np.argsort(x, axis=1, kind="stable")
+        assert (np.diff(np.take_along_axis(c.astype(int), order, axis=1), axis=1) >= 0).all()
+
+
+def test_kivi_keys_quantize_per_channel_and_values_per_token():
+    # keys constant along tokens within each channel, values constant along
+    # each token's 32-channel groups: the stated granularities reproduce them
+    # exactly, the transposed ones would not
+    rng = np.random.default_rng(2)
+    D = 128
+    K = np.repeat(rng.standard_normal((1, D)), 32, axis=0)
+    V = np.repeat(rng.standard_normal((32, D // 32)), 32, axis=1)
+    g = oracle.KiviGroup(K, V, bits=4, cgroup=32)
+    np.testing.assert_array_equal(g.keys(), K.astype(np.float32))
+    np.testing.assert_array_equal(g.values(), V.astype(np.float32))
+    # swapped, each tensor meets the other granularity and is not reproduced
+    g2 = oracle.KiviGroup(V, K, bits=4, cgroup=32)
+    assert np.abs(g2.keys() - V).max() > 1e-3 and np.abs(g2.values() - K).max() > 1e-3
+    # an outlier channel of the keys does not widen the other channels' grids
+    K2 = rng.standard_normal((32, D))
+    K2[:, 0] *= 1000
+    err = np.abs(oracle.KiviGroup(K2, V, 4, 32).keys() - K2)
+    rng_ch = K2.max(axis=0) - K2.min(axis=0)
+    assert (err[:, 1:] <= rng_ch[1:] / 30 * (1 + 1e-6)).all()
+
+
+def _kivi_bf16(shape, seed):
+    return synth.bf16_bits(np.random.default_rng(seed).standard_normal(shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("L", [20, 128, 129, 200, 2050])
+def test_kivi_residual_schedule_closed_form(L):
+    # after t steps from a prompt of L tokens the cache holds N = L + t tokens:
+    # ceil((N - 128) / 32) whole groups of the oldest (none while N <= 128) and
+    # the rest, the newest 97 .. 128 once N > 128, in the residual, in order
+    H, D = 2, 64
+    kv = oracle.Kivi(2, H, D)
+    kp = _kivi_bf16((H, L, D), 3)
+    kv.load(0, kp, _kivi_bf16((H, L, D), 4))
+    seen = [oracle.decode(kp, "bf16")[0]]
+    for t in range(1, 80):
+        kn = _kivi_bf16((H, D), 100 + t)
+        kv.step(0, _kivi_bf16((2, D), 200 + t), kn, _kivi_bf16((H, D), 300 + t))
+        seen.append(oracle.decode(kn, "bf16")[0][None])
+        N = L + t
+        q = 32 * max(0, -(-(N - 128) // 32))
+        u = kv.units[0][0]
+        assert (u.n_quant, u.n_res) == (q, N - q)
+        if N > 128:
+            assert 97 <= u.n_res <= 128
+        allk = np.vstack(seen)
+        np.testing.assert_array_equal(u.res_k, allk[q:])
+
+
+def test_kivi_attention_without_quantized_tokens_is_plain_attention():
+    H, G, D, L = 2, 4, 64, 90
+    kv = oracle.Kivi(H * G, H, D)
+    k, v = _kivi_bf16((H, L, D), 5), _kivi_bf16((H, L, D), 6)
+    kv.load(0, k, v)
+    q, kn, vn = _kivi_bf16((H * G, D), 7), _kivi_bf16((H, D), 8), _kivi_bf16((H, D), 9)
+    out = kv.step(0, q, kn, vn)
+    K = np.concatenate([oracle.decode(k, "bf16"), oracle.decode(kn, "bf16")[:, None]], axis=1)
+    V = np.concatenate([oracle.decode(v, "bf16"), oracle.decode(vn, "bf16")[:, None]], axis=1)
+    Q = oracle.decode(q, "bf16")
+    for h in range(H):
+        z = Q[h * G:(h + 1) * G] @ K[h].T / math.sqrt(D)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(out[h * G:(h + 1) * G], p @ V[h], rtol=0, atol=1e-12)
+
+
+def test_kivi_attention_is_exact_on_inputs_the_grids_represent():
+    # every group's keys constant per channel and values constant per token
+    # group: the quantized cache holds the values exactly, so the step equals
+    # plain attention over them
+    H, G, D, L = 1, 2, 64, 300
+    rng = np.random.default_rng(10)
+    Kf = np.repeat(rng.standard_normal((L // 32 + 1, 1, D)), 32, axis=1).reshape(-1, D)[:L]
+    Vf = np.repeat(rng.standard_normal((L, D // 32, 1)), 32, axis=2).reshape(L, D)
+    k = synth.bf16_bits(Kf.astype(np.float32))[None]
+    v = synth.bf16_bits(Vf.astype(np.float32))[None]
+    kv = oracle.Kivi(G, H, D)
+    kv.load(0, k, v)
+    assert kv.units[0][0].n_quant == 192
+    q, kn, vn = _kivi_bf16((G, D), 11), _kivi_bf16((H, D), 12), _kivi_bf16((H, D), 13)
+    out = kv.step(0, q, kn, vn)
+    K = np.vstack([oracle.decode(k, "bf16")[0], oracle.decode(kn, "bf16")])
+    V = np.vstack([oracle.decode(v, "bf16")[0], oracle.decode(vn, "bf16")])
+    z = oracle.decode(q, "bf16") @ K.T / math.sqrt(D)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(out, p @ V, rtol=0, atol=1e-12)
