@@ -37,7 +37,8 @@ EXPORTED = (
     "kvc_bytes_per_token", "kvc_n_keep", "kvc_status_string", "kvc_last_error",
     "kvc_workspace_bytes", "kvc_decode_attn", "kvc_h2o_accumulate", "kvc_evict_streaming",
     "kvc_evict_h2o", "kvc_evict_random", "kvc_compact", "kvc_decode_step", "kvc_stream_read",
-    "kvc_h2o_accumulate_workspace_bytes",
+    "kvc_h2o_accumulate_workspace_bytes", "kvc_kivi_workspace_bytes", "kvc_kivi_prefill",
+    "kvc_kivi_decode",
 )
 
 
@@ -60,8 +61,21 @@ class kvc_policy(ctypes.Structure):
     ]
 
 
+class kvc_kivi_cache(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("max_quant", ctypes.c_int32), ("bits", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("k_lo", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p), ("v_lo", ctypes.c_void_p),
+        ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+        ("n_quant", ctypes.c_void_p), ("n_res", ctypes.c_void_p), ("flags", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.c_void_p
 _CP = ctypes.POINTER(kvc_cache)
+_KP = ctypes.POINTER(kvc_kivi_cache)
 _lib.kvc_bytes_per_token.restype = ctypes.c_size_t
 _lib.kvc_bytes_per_token.argtypes = [ctypes.c_int32] * 4
 _lib.kvc_n_keep.restype = ctypes.c_int64
@@ -95,6 +109,13 @@ _lib.kvc_decode_step.argtypes = [_CP, ctypes.POINTER(kvc_policy), ctypes.c_uint3
                                  ctypes.c_size_t, _P]
 _lib.kvc_stream_read.restype = ctypes.c_int
 _lib.kvc_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+_lib.kvc_kivi_workspace_bytes.restype = ctypes.c_size_t
+_lib.kvc_kivi_workspace_bytes.argtypes = [_KP, ctypes.c_int32]
+_lib.kvc_kivi_prefill.restype = ctypes.c_int
+_lib.kvc_kivi_prefill.argtypes = [_KP, _P, _P, ctypes.c_int32, _P, _P]
+_lib.kvc_kivi_decode.restype = ctypes.c_int
+_lib.kvc_kivi_decode.argtypes = [_KP, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
+                                 ctypes.c_size_t, _P]
 
 
 class KvcError(RuntimeError):
@@ -323,3 +344,72 @@ def stream_read(buf, sink, nbytes: Optional[int] = None, stream=None):
     tensor that is written only for an impossible data pattern."""
     n = buf.numel() * buf.element_size() if nbytes is None else nbytes
     _check(_lib.kvc_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# KIVI-style quantized cache
+# ---------------------------------------------------------------------------
+KIVI_GROUP, KIVI_RESIDUAL = 32, 128
+
+
+class KiviCache:
+    """Device buffers of a KIVI-style quantized cache (layout of kvc.h) and
+    its C descriptor; max_quant quantized tokens per (sequence, kv head)."""
+
+    def __init__(self, batch: int, q_heads: int, kv_heads: int, head_dim: int, max_quant: int,
+                 bits: int = 4, device="cuda"):
+        self.batch, self.q_heads, self.kv_heads = batch, q_heads, kv_heads
+        self.head_dim, self.max_quant, self.bits = head_dim, max_quant, bits
+        U, T, D = batch * kv_heads, max_quant, head_dim
+        row = D * bits // 8
+        self.k_codes = torch.zeros((U, T, row), dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros((U, T, row), dtype=torch.uint8, device=device)
+        self.k_scale = torch.zeros((U, T // KIVI_GROUP, D), dtype=torch.float32, device=device)
+        self.k_lo = torch.zeros_like(self.k_scale)
+        self.v_scale = torch.zeros((U, T, D // 32), dtype=torch.float32, device=device)
+        self.v_lo = torch.zeros_like(self.v_scale)
+        self.k_res = torch.zeros((U, KIVI_RESIDUAL, D), dtype=torch.bfloat16, device=device)
+        self.v_res = torch.zeros_like(self.k_res)
+        self.n_quant = torch.zeros((batch, kv_heads), dtype=torch.int32, device=device)
+        self.n_res = torch.zeros((batch, kv_heads), dtype=torch.int32, device=device)
+        self.flags = torch.zeros((1,), dtype=torch.int32, device=device)
+        self._c = None
+
+    @property
+    def group(self) -> int:
+        return self.q_heads // self.kv_heads
+
+    def c(self) -> kvc_kivi_cache:
+        if self._c is None:
+            c = kvc_kivi_cache()
+            c.batch, c.q_heads, c.kv_heads = self.batch, self.q_heads, self.kv_heads
+            c.head_dim, c.max_quant, c.bits = self.head_dim, self.max_quant, self.bits
+            for name in ("k_codes", "v_codes", "k_scale", "k_lo", "v_scale", "v_lo", "k_res",
+                         "v_res", "n_quant", "n_res", "flags"):
+                setattr(c, name, _ptr(getattr(self, name)))
+            self._c = c
+        return self._c
+
+    def workspace_bytes(self, max_quant_hint: int = 0) -> int:
+        return int(_lib.kvc_kivi_workspace_bytes(ctypes.byref(self.c()), max_quant_hint))
+
+    def workspace(self, max_quant_hint: int = 0) -> torch.Tensor:
+        n = self.workspace_bytes(max_quant_hint)
+        return torch.empty((max(n, 1),), dtype=torch.uint8, device=self.k_codes.device)
+
+
+def kivi_prefill(cache: KiviCache, k, v, lengths, stream=None):
+    """k, v [batch, kv_heads, max_len, head_dim] bf16; lengths [batch] int32 (device)."""
+    max_len = k.shape[2]
+    _check(_lib.kvc_kivi_prefill(ctypes.byref(cache.c()), _ptr(k), _ptr(v), max_len,
+                                 _ptr(lengths), _stream(stream)))
+
+
+def kivi_decode(cache: KiviCache, q, k_new, v_new, out, scale=None, max_quant_hint: int = 0,
+                workspace=None, stream=None):
+    if workspace is None:
+        workspace = cache.workspace(max_quant_hint)
+    wp, wn = _ws(workspace)
+    sc = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
+    _check(_lib.kvc_kivi_decode(ctypes.byref(cache.c()), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                _ptr(out), sc, max_quant_hint, wp, wn, _stream(stream)))

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build", "kvc")
 LIB = os.path.join(PKG, "libkvc.so")
 
 SOURCES = ["kvc_api.hip", "attn.hip", "select.hip", "compact.hip", "fused.hip", "split.hip",
-           "stream.hip", "prompt.hip"]
+           "stream.hip", "prompt.hip", "kivi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -39,8 +39,8 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
     auto &pv = L.pv;
 
     const int n = load_count(c, u, s == 0 && tid == 0);
-    const bool can_store = n < c.cap;
-    if (!can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
+    const bool can_store = a.append && n < c.cap;
+    if (a.append && !can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
     const int T_len = n + 1;
     const int chunk = split_chunk(T_len, a.nsplit);
     const int j0 = min(s * chunk, T_len), j1 = min(T_len, j0 + chunk);

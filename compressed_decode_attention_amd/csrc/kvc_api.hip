@@ -201,6 +201,7 @@ kvc::AttnArgs attn_args(const kvc_cache *c, const int32_t *new_pos, const void *
     a.scale = scale;
     a.nsplit = w.nsplit;
     a.max_len = w.max_len;
+    a.append = true;
     a.part = w.part_bytes ? (float *)((char *)ws + w.part_off) : nullptr;
     a.logits = (float *)((char *)ws + w.logit_off);
     return a;
@@ -480,4 +481,154 @@ KVC_EXPORT kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *s
         return fail(KVC_ERR_INVALID_ARG,
                     "%s: src must be 16-byte aligned and bytes a positive multiple of 16", what);
     return hip_status(kvc::launch_stream_read(src, bytes, sink, (hipStream_t)stream), what);
+}
+
+// ---------------------------------------------------------------------------
+// KIVI-style quantized cache
+// ---------------------------------------------------------------------------
+namespace {
+
+kvc_status check_kivi(const kvc_kivi_cache *c, const char *what) {
+    if (!c) return fail(KVC_ERR_INVALID_ARG, "%s: cache is NULL", what);
+    if (c->batch <= 0 || c->q_heads <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 ||
+        c->max_quant < 0)
+        return fail(KVC_ERR_INVALID_ARG, "%s: batch, heads, head_dim must be > 0, max_quant >= 0",
+                    what);
+    if (c->q_heads % c->kv_heads != 0)
+        return fail(KVC_ERR_SHAPE, "%s: q_heads %d is not a multiple of kv_heads %d", what,
+                    c->q_heads, c->kv_heads);
+    if (c->q_heads / c->kv_heads > 8)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: group size %d > 8", what, c->q_heads / c->kv_heads);
+    if (c->head_dim != 128)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: head_dim %d (built: 128)", what, c->head_dim);
+    if (c->bits != 4) return fail(KVC_ERR_UNSUPPORTED, "%s: bits %d (built: 4)", what, c->bits);
+    if (c->max_quant % kvc::kKivGroup != 0)
+        return fail(KVC_ERR_SHAPE, "%s: max_quant %d is not a multiple of %d", what, c->max_quant,
+                    kvc::kKivGroup);
+    if (!c->k_codes || !c->v_codes || !c->k_scale || !c->k_lo || !c->v_scale || !c->v_lo ||
+        !c->k_res || !c->v_res || !c->n_quant || !c->n_res)
+        return fail(KVC_ERR_INVALID_ARG, "%s: cache buffers must not be NULL", what);
+    const void *al[] = {c->k_codes, c->v_codes, c->k_scale, c->k_lo, c->v_scale,
+                        c->v_lo,    c->k_res,   c->v_res};
+    for (const void *p : al)
+        if ((uintptr_t)p % 16)
+            return fail(KVC_ERR_INVALID_ARG, "%s: cache buffers must be 16-byte aligned", what);
+    return KVC_OK;
+}
+
+// splits of the quantized tokens: pieces of at most 16 groups (512 tokens),
+// about 4,096 workgroups, no share under 4 groups, at most 64 splits
+int kivi_nsq(const kvc_kivi_cache *c, int hint) {
+    const int mq = (hint <= 0 || hint > c->max_quant) ? c->max_quant : hint;
+    const int groups = mq / kvc::kKivGroup;
+    if (c->max_quant == 0) return 0;
+    if (groups == 0) return 1;
+    const int units = c->batch * c->kv_heads;
+    int ns = (groups + 15) / 16;
+    const int fill = (4096 + units - 1) / units, by_len = (groups + 3) / 4;
+    const int want = fill < by_len ? fill : by_len;
+    ns = ns > want ? ns : want;
+    return ns > 64 ? 64 : (ns < 1 ? 1 : ns);
+}
+
+struct KiviWs {
+    size_t part_q, part_r, total;
+    int nsq;
+};
+
+KiviWs kivi_layout(const kvc_kivi_cache *c, int hint) {
+    KiviWs w;
+    const size_t units = (size_t)c->batch * c->kv_heads;
+    const size_t G = (size_t)(c->q_heads / c->kv_heads);
+    w.nsq = kivi_nsq(c, hint);
+    const size_t pq = units * (size_t)w.nsq * G * (c->head_dim + 2) * sizeof(float);
+    const size_t pr = units * G * (c->head_dim + 2) * sizeof(float);
+    w.part_q = 0;
+    w.part_r = align_up(pq);
+    w.total = w.part_r + align_up(pr);
+    return w;
+}
+
+kvc::KiviArgs kivi_args(const kvc_kivi_cache *c) {
+    kvc::KiviArgs a;
+    memset(&a, 0, sizeof a);
+    a.B = c->batch;
+    a.Hq = c->q_heads;
+    a.Hkv = c->kv_heads;
+    a.G = c->q_heads / c->kv_heads;
+    a.max_quant = c->max_quant;
+    a.k_codes = c->k_codes;
+    a.v_codes = c->v_codes;
+    a.k_scale = c->k_scale;
+    a.k_lo = c->k_lo;
+    a.v_scale = c->v_scale;
+    a.v_lo = c->v_lo;
+    a.k_res = (uint16_t *)c->k_res;
+    a.v_res = (uint16_t *)c->v_res;
+    a.n_quant = c->n_quant;
+    a.n_res = c->n_res;
+    a.flags = c->flags;
+    return a;
+}
+
+}  // namespace
+
+KVC_EXPORT size_t kvc_kivi_workspace_bytes(const kvc_kivi_cache *c, int32_t max_quant_hint) {
+    if (check_kivi(c, "kvc_kivi_workspace_bytes") != KVC_OK) return 0;
+    return kivi_layout(c, max_quant_hint).total;
+}
+
+KVC_EXPORT kvc_status kvc_kivi_prefill(const kvc_kivi_cache *c, const void *k, const void *v,
+                                       int32_t max_len, const int32_t *lengths, void *stream) {
+    const char *what = "kvc_kivi_prefill";
+    kvc_status s = check_kivi(c, what);
+    if (s != KVC_OK) return s;
+    if (max_len < 0) return fail(KVC_ERR_INVALID_ARG, "%s: max_len < 0", what);
+    if (!lengths || (max_len > 0 && (!k || !v)))
+        return fail(KVC_ERR_INVALID_ARG, "%s: k, v and lengths must not be NULL", what);
+    if ((uintptr_t)k % 16 || (uintptr_t)v % 16)
+        return fail(KVC_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", what);
+    const int over = max_len > kvc::kKivResidual ? max_len - kvc::kKivResidual : 0;
+    const int64_t need = (int64_t)(over + kvc::kKivGroup - 1) / kvc::kKivGroup * kvc::kKivGroup;
+    if (need > c->max_quant)
+        return fail(KVC_ERR_SHAPE, "%s: %d prompt tokens need %lld quantized slots > max_quant %d",
+                    what, max_len, (long long)need, c->max_quant);
+    kvc::KiviArgs a = kivi_args(c);
+    a.pk = (const uint16_t *)k;
+    a.pv = (const uint16_t *)v;
+    a.lengths = lengths;
+    a.max_len = max_len;
+    return hip_status(kvc::launch_kivi_prefill(a, (hipStream_t)stream), what);
+}
+
+KVC_EXPORT kvc_status kvc_kivi_decode(const kvc_kivi_cache *c, const void *q, const void *k_new,
+                                      const void *v_new, float *out, float scale,
+                                      int32_t max_quant_hint, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    const char *what = "kvc_kivi_decode";
+    kvc_status s = check_kivi(c, what);
+    if (s != KVC_OK) return s;
+    if (!q || !k_new || !v_new || !out)
+        return fail(KVC_ERR_INVALID_ARG, "%s: q, k_new, v_new and out must not be NULL", what);
+    if ((uintptr_t)q % 16 || (uintptr_t)k_new % 16 || (uintptr_t)v_new % 16)
+        return fail(KVC_ERR_INVALID_ARG, "%s: q, k_new and v_new must be 16-byte aligned", what);
+    if (!isfinite(scale)) return fail(KVC_ERR_INVALID_ARG, "%s: scale is not finite", what);
+    const KiviWs w = kivi_layout(c, max_quant_hint);
+    if (!workspace)
+        return fail(KVC_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", what, w.total);
+    if (workspace_bytes < w.total)
+        return fail(KVC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what,
+                    workspace_bytes, w.total);
+    if ((uintptr_t)workspace % kAlign)
+        return fail(KVC_ERR_WORKSPACE, "%s: workspace must be %zu-byte aligned", what, kAlign);
+    kvc::KiviArgs a = kivi_args(c);
+    a.q = (const uint16_t *)q;
+    a.k_new = (const uint16_t *)k_new;
+    a.v_new = (const uint16_t *)v_new;
+    a.out = out;
+    a.scale = scale;
+    a.nsq = w.nsq;
+    a.part_q = (float *)((char *)workspace + w.part_q);
+    a.part_r = (float *)((char *)workspace + w.part_r);
+    return hip_status(kvc::launch_kivi_decode(a, (hipStream_t)stream), what);
 }

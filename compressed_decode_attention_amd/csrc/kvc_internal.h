@@ -255,6 +255,7 @@ struct AttnArgs {
     float decay;          // 0: scores += p; in (0, 1): scores = decay*scores + (1-decay)*p
     int nsplit;
     int max_len;          // attended length bound of every unit (n_slots + 1)
+    bool append;          // store the new token at slot n (false: attend it only)
     float *part;          // [units][nsplit][G][D+2] when nsplit > 1
     float *logits;        // [units][G][cap+1] scratch (scores and/or nsplit > 1)
 };
@@ -326,6 +327,30 @@ struct CompactArgs {
     CacheDev dst;         // ordered destination
 };
 hipError_t launch_compact(const CompactArgs &a, int dtype, hipStream_t s);
+
+// KIVI-style quantized cache (kivi.hip); the layout is the one kvc.h states.
+struct KiviArgs {
+    int B, Hq, Hkv, G, max_quant;
+    uint8_t *k_codes, *v_codes;
+    float *k_scale, *k_lo, *v_scale, *v_lo;
+    uint16_t *k_res, *v_res;
+    int32_t *n_quant, *n_res, *flags;
+    // decode
+    const uint16_t *q, *k_new, *v_new;
+    float *out;
+    float scale;
+    int nsq;              // splits of the quantized tokens per unit (0: none)
+    float *part_q;        // [units][nsq][G][D+2]
+    float *part_r;        // [units][G][D+2]: the residual and the new token
+    // prefill
+    const uint16_t *pk, *pv;
+    const int32_t *lengths;
+    int max_len;
+};
+constexpr int kKivGroup = 32;      // quantized tokens per group
+constexpr int kKivResidual = 128;  // residual tokens at most
+hipError_t launch_kivi_prefill(const KiviArgs &a, hipStream_t s);
+hipError_t launch_kivi_decode(const KiviArgs &a, hipStream_t s);
 
 // A whole decode step through the split kernels (attended lengths above the
 // one-workgroup kernel's): attention partials, then one workgroup per unit

@@ -72,8 +72,8 @@ void split_kernel(AttnArgs a) {
         attn_unit_generic<TK, kHD>(a, u, s, *reinterpret_cast<AttnLds<kHD> *>(smem));
         return;
     }
-    const bool can_store = n < c.cap;
-    if (!can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
+    const bool can_store = a.append && n < c.cap;
+    if (a.append && !can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
     const int j0 = min(s * chunk, T), j1 = min(T, j0 + chunk);   // attended slots
     const int jend = min(j1, n);                                   // of them cached
 

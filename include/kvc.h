@@ -310,6 +310,86 @@ kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *policy,
  */
 kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+/* ============================================================================
+ * KIVI-style quantized KV cache: keep every token, fewer bits per element
+ * [GUIDE] section 2 (KIVI with group 32 and a 128-token residual), section 16
+ * "KV capacity formula" (quantisation keeps all tokens at 4 bits instead of
+ * 16, with a full-precision residual of recent tokens), "the four methods"
+ * (K quantised along channels, V along tokens, groups of 32; a decode step
+ * dequantises or runs a quantised kernel) and "limits" (scale granularity;
+ * a full residual converts its old tokens, periodic work).
+ *
+ * Per unit (sequence b, kv head h) the cache holds n_quant[u] tokens
+ * (a multiple of 32) as 4-bit codes, oldest first, then n_res[u] <= 128
+ * newest tokens as given (bf16), oldest first.  Grids: every group of 32
+ * consecutive quantised tokens has, per channel d, one grid for K (those 32
+ * tokens' K[., d]), and per token, one grid for V per 32 consecutive channels.
+ * A grid over values x: lo = min x, scale = (max x - lo) / 15,
+ * code = round-half-to-even((x - lo) / scale) clamped to [0, 15] (0 when
+ * scale is 0), every operation in binary32; the element's value is
+ * code * scale + lo.
+ *
+ * A decode step attends each of the G query heads over the dequantised
+ * tokens, the residual and the new token, and writes out[b, i, :] (fp32);
+ * then, if the residual holds 128 tokens, its 32 oldest become the next
+ * quantised group and leave it; then the new token joins the residual.  So
+ * the residual keeps 97..128 tokens once a sequence is longer than 128, and
+ * the conversion runs every 32 steps.
+ *
+ * Layout (head_dim 128, 4-bit codes, 64 bytes per token and tensor; u = b *
+ * kv_heads + h, T = max_quant):
+ *   k_codes [u][T][64] uint8.  Dim d of a token: dword 4*((d%32)/8) + d/32 of
+ *           its row (bytes 16*((d%32)/8) + 4*(d/32) ..), nibble slot k of
+ *           that dword (bits 4k..4k+3) with e = d % 8 = 2k (k < 4) or
+ *           2(k-4)+1 (k >= 4).
+ *   k_scale, k_lo [u][T/32][128] float: the grid of channel d of group g.
+ *   v_codes [u][T][64] uint8.  Dim d of a token: dword d % 16 of its row,
+ *           nibble slot k with m = d / 16 = 2k (k < 4) or 2(k-4)+1 (k >= 4).
+ *   v_scale, v_lo [u][T][4] float: the grid of channels 32c..32c+31 of a token.
+ *   k_res, v_res [u][128][128] bf16: residual rows 0 .. n_res-1, oldest first.
+ *   n_quant, n_res [u] int32.
+ * These layouts put one lane's matrix-core operands in one load and widen
+ * two codes with two ALU instructions.
+ * ========================================================================== */
+typedef struct kvc_kivi_cache {
+    int32_t batch, q_heads, kv_heads, head_dim;  /* head_dim 128; q_heads / kv_heads <= 8 */
+    int32_t max_quant;                           /* T: quantised tokens per unit, a multiple of 32 */
+    int32_t bits;                                /* 4 */
+    uint8_t *k_codes, *v_codes;
+    float *k_scale, *k_lo, *v_scale, *v_lo;
+    void *k_res, *v_res;                         /* bf16 */
+    int32_t *n_quant, *n_res;
+    int32_t *flags;                              /* nullable; KVC_FLAG_* as for kvc_cache */
+} kvc_kivi_cache;
+
+/* Device bytes of the workspace of kvc_kivi_decode when every unit holds at
+ * most max_quant_hint quantised tokens (<= 0: max_quant). */
+size_t kvc_kivi_workspace_bytes(const kvc_kivi_cache *c, int32_t max_quant_hint);
+
+/*
+ * Prefill: sequence b's prompt of lengths[b] tokens (device int32, clipped
+ * to [0, max_len]) from k, v [batch][kv_heads][max_len][128] bf16 (device).
+ * The oldest tokens become whole quantised groups, as few as keep the
+ * residual within 128 (32 * ceil(max(L - 128, 0) / 32) tokens), the rest
+ * the residual; n_quant and n_res are set.  The grids of max_len tokens must
+ * fit: 32 * ceil(max(max_len - 128, 0) / 32) <= max_quant (KVC_ERR_SHAPE).
+ */
+kvc_status kvc_kivi_prefill(const kvc_kivi_cache *c, const void *k, const void *v,
+                            int32_t max_len, const int32_t *lengths, void *stream);
+
+/*
+ * One decode step as described above.  q [batch][q_heads][128], k_new and
+ * v_new [batch][kv_heads][128] bf16; out [batch][q_heads][128] fp32.
+ * max_quant_hint bounds n_quant of every unit (<= 0: max_quant) and sizes the
+ * split of the quantised tokens over workgroups; a unit above it is still
+ * exact, only slower.  A conversion that would exceed max_quant is skipped,
+ * the new token is not stored, and KVC_FLAG_FULL is raised.
+ */
+kvc_status kvc_kivi_decode(const kvc_kivi_cache *c, const void *q, const void *k_new,
+                           const void *v_new, float *out, float scale,
+                           int32_t max_quant_hint, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif
