@@ -317,6 +317,114 @@ def sweep_point(torch, kvc, synth, B: int, P: int, policy: str, steps: int, warm
             "algorithmic_gbs": gbs, "frac_of_8tbs": gbs / HBM_PEAK_GBS}
 
 
+def kivi_unit_bytes(nq: int, nr: int, G: int, D: int = 128) -> float:
+    """Algorithmic HBM bytes of one unit in one KIVI-4 decode step with nq
+    quantized and nr residual tokens before the step: codes (D/2 bytes per
+    token for K and for V), binary32 grids (per group 2 x D for K, per token
+    2 x D/32 for V), the bf16 residual rows, the new token read (bf16) and
+    written into the residual, q and the fp32 output, the two counts, and the
+    conversion of 32 residual tokens every 32 steps (read 32 rows, write their
+    codes and grids, move 96 rows) spread over those steps."""
+    codes = nq * D                                     # K and V, 4 bits each
+    grids = (nq // 32) * 2 * D * 4 + nq * 2 * (D // 32) * 4
+    res = nr * 2 * D * 2
+    new = 2 * D * 2 + 2 * D * 2
+    qo = G * D * (2 + 4)
+    conv = (32 * 2 * D * 2 + 32 * (D + 2 * D * 4 / 32 + 2 * (D // 32) * 4) + 2 * 96 * 2 * D * 2) / 32
+    return codes + grids + res + new + qo + 8 + conv
+
+
+def kivi_bench(torch, kvc, synth, args):
+    """KIVI-4 decode steps at a workload's shape: the prompt is quantized
+    (group 32, 128-token residual), then whole decode steps (attention over
+    the dequantized tokens, the residual and the new token; residual
+    conversion every 32 steps) are timed back to back."""
+    w = synth.workload(args.workload)
+    B, Hq, Hkv, D, P = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.prompt_len
+    G = Hq // Hkv
+    dev = torch.device("cuda", 0)
+    total = 1 + args.warmup + 2 * args.steps
+    mq = oracle_free_split(P + total)[0]
+    cache = kvc.KiviCache(B, Hq, Hkv, D, mq, device=dev)
+    k = torch.empty((B, Hkv, P, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    for b0 in range(0, B, 64):
+        sl = slice(b0, min(B, b0 + 64))
+        k[sl] = synth.device_normal(k[sl].shape, w.seed, w.wid, 21, b0)
+        v[sl] = synth.device_normal(v[sl].shape, w.seed, w.wid, 22, b0)
+    lengths = torch.full((B,), P, dtype=torch.int32, device=dev)
+    kvc.kivi_prefill(cache, k, v, lengths)
+    del k, v
+    pool = [(synth.device_normal((B, Hq, D), w.seed, w.wid, 23, i),
+             synth.device_normal((B, Hkv, D), w.seed, w.wid, 24, i),
+             synth.device_normal((B, Hkv, D), w.seed, w.wid, 25, i)) for i in range(4)]
+    out = torch.empty((B, Hq, D), device=dev)
+    ws = cache.workspace(mq)
+    stream = torch.cuda.current_stream()
+
+    def step(t):
+        q, kn, vn = pool[t % 4]
+        kvc.kivi_decode(cache, q, kn, vn, out, max_quant_hint=mq, workspace=ws, stream=stream)
+
+    t = 1
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+    t_first = t
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step(t)
+        t += 1
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(t)
+        evs[i][1].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    assert int(cache.flags.item()) == 0, "device contract flag raised"
+    # mean algorithmic bytes over the event-bracketed steps (counts follow the
+    # schedule: N tokens before a step -> kivi_split(N))
+    n0 = P + (t_first - 1) + args.steps
+    unit = sum(kivi_unit_bytes(*oracle_free_split(n0 + i), G, D) for i in range(args.steps)) / args.steps
+    step_bytes = unit * B * Hkv
+    achieved = step_bytes / (launch_ms * 1e-3) / 1e9
+    attain = attainable_read_gbs(torch, kvc)
+    log(f"KIVI-4 {w.name}: {ms * 1e3:.1f} us/step back to back, {launch_ms * 1e3:.1f} us per "
+        f"event-bracketed step, {achieved:.0f} GB/s algorithmic")
+    print(json.dumps({
+        "metric": f"KIVI-4 decode steps/s and achieved HBM GB/s, B={B} L={P}",
+        "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + "_kivi4", "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "prompt": P, "group": 32, "residual": 128, "bits": 4,
+                   "tokens_per_s": B * 1e3 / ms},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvc_kivi_decode (whole step: quantized attention, residual "
+                               "attention, combine + conversion + append)",
+                     "bytes_per_unit": unit, "units_per_launch": B * Hkv, "launch_ms": launch_ms,
+                     "attainable_read_gbs": attain["gbs"],
+                     "frac_of_attainable": achieved / attain["gbs"]},
+    }), flush=True)
+
+
+def oracle_free_split(n_tokens: int, group: int = 32, residual: int = 128):
+    """(quantized, residual) token counts of a KIVI cache holding n_tokens
+    (the schedule kvc.h states; used only to size and count bytes)."""
+    over = max(n_tokens - residual, 0)
+    q = group * ((over + group - 1) // group)
+    return q, n_tokens - q
+
+
 def sweep(torch, kvc, synth, args):
     """Where eviction pays: full vs StreamingLLM-512 vs H2O-512 (and H2O with an
     unfused score pass) over batch and prompt length.  One JSON line per point."""
@@ -351,6 +459,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="full / StreamingLLM / H2O (fused and unfused) over batch and prompt "
                          "length; one JSON line per point")
+    ap.add_argument("--kivi", action="store_true",
+                    help="KIVI-4 quantized-cache decode steps at the workload's shape")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -375,6 +485,9 @@ def main():
         return
     if args.sweep:
         sweep(torch, kvc, synth, args)
+        return
+    if args.kivi:
+        kivi_bench(torch, kvc, synth, args)
         return
 
     f8 = args.kv_dtype == "fp8"

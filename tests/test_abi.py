@@ -175,3 +175,73 @@ def test_stream_read_argument_errors():
     assert lib.kvc_stream_read(0x10000, 1000, 0x20000, None) == kvc.ERR_INVALID_ARG  # not x16
     assert lib.kvc_stream_read(0x10000, 0, 0x20000, None) == kvc.ERR_INVALID_ARG
     assert b"16-byte aligned" in lib.kvc_last_error()
+
+
+def _fake_kivi(**kw):
+    c = kvc.kvc_kivi_cache()
+    c.batch, c.q_heads, c.kv_heads, c.head_dim, c.max_quant, c.bits = 2, 8, 2, 128, 256, 4
+    for i, name in enumerate(("k_codes", "v_codes", "k_scale", "k_lo", "v_scale", "v_lo", "k_res",
+                              "v_res", "n_quant", "n_res")):
+        setattr(c, name, 0x100000 * (i + 1))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@no_gpu
+@pytest.mark.parametrize("change,status", [
+    (dict(head_dim=64), kvc.ERR_UNSUPPORTED),
+    (dict(bits=2), kvc.ERR_UNSUPPORTED),
+    (dict(q_heads=18), kvc.ERR_UNSUPPORTED),        # group of 9
+    (dict(q_heads=9), kvc.ERR_SHAPE),
+    (dict(max_quant=100), kvc.ERR_SHAPE),
+    (dict(max_quant=-32), kvc.ERR_INVALID_ARG),
+    (dict(k_res=None), kvc.ERR_INVALID_ARG),
+    (dict(v_codes=0x100008), kvc.ERR_INVALID_ARG),  # misaligned
+])
+def test_kivi_cache_validation(change, status):
+    lib = kvc.library()
+    c = _fake_kivi(**change)
+    ws = 0x4000000
+    assert lib.kvc_kivi_decode(ctypes.byref(c), 0x1000, 0x2000, 0x3000, 0x4000, 0.1, 0, ws,
+                               1 << 30, None) == status
+    assert lib.kvc_kivi_workspace_bytes(ctypes.byref(c), 0) == 0
+    assert kvc.last_error()
+
+
+@no_gpu
+def test_kivi_call_errors():
+    lib = kvc.library()
+    c = _fake_kivi()
+    need = lib.kvc_kivi_workspace_bytes(ctypes.byref(c), 0)
+    assert need > 0
+    # workspace missing, short, misaligned; bad scale; NULL activations
+    assert lib.kvc_kivi_decode(ctypes.byref(c), 0x1000, 0x2000, 0x3000, 0x4000, 0.1, 0, None, 0,
+                               None) == kvc.ERR_WORKSPACE
+    assert lib.kvc_kivi_decode(ctypes.byref(c), 0x1000, 0x2000, 0x3000, 0x4000, 0.1, 0,
+                               0x4000000, need - 1, None) == kvc.ERR_WORKSPACE
+    assert lib.kvc_kivi_decode(ctypes.byref(c), 0x1000, 0x2000, 0x3000, 0x4000, 0.1, 0,
+                               0x4000010, need, None) == kvc.ERR_WORKSPACE
+    assert lib.kvc_kivi_decode(ctypes.byref(c), 0x1000, 0x2000, 0x3000, 0x4000,
+                               float("nan"), 0, 0x4000000, need, None) == kvc.ERR_INVALID_ARG
+    assert lib.kvc_kivi_decode(ctypes.byref(c), None, 0x2000, 0x3000, 0x4000, 0.1, 0,
+                               0x4000000, need, None) == kvc.ERR_INVALID_ARG
+    # prefill: 256 quantized slots hold prompts up to 384 tokens
+    assert lib.kvc_kivi_prefill(ctypes.byref(c), 0x1000, 0x2000, 385, 0x3000, None) == \
+        kvc.ERR_SHAPE
+    assert b"max_quant" in lib.kvc_last_error()
+    assert lib.kvc_kivi_prefill(ctypes.byref(c), 0x1000, 0x2000, 100, None, None) == \
+        kvc.ERR_INVALID_ARG
+    assert lib.kvc_kivi_prefill(ctypes.byref(c), 0x1000, 0x2000, -1, 0x3000, None) == \
+        kvc.ERR_INVALID_ARG
+    assert lib.kvc_kivi_prefill(None, 0x1000, 0x2000, 10, 0x3000, None) == kvc.ERR_INVALID_ARG
+
+
+def test_kivi_workspace_grows_with_the_split():
+    lib = kvc.library()
+    small = lib.kvc_kivi_workspace_bytes(ctypes.byref(_fake_kivi(batch=512, max_quant=2048)), 0)
+    few = lib.kvc_kivi_workspace_bytes(ctypes.byref(_fake_kivi(batch=1, max_quant=2048)), 0)
+    assert small > 0 and few > 0
+    # a bound of one group gives one split per unit
+    one = lib.kvc_kivi_workspace_bytes(ctypes.byref(_fake_kivi(batch=1, max_quant=2048)), 32)
+    assert one < few
