@@ -9,18 +9,23 @@
 // (unit, share of its groups):
 //  * K of group g, channel d: k = c * s_gd + lo_gd, so
 //        q . k_j = sum_d (q_d s_gd) c_jd + sum_d q_d lo_gd.
-//    The scale folds into the query: A = 16 q_d s_gd as a bf16 high part in
+//    The scale folds into the query: A = 128 q_d s_gd as a bf16 high part in
 //    rows 0..7 and the bf16 rounding of the rest in rows 8..15; a code enters
-//    B exactly as the bf16 value 1 + c/16 (bits 0x3F80 | c << 3).  The
-//    product is then sum_d A_d + sum_d (A_d / 16) c_jd, and the first sum with
-//    the lo term is one constant per (group, head) added to the group's logits.
+//    B exactly as the bf16 value 1 + c/128 (bits 0x3F80 | c).  The product is
+//    then sum_d A_d + sum_d (A_d / 128) c_jd, and the first sum with the lo
+//    term is one constant per (group, head) added to the group's logits.  The
+//    operand is built once per (wave, group): each lane scales 16 of the
+//    group's (head, dim) pairs into the wave's LDS tile and reads its own
+//    operand back.
 //  * V of token j, channel group c (32 channels): v = code * s_jc + lo_jc.  In
 //    the P.V tile MFMA m covers dims 16m .. 16m + 15, inside one channel
-//    group, so the token scale folds into P: A = 16 p_j s_jc (high / low
+//    group, so the token scale folds into P: A = 128 p_j s_jc (high / low
 //    rows), B the codes as above, and sum_j (p_j lo_jc - A_j) is added per
-//    (head, channel group) at the end.
-//  * the logits of up to 512 tokens stay in LDS; a longer share runs in pieces
-//    of 512 with the running maximum rescaling the partial sums.
+//    (head, channel group) at the end; those two sums come from one more MFMA
+//    per tile, P against a B of the tile's lo and 128 s values (high / low
+//    columns), whose error is that of the bf16 pairs, 2^-17 relative.
+//  * the logits of 256 tokens (8 groups) stay in LDS; a longer share runs in
+//    pieces with the running maximum rescaling the partial sums.
 // The residual and the new token go through split_kernel (bf16, attend
 // only).  kivi_update_kernel merges the partials, turns a full residual's 32
 // oldest tokens into a group, and appends the new token; kivi_prefill_kernel
@@ -30,22 +35,38 @@
 namespace kvc {
 
 constexpr int kKivRow = kHD / 2;                     // bytes of one token's 4-bit codes
-constexpr int kKivSub = 16;                          // groups per LDS piece
-constexpr int kKivSubT = kKivSub * kKivGroup;        // 512 tokens
+#ifndef KVC_KIV_SUB
+#define KVC_KIV_SUB 8
+#endif
+#ifndef KVC_KIV_WAVES
+#define KVC_KIV_WAVES 3
+#endif
+constexpr int kKivSub = KVC_KIV_SUB;                 // groups per LDS piece
+constexpr int kKivSubT = kKivSub * kKivGroup;        // tokens per LDS piece
 constexpr int kKivLD = kKivSubT + 4;
 constexpr int kKivVG = kHD / 32;                     // V grids per token
 
-// Two codes of one dword -> two bf16 values 1 + c/16.  A dword holds eight
-// codes, slots 0..3 (bits 0..15) the even elements and slots 4..7 the odd
-// ones, so pair J (elements 2J and 2J + 1) sits at bits 4J and 16 + 4J.
+// Two codes of one dword -> two bf16 values 1 + c/128 (the code in the low
+// mantissa bits: bits 0x3F80 | c).  A dword holds eight codes, slots 0..3
+// (bits 0..15) the even elements and slots 4..7 the odd ones, so pair J
+// (elements 2J and 2J + 1) sits at bits 4J and 16 + 4J: one shift and one
+// bit-field select.
+// The mask and the bits of 1.0 are passed in registers (KivMagic) so that
+// each pair is one v_and_or_b32 (VOP3 takes no literal constants here).
+struct KivMagic {
+    uint32_t mask, one;
+    __device__ inline KivMagic() : mask(0x000F000Fu), one(0x3F803F80u) {
+        asm volatile("" : "+s"(mask));
+        asm volatile("" : "+v"(one));
+    }
+};
 template <int J>
-__device__ inline uint32_t kiv_pair(uint32_t x) {
-    if constexpr (J == 0) return ((x << 3) & 0x00780078u) | 0x3F803F80u;
-    else return ((x >> (4 * J - 3)) & 0x00780078u) | 0x3F803F80u;
+__device__ inline uint32_t kiv_pair(uint32_t x, const KivMagic &km) {
+    return ((J == 0 ? x : x >> (4 * J)) & km.mask) | km.one;
 }
-__device__ inline u16x8_t kiv_widen8(uint32_t x) {
-    return __builtin_bit_cast(u16x8_t, uint4{kiv_pair<0>(x), kiv_pair<1>(x), kiv_pair<2>(x),
-                                             kiv_pair<3>(x)});
+__device__ inline u16x8_t kiv_widen8(uint32_t x, const KivMagic &km) {
+    return __builtin_bit_cast(u16x8_t, uint4{kiv_pair<0>(x, km), kiv_pair<1>(x, km),
+                                             kiv_pair<2>(x, km), kiv_pair<3>(x, km)});
 }
 
 // Quantize one group of kKivGroup tokens, K rows Kr and V rows Vr (bf16,
@@ -163,18 +184,26 @@ __global__ __launch_bounds__(256) void kivi_prefill_kernel(KiviArgs a) {
 // attention over the quantized tokens
 // ---------------------------------------------------------------------------
 struct KivSmall {
-    float mrun[kMaxGroup];                   // running max per head
-    float alpha[kMaxGroup];                  // rescale of the running sums at a new piece
-    float wred[kFWaves][kMaxGroup];
-    float corr[kFWaves][kMaxGroup][kKivVG];
+    float mrun[8];                   // running max per head
+    float alpha[8];                  // rescale of the running sums at a new piece
+    float wred[kFWaves][8];
+    float corr[kFWaves][8][kKivVG];
 };
+constexpr int kKivAS = kHD + 8;      // bf16 row stride of a wave's A tile (padded against bank clashes)
 
 __host__ __device__ constexpr size_t kivi_qattn_smem(int G) {
     return (size_t)G * kKivLD * 4 + (size_t)kKivSub * 2 * kHD * 4 +
-           (size_t)kKivSubT * 2 * kKivVG * 4 + sizeof(KivSmall);
+           (size_t)kKivSubT * 2 * kKivVG * 4 + (size_t)kFWaves * 16 * kKivAS * 2 + sizeof(KivSmall);
 }
 
-__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// bf16 high part of a pair of floats, packed, and the value of each half
+__device__ inline uint32_t bf16_pack2(float x, float y) {
+    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)x, (__bf16)y});
+}
+__device__ inline float bf16_lo_half(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ inline float bf16_hi_half(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(KVC_KIV_WAVES)))
 void kivi_qattn_kernel(KiviArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int ns = a.nsq;
@@ -189,13 +218,24 @@ void kivi_qattn_kernel(KiviArgs a) {
     const bool hi_lane = col < 8;
 
     float *lg = reinterpret_cast<float *>(smem);             // [G][kKivLD] logits of a piece
-    float *kgr = lg + G * kKivLD;                             // [group][scale | lo][kHD]
-    float *vgr = kgr + kKivSub * 2 * kHD;                     // [token][4 scales, 4 lo]
-    KivSmall &sm = *reinterpret_cast<KivSmall *>(vgr + kKivSubT * 2 * kKivVG);
+    float *kgr = lg + G * kKivLD;                             // [group][128 scale | lo][kHD]
+    float *vgr = kgr + kKivSub * 2 * kHD;                     // [token][4 x 128 scale, 4 x lo]
+    uint16_t *ast_all = reinterpret_cast<uint16_t *>(vgr + kKivSubT * 2 * kKivVG);
+    uint16_t *ast = ast_all + w * 16 * kKivAS;                // this wave's A tile [16][kKivAS]
+    KivSmall &sm = *reinterpret_cast<KivSmall *>(ast_all + kFWaves * 16 * kKivAS);
 
-    // this lane's query: dims 32 c4 + 8 r + e of head ga (16x16x32 A layout)
-    u16x8_t qa[4];
-    load_q(qa, a.q + ((size_t)b * a.Hq + (size_t)h * G + (arow ? ga : 0)) * kHD, arow, r);
+    // the query slice this lane scales for the K products: head gh, dims d0 .. d0 + 15
+    const int gh = lane >> 3, d0 = 16 * (lane & 7);
+    uint32_t qw[8];   // bf16 pairs, widened where used
+    {
+        const bool ok = gh < G;
+        const uint16_t *qp = a.q + ((size_t)b * a.Hq + (size_t)h * G + (ok ? gh : 0)) * kHD + d0;
+        const uint4 z4 = {0, 0, 0, 0};
+        const uint4 q0 = ok ? *reinterpret_cast<const uint4 *>(qp) : z4;
+        const uint4 q1 = ok ? *reinterpret_cast<const uint4 *>(qp + 8) : z4;
+        qw[0] = q0.x; qw[1] = q0.y; qw[2] = q0.z; qw[3] = q0.w;
+        qw[4] = q1.x; qw[5] = q1.y; qw[6] = q1.z; qw[7] = q1.w;
+    }
 
     int nq = __builtin_amdgcn_readfirstlane(a.n_quant[u]);
     if (nq < 0 || nq > a.max_quant || (nq % kKivGroup) != 0) {
@@ -209,64 +249,91 @@ void kivi_qattn_kernel(KiviArgs a) {
     const size_t gbase = (size_t)u * (a.max_quant / kKivGroup);
 
     if (tid < G) sm.mrun[tid] = -INFINITY;
+    const KivMagic km;
     f32x4_t oacc[8];
 #pragma unroll
     for (int m8 = 0; m8 < 8; ++m8) oacc[m8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t cacc = {0.f, 0.f, 0.f, 0.f};   // sum_j p_j x_j for the columns of the V grids
     float lsum = 0.f;
-    float corr[kKivVG] = {0.f, 0.f, 0.f, 0.f};
 
     for (int gs = g0; gs < g1; gs += kKivSub) {
         const int ng = min(kKivSub, g1 - gs);
         __syncthreads();   // the previous piece is done with the LDS
         for (int i = tid; i < ng * kHD; i += kFThreads) {
             const int gi = i / kHD, d = i % kHD;
-            kgr[gi * 2 * kHD + d] = a.k_scale[(gbase + gs + gi) * kHD + d];
+            kgr[gi * 2 * kHD + d] = 128.f * a.k_scale[(gbase + gs + gi) * kHD + d];
             kgr[gi * 2 * kHD + kHD + d] = a.k_lo[(gbase + gs + gi) * kHD + d];
         }
         for (int i = tid; i < ng * kKivGroup * kKivVG; i += kFThreads) {
             const int t = i / kKivVG, c = i % kKivVG;
             const size_t src = (ubase + (size_t)gs * kKivGroup + t) * kKivVG + c;
-            vgr[t * 2 * kKivVG + c] = a.v_scale[src];
+            vgr[t * 2 * kKivVG + c] = 128.f * a.v_scale[src];
             vgr[t * 2 * kKivVG + kKivVG + c] = a.v_lo[src];
+        }
+        // codes of the wave's first group, requested before the barrier
+        auto kload = [&](int gi, int tt) -> uint4 {
+            const size_t tok = ubase + (size_t)(gs + gi) * kKivGroup + 16 * tt + col;
+            return *reinterpret_cast<const uint4 *>(a.k_codes + tok * kKivRow + 16 * r);
+        };
+        uint4 kc0 = {0, 0, 0, 0}, kc1 = {0, 0, 0, 0};
+        if (w < ng) {
+            kc0 = kload(w, 0);
+            kc1 = kload(w, 1);
         }
         __syncthreads();
 
-        // ---------------- logits: wave w takes groups w, w + 4, w + 8, w + 12
+        // ---------------- logits: wave w takes groups w, w + 4
         float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll 1
         for (int i = 0; i < kKivSub / kFWaves; ++i) {
             const int gi = w + kFWaves * i;
             if (gi >= ng) break;   // wave-uniform
-            u16x8_t aop[4];
+            // A = 128 q_d s_gd of this lane's 16 (head, dim), high and low
+            // parts into the wave's A tile; the head's constant
+            // sum_d q_d lo_gd - sum_d (high + low)
+            const float *sg = kgr + gi * 2 * kHD + d0;
             float cst = 0.f;
-            const float *sg = kgr + gi * 2 * kHD;
+            uint32_t hw[8], lw[8];
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const int d0 = 32 * c4 + 8 * r;
-                const float4 s0 = *reinterpret_cast<const float4 *>(sg + d0);
-                const float4 s1 = *reinterpret_cast<const float4 *>(sg + d0 + 4);
-                const float4 l0 = *reinterpret_cast<const float4 *>(sg + kHD + d0);
-                const float4 l1 = *reinterpret_cast<const float4 *>(sg + kHD + d0 + 4);
-                const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-                const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float qd = bf16_value((short)qa[c4][e]);
-                    const float av = 16.f * (qd * sv[e]);
-                    const short hb = bf16_bits(av);
-                    const short lb = bf16_bits(av - bf16_value(hb));
-                    aop[c4][e] = (uint16_t)(hi_lane ? hb : lb);
-                    cst += qd * lv[e] - (bf16_value(hb) + bf16_value(lb));
-                }
+            for (int j = 0; j < 16; j += 2) {
+                const float2 s2 = *reinterpret_cast<const float2 *>(sg + j);
+                const float2 l2 = *reinterpret_cast<const float2 *>(sg + kHD + j);
+                const float q0 = bf16_lo_half(qw[j / 2]), q1 = bf16_hi_half(qw[j / 2]);
+                const float a0 = q0 * s2.x, a1 = q1 * s2.y;
+                const uint32_t hp = bf16_pack2(a0, a1);
+                const float h0 = bf16_lo_half(hp), h1 = bf16_hi_half(hp);
+                const uint32_t lp = bf16_pack2(a0 - h0, a1 - h1);
+                hw[j / 2] = hp;
+                lw[j / 2] = lp;
+                cst += (q0 * l2.x + q1 * l2.y) -
+                       ((h0 + bf16_lo_half(lp)) + (h1 + bf16_hi_half(lp)));
             }
-            cst += __shfl_xor(cst, 16, 64);
-            cst += __shfl_xor(cst, 32, 64);   // the head's constant, in every lane of its row
+            uint4 *arow_hi = reinterpret_cast<uint4 *>(ast + gh * kKivAS + d0);
+            uint4 *arow_lo = reinterpret_cast<uint4 *>(ast + (gh + 8) * kKivAS + d0);
+            arow_hi[0] = uint4{hw[0], hw[1], hw[2], hw[3]};
+            arow_hi[1] = uint4{hw[4], hw[5], hw[6], hw[7]};
+            arow_lo[0] = uint4{lw[0], lw[1], lw[2], lw[3]};
+            arow_lo[1] = uint4{lw[4], lw[5], lw[6], lw[7]};
+            cst += __shfl_xor(cst, 1, 64);
+            cst += __shfl_xor(cst, 2, 64);
+            cst += __shfl_xor(cst, 4, 64);   // lanes 8 gh .. 8 gh + 7: head gh's constant
+            __builtin_amdgcn_wave_barrier();
+            u16x8_t aop[4];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                aop[c4] = *reinterpret_cast<const u16x8_t *>(ast + col * kKivAS + 32 * c4 + 8 * r);
+            // the next group's codes
+            const int gn = gi + kFWaves;
+            uint4 kn0 = {0, 0, 0, 0}, kn1 = {0, 0, 0, 0};
+            if (gn < ng) {
+                kn0 = kload(gn, 0);
+                kn1 = kload(gn, 1);
+            }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const size_t tok = ubase + (size_t)(gs + gi) * kKivGroup + 16 * tt + col;
-                const uint4 kc = *reinterpret_cast<const uint4 *>(a.k_codes + tok * kKivRow + 16 * r);
-                const u16x8_t kop[4] = {kiv_widen8(kc.x), kiv_widen8(kc.y), kiv_widen8(kc.z),
-                                        kiv_widen8(kc.w)};
+                const uint4 kc = tt ? kc1 : kc0;
+                const u16x8_t kop[4] = {kiv_widen8(kc.x, km), kiv_widen8(kc.y, km), kiv_widen8(kc.z, km),
+                                        kiv_widen8(kc.w, km)};
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4)
@@ -277,11 +344,13 @@ void kivi_qattn_kernel(KiviArgs a) {
                 for (int ii = 0; ii < 4; ++ii) {
                     const int g = 4 * (r & 1) + ii;   // rows g and g + 8 hold its two parts
                     const float tot = acc[ii] + __shfl_xor(acc[ii], 32, 64);
-                    const float z = (tot + __shfl(cst, g, 64)) * a.scale;
+                    const float z = (tot + __shfl(cst, 8 * g, 64)) * a.scale;
                     if (r < 2 && g < G) lg[g * kKivLD + jc] = z;
                     mx[ii] = fmaxf(mx[ii], g < G ? z : -INFINITY);
                 }
             }
+            kc0 = kn0;
+            kc1 = kn1;
         }
         // new running maximum of each head and the rescale of the old sums
 #pragma unroll
@@ -297,7 +366,6 @@ void kivi_qattn_kernel(KiviArgs a) {
         if (tid < G) {
             float m = sm.wred[0][tid];
             for (int v = 1; v < kFWaves; ++v) m = fmaxf(m, sm.wred[v][tid]);
-            // a wave without groups in this piece left -inf
             const float mold = sm.mrun[tid];
             const float mnew = fmaxf(mold, m);
             sm.alpha[tid] = (mold == -INFINITY) ? 0.f : __expf(mold - mnew);
@@ -305,20 +373,30 @@ void kivi_qattn_kernel(KiviArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int m8 = 0; m8 < 8; ++m8)
+        for (int ii = 0; ii < 4; ++ii) {
+            const int g = (4 * r + ii) & 7;
+            const float al = (g < G) ? sm.alpha[g] : 0.f;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int g = (4 * r + ii) & 7;
-                oacc[m8][ii] *= (g < G) ? sm.alpha[g] : 0.f;
-            }
-        const float al = arow ? sm.alpha[ga] : 0.f;
-        lsum *= al;
-#pragma unroll
-        for (int c = 0; c < kKivVG; ++c) corr[c] *= al;
+            for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] *= al;
+            cacc[ii] *= al;
+        }
+        lsum *= arow ? sm.alpha[ga] : 0.f;
         const float mrow = arow ? sm.mrun[ga] : 0.f;
         const float *lrow = lg + (arow ? ga : 0) * kKivLD;
 
         // ---------------- P.V over the same groups' tiles
+        auto vload = [&](int t, uint32_t (&x)[4]) {
+            const size_t tok0 = ubase + (size_t)gs * kKivGroup + 16 * t + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[e] = *reinterpret_cast<const uint32_t *>(a.v_codes + (tok0 + 4 * e) * kKivRow + 4 * col);
+        };
+        uint32_t xv[4] = {0, 0, 0, 0};
+        if (w < ng) vload(2 * w, xv);
+        // this lane's column of the V-grid product: n < 8 the lo of grid n & 3,
+        // n >= 8 the 128x scale; n & 4 selects the low bf16 part
+        const int vcol = (col & 8) ? (col & 3) : kKivVG + (col & 3);
+        const bool vlow = (col & 4) != 0;
 #pragma unroll 1
         for (int i = 0; i < kKivSub / kFWaves; ++i) {
             const int gi = w + kFWaves * i;
@@ -326,77 +404,102 @@ void kivi_qattn_kernel(KiviArgs a) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int t = 2 * gi + tt;                       // tile of the piece
+                uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]};
+                const int tn = tt ? 2 * (gi + kFWaves) : t + 1;
+                if (tn < 2 * ng) vload(tn, xv);
                 const f32x4_t z = *reinterpret_cast<const f32x4_t *>(lrow + 16 * t + 4 * r);
                 float p[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) p[e] = arow ? __expf(z[e] - mrow) : 0.f;
                 if (hi_lane) lsum += (p[0] + p[1]) + (p[2] + p[3]);
-                // codes: dword col of keys 16t + 4e + r
-                const size_t tok0 = ubase + (size_t)gs * kKivGroup + 16 * t + r;
-                uint32_t x[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    x[e] = *reinterpret_cast<const uint32_t *>(a.v_codes + (tok0 + 4 * e) * kKivRow +
-                                                               4 * col);
+                // p as a bf16 pair (rows 0..7 high, 8..15 low), for the grid columns
+                s16x4_t ap;
+                {
+                    const uint32_t h01 = bf16_pack2(p[0], p[1]), h23 = bf16_pack2(p[2], p[3]);
+                    const uint32_t l01 = bf16_pack2(p[0] - bf16_lo_half(h01), p[1] - bf16_hi_half(h01));
+                    const uint32_t l23 = bf16_pack2(p[2] - bf16_lo_half(h23), p[3] - bf16_hi_half(h23));
+                    ap = __builtin_bit_cast(s16x4_t, hi_lane ? uint2{h01, h23} : uint2{l01, l23});
+                }
+                // B operands of the codes
                 const uint32_t za = (x[0] & 0xFFFFu) | (x[1] << 16), zb = (x[0] >> 16) | (x[1] & 0xFFFF0000u);
                 const uint32_t zc = (x[2] & 0xFFFFu) | (x[3] << 16), zd = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
-                const uint2 bw[8] = {{kiv_pair<0>(za), kiv_pair<0>(zc)}, {kiv_pair<0>(zb), kiv_pair<0>(zd)},
-                                     {kiv_pair<1>(za), kiv_pair<1>(zc)}, {kiv_pair<1>(zb), kiv_pair<1>(zd)},
-                                     {kiv_pair<2>(za), kiv_pair<2>(zc)}, {kiv_pair<2>(zb), kiv_pair<2>(zd)},
-                                     {kiv_pair<3>(za), kiv_pair<3>(zc)}, {kiv_pair<3>(zb), kiv_pair<3>(zd)}};
-                // A per channel group c: 16 p_e s_{key e, c}, high / low part
-                s16x4_t av[kKivVG];
+                const uint2 bw[8] = {{kiv_pair<0>(za, km), kiv_pair<0>(zc, km)}, {kiv_pair<0>(zb, km), kiv_pair<0>(zd, km)},
+                                     {kiv_pair<1>(za, km), kiv_pair<1>(zc, km)}, {kiv_pair<1>(zb, km), kiv_pair<1>(zd, km)},
+                                     {kiv_pair<2>(za, km), kiv_pair<2>(zc, km)}, {kiv_pair<2>(zb, km), kiv_pair<2>(zd, km)},
+                                     {kiv_pair<3>(za, km), kiv_pair<3>(zc, km)}, {kiv_pair<3>(zb, km), kiv_pair<3>(zd, km)}};
+                // A per V grid c: 128 p_e s_{key e, c}, high / low part, built as
+                // the operand's two dwords (keys 0, 1 and keys 2, 3); the grid column
+                float4 sv[4];
+                float bx[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float *vg = vgr + (16 * t + 4 * e + r) * 2 * kKivVG;
-                    const float4 sv = *reinterpret_cast<const float4 *>(vg);
-                    const float4 lv = *reinterpret_cast<const float4 *>(vg + kKivVG);
-                    const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
-                    const float lvv[4] = {lv.x, lv.y, lv.z, lv.w};
+                    sv[e] = *reinterpret_cast<const float4 *>(vg);
+                    bx[e] = vg[vcol];
+                }
+                uint32_t avw[kKivVG][2];
 #pragma unroll
-                    for (int c = 0; c < kKivVG; ++c) {
-                        const float aa = 16.f * (p[e] * svv[c]);
-                        const short hb = bf16_bits(aa);
-                        const short lb = bf16_bits(aa - bf16_value(hb));
-                        av[c][e] = hi_lane ? hb : lb;
-                        corr[c] += p[e] * lvv[c] - (bf16_value(hb) + bf16_value(lb));
+                for (int c = 0; c < kKivVG; ++c) {
+#pragma unroll
+                    for (int hpair = 0; hpair < 2; ++hpair) {
+                        const int e0 = 2 * hpair;
+                        const float a0 = p[e0] * sv[e0][c], a1 = p[e0 + 1] * sv[e0 + 1][c];
+                        const uint32_t hp = bf16_pack2(a0, a1);
+                        const uint32_t lp = bf16_pack2(a0 - bf16_lo_half(hp), a1 - bf16_hi_half(hp));
+                        avw[c][hpair] = hi_lane ? hp : lp;
                     }
                 }
+                s16x4_t bc;
+                {
+                    const uint32_t h01 = bf16_pack2(bx[0], bx[1]), h23 = bf16_pack2(bx[2], bx[3]);
+                    const uint32_t l01 = bf16_pack2(bx[0] - bf16_lo_half(h01), bx[1] - bf16_hi_half(h01));
+                    const uint32_t l23 = bf16_pack2(bx[2] - bf16_lo_half(h23), bx[3] - bf16_hi_half(h23));
+                    bc = __builtin_bit_cast(s16x4_t, vlow ? uint2{l01, l23} : uint2{h01, h23});
+                }
+                cacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, bc, cacc, 0, 0, 0);
 #pragma unroll
                 for (int m8 = 0; m8 < 8; ++m8)
                     oacc[m8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        av[m8 >> 1], __builtin_bit_cast(s16x4_t, bw[m8]), oacc[m8], 0, 0, 0);
+                        __builtin_bit_cast(s16x4_t, uint2{avw[m8 >> 1][0], avw[m8 >> 1][1]}),
+                        __builtin_bit_cast(s16x4_t, bw[m8]), oacc[m8], 0, 0, 0);
             }
         }
     }
 
     // ---------------- the split's partial (o, m, l)
 #pragma unroll
-    for (int m8 = 0; m8 < 8; ++m8)
+    for (int ii = 0; ii < 4; ++ii) {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) oacc[m8][ii] += __shfl_xor(oacc[m8][ii], 32, 64);
+        for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] += __shfl_xor(oacc[m8][ii], 32, 64);
+        cacc[ii] += __shfl_xor(cacc[ii], 32, 64);
+    }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
+    // correction of grid c for head g: sum_j p_j lo_jc - sum_j 128 p_j s_jc, the
+    // columns c and 4 + c minus the columns 8 + c and 12 + c
+    float cv[4];
 #pragma unroll
-    for (int c = 0; c < kKivVG; ++c) {
-        corr[c] += __shfl_xor(corr[c], 16, 64);
-        corr[c] += __shfl_xor(corr[c], 32, 64);
+    for (int ii = 0; ii < 4; ++ii) {
+        float v = (col & 8) ? -cacc[ii] : cacc[ii];
+        v += __shfl_xor(v, 4, 64);
+        v += __shfl_xor(v, 8, 64);
+        cv[ii] = v;
     }
-    __syncthreads();   // the LDS grids are free: partial P.V of the waves go there
-    float *opart = kgr;   // [waves][G][kHD] (G <= 8: 16 KB)
-    if (r < 2)
+    __syncthreads();   // the A tiles are free: partial P.V of the waves go there
+    float *opart = reinterpret_cast<float *>(ast_all);   // [waves][G][kHD] (G <= 8: 16 KB)
+    if (r < 2) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int g = 4 * r + ii;
-            if (g < G)
+            if (g < G) {
 #pragma unroll
-                for (int m8 = 0; m8 < 8; ++m8) opart[((size_t)w * G + g) * kHD + 16 * m8 + col] = oacc[m8][ii];
+                for (int m8 = 0; m8 < 8; ++m8)
+                    opart[((size_t)w * G + g) * kHD + 16 * m8 + col] = oacc[m8][ii];
+                if (col < kKivVG) sm.corr[w][g][col] = cv[ii];
+            }
         }
-    if (lane < G) {
-        sm.wred[w][lane] = lsum;
-#pragma unroll
-        for (int c = 0; c < kKivVG; ++c) sm.corr[w][lane][c] = corr[c];
     }
+    if (lane < G) sm.wred[w][lane] = lsum;
     __syncthreads();
     float *pp = a.part_q + ((size_t)u * ns + s) * G * (kHD + 2);
     for (int e = tid; e < G * kHD; e += kFThreads) {

@@ -523,8 +523,11 @@ int kivi_nsq(const kvc_kivi_cache *c, int hint) {
     const int groups = mq / kvc::kKivGroup;
     if (c->max_quant == 0) return 0;
     if (groups == 0) return 1;
+#ifndef KVC_KIV_SPLIT_GROUPS
+#define KVC_KIV_SPLIT_GROUPS 16
+#endif
     const int units = c->batch * c->kv_heads;
-    int ns = (groups + 15) / 16;
+    int ns = (groups + KVC_KIV_SPLIT_GROUPS - 1) / KVC_KIV_SPLIT_GROUPS;
     const int fill = (4096 + units - 1) / units, by_len = (groups + 3) / 4;
     const int want = fill < by_len ? fill : by_len;
     ns = ns > want ? ns : want;
