@@ -6,7 +6,9 @@
 // step are the ones kvc.h states.
 //
 // Attention over the quantized tokens (kivi_qattn_kernel), one workgroup per
-// (unit, share of its groups):
+// (unit, share of its groups); each of its four waves walks its own groups
+// with its own running maximum, sums and accumulators (online softmax), and
+// the waves merge once at the end, so the loop has no workgroup barrier:
 //  * K of group g, channel d: k = c * s_gd + lo_gd, so
 //        q . k_j = sum_d (q_d s_gd) c_jd + sum_d q_d lo_gd.
 //    The scale folds into the query: A = 128 q_d s_gd as a bf16 high part in
@@ -24,8 +26,9 @@
 //    (head, channel group) at the end; those two sums come from one more MFMA
 //    per tile, P against a B of the tile's lo and 128 s values (high / low
 //    columns), whose error is that of the bf16 pairs, 2^-17 relative.
-//  * the logits of 256 tokens (8 groups) stay in LDS; a longer share runs in
-//    pieces with the running maximum rescaling the partial sums.
+//  * the weights of a group's 32 keys go from the product layout to the P.V
+//    operand layout through the wave's LDS; the group's grids are staged
+//    there too.
 // The residual and the new token go through split_kernel (bf16, attend
 // only).  kivi_update_kernel merges the partials, turns a full residual's 32
 // oldest tokens into a group, and appends the new token; kivi_prefill_kernel
@@ -35,15 +38,9 @@
 namespace kvc {
 
 constexpr int kKivRow = kHD / 2;                     // bytes of one token's 4-bit codes
-#ifndef KVC_KIV_SUB
-#define KVC_KIV_SUB 8
-#endif
 #ifndef KVC_KIV_WAVES
 #define KVC_KIV_WAVES 3
 #endif
-constexpr int kKivSub = KVC_KIV_SUB;                 // groups per LDS piece
-constexpr int kKivSubT = kKivSub * kKivGroup;        // tokens per LDS piece
-constexpr int kKivLD = kKivSubT + 4;
 constexpr int kKivVG = kHD / 32;                     // V grids per token
 
 // Two codes of one dword -> two bf16 values 1 + c/128 (the code in the low
@@ -184,16 +181,20 @@ __global__ __launch_bounds__(256) void kivi_prefill_kernel(KiviArgs a) {
 // attention over the quantized tokens
 // ---------------------------------------------------------------------------
 struct KivSmall {
-    float mrun[8];                   // running max per head
-    float alpha[8];                  // rescale of the running sums at a new piece
-    float wred[kFWaves][8];
+    float m[kFWaves][8];             // each wave's running max per head
+    float l[kFWaves][8];             // each wave's running sum per head
     float corr[kFWaves][8][kKivVG];
 };
 constexpr int kKivAS = kHD + 8;      // bf16 row stride of a wave's A tile (padded against bank clashes)
+constexpr int kKivPL = 2 * 16 + 4;   // fp32 row stride of a wave's P tile (32 keys)
+// one wave's LDS: A tile [16][kKivAS] bf16, K grids [128 s | lo][128], V grids
+// [32 tokens][4 x 128 s, 4 x lo], P tile [8][kKivPL], alpha [8]
+constexpr size_t kKivWaveLds = 16 * kKivAS * 2 + 2 * kHD * 4 + kKivGroup * 2 * kKivVG * 4 +
+                               8 * kKivPL * 4 + 8 * 4;
 
 __host__ __device__ constexpr size_t kivi_qattn_smem(int G) {
-    return (size_t)G * kKivLD * 4 + (size_t)kKivSub * 2 * kHD * 4 +
-           (size_t)kKivSubT * 2 * kKivVG * 4 + (size_t)kFWaves * 16 * kKivAS * 2 + sizeof(KivSmall);
+    (void)G;
+    return (size_t)kFWaves * kKivWaveLds + sizeof(KivSmall);
 }
 
 // bf16 high part of a pair of floats, packed, and the value of each half
@@ -203,6 +204,11 @@ __device__ inline uint32_t bf16_pack2(float x, float y) {
 __device__ inline float bf16_lo_half(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ inline float bf16_hi_half(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
 
+// Every wave walks its own groups (w, w + 4, ...) with its own running max,
+// sums and P.V accumulators; the waves merge once at the end.  Per group the
+// wave stages the group's grids in its own LDS, builds the scaled query
+// operand there, runs the K products, the softmax update and the P.V
+// products; LDS traffic of one wave needs no workgroup barrier.
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(KVC_KIV_WAVES)))
 void kivi_qattn_kernel(KiviArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -217,16 +223,17 @@ void kivi_qattn_kernel(KiviArgs a) {
     const bool arow = ga < G;
     const bool hi_lane = col < 8;
 
-    float *lg = reinterpret_cast<float *>(smem);             // [G][kKivLD] logits of a piece
-    float *kgr = lg + G * kKivLD;                             // [group][128 scale | lo][kHD]
-    float *vgr = kgr + kKivSub * 2 * kHD;                     // [token][4 x 128 scale, 4 x lo]
-    uint16_t *ast_all = reinterpret_cast<uint16_t *>(vgr + kKivSubT * 2 * kKivVG);
-    uint16_t *ast = ast_all + w * 16 * kKivAS;                // this wave's A tile [16][kKivAS]
-    KivSmall &sm = *reinterpret_cast<KivSmall *>(ast_all + kFWaves * 16 * kKivAS);
+    unsigned char *wl = smem + (size_t)w * kKivWaveLds;
+    uint16_t *ast = reinterpret_cast<uint16_t *>(wl);                      // [16][kKivAS]
+    float *kg = reinterpret_cast<float *>(wl + 16 * kKivAS * 2);           // [2][kHD]
+    float *vg = kg + 2 * kHD;                                              // [32][8]
+    float *pt = vg + kKivGroup * 2 * kKivVG;                               // [8][kKivPL]
+    float *al = pt + 8 * kKivPL;                                           // [8]
+    KivSmall &sm = *reinterpret_cast<KivSmall *>(smem + (size_t)kFWaves * kKivWaveLds);
 
     // the query slice this lane scales for the K products: head gh, dims d0 .. d0 + 15
     const int gh = lane >> 3, d0 = 16 * (lane & 7);
-    uint32_t qw[8];   // bf16 pairs, widened where used
+    uint32_t qw[8];
     {
         const bool ok = gh < G;
         const uint16_t *qp = a.q + ((size_t)b * a.Hq + (size_t)h * G + (ok ? gh : 0)) * kHD + d0;
@@ -247,57 +254,66 @@ void kivi_qattn_kernel(KiviArgs a) {
     const int g0 = min(s * cg, ngr), g1 = min(ngr, g0 + cg);
     const size_t ubase = (size_t)u * a.max_quant;
     const size_t gbase = (size_t)u * (a.max_quant / kKivGroup);
-
-    if (tid < G) sm.mrun[tid] = -INFINITY;
     const KivMagic km;
+
     f32x4_t oacc[8];
 #pragma unroll
     for (int m8 = 0; m8 < 8; ++m8) oacc[m8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t cacc = {0.f, 0.f, 0.f, 0.f};   // sum_j p_j x_j for the columns of the V grids
-    float lsum = 0.f;
+    float lsum = 0.f;                        // A-layout lanes: head ga
+    float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // C-layout rows' heads
+    // this lane's column of the V-grid product: n < 8 the lo of grid n & 3,
+    // n >= 8 the 128x scale; n & 4 selects the low bf16 part
+    const int vcol = (col & 8) ? (col & 3) : kKivVG + (col & 3);
+    const bool vlow = (col & 4) != 0;
 
-    for (int gs = g0; gs < g1; gs += kKivSub) {
-        const int ng = min(kKivSub, g1 - gs);
-        __syncthreads();   // the previous piece is done with the LDS
-        for (int i = tid; i < ng * kHD; i += kFThreads) {
-            const int gi = i / kHD, d = i % kHD;
-            kgr[gi * 2 * kHD + d] = 128.f * a.k_scale[(gbase + gs + gi) * kHD + d];
-            kgr[gi * 2 * kHD + kHD + d] = a.k_lo[(gbase + gs + gi) * kHD + d];
+    // the group's data for this lane: K codes of both tiles, V codes (dword
+    // col of keys 16 tt + 4 e + r), 16 B of the K grids and of the V grids
+    struct GroupData {
+        uint4 kc[2];
+        uint32_t vc[2][4];
+        float4 kgr, vgr;
+    };
+    auto gload = [&](int g, GroupData &d) {
+        const size_t tok = ubase + (size_t)g * kKivGroup;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            d.kc[tt] = *reinterpret_cast<const uint4 *>(a.k_codes + (tok + 16 * tt + col) * kKivRow + 16 * r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                d.vc[tt][e] = *reinterpret_cast<const uint32_t *>(
+                    a.v_codes + (tok + 16 * tt + 4 * e + r) * kKivRow + 4 * col);
         }
-        for (int i = tid; i < ng * kKivGroup * kKivVG; i += kFThreads) {
-            const int t = i / kKivVG, c = i % kKivVG;
-            const size_t src = (ubase + (size_t)gs * kKivGroup + t) * kKivVG + c;
-            vgr[t * 2 * kKivVG + c] = 128.f * a.v_scale[src];
-            vgr[t * 2 * kKivVG + kKivVG + c] = a.v_lo[src];
-        }
-        // codes of the wave's first group, requested before the barrier
-        auto kload = [&](int gi, int tt) -> uint4 {
-            const size_t tok = ubase + (size_t)(gs + gi) * kKivGroup + 16 * tt + col;
-            return *reinterpret_cast<const uint4 *>(a.k_codes + tok * kKivRow + 16 * r);
-        };
-        uint4 kc0 = {0, 0, 0, 0}, kc1 = {0, 0, 0, 0};
-        if (w < ng) {
-            kc0 = kload(w, 0);
-            kc1 = kload(w, 1);
-        }
-        __syncthreads();
+        // K grids: lanes 0..31 the scales (4 each), 32..63 the lo
+        const float *kgsrc = (lane < 32 ? a.k_scale : a.k_lo) + (gbase + g) * kHD + 4 * (lane & 31);
+        d.kgr = *reinterpret_cast<const float4 *>(kgsrc);
+        // V grids: lanes 0..31 token lane's scales, 32..63 its lo
+        const float *vgsrc = (lane < 32 ? a.v_scale : a.v_lo) + (tok + (lane & 31)) * kKivVG;
+        d.vgr = *reinterpret_cast<const float4 *>(vgsrc);
+    };
 
-        // ---------------- logits: wave w takes groups w, w + 4
-        float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll 1
-        for (int i = 0; i < kKivSub / kFWaves; ++i) {
-            const int gi = w + kFWaves * i;
-            if (gi >= ng) break;   // wave-uniform
-            // A = 128 q_d s_gd of this lane's 16 (head, dim), high and low
-            // parts into the wave's A tile; the head's constant
-            // sum_d q_d lo_gd - sum_d (high + low)
-            const float *sg = kgr + gi * 2 * kHD + d0;
-            float cst = 0.f;
+    for (int gi = g0 + w; gi < g1; gi += kFWaves) {
+        GroupData cur;
+        gload(gi, cur);
+        // ---- the group's grids into the wave's LDS (scales x 128)
+        {
+            const float m = lane < 32 ? 128.f : 1.f;
+            const float4 kv = {cur.kgr.x * m, cur.kgr.y * m, cur.kgr.z * m, cur.kgr.w * m};
+            *reinterpret_cast<float4 *>(kg + (lane < 32 ? 0 : kHD) + 4 * (lane & 31)) = kv;
+            const float4 vv = {cur.vgr.x * m, cur.vgr.y * m, cur.vgr.z * m, cur.vgr.w * m};
+            *reinterpret_cast<float4 *>(vg + (lane & 31) * 2 * kKivVG + (lane < 32 ? 0 : kKivVG)) = vv;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // ---- A = 128 q_d s_gd of this lane's 16 (head, dim), high and low
+        // parts into the A tile; the head's constant sum_d q_d lo_gd - sum_d A_d
+        float cst = 0.f;
+        {
             uint32_t hw[8], lw[8];
 #pragma unroll
             for (int j = 0; j < 16; j += 2) {
-                const float2 s2 = *reinterpret_cast<const float2 *>(sg + j);
-                const float2 l2 = *reinterpret_cast<const float2 *>(sg + kHD + j);
+                const float2 s2 = *reinterpret_cast<const float2 *>(kg + d0 + j);
+                const float2 l2 = *reinterpret_cast<const float2 *>(kg + kHD + d0 + j);
                 const float q0 = bf16_lo_half(qw[j / 2]), q1 = bf16_hi_half(qw[j / 2]);
                 const float a0 = q0 * s2.x, a1 = q1 * s2.y;
                 const uint32_t hp = bf16_pack2(a0, a1);
@@ -305,168 +321,140 @@ void kivi_qattn_kernel(KiviArgs a) {
                 const uint32_t lp = bf16_pack2(a0 - h0, a1 - h1);
                 hw[j / 2] = hp;
                 lw[j / 2] = lp;
-                cst += (q0 * l2.x + q1 * l2.y) -
-                       ((h0 + bf16_lo_half(lp)) + (h1 + bf16_hi_half(lp)));
+                cst += (q0 * l2.x + q1 * l2.y) - ((h0 + bf16_lo_half(lp)) + (h1 + bf16_hi_half(lp)));
             }
-            uint4 *arow_hi = reinterpret_cast<uint4 *>(ast + gh * kKivAS + d0);
-            uint4 *arow_lo = reinterpret_cast<uint4 *>(ast + (gh + 8) * kKivAS + d0);
-            arow_hi[0] = uint4{hw[0], hw[1], hw[2], hw[3]};
-            arow_hi[1] = uint4{hw[4], hw[5], hw[6], hw[7]};
-            arow_lo[0] = uint4{lw[0], lw[1], lw[2], lw[3]};
-            arow_lo[1] = uint4{lw[4], lw[5], lw[6], lw[7]};
-            cst += __shfl_xor(cst, 1, 64);
-            cst += __shfl_xor(cst, 2, 64);
-            cst += __shfl_xor(cst, 4, 64);   // lanes 8 gh .. 8 gh + 7: head gh's constant
-            __builtin_amdgcn_wave_barrier();
+            uint4 *ah = reinterpret_cast<uint4 *>(ast + gh * kKivAS + d0);
+            uint4 *alo = reinterpret_cast<uint4 *>(ast + (gh + 8) * kKivAS + d0);
+            ah[0] = uint4{hw[0], hw[1], hw[2], hw[3]};
+            ah[1] = uint4{hw[4], hw[5], hw[6], hw[7]};
+            alo[0] = uint4{lw[0], lw[1], lw[2], lw[3]};
+            alo[1] = uint4{lw[4], lw[5], lw[6], lw[7]};
+        }
+        cst += __shfl_xor(cst, 1, 64);
+        cst += __shfl_xor(cst, 2, 64);
+        cst += __shfl_xor(cst, 4, 64);   // lanes 8 gh .. 8 gh + 7: head gh's constant
+        __builtin_amdgcn_wave_barrier();
+        // ---- logits of the group's 32 keys (C layout: rows 4 (r & 1) + ii)
+        float z[2][4];
+        {
             u16x8_t aop[4];
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4)
                 aop[c4] = *reinterpret_cast<const u16x8_t *>(ast + col * kKivAS + 32 * c4 + 8 * r);
-            // the next group's codes
-            const int gn = gi + kFWaves;
-            uint4 kn0 = {0, 0, 0, 0}, kn1 = {0, 0, 0, 0};
-            if (gn < ng) {
-                kn0 = kload(gn, 0);
-                kn1 = kload(gn, 1);
-            }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const uint4 kc = tt ? kc1 : kc0;
-                const u16x8_t kop[4] = {kiv_widen8(kc.x, km), kiv_widen8(kc.y, km), kiv_widen8(kc.z, km),
-                                        kiv_widen8(kc.w, km)};
+                const uint4 kc = cur.kc[tt];
+                const u16x8_t kop[4] = {kiv_widen8(kc.x, km), kiv_widen8(kc.y, km),
+                                        kiv_widen8(kc.z, km), kiv_widen8(kc.w, km)};
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aop[c4]),
                                                                   as_bf16x8(kop[c4]), acc, 0, 0, 0);
-                const int jc = 32 * gi + 16 * tt + (((col & 3) << 2) | (col >> 2));
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    const int g = 4 * (r & 1) + ii;   // rows g and g + 8 hold its two parts
+                    const int g = 4 * (r & 1) + ii;
+                    // every lane takes part in both exchanges (a read from an
+                    // inactive lane is not defined)
                     const float tot = acc[ii] + __shfl_xor(acc[ii], 32, 64);
-                    const float z = (tot + __shfl(cst, 8 * g, 64)) * a.scale;
-                    if (r < 2 && g < G) lg[g * kKivLD + jc] = z;
-                    mx[ii] = fmaxf(mx[ii], g < G ? z : -INFINITY);
+                    const float cb = __shfl(cst, 8 * g, 64);
+                    z[tt][ii] = (g < G) ? (tot + cb) * a.scale : -INFINITY;
                 }
             }
-            kc0 = kn0;
-            kc1 = kn1;
         }
-        // new running maximum of each head and the rescale of the old sums
+        // ---- softmax update: the group max per head, the rescale, the weights
+        float alpha[4];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            float m = mx[ii];
+            float m = fmaxf(z[0][ii], z[1][ii]);
             m = fmaxf(m, __shfl_xor(m, 8, 64));
             m = fmaxf(m, __shfl_xor(m, 4, 64));
             m = fmaxf(m, __shfl_xor(m, 2, 64));
             m = fmaxf(m, __shfl_xor(m, 1, 64));
-            if (col == 0 && r < 2 && 4 * r + ii < G) sm.wred[w][4 * r + ii] = m;
+            const float mnew = fmaxf(mrun[ii], m);
+            alpha[ii] = (mrun[ii] == -INFINITY) ? 0.f : __expf(mrun[ii] - mnew);
+            mrun[ii] = mnew;
+            const int g = 4 * (r & 1) + ii;
+            if (r < 2 && g < G) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    // key col of tile tt at column lg_col(16 tt + col)
+                    const int jc = 16 * tt + (((col & 3) << 2) | (col >> 2));
+                    pt[g * kKivPL + jc] = (mnew == -INFINITY) ? 0.f : __expf(z[tt][ii] - mnew);
+                }
+                if (col == 0) al[g] = alpha[ii];
+            }
         }
-        __syncthreads();
-        if (tid < G) {
-            float m = sm.wred[0][tid];
-            for (int v = 1; v < kFWaves; ++v) m = fmaxf(m, sm.wred[v][tid]);
-            const float mold = sm.mrun[tid];
-            const float mnew = fmaxf(mold, m);
-            sm.alpha[tid] = (mold == -INFINITY) ? 0.f : __expf(mold - mnew);
-            sm.mrun[tid] = mnew;
-        }
-        __syncthreads();
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int g = (4 * r + ii) & 7;
-            const float al = (g < G) ? sm.alpha[g] : 0.f;
 #pragma unroll
-            for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] *= al;
-            cacc[ii] *= al;
+            for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] *= alpha[ii];
+            cacc[ii] *= alpha[ii];
         }
-        lsum *= arow ? sm.alpha[ga] : 0.f;
-        const float mrow = arow ? sm.mrun[ga] : 0.f;
-        const float *lrow = lg + (arow ? ga : 0) * kKivLD;
-
-        // ---------------- P.V over the same groups' tiles
-        auto vload = [&](int t, uint32_t (&x)[4]) {
-            const size_t tok0 = ubase + (size_t)gs * kKivGroup + 16 * t + r;
+        __builtin_amdgcn_wave_barrier();
+        lsum *= arow ? al[ga] : 0.f;
+        // ---- P.V of the two tiles
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                x[e] = *reinterpret_cast<const uint32_t *>(a.v_codes + (tok0 + 4 * e) * kKivRow + 4 * col);
-        };
-        uint32_t xv[4] = {0, 0, 0, 0};
-        if (w < ng) vload(2 * w, xv);
-        // this lane's column of the V-grid product: n < 8 the lo of grid n & 3,
-        // n >= 8 the 128x scale; n & 4 selects the low bf16 part
-        const int vcol = (col & 8) ? (col & 3) : kKivVG + (col & 3);
-        const bool vlow = (col & 4) != 0;
-#pragma unroll 1
-        for (int i = 0; i < kKivSub / kFWaves; ++i) {
-            const int gi = w + kFWaves * i;
-            if (gi >= ng) break;
+        for (int tt = 0; tt < 2; ++tt) {
+            float p[4];
+            {
+                const f32x4_t pv = *reinterpret_cast<const f32x4_t *>(pt + (arow ? ga : 0) * kKivPL +
+                                                                      16 * tt + 4 * r);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int t = 2 * gi + tt;                       // tile of the piece
-                uint32_t x[4] = {xv[0], xv[1], xv[2], xv[3]};
-                const int tn = tt ? 2 * (gi + kFWaves) : t + 1;
-                if (tn < 2 * ng) vload(tn, xv);
-                const f32x4_t z = *reinterpret_cast<const f32x4_t *>(lrow + 16 * t + 4 * r);
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = arow ? __expf(z[e] - mrow) : 0.f;
-                if (hi_lane) lsum += (p[0] + p[1]) + (p[2] + p[3]);
-                // p as a bf16 pair (rows 0..7 high, 8..15 low), for the grid columns
-                s16x4_t ap;
-                {
-                    const uint32_t h01 = bf16_pack2(p[0], p[1]), h23 = bf16_pack2(p[2], p[3]);
-                    const uint32_t l01 = bf16_pack2(p[0] - bf16_lo_half(h01), p[1] - bf16_hi_half(h01));
-                    const uint32_t l23 = bf16_pack2(p[2] - bf16_lo_half(h23), p[3] - bf16_hi_half(h23));
-                    ap = __builtin_bit_cast(s16x4_t, hi_lane ? uint2{h01, h23} : uint2{l01, l23});
-                }
-                // B operands of the codes
-                const uint32_t za = (x[0] & 0xFFFFu) | (x[1] << 16), zb = (x[0] >> 16) | (x[1] & 0xFFFF0000u);
-                const uint32_t zc = (x[2] & 0xFFFFu) | (x[3] << 16), zd = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
-                const uint2 bw[8] = {{kiv_pair<0>(za, km), kiv_pair<0>(zc, km)}, {kiv_pair<0>(zb, km), kiv_pair<0>(zd, km)},
-                                     {kiv_pair<1>(za, km), kiv_pair<1>(zc, km)}, {kiv_pair<1>(zb, km), kiv_pair<1>(zd, km)},
-                                     {kiv_pair<2>(za, km), kiv_pair<2>(zc, km)}, {kiv_pair<2>(zb, km), kiv_pair<2>(zd, km)},
-                                     {kiv_pair<3>(za, km), kiv_pair<3>(zc, km)}, {kiv_pair<3>(zb, km), kiv_pair<3>(zd, km)}};
-                // A per V grid c: 128 p_e s_{key e, c}, high / low part, built as
-                // the operand's two dwords (keys 0, 1 and keys 2, 3); the grid column
-                float4 sv[4];
-                float bx[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float *vg = vgr + (16 * t + 4 * e + r) * 2 * kKivVG;
-                    sv[e] = *reinterpret_cast<const float4 *>(vg);
-                    bx[e] = vg[vcol];
-                }
-                uint32_t avw[kKivVG][2];
-#pragma unroll
-                for (int c = 0; c < kKivVG; ++c) {
-#pragma unroll
-                    for (int hpair = 0; hpair < 2; ++hpair) {
-                        const int e0 = 2 * hpair;
-                        const float a0 = p[e0] * sv[e0][c], a1 = p[e0 + 1] * sv[e0 + 1][c];
-                        const uint32_t hp = bf16_pack2(a0, a1);
-                        const uint32_t lp = bf16_pack2(a0 - bf16_lo_half(hp), a1 - bf16_hi_half(hp));
-                        avw[c][hpair] = hi_lane ? hp : lp;
-                    }
-                }
-                s16x4_t bc;
-                {
-                    const uint32_t h01 = bf16_pack2(bx[0], bx[1]), h23 = bf16_pack2(bx[2], bx[3]);
-                    const uint32_t l01 = bf16_pack2(bx[0] - bf16_lo_half(h01), bx[1] - bf16_hi_half(h01));
-                    const uint32_t l23 = bf16_pack2(bx[2] - bf16_lo_half(h23), bx[3] - bf16_hi_half(h23));
-                    bc = __builtin_bit_cast(s16x4_t, vlow ? uint2{l01, l23} : uint2{h01, h23});
-                }
-                cacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, bc, cacc, 0, 0, 0);
-#pragma unroll
-                for (int m8 = 0; m8 < 8; ++m8)
-                    oacc[m8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        __builtin_bit_cast(s16x4_t, uint2{avw[m8 >> 1][0], avw[m8 >> 1][1]}),
-                        __builtin_bit_cast(s16x4_t, bw[m8]), oacc[m8], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) p[e] = arow ? pv[e] : 0.f;
             }
+            if (hi_lane) lsum += (p[0] + p[1]) + (p[2] + p[3]);
+            s16x4_t ap;
+            {
+                const uint32_t h01 = bf16_pack2(p[0], p[1]), h23 = bf16_pack2(p[2], p[3]);
+                const uint32_t l01 = bf16_pack2(p[0] - bf16_lo_half(h01), p[1] - bf16_hi_half(h01));
+                const uint32_t l23 = bf16_pack2(p[2] - bf16_lo_half(h23), p[3] - bf16_hi_half(h23));
+                ap = __builtin_bit_cast(s16x4_t, hi_lane ? uint2{h01, h23} : uint2{l01, l23});
+            }
+            const uint32_t *x = cur.vc[tt];
+            const uint32_t za = (x[0] & 0xFFFFu) | (x[1] << 16), zb = (x[0] >> 16) | (x[1] & 0xFFFF0000u);
+            const uint32_t zc = (x[2] & 0xFFFFu) | (x[3] << 16), zd = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
+            const uint2 bw[8] = {{kiv_pair<0>(za, km), kiv_pair<0>(zc, km)}, {kiv_pair<0>(zb, km), kiv_pair<0>(zd, km)},
+                                 {kiv_pair<1>(za, km), kiv_pair<1>(zc, km)}, {kiv_pair<1>(zb, km), kiv_pair<1>(zd, km)},
+                                 {kiv_pair<2>(za, km), kiv_pair<2>(zc, km)}, {kiv_pair<2>(zb, km), kiv_pair<2>(zd, km)},
+                                 {kiv_pair<3>(za, km), kiv_pair<3>(zc, km)}, {kiv_pair<3>(zb, km), kiv_pair<3>(zd, km)}};
+            float4 sv[4];
+            float bx[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float *vgk = vg + (16 * tt + 4 * e + r) * 2 * kKivVG;
+                sv[e] = *reinterpret_cast<const float4 *>(vgk);
+                bx[e] = vgk[vcol];
+            }
+            uint32_t avw[kKivVG][2];
+#pragma unroll
+            for (int c = 0; c < kKivVG; ++c) {
+#pragma unroll
+                for (int hpair = 0; hpair < 2; ++hpair) {
+                    const int e0 = 2 * hpair;
+                    const float a0 = p[e0] * sv[e0][c], a1 = p[e0 + 1] * sv[e0 + 1][c];
+                    const uint32_t hp = bf16_pack2(a0, a1);
+                    const uint32_t lp = bf16_pack2(a0 - bf16_lo_half(hp), a1 - bf16_hi_half(hp));
+                    avw[c][hpair] = hi_lane ? hp : lp;
+                }
+            }
+            s16x4_t bc;
+            {
+                const uint32_t h01 = bf16_pack2(bx[0], bx[1]), h23 = bf16_pack2(bx[2], bx[3]);
+                const uint32_t l01 = bf16_pack2(bx[0] - bf16_lo_half(h01), bx[1] - bf16_hi_half(h01));
+                const uint32_t l23 = bf16_pack2(bx[2] - bf16_lo_half(h23), bx[3] - bf16_hi_half(h23));
+                bc = __builtin_bit_cast(s16x4_t, vlow ? uint2{l01, l23} : uint2{h01, h23});
+            }
+            cacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, bc, cacc, 0, 0, 0);
+#pragma unroll
+            for (int m8 = 0; m8 < 8; ++m8)
+                oacc[m8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(s16x4_t, uint2{avw[m8 >> 1][0], avw[m8 >> 1][1]}),
+                    __builtin_bit_cast(s16x4_t, bw[m8]), oacc[m8], 0, 0, 0);
         }
     }
 
-    // ---------------- the split's partial (o, m, l)
+    // ---------------- merge the four waves into the split's partial (o, m, l)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
 #pragma unroll
@@ -475,8 +463,6 @@ void kivi_qattn_kernel(KiviArgs a) {
     }
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
-    // correction of grid c for head g: sum_j p_j lo_jc - sum_j 128 p_j s_jc, the
-    // columns c and 4 + c minus the columns 8 + c and 12 + c
     float cv[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -485,8 +471,13 @@ void kivi_qattn_kernel(KiviArgs a) {
         v += __shfl_xor(v, 8, 64);
         cv[ii] = v;
     }
-    __syncthreads();   // the A tiles are free: partial P.V of the waves go there
-    float *opart = reinterpret_cast<float *>(ast_all);   // [waves][G][kHD] (G <= 8: 16 KB)
+    if (r < 2 && col == 0)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            if (4 * r + ii < G) sm.m[w][4 * r + ii] = mrun[ii];
+    if (lane < G) sm.l[w][lane] = lsum;
+    __syncthreads();   // every wave is done with its LDS: partial P.V of the waves go there
+    float *opart = reinterpret_cast<float *>(smem);   // [waves][G][kHD] (G <= 8: 16 KB)
     if (r < 2) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -499,19 +490,29 @@ void kivi_qattn_kernel(KiviArgs a) {
             }
         }
     }
-    if (lane < G) sm.wred[w][lane] = lsum;
     __syncthreads();
     float *pp = a.part_q + ((size_t)u * ns + s) * G * (kHD + 2);
     for (int e = tid; e < G * kHD; e += kFThreads) {
         const int g = e / kHD, d = e % kHD;
+        float M = -INFINITY;
+        for (int v = 0; v < kFWaves; ++v) M = fmaxf(M, sm.m[v][g]);
         float o = 0.f;
-        for (int v = 0; v < kFWaves; ++v) o += opart[((size_t)v * G + g) * kHD + d] + sm.corr[v][g][d / 32];
+        for (int v = 0; v < kFWaves; ++v) {
+            const float mv = sm.m[v][g];
+            const float f = (mv == -INFINITY) ? 0.f : __expf(mv - M);
+            o += f * (opart[((size_t)v * G + g) * kHD + d] + sm.corr[v][g][d / 32]);
+        }
         pp[g * (kHD + 2) + d] = o;
     }
     if (tid < G) {
+        float M = -INFINITY;
+        for (int v = 0; v < kFWaves; ++v) M = fmaxf(M, sm.m[v][tid]);
         float l = 0.f;
-        for (int v = 0; v < kFWaves; ++v) l += sm.wred[v][tid];
-        pp[tid * (kHD + 2) + kHD] = sm.mrun[tid];
+        for (int v = 0; v < kFWaves; ++v) {
+            const float mv = sm.m[v][tid];
+            l += (mv == -INFINITY) ? 0.f : __expf(mv - M) * sm.l[v][tid];
+        }
+        pp[tid * (kHD + 2) + kHD] = M;
         pp[tid * (kHD + 2) + kHD + 1] = l;
     }
 }
