@@ -516,15 +516,17 @@ kvc_status check_kivi(const kvc_kivi_cache *c, const char *what) {
     return KVC_OK;
 }
 
-// splits of the quantized tokens: pieces of at most 16 groups (512 tokens),
-// about 4,096 workgroups, no share under 4 groups, at most 64 splits
+// splits of the quantized tokens: shares of at most 64 groups (2,048 tokens;
+// each wave walks its own groups, so a long share costs no LDS), enough
+// splits for about 4,096 workgroups, no share under 4 groups, at most 64
+// splits
 int kivi_nsq(const kvc_kivi_cache *c, int hint) {
     const int mq = (hint <= 0 || hint > c->max_quant) ? c->max_quant : hint;
     const int groups = mq / kvc::kKivGroup;
     if (c->max_quant == 0) return 0;
     if (groups == 0) return 1;
 #ifndef KVC_KIV_SPLIT_GROUPS
-#define KVC_KIV_SPLIT_GROUPS 16
+#define KVC_KIV_SPLIT_GROUPS 64
 #endif
     const int units = c->batch * c->kv_heads;
     int ns = (groups + KVC_KIV_SPLIT_GROUPS - 1) / KVC_KIV_SPLIT_GROUPS;
