@@ -425,6 +425,102 @@ def oracle_free_split(n_tokens: int, group: int = 32, residual: int = 128):
     return q, n_tokens - q
 
 
+def paged_bench(torch, kvc, synth, args, w):
+    """H2O-512 on a paged cache of mixed-length sequences (log-uniform
+    512..32,768 tokens, blocks of 16 slots, a shuffled block table): the first
+    step (attention over every prompt, then the trim to 512) is timed alone,
+    then whole steady steps back to back (one launch each)."""
+    import numpy as np
+    B, Hq, Hkv, D, bs = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.paged_block
+    G = Hq // Hkv
+    dev = torch.device("cuda", 0)
+    lengths = synth.mixed_lengths(w)
+    cap = (int(lengths.max()) + 1 + bs - 1) // bs * bs
+    max_blocks = cap // bs
+    nblk = B * max_blocks
+    perm = synth.block_permutation(nblk, w.seed, w.wid, 0)
+    table = torch.from_numpy(perm.reshape(B, max_blocks).copy())
+    cache = kvc.KvCache(B, Hq, Hkv, D, cap, kvc.BF16, device=dev, block_size=bs, num_blocks=nblk,
+                        block_table=table)
+    step_blocks = 4096
+    for i0 in range(0, nblk, step_blocks):
+        sl = slice(i0, min(nblk, i0 + step_blocks))
+        cache.k[sl] = synth.device_normal(cache.k[sl].shape, w.seed, w.wid, 31, i0)
+        cache.v[sl] = synth.device_normal(cache.v[sl].shape, w.seed, w.wid, 32, i0)
+    cache.pos.copy_(torch.arange(cap, dtype=torch.int32, device=dev).expand(B, Hkv, cap))
+    cache.n_slots.copy_(torch.from_numpy(lengths.astype(np.int32)).view(B, 1).expand(B, Hkv))
+    scores = torch.zeros((B, Hkv, cap), device=dev)
+    pool = [(synth.device_normal((B, Hq, D), w.seed, w.wid, 33, i),
+             synth.device_normal((B, Hkv, D), w.seed, w.wid, 34, i),
+             synth.device_normal((B, Hkv, D), w.seed, w.wid, 35, i)) for i in range(4)]
+    total = 1 + args.warmup + 2 * args.steps
+    lens = torch.from_numpy(lengths.astype(np.int32)).to(dev)
+    new_pos = (lens.view(1, B) + torch.arange(total, dtype=torch.int32, device=dev).view(-1, 1)).contiguous()
+    out = torch.empty((B, Hq, D), device=dev)
+    pol = kvc.policy_h2o(w.n_heavy, w.n_recent)
+    ws = cache.workspace(cap)
+    stream = torch.cuda.current_stream()
+    hint = [cap]
+
+    def step(t):
+        q, kn, vn = pool[t % 4]
+        kvc.decode_step(cache, pol, t, new_pos[t - 1], q, kn, vn, out, scores,
+                        max_len_hint=hint[0], workspace=ws, stream=stream)
+
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    step(1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    trim_ms = e0.elapsed_time(e1)
+    assert bool((cache.n_slots == 512).all())
+    hint[0] = 513
+    t = 2
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step(t)
+        t += 1
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(t)
+        evs[i][1].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    launch_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    assert int(cache.flags.item()) == 0, "device contract flag raised"
+    unit = per_unit_bytes(512, G, D, 2, "h2o")
+    achieved = unit * B * Hkv / (launch_ms * 1e-3) / 1e9
+    first_bytes = sum(per_unit_bytes(int(L), G, D, 2, "h2o") for L in lengths) * Hkv
+    log(f"{w.name}: first step {trim_ms:.3f} ms ({first_bytes / (trim_ms * 1e-3) / 1e9:.0f} GB/s "
+        f"for the attention's bytes, trim included), steady {ms * 1e3:.1f} us/step, "
+        f"{achieved:.0f} GB/s")
+    print(json.dumps({
+        "metric": f"decode steps/s and achieved HBM GB/s, paged mixed lengths, B={B}",
+        "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "block": bs, "lengths": f"log-uniform {w.min_len}..{w.max_len}, "
+                                           f"mean {float(lengths.mean()):.0f}",
+                   "policy": "h2o", "budget": "64+448", "first_step_ms": trim_ms,
+                   "tokens_per_s": B * 1e3 / ms},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvc_decode_step (whole step, paged)", "bytes_per_unit": unit,
+                     "units_per_launch": B * Hkv, "launch_ms": launch_ms},
+    }), flush=True)
+
+
 def sweep(torch, kvc, synth, args):
     """Where eviction pays: full vs StreamingLLM-512 vs H2O-512 (and H2O with an
     unfused score pass) over batch and prompt length.  One JSON line per point."""
@@ -492,6 +588,9 @@ def main():
 
     f8 = args.kv_dtype == "fp8"
     w = synth.workload(args.workload, dtype="e5m2" if f8 else "bf16")
+    if w.paged_block:
+        paged_bench(torch, kvc, synth, args, w)
+        return
     policy = args.policy
     B, Hq, Hkv, D, P = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.prompt_len
     if policy == "random":   # filled to the budget: every step evicts one per head
