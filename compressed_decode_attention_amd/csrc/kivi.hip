@@ -43,6 +43,19 @@ constexpr int kKivRow = kHD / 2;                     // bytes of one token's 4-b
 #endif
 constexpr int kKivVG = kHD / 32;                     // V grids per token
 
+// codes and grids are read once per step: non-temporal loads
+#ifndef KVC_KIV_NT
+#define KVC_KIV_NT 1
+#endif
+template <typename T>
+__device__ inline T kiv_load(const T *p) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    if constexpr (!KVC_KIV_NT) return *p;
+    else if constexpr (sizeof(T) == 16)
+        return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p)));
+    else return __builtin_nontemporal_load(p);
+}
+
 // Two codes of one dword -> two bf16 values 1 + c/128 (the code in the low
 // mantissa bits: bits 0x3F80 | c).  A dword holds eight codes, slots 0..3
 // (bits 0..15) the even elements and slots 4..7 the odd ones, so pair J
@@ -278,18 +291,18 @@ void kivi_qattn_kernel(KiviArgs a) {
         const size_t tok = ubase + (size_t)g * kKivGroup;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            d.kc[tt] = *reinterpret_cast<const uint4 *>(a.k_codes + (tok + 16 * tt + col) * kKivRow + 16 * r);
+            d.kc[tt] = kiv_load(reinterpret_cast<const uint4 *>(a.k_codes + (tok + 16 * tt + col) * kKivRow + 16 * r));
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                d.vc[tt][e] = *reinterpret_cast<const uint32_t *>(
-                    a.v_codes + (tok + 16 * tt + 4 * e + r) * kKivRow + 4 * col);
+                d.vc[tt][e] = kiv_load(reinterpret_cast<const uint32_t *>(
+                    a.v_codes + (tok + 16 * tt + 4 * e + r) * kKivRow + 4 * col));
         }
         // K grids: lanes 0..31 the scales (4 each), 32..63 the lo
         const float *kgsrc = (lane < 32 ? a.k_scale : a.k_lo) + (gbase + g) * kHD + 4 * (lane & 31);
-        d.kgr = *reinterpret_cast<const float4 *>(kgsrc);
+        d.kgr = kiv_load(reinterpret_cast<const float4 *>(kgsrc));
         // V grids: lanes 0..31 token lane's scales, 32..63 its lo
         const float *vgsrc = (lane < 32 ? a.v_scale : a.v_lo) + (tok + (lane & 31)) * kKivVG;
-        d.vgr = *reinterpret_cast<const float4 *>(vgsrc);
+        d.vgr = kiv_load(reinterpret_cast<const float4 *>(vgsrc));
     };
 
 #pragma unroll 1
