@@ -36,12 +36,12 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE reads 1,048,576 KiB (x 1.000).  Valid only for the kernel
 # sources whose digest is recorded; otherwise the bench reports null.
 PROFILED_TRAFFIC = {
-    "sources_digest": "2d054446d1785a42",
+    "sources_digest": "3562727d22ceca3e",
     "workload": "heavy_load_b512_l2048",
     "policy": "h2o",
-    "fetch_kib": 539807.75,
-    "write_kib": 27720.64,
-    "fetch_scale": 1048576.0 / 524302.85,
+    "fetch_kib": 538433.32,
+    "write_kib": 26995.61,
+    "fetch_scale": 1048576.0 / 524303.75,
     "write_scale": 1.0,
 }
 
