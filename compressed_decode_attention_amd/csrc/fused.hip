@@ -190,7 +190,7 @@ void fused_kernel(FusedArgs fa) {
         __amdgpu_buffer_rsrc_t rs;
         int toff;
         src.tile(t, false, rs, toff);
-        return buffer_row<F8>(rs, lane_off + toff + 4 * RB * k);
+        return buffer_row<F8, PAGED>(rs, lane_off + toff + 4 * RB * k);
     };
     const int tn = n >> 4, qn = n & 15;   // tile and row of the new token
     int pmax = -1;
@@ -265,7 +265,7 @@ void fused_kernel(FusedArgs fa) {
         __amdgpu_buffer_rsrc_t rs;
         int toff;
         src.tile(t, true, rs, toff);
-        return buffer_row<F8>(rs, lane_off + toff + 4 * RB * k);
+        return buffer_row<F8, PAGED>(rs, lane_off + toff + 4 * RB * k);
     };
     u16x8_t vnc = *reinterpret_cast<const u16x8_t *>(vn + 8 * col);
     if constexpr (F8) {
