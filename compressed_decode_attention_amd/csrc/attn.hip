@@ -23,11 +23,106 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
     attn_unit_generic<T, D>(a, blockIdx.x / a.nsplit, blockIdx.x % a.nsplit, L);
 }
 
+// Partials staged per pass of the output combine: 48 float per thread.
+constexpr int kCombStage = 48 * kAttnThreads;
+
 struct CombLds {
-    float fac[kMaxSplit][kMaxGroup];   // exp(m_s - M) / L
+    float fac[kMaxSplit][kMaxGroup];   // exp(m_s - M), then exp(m_s - M) / L
     float ms[kMaxSplit][kMaxGroup], ls[kMaxSplit][kMaxGroup];   // the splits' m, l
     float Mg[kMaxGroup], Lg[kMaxGroup];
+    float stage[kCombStage + kMaxGroup * 128];   // raw partials of a block of splits (+ pad)
 };
+
+// The splits' (m, l) of one unit into LDS (the caller syncs).
+template <int D>
+__device__ inline void combine_load_ml(const float *pp, int ns, int G, CombLds &CB) {
+    for (int i = threadIdx.x; i < ns * G; i += kAttnThreads) {
+        const int s = i / G, g = i % G;
+        CB.ms[s][g] = pp[(s * G + g) * (D + 2) + D];
+        CB.ls[s][g] = pp[(s * G + g) * (D + 2) + D + 1];
+    }
+}
+
+// Global max M and normaliser L per head, then the factor of each split,
+// exp(m_s - M) / L (0 for an empty split); L sums the splits in order.
+__device__ inline void combine_factors(int ns, int G, CombLds &CB) {
+    const int tid = threadIdx.x;
+    if (tid < G) {
+        float M = -INFINITY;
+#pragma unroll 8
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, CB.ms[s][tid]);
+        CB.Mg[tid] = M;
+    }
+    __syncthreads();
+    for (int i = tid; i < ns * G; i += kAttnThreads) {
+        const int s = i / G, g = i % G;
+        const float ms = CB.ms[s][g];
+        CB.fac[s][g] = (ms == -INFINITY) ? 0.f : __expf(ms - CB.Mg[g]);
+    }
+    __syncthreads();
+    if (tid < G) {
+        float L = 0.f;
+#pragma unroll 8
+        for (int s = 0; s < ns; ++s) L += CB.ls[s][tid] * CB.fac[s][tid];
+        CB.Lg[tid] = L;
+    }
+    __syncthreads();
+    for (int i = tid; i < ns * G; i += kAttnThreads) {
+        const int s = i / G, g = i % G;
+        CB.fac[s][g] = CB.fac[s][g] / CB.Lg[g];
+    }
+    __syncthreads();
+}
+
+// o[g][d] = sum over splits, in split order, of part[s][g][d] * fac[s][g],
+// written to out_row[g * D + d].  Each pass stages the raw partials of as
+// many splits as fit in LDS; the loads are branch-free (a buffer resource over
+// the unit's partials returns zeros past its end), so all of a thread's loads
+// of a pass are in flight at once.  Lanes past the live elements compute on
+// padding and store nothing.
+template <int D>
+__device__ inline void combine_output(const float *pp, int ns, int G, CombLds &CB, float *out_row) {
+    const int tid = threadIdx.x;
+    const int GD = G * D, GD2 = GD / 2;
+    const int sb_max = kCombStage / GD;
+    const uint32_t bytes = (uint32_t)(ns * G * (D + 2)) * 4u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(pp, bytes);
+    constexpr int kE = (kMaxGroup * D + kAttnThreads - 1) / kAttnThreads;
+    constexpr int kL = kCombStage / 2 / kAttnThreads;   // float2 loads per thread and pass
+    float o[kE];
+#pragma unroll
+    for (int k = 0; k < kE; ++k) o[k] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += sb_max) {
+        const int sb = min(sb_max, ns - s0);
+        const int n2 = sb * GD2;
+        u32x2_t r[kL];
+#pragma unroll
+        for (int k = 0; k < kL; ++k) {
+            const int i = tid + k * kAttnThreads;   // float2 index within the block
+            const int s = s0 + i / GD2, e2 = 2 * (i % GD2);
+            const uint32_t off = (i < n2) ? (uint32_t)((s * G + e2 / D) * (D + 2) + e2 % D) * 4u : bytes;
+            r[k] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+        }
+#pragma unroll
+        for (int k = 0; k < kL; ++k)
+            reinterpret_cast<u32x2_t *>(CB.stage)[tid + k * kAttnThreads] = r[k];
+        __syncthreads();
+        for (int s = 0; s < sb; ++s) {
+            const float *st = CB.stage + s * GD;
+#pragma unroll
+            for (int k = 0; k < kE; ++k) {
+                const int el = tid + k * kAttnThreads;
+                o[k] += st[el] * CB.fac[s0 + s][el / D];
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < kE; ++k) {
+        const int el = tid + k * kAttnThreads;
+        if (el < GD) out_row[el] = o[k];
+    }
+}
 
 // Combine the splits of one unit: rescale partial sums to the global max,
 // normalise, update scores and the slot count.
@@ -38,7 +133,6 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLds &CB) {
     const int b = u / c.Hkv, h = u % c.Hkv;
     const int tid = threadIdx.x;
     auto &fac = CB.fac;
-    float *Mg = CB.Mg, *Lg = CB.Lg;
 
     const int n = load_count(c, u, false);
     const bool can_store = n < c.cap;
@@ -46,36 +140,10 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLds &CB) {
     const int chunk = split_chunk(T_len, ns);
     const float *pp = a.part + (size_t)u * ns * G * (D + 2);
 
-    // the splits' (m, l), one load per thread, then the global max and sum
-    for (int i = tid; i < ns * G; i += kAttnThreads) {
-        const int s = i / G, g = i % G;
-        CB.ms[s][g] = pp[(s * G + g) * (D + 2) + D];
-        CB.ls[s][g] = pp[(s * G + g) * (D + 2) + D + 1];
-    }
+    combine_load_ml<D>(pp, ns, G, CB);
     __syncthreads();
-    if (tid < G) {
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, CB.ms[s][tid]);
-        float L = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            const float ms = CB.ms[s][tid];
-            L += (ms == -INFINITY) ? 0.f : CB.ls[s][tid] * __expf(ms - M);
-        }
-        Mg[tid] = M;
-        Lg[tid] = L;
-        for (int s = 0; s < ns; ++s) {
-            const float ms = CB.ms[s][tid];
-            fac[s][tid] = (ms == -INFINITY) ? 0.f : __expf(ms - M) / L;
-        }
-    }
-    __syncthreads();
-    for (int e = tid; e < G * D; e += kAttnThreads) {
-        const int g = e / D, d = e % D;
-        float o = 0.f;
-#pragma unroll 8
-        for (int s = 0; s < ns; ++s) o += pp[(s * G + g) * (D + 2) + d] * fac[s][g];
-        a.out[((size_t)b * c.Hq + (size_t)h * G + g) * D + d] = o;
-    }
+    combine_factors(ns, G, CB);
+    combine_output<D>(pp, ns, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
     if (a.scores) {
         const size_t ld = (size_t)c.cap + 1;
         const float *lg = a.logits + (size_t)u * G * ld;
@@ -107,11 +175,103 @@ union FinishLds {
     CompLds comp;
 };
 
+// Random eviction after split kernels that ranked their own chunks: the
+// unit's candidate count and worst candidate from the splits' records
+// (wave 0).  Returns the slot that leaves, -1 when none does, or -2 when
+// more than one does (the full selection runs then).
+__device__ inline int presel_finish(const AttnArgs &a, const SelectArgs &sa, int u) {
+    const int lane = threadIdx.x & 63;
+    const int nrec = a.nsplit * kPreselWaves;
+    const PreselRecord *R = reinterpret_cast<const PreselRecord *>(a.presel) + (size_t)u * nrec;
+    uint32_t cnt = 0;
+    uint64_t best = ~0ull;
+    int arg = -1;
+    for (int i = lane; i < nrec; i += 64) {
+        const PreselRecord r = R[i];
+        cnt += r.ncand;
+        const uint64_t key = ((uint64_t)r.key_hi << 32) | r.key_lo;
+        if (r.slot >= 0 && (arg < 0 || key < best || (key == best && r.slot < arg))) {
+            best = key;
+            arg = r.slot;
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        cnt += __shfl_xor(cnt, o, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
+        const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
+        const int oa = __shfl_xor(arg, o, 64);
+        const uint64_t ok = ((uint64_t)hi << 32) | lo;
+        if (ok < best || (ok == best && (unsigned)oa < (unsigned)arg)) {
+            best = ok;
+            arg = oa;
+        }
+    }
+    // the selection's rule: keep n_keep candidates (none when n_keep <= 0)
+    const int ncand = (int)cnt, want = sa.n_keep;
+    const int extra = (ncand > want) ? (want <= 0 ? ncand : ncand - want) : 0;
+    return extra == 0 ? -1 : (extra == 1 ? arg : -2);
+}
+
+// The rest of a random-eviction step whose split kernels ranked their own
+// chunks, when at most one slot leaves: the same results as combine_unit,
+// then the selection's one-eviction case, then compact_one, with fewer
+// dependent memory round trips (the first loads go out together, and the
+// moved row is copied while the output is combined).  Returns false, having
+// written nothing, when more than one slot leaves.
+template <typename T, int D>
+__device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, int u, CombLds &CB,
+                                     int &sh_e) {
+    const CacheDev &c = a.c;
+    const int G = c.G, ns = a.nsplit;
+    const int b = u / c.Hkv, h = u % c.Hkv;
+    const int tid = threadIdx.x;
+    const float *pp = a.part + (size_t)u * ns * G * (D + 2);
+
+    int n = c.n_slots[u];
+    combine_load_ml<D>(pp, ns, G, CB);
+    if (tid < 64) {
+        const int e = presel_finish(a, sa, u);
+        if (tid == 0) sh_e = e;
+    }
+    n = (n < 0) ? 0 : (n > c.cap ? c.cap : n);
+    __syncthreads();
+    const int e = sh_e;
+    if (e == -2) return false;
+
+    // the slot count after the append (the selection ran over these slots);
+    // one eviction e fills its hole from the last slot, whose row is read
+    // now and written after the output pass
+    const int cnt = (n < c.cap) ? n + 1 : n;
+    const int src = cnt - 1;
+    const bool move = e >= 0 && e < src;
+    constexpr int kParts = (int)(D * sizeof(T) / 16);
+    T *X = (tid < kParts) ? (T *)c.k : (T *)c.v;
+    uint4 row;
+    int32_t psrc = 0;
+    int32_t *P = c.pos + (size_t)u * c.cap;
+    if (move && tid < 2 * kParts)
+        row = reinterpret_cast<const uint4 *>(X + row_of(c, b, h, src) * D)[tid % kParts];
+    if (move && tid == 0) psrc = P[src];
+
+    combine_factors(ns, G, CB);
+    combine_output<D>(pp, ns, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
+    if (move && tid < 2 * kParts)
+        reinterpret_cast<uint4 *>(X + row_of(c, b, h, e) * D)[tid % kParts] = row;
+    if (move && tid == 0) P[e] = psrc;
+    if (tid == 0) c.n_slots[u] = (e >= 0 && e < cnt) ? cnt - 1 : cnt;
+    return true;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kAttnThreads) void finish_kernel(AttnArgs a, SelectArgs sa,
                                                             CompactArgs ca) {
     __shared__ FinishLds F;
+    __shared__ int sh_e;
     const int u = blockIdx.x;
+    if (a.presel && !a.scores && a.nsplit > 1) {
+        if (finish_presel<T, D>(a, sa, u, F.comb, sh_e)) return;
+        __syncthreads();
+    }
     if (a.nsplit > 1) {
         combine_unit<D>(a, u, F.comb);
         __syncthreads();

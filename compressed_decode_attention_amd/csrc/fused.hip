@@ -467,7 +467,7 @@ void fused_kernel(FusedArgs fa) {
             key_s[j] = key;
             ++ncand;
             const uint64_t wd = rank_word(key, p);
-            if (wd < best) {
+            if (barg < 0 || wd < best) {
                 best = wd;
                 barg = j;
             }
@@ -485,7 +485,7 @@ void fused_kernel(FusedArgs fa) {
         const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
         const int oa = __shfl_xor(barg, o, 64);
         const uint64_t ob = ((uint64_t)hi << 32) | lo;
-        if (ob < best) {
+        if (ob < best || (ob == best && (unsigned)oa < (unsigned)barg)) {
             best = ob;
             barg = oa;
         }
@@ -509,7 +509,7 @@ void fused_kernel(FusedArgs fa) {
         ndrop += sm.r_nd[v];
         dslot = max(dslot, sm.r_ds[v]);
         const uint64_t ob = ((uint64_t)sm.mn_hi[v] << 32) | sm.mn_lo[v];
-        if (sm.r_arg[v] >= 0 && ob < best) {
+        if (sm.r_arg[v] >= 0 && (barg < 0 || ob < best)) {
             best = ob;
             barg = sm.r_arg[v];
         }

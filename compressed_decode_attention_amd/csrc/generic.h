@@ -309,7 +309,7 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
             const uint32_t pr = h2o_keys ? prim_s[j] : sel_primary(v, j, p);
             if (in_lds) prim_s[j] = pr;
             const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
-            if (key < best) {
+            if (barg < 0 || key < best) {
                 best = key;
                 barg = j;
             }

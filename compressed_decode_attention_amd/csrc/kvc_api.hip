@@ -117,6 +117,7 @@ struct Workspace {
     size_t logit_off, logit_bytes;
     size_t keep_off, keep_bytes;
     size_t nout_off, nout_bytes;
+    size_t presel_off, presel_bytes;
     size_t total;
     int nsplit;
     int max_len;   // attended length bound of every unit
@@ -132,6 +133,8 @@ Workspace layout(const kvc_cache *c, int hint) {
     w.logit_bytes = units * G * ((size_t)c->capacity + 1) * sizeof(float);
     w.keep_bytes = units * (size_t)c->capacity * sizeof(int32_t);
     w.nout_bytes = units * sizeof(int32_t);
+    w.presel_bytes =
+        w.nsplit > 1 ? units * w.nsplit * kvc::kPreselWaves * sizeof(kvc::PreselRecord) : 0;
     size_t off = 0;
     w.part_off = off;
     off += align_up(w.part_bytes);
@@ -141,6 +144,8 @@ Workspace layout(const kvc_cache *c, int hint) {
     off += align_up(w.keep_bytes);
     w.nout_off = off;
     off += align_up(w.nout_bytes);
+    w.presel_off = off;
+    off += align_up(w.presel_bytes);
     w.total = off;
     return w;
 }
@@ -470,6 +475,14 @@ KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *poli
     ca.scores = scores;
     ca.ordered = false;
     ca.dst = ca.c;
+    if (policy->kind == KVC_POLICY_RANDOM && a.nsplit > 1 &&
+        kvc::mfma_tiles_ok(c->dtype, c->head_dim, c->block_size)) {
+        // the matrix-core split kernels rank their own chunks' candidates
+        a.presel = (uint32_t *)((char *)workspace + w.presel_off);
+        a.presel_prompt_len = policy->prompt_len;
+        a.presel_step = step;
+        a.presel_seed = policy->seed;
+    }
     return hip_status(kvc::launch_step_split(a, sa, ca, c->dtype, st), what);
 }
 

@@ -49,6 +49,16 @@ __device__ inline void raise_flag(const CacheDev &c, int32_t bit) {
 // Row index (in units of head_dim elements) of slot j of unit (b, h).
 // Paged caches look the block up in the block table; an id outside the pool
 // is reported and redirected to block 0 so that no access leaves the pool.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// A buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros (no fault), so a load needs no branch to stay in bounds.
+constexpr int kRsrcWord3 = 0x00020000;   // buffer resource dword 3 on gfx9-family parts
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
 __device__ inline size_t row_of(const CacheDev &c, int b, int h, int j) {
     if (c.bs == 0) return ((size_t)(b * c.Hkv + h)) * (size_t)c.cap + (size_t)j;
     int blk = c.bt[(size_t)b * c.max_blocks + j / c.bs];
@@ -158,15 +168,16 @@ __device__ inline int block_max_i(int x, int *red) {
     return r;
 }
 
-// Block-wide minimum of 64-bit keys with the argument that holds it (the
-// keys are unique, so the argument is too); red needs 3 words per wave.
+// Block-wide minimum of 64-bit keys with the argument that holds it (equal
+// keys: the lower argument, compared unsigned so that -1, "none", loses);
+// red needs 3 words per wave.
 __device__ inline void block_min_u64(uint64_t &key, int &arg, uint32_t *red) {
     for (int o = 32; o > 0; o >>= 1) {
         const uint32_t hi = __shfl_xor((uint32_t)(key >> 32), o, kWave);
         const uint32_t lo = __shfl_xor((uint32_t)key, o, kWave);
         const int oa = __shfl_xor(arg, o, kWave);
         const uint64_t ok = ((uint64_t)hi << 32) | lo;
-        if (ok < key) {
+        if (ok < key || (ok == key && (unsigned)oa < (unsigned)arg)) {
             key = ok;
             arg = oa;
         }
@@ -181,7 +192,7 @@ __device__ inline void block_min_u64(uint64_t &key, int &arg, uint32_t *red) {
     __syncthreads();
     for (int i = 0; i < nw; ++i) {
         const uint64_t ok = ((uint64_t)red[3 * i] << 32) | red[3 * i + 1];
-        if (ok < key) {
+        if (ok < key || (ok == key && red[3 * i + 2] < (uint32_t)arg)) {
             key = ok;
             arg = (int)red[3 * i + 2];
         }
@@ -258,7 +269,25 @@ struct AttnArgs {
     bool append;          // store the new token at slot n (false: attend it only)
     float *part;          // [units][nsplit][G][D+2] when nsplit > 1
     float *logits;        // [units][G][cap+1] scratch (scores and/or nsplit > 1)
+    // Whole steps under random eviction over long units: each split also
+    // ranks its own chunk's candidates (slots past the pinned prompt) and
+    // writes one PreselRecord per wave, so that the step's finish pass needs no
+    // second look at positions when at most one slot leaves.  Null otherwise.
+    uint32_t *presel = nullptr;   // [units][nsplit][kPreselWaves] PreselRecord
+    int32_t presel_prompt_len = 0;
+    uint32_t presel_step = 0;
+    uint64_t presel_seed = 0;
 };
+
+// One wave's share of a split's random-eviction ranking: the number of
+// candidate slots among those it ranked and the smallest composite key among them (the key the
+// selection ranks by: inverted Philox word, then inverted position) with its
+// slot; an empty share has ncand 0, key ~0 and slot -1.
+struct PreselRecord {
+    uint32_t ncand, key_hi, key_lo;
+    int32_t slot;
+};
+constexpr int kPreselWaves = 4;   // records per split: one per wave of the split kernel
 
 hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s);
 

@@ -11,7 +11,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kFThreads = 256;
@@ -93,11 +92,6 @@ __device__ inline void load_q(u16x8_t (&qa)[4], const uint16_t *qp, bool valid, 
 // immediate.  Contiguous caches take one resource per workgroup; paged caches
 // one per 16-slot tile (block sizes are powers of two of at least 16, so a
 // tile never straddles a block).
-constexpr int kRsrcWord3 = 0x00020000;   // buffer resource dword 3 on gfx9-family parts
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
-}
 // K and V rows are read once per step.  From a contiguous cache,
 // non-temporal loads (the "nt" cache policy bit) keep them from displacing
 // what the caches hold for others: about 10% faster for the whole step than

@@ -42,6 +42,99 @@ size_t split_smem_bytes(int G, int tc) {
     return fast > sizeof(AttnLds<kHD>) ? fast : sizeof(AttnLds<kHD>);
 }
 
+// The random-eviction share of split s of unit u over the slots [j0, jsel)
+// it holds after this step (the new token's slot n included when it was
+// stored): candidates are the slots whose position is past the pinned
+// prompt, ranked by the same composite key as the selection (blog, "scorers
+// are overrated": per-head uniform draws; the key is the inverted Philox word
+// of (position, step, kv head, sequence), then the inverted position).
+// Positions are loaded early (presel_load, KPS per thread) so that ranking
+// them at the end of the kernel waits for no memory.
+template <int KPS>
+__device__ inline void presel_load(const AttnArgs &a, int u, int b, int j0, int jsel, int n,
+                                   int32_t (&p)[KPS]) {
+    const int32_t *P = a.c.pos + (size_t)u * a.c.cap;
+    const int32_t np = a.new_pos[b];
+#pragma unroll
+    for (int k = 0; k < KPS; ++k) {
+        const int j = j0 + (int)threadIdx.x + k * kFThreads;
+        p[k] = 0;
+        if (j < jsel) p[k] = (j == n) ? np : P[j];
+    }
+}
+
+static_assert(kPreselWaves == kFWaves, "one random-eviction record per wave of a split");
+
+// A thread's running minimum of the candidates' keys and their count.
+struct PreselAcc {
+    uint32_t cnt = 0;
+    uint64_t best = ~0ull;
+    int arg = -1;
+};
+
+__device__ inline void presel_add(const AttnArgs &a, int b, int h, int j, int32_t p,
+                                  PreselAcc &acc) {
+    if (p < a.presel_prompt_len) return;
+    ++acc.cnt;
+    const uint32_t pr = ~philox_word0((uint32_t)p, a.presel_step, (uint32_t)h, (uint32_t)b,
+                                      (uint32_t)(a.presel_seed & 0xFFFFFFFFu),
+                                      (uint32_t)(a.presel_seed >> 32));
+    const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+    if (acc.arg < 0 || key < acc.best) {
+        acc.best = key;
+        acc.arg = j;
+    }
+}
+
+// Wave reduction of the threads' shares (equal keys: the lower slot); each
+// wave writes its own record, so the split needs no barrier (one waiting for
+// its output stores) to publish them.
+__device__ inline void presel_write(const AttnArgs &a, int u, int s, PreselAcc acc) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int o = 32; o > 0; o >>= 1) {
+        acc.cnt += __shfl_xor(acc.cnt, o, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)(acc.best >> 32), o, 64);
+        const uint32_t lo = __shfl_xor((uint32_t)acc.best, o, 64);
+        const int oa = __shfl_xor(acc.arg, o, 64);
+        const uint64_t ok = ((uint64_t)hi << 32) | lo;
+        if (ok < acc.best || (ok == acc.best && (unsigned)oa < (unsigned)acc.arg)) {
+            acc.best = ok;
+            acc.arg = oa;
+        }
+    }
+    if (lane == 0) {
+        PreselRecord rec;
+        rec.ncand = acc.cnt;
+        rec.key_hi = (uint32_t)(acc.best >> 32);
+        rec.key_lo = (uint32_t)acc.best;
+        rec.slot = acc.arg;
+        reinterpret_cast<PreselRecord *>(a.presel)[((size_t)u * a.nsplit + s) * kPreselWaves + w] =
+            rec;
+    }
+}
+
+template <int KPS>
+__device__ inline void presel_rank(const AttnArgs &a, int u, int s, int b, int h, int j0, int jsel,
+                                   const int32_t (&p)[KPS]) {
+    PreselAcc acc;
+#pragma unroll
+    for (int k = 0; k < KPS; ++k) {
+        const int j = j0 + (int)threadIdx.x + k * kFThreads;
+        if (j < jsel) presel_add(a, b, h, j, p[k], acc);
+    }
+    presel_write(a, u, s, acc);
+}
+
+// Both steps over a chunk of any length (the generic routine's chunks).
+__device__ inline void presel_chunk(const AttnArgs &a, int u, int s, int b, int h, int j0,
+                                    int jsel, int n) {
+    const int32_t *P = a.c.pos + (size_t)u * a.c.cap;
+    PreselAcc acc;
+    for (int j = j0 + (int)threadIdx.x; j < jsel; j += kFThreads)
+        presel_add(a, b, h, j, (j == n) ? a.new_pos[b] : P[j], acc);
+    presel_write(a, u, s, acc);
+}
+
 template <bool PAGED, int TC, bool PACK2, bool F8>
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
 void split_kernel(AttnArgs a) {
@@ -70,6 +163,10 @@ void split_kernel(AttnArgs a) {
     if (chunk > TC) {   // longer than the launch promised: the generic routine
         using TK = typename std::conditional<F8, e5m2_t, uint16_t>::type;
         attn_unit_generic<TK, kHD>(a, u, s, *reinterpret_cast<AttnLds<kHD> *>(smem));
+        if (a.presel) {
+            const int j0 = min(s * chunk, T), j1 = min(T, j0 + chunk);
+            presel_chunk(a, u, s, b, h, j0, (a.append && n < c.cap) ? j1 : min(j1, n), n);
+        }
         return;
     }
     const bool can_store = a.append && n < c.cap;
@@ -179,6 +276,11 @@ void split_kernel(AttnArgs a) {
     for (int d = 0; d < DV; ++d)
 #pragma unroll
         for (int k = 0; k < 4; ++k) vb[d][k] = vload(w + kFWaves * d, k);
+    // random eviction: the chunk's positions, ranked after P.V
+    constexpr int kPS = (TC + kFThreads - 1) / kFThreads;
+    const int jsel = can_store ? j1 : jend;
+    int32_t psel[kPS];
+    if (a.presel) presel_load<kPS>(a, u, b, j0, jsel, n, psel);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float m = mx[i];
@@ -317,6 +419,9 @@ void split_kernel(AttnArgs a) {
         }
         if (tid == 0) c.pos[(size_t)u * c.cap + n] = a.new_pos[b];
     }
+
+    // ---------------- random eviction: rank this chunk's candidates
+    if (a.presel) presel_rank<kPS>(a, u, s, b, h, j0, jsel, psel);
 }
 
 template <bool PAGED, int TC, bool F8>
