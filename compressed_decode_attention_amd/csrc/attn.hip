@@ -23,19 +23,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
     attn_unit_generic<T, D>(a, blockIdx.x / a.nsplit, blockIdx.x % a.nsplit, L);
 }
 
-// Partials staged per pass of the output combine: 48 float per thread.
+// Partials staged per pass of the output combine: 48 float per thread where
+// the kernel's LDS holds a larger union anyway (the finish pass), 16 in the
+// attention-only combine kernel (which then keeps four workgroups per CU).
 constexpr int kCombStage = 48 * kAttnThreads;
+constexpr int kCombStageSmall = 16 * kAttnThreads;
 
-struct CombLds {
+template <int STAGE>
+struct CombLdsT {
     float fac[kMaxSplit][kMaxGroup];   // exp(m_s - M), then exp(m_s - M) / L
     float ms[kMaxSplit][kMaxGroup], ls[kMaxSplit][kMaxGroup];   // the splits' m, l
     float Mg[kMaxGroup], Lg[kMaxGroup];
-    float stage[kCombStage + kMaxGroup * 128];   // raw partials of a block of splits (+ pad)
+    float stage[STAGE + kMaxGroup * 128];   // raw partials of a block of splits (+ pad)
 };
+using CombLds = CombLdsT<kCombStage>;
 
 // The splits' (m, l) of one unit into LDS (the caller syncs).
-template <int D>
-__device__ inline void combine_load_ml(const float *pp, int ns, int G, CombLds &CB) {
+template <int D, typename CL>
+__device__ inline void combine_load_ml(const float *pp, int ns, int G, CL &CB) {
     for (int i = threadIdx.x; i < ns * G; i += kAttnThreads) {
         const int s = i / G, g = i % G;
         CB.ms[s][g] = pp[(s * G + g) * (D + 2) + D];
@@ -45,7 +50,8 @@ __device__ inline void combine_load_ml(const float *pp, int ns, int G, CombLds &
 
 // Global max M and normaliser L per head, then the factor of each split,
 // exp(m_s - M) / L (0 for an empty split); L sums the splits in order.
-__device__ inline void combine_factors(int ns, int G, CombLds &CB) {
+template <typename CL>
+__device__ inline void combine_factors(int ns, int G, CL &CB) {
     const int tid = threadIdx.x;
     if (tid < G) {
         float M = -INFINITY;
@@ -80,15 +86,16 @@ __device__ inline void combine_factors(int ns, int G, CombLds &CB) {
 // the unit's partials returns zeros past its end), so all of a thread's loads
 // of a pass are in flight at once.  Lanes past the live elements compute on
 // padding and store nothing.
-template <int D>
-__device__ inline void combine_output(const float *pp, int ns, int G, CombLds &CB, float *out_row) {
+template <int D, int STAGE>
+__device__ inline void combine_output(const float *pp, int ns, int G, CombLdsT<STAGE> &CB,
+                                      float *out_row) {
     const int tid = threadIdx.x;
     const int GD = G * D, GD2 = GD / 2;
-    const int sb_max = kCombStage / GD;
+    const int sb_max = STAGE / GD;
     const uint32_t bytes = (uint32_t)(ns * G * (D + 2)) * 4u;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(pp, bytes);
     constexpr int kE = (kMaxGroup * D + kAttnThreads - 1) / kAttnThreads;
-    constexpr int kL = kCombStage / 2 / kAttnThreads;   // float2 loads per thread and pass
+    constexpr int kL = STAGE / 2 / kAttnThreads;   // float2 loads per thread and pass
     float o[kE];
 #pragma unroll
     for (int k = 0; k < kE; ++k) o[k] = 0.f;
@@ -126,8 +133,8 @@ __device__ inline void combine_output(const float *pp, int ns, int G, CombLds &C
 
 // Combine the splits of one unit: rescale partial sums to the global max,
 // normalise, update scores and the slot count.
-template <int D>
-__device__ inline void combine_unit(const AttnArgs &a, int u, CombLds &CB) {
+template <int D, int STAGE>
+__device__ inline void combine_unit(const AttnArgs &a, int u, CombLdsT<STAGE> &CB) {
     const CacheDev &c = a.c;
     const int G = c.G, ns = a.nsplit;
     const int b = u / c.Hkv, h = u % c.Hkv;
@@ -145,16 +152,45 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLds &CB) {
     combine_factors(ns, G, CB);
     combine_output<D>(pp, ns, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
     if (a.scores) {
+        // p summed over the group for every attended slot (heads in order),
+        // kJ slots per thread at a time; every logit load of a batch goes out
+        // before the sums (a buffer resource over the unit's logits returns
+        // zeros for heads past G, which the sums skip)
         const size_t ld = (size_t)c.cap + 1;
         const float *lg = a.logits + (size_t)u * G * ld;
+        const uint32_t lbytes = (uint32_t)((size_t)G * ld * 4);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(lg, lbytes);
         float *sc = a.scores + (size_t)u * c.cap;
-#pragma unroll 2
-        for (int j = tid; j < T_len; j += kAttnThreads) {
-            const int s = j / chunk;
-            float ps = 0.f;
-            for (int g = 0; g < G; ++g) ps += lg[g * ld + j] * fac[s][g];
-            if (j < n) sc[j] = score_update(sc[j], ps, a.decay);
-            else if (can_store) sc[n] = score_update(0.f, ps, a.decay);
+        constexpr int kJ = (STAGE == kCombStage) ? 4 : 2;
+        for (int j0 = tid; j0 < T_len; j0 += kJ * kAttnThreads) {
+            int jj[kJ], sj[kJ];
+            float ps[kJ], old[kJ], lv[kMaxGroup][kJ];
+#pragma unroll
+            for (int q = 0; q < kJ; ++q) {
+                const int j = j0 + q * kAttnThreads;
+                jj[q] = j < T_len ? j : T_len - 1;
+                sj[q] = jj[q] / chunk;
+                ps[q] = 0.f;
+                old[q] = jj[q] < n ? sc[jj[q]] : 0.f;
+            }
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+#pragma unroll
+                for (int q = 0; q < kJ; ++q) {
+                    const uint32_t off = g < G ? (uint32_t)((g * ld + jj[q]) * 4) : lbytes;
+                    lv[g][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+                }
+#pragma unroll
+            for (int g = 0; g < kMaxGroup; ++g)
+                if (g < G)
+#pragma unroll
+                    for (int q = 0; q < kJ; ++q) ps[q] += lv[g][q] * fac[sj[q]][g];
+#pragma unroll
+            for (int q = 0; q < kJ; ++q) {
+                const int j = j0 + q * kAttnThreads;
+                if (j < n) sc[j] = score_update(old[q], ps[q], a.decay);
+                else if (j == n && can_store) sc[n] = score_update(0.f, ps[q], a.decay);
+            }
         }
     }
     if (tid == 0 && can_store) c.n_slots[u] = n + 1;
@@ -162,16 +198,21 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLds &CB) {
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(AttnArgs a) {
-    __shared__ CombLds CB;
+    __shared__ CombLdsT<kCombStageSmall> CB;
     combine_unit<D>(a, blockIdx.x, CB);
 }
 
 // The rest of a decode step after the split kernels, one workgroup per unit:
 // combine (output, scores, the appended slot), then selection, then
-// compaction, each phase reading what the previous one wrote.
-union FinishLds {
-    CombLds comb;
-    SelLds<kSelLdsSlots> sel;
+// compaction, each phase reading what the previous one wrote.  Two LDS
+// sizes: units of up to kSelLdsSmall attended slots (over-budget first steps
+// of prompts of a few thousand tokens) keep four workgroups per CU; longer
+// ones keep up to kSelLdsSlots selection keys in LDS, two per CU.
+constexpr int kSelLdsSmall = 3072;
+template <int SEL, int STAGE>
+union FinishLdsT {
+    CombLdsT<STAGE> comb;
+    SelLds<SEL> sel;
     CompLds comp;
 };
 
@@ -218,8 +259,8 @@ __device__ inline int presel_finish(const AttnArgs &a, const SelectArgs &sa, int
 // dependent memory round trips (the first loads go out together, and the
 // moved row is copied while the output is combined).  Returns false, having
 // written nothing, when more than one slot leaves.
-template <typename T, int D>
-__device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, int u, CombLds &CB,
+template <typename T, int D, typename CL>
+__device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, int u, CL &CB,
                                      int &sh_e) {
     const CacheDev &c = a.c;
     const int G = c.G, ns = a.nsplit;
@@ -262,10 +303,12 @@ __device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, in
     return true;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kAttnThreads) void finish_kernel(AttnArgs a, SelectArgs sa,
-                                                            CompactArgs ca) {
-    __shared__ FinishLds F;
+template <typename T, int D, bool SMALL>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(SMALL ? 4 : 1)))
+void finish_kernel(AttnArgs a, SelectArgs sa, CompactArgs ca) {
+    constexpr int SEL = SMALL ? kSelLdsSmall : kSelLdsSlots;
+    constexpr int STAGE = SMALL ? kCombStageSmall : kCombStage;
+    __shared__ FinishLdsT<SEL, STAGE> F;
     __shared__ int sh_e;
     const int u = blockIdx.x;
     if (a.presel && !a.scores && a.nsplit > 1) {
@@ -276,10 +319,10 @@ __global__ __launch_bounds__(kAttnThreads) void finish_kernel(AttnArgs a, Select
         combine_unit<D>(a, u, F.comb);
         __syncthreads();
     }
-    const int e = select_unit<kSelLdsSlots>(sa, u, F.sel);
+    const int e = select_unit<SEL>(sa, u, F.sel);
     __syncthreads();
     if (e >= -1) compact_one<T, D>(ca, u, e);
-    else compact_unit<T, D>(ca, u, F.comp);
+    else compact_unit<T, D, !SMALL>(ca, u, F.comp);   // (the small instance's registers are capped)
 }
 
 template <typename T, int D>
@@ -321,8 +364,12 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
 template <typename T, int D>
 static void launch_finish_typed(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,
                                 hipStream_t s) {
-    hipLaunchKernelGGL((finish_kernel<T, D>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0, s, a,
-                       sa, ca);
+    if (a.max_len <= kSelLdsSmall)
+        hipLaunchKernelGGL((finish_kernel<T, D, true>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0,
+                           s, a, sa, ca);
+    else
+        hipLaunchKernelGGL((finish_kernel<T, D, false>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0,
+                           s, a, sa, ca);
 }
 
 hipError_t launch_step_split(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,

@@ -83,7 +83,7 @@ __device__ void fused_generic(const FusedArgs &fa, int u, unsigned char *smem) {
     __syncthreads();
     select_unit<1>(fa.sel, u, *reinterpret_cast<SelLds<1> *>(smem));
     __syncthreads();
-    compact_unit<TK, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
+    compact_unit<TK, kHD, false>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
 }
 
 // PACK2: G <= 8, so one P.V MFMA carries both bf16 parts of p (rows 0..7 and
@@ -553,22 +553,10 @@ void fused_kernel(FusedArgs fa) {
                 for (int j = tid; j < T; j += kFThreads)
                     if (flg_s[j] == kCand) {
                         const uint64_t wd = rank_word(key_s[j], pos_s[j]);
-                        if ((wd & mask) == prefix) atomicAdd(&sm.hist[(wd >> shift) & 255], 1);
+                        if ((wd & mask) == prefix) hist_add_wave(sm.hist, (int)((wd >> shift) & 255));
                     }
                 __syncthreads();
-                if (tid == 0) {
-                    int cum = 0, dsel = 0;
-                    for (int d = 255; d >= 0; --d) {
-                        if (cum + sm.hist[d] >= krem) {
-                            dsel = d;
-                            break;
-                        }
-                        cum += sm.hist[d];
-                    }
-                    sm.sh[0] = dsel;
-                    sm.sh[1] = krem - cum;
-                    sm.sh[2] = (sm.hist[dsel] == krem - cum);
-                }
+                if (tid < 64) radix_pick_bin(sm.hist, krem, sm.sh[0], sm.sh[1], sm.sh[2]);
                 __syncthreads();
                 krem = sm.sh[1];
                 prefix |= (uint64_t)sm.sh[0] << shift;

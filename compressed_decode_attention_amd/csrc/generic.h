@@ -362,23 +362,10 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
                 if (k != kCand) continue;
                 const uint32_t pr = in_lds ? prim_s[j] : sel_primary(v, j, p);
                 const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
-                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+                if ((key & mask) == prefix) hist_add_wave(hist, (int)((key >> shift) & 255));
             }
             __syncthreads();
-            if (tid == 0) {
-                // digit holding the krem-th largest matching key
-                int cum = 0, dsel = 0;
-                for (int d = 255; d >= 0; --d) {
-                    if (cum + hist[d] >= krem) {
-                        dsel = d;
-                        break;
-                    }
-                    cum += hist[d];
-                }
-                sh_digit = dsel;
-                sh_krem = krem - cum;
-                sh_done = (hist[dsel] == krem - cum);
-            }
+            if (tid < 64) radix_pick_bin(hist, krem, sh_digit, sh_krem, sh_done);
             __syncthreads();
             krem = sh_krem;
             prefix |= (uint64_t)sh_digit << shift;
@@ -389,37 +376,35 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
         }
     }
 
-    // keep flags -> ascending slot list
+    // keep flags -> ascending slot list: each thread owns a run of
+    // consecutive slots, so one scan orders the whole list
     int32_t *ks = a.keep_slots + (size_t)u * c.cap;
-    int base = 0;
-    for (int j0 = 0; j0 < n; j0 += kSelThreads) {
-        const int j = j0 + tid;
-        int keep = 0;
-        if (j < n) {
-            int32_t p;
-            uint8_t k;
-            if (in_lds) {
-                k = cls_s[j];
-                p = pos_s[j];
-            } else {
-                p = v.P[j];
-                k = sel_class(v, j, p);
-            }
-            if (k == kKeep) keep = 1;
-            else if (k == kCand) {
-                if (!rank) keep = 1;
-                else if (!keep_none) {
-                    const uint32_t pr = in_lds ? prim_s[j] : sel_primary(v, j, p);
-                    const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
-                    keep = (key & mask) >= prefix;
-                }
-            }
+    const int per = (n + kSelThreads - 1) / kSelThreads;
+    const int r0 = min(n, tid * per), r1 = min(n, r0 + per);
+    auto kept = [&](int j) -> bool {
+        int32_t p;
+        uint8_t k;
+        if (in_lds) {
+            k = cls_s[j];
+            p = pos_s[j];
+        } else {
+            p = v.P[j];
+            k = sel_class(v, j, p);
         }
-        int t;
-        const int off = block_excl_scan(keep, red, &t);
-        if (keep) ks[base + off] = j;
-        base += t;
-    }
+        if (k == kKeep) return true;
+        if (k != kCand) return false;
+        if (!rank) return true;
+        if (keep_none) return false;
+        const uint32_t pr = in_lds ? prim_s[j] : sel_primary(v, j, p);
+        const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+        return (key & mask) >= prefix;
+    };
+    int mine = 0;
+    for (int j = r0; j < r1; ++j) mine += kept(j) ? 1 : 0;
+    int base;
+    int off = block_excl_scan(mine, red, &base);
+    for (int j = r0; j < r1; ++j)
+        if (kept(j)) ks[off++] = j;
     if (tid == 0) a.n_out[u] = base;
     return -2;
 }
@@ -471,7 +456,44 @@ __device__ inline void compact_one(const CompactArgs &a, int u, int e) {
     if (tid == 0) c.n_slots[u] = src;
 }
 
-template <typename T, int D>
+// Move one kept row from slot src to hole j (K, V, position, score).  With
+// BOTH, every load of the move goes out before its stores (rows of at most
+// 256 bytes: 2 x 16 sixteen-byte parts in registers); otherwise K then V.
+template <typename T, int D, bool BOTH>
+__device__ inline void move_row(const CacheDev &c, int b, int h, int j, int src, int32_t *P,
+                                float *S) {
+    constexpr int kParts = (int)(D * sizeof(T) / 16);
+    T *K = (T *)c.k;
+    T *V = (T *)c.v;
+    if constexpr (BOTH && kParts <= 16) {
+        uint4 kr[kParts], vr[kParts];
+        const uint4 *ksrc = reinterpret_cast<const uint4 *>(K + row_of(c, b, h, src) * D);
+        const uint4 *vsrc = reinterpret_cast<const uint4 *>(V + row_of(c, b, h, src) * D);
+#pragma unroll
+        for (int i = 0; i < kParts; ++i) {
+            kr[i] = ksrc[i];
+            vr[i] = vsrc[i];
+        }
+        const int32_t p = P[src];
+        const float sv = S ? S[src] : 0.f;
+        uint4 *kdst = reinterpret_cast<uint4 *>(K + row_of(c, b, h, j) * D);
+        uint4 *vdst = reinterpret_cast<uint4 *>(V + row_of(c, b, h, j) * D);
+#pragma unroll
+        for (int i = 0; i < kParts; ++i) {
+            kdst[i] = kr[i];
+            vdst[i] = vr[i];
+        }
+        P[j] = p;
+        if (S) S[j] = sv;
+    } else {
+        copy_row<T, D>(K + row_of(c, b, h, j) * D, K + row_of(c, b, h, src) * D);
+        copy_row<T, D>(V + row_of(c, b, h, j) * D, V + row_of(c, b, h, src) * D);
+        P[j] = P[src];
+        if (S) S[j] = S[src];
+    }
+}
+
+template <typename T, int D, bool BOTH = true>
 __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
     const CacheDev &c = a.c;
     const int b = u / c.Hkv, h = u % c.Hkv;
@@ -503,8 +525,6 @@ __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
     below = cnt;   // sources are ks[below .. m)
     __syncthreads();
 
-    T *K = (T *)c.k;
-    T *V = (T *)c.v;
     int32_t *P = c.pos + (size_t)u * c.cap;
     float *S = a.scores ? a.scores + (size_t)u * c.cap : nullptr;
     int base = 0;
@@ -516,12 +536,7 @@ __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
         const int idx = below + base + r;
         if (hole && idx < m) {
             const int src = ks[idx];
-            if (src >= m && src < n) {
-                copy_row<T, D>(K + row_of(c, b, h, j) * D, K + row_of(c, b, h, src) * D);
-                copy_row<T, D>(V + row_of(c, b, h, j) * D, V + row_of(c, b, h, src) * D);
-                P[j] = P[src];
-                if (S) S[j] = S[src];
-            }
+            if (src >= m && src < n) move_row<T, D, BOTH>(c, b, h, j, src, P, S);
         }
         base += t;
     }

@@ -200,6 +200,71 @@ __device__ inline void block_min_u64(uint64_t &key, int &arg, uint32_t *red) {
     __syncthreads();
 }
 
+// One pass of an MSB-first radix select, run by the 64 lanes of one wave:
+// among 256 digit bins (hist[d] = matching keys whose current digit is d),
+// the bin holding the krem-th largest key is the d with (matches in bins
+// above d) < krem <= (that + hist[d]).  Writes that digit, the rank left
+// inside the bin (krem minus the matches above it) and whether the bin is
+// kept whole.  Lane l reads bins 4l..4l+3 and a suffix scan over the lanes
+// gives each lane the count above its bins.
+__device__ inline void radix_pick_bin(const int *hist, int krem, int &digit, int &krem_out,
+                                      int &done) {
+    const int l = threadIdx.x & 63;
+    const int h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
+    const int mine = h0 + h1 + h2 + h3;
+    int suf = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o, kWave);
+        if (l + o < 64) suf += y;
+    }
+    int cum = suf - mine, dsel = -1, dcum = 0;
+    const int hb[4] = {h3, h2, h1, h0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (dsel < 0 && cum < krem && cum + hb[i] >= krem) {
+            dsel = 4 * l + 3 - i;
+            dcum = cum;
+        }
+        cum += hb[i];
+    }
+    if (__ballot(dsel >= 0) == 0) {
+        // fewer matches than krem (not reached for valid counts): what a
+        // scan from the top that never stops leaves, bin 0 and the count of
+        // every bin (lane 0's suffix is the total)
+        if (l == 0) {
+            digit = 0;
+            krem_out = krem - suf;
+            done = (h0 == krem - suf);
+        }
+    } else if (dsel >= 0) {
+        digit = dsel;
+        krem_out = krem - dcum;
+        done = (hist[dsel] == krem - dcum);
+    }
+}
+
+// hist[digit] += 1 for every calling lane, lanes of a wave that share a
+// digit adding together: up to four rounds take the first lane's digit and
+// its whole group (the few crowded bins of a radix pass's early digits),
+// then each remaining lane adds alone.  Integer counts: the totals are those
+// of one atomic add per lane.
+__device__ inline void hist_add_wave(int *hist, int digit) {
+    const int lane = threadIdx.x & 63;
+    bool active = true;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const unsigned long long act = __ballot(active);
+        if (act == 0) return;
+        const int leader = __ffsll(act) - 1;
+        const int d0 = __shfl(digit, leader, kWave);
+        const bool mine = active && digit == d0;
+        const unsigned long long same = __ballot(mine);
+        if (lane == leader) atomicAdd(&hist[d0], (int)__popcll(same));
+        if (mine) active = false;
+    }
+    if (active) atomicAdd(&hist[digit], 1);
+}
+
 // Block-wide exclusive prefix sum of small ints; returns the exclusive prefix
 // of the calling thread and writes the block total to *total.
 __device__ inline int block_excl_scan(int x, int *red, int *total) {
