@@ -322,7 +322,7 @@ void finish_kernel(AttnArgs a, SelectArgs sa, CompactArgs ca) {
     const int e = select_unit<SEL>(sa, u, F.sel);
     __syncthreads();
     if (e >= -1) compact_one<T, D>(ca, u, e);
-    else compact_unit<T, D, !SMALL>(ca, u, F.comp);   // (the small instance's registers are capped)
+    else compact_unit<T, D>(ca, u, F.comp);
 }
 
 template <typename T, int D>

@@ -83,7 +83,7 @@ __device__ void fused_generic(const FusedArgs &fa, int u, unsigned char *smem) {
     __syncthreads();
     select_unit<1>(fa.sel, u, *reinterpret_cast<SelLds<1> *>(smem));
     __syncthreads();
-    compact_unit<TK, kHD, false>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
+    compact_unit<TK, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
 }
 
 // PACK2: G <= 8, so one P.V MFMA carries both bf16 parts of p (rows 0..7 and

@@ -297,17 +297,34 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
     }
     v.L = block_max_i(mx, red) + 1;   // (its barriers publish the LDS copies)
 
+    // Units longer than the LDS copy are read from global memory kU slots per
+    // thread at a time (slots j0 + q * kSelThreads, the same order as one at
+    // a time), every load of a group issued before any is used; scores are
+    // fetched for every policy (positions stand in when there are none).  A
+    // caller with no LDS copy (a fallback inside another kernel) takes one
+    // slot at a time and keeps its registers for its own work.
+    constexpr int kU = kSelLds > 1 ? 8 : 1;
+    const float *Sg = v.S ? v.S : reinterpret_cast<const float *>(v.P);
+    auto fetch = [&](int j0, int32_t (&pg)[kU], uint32_t (&sg)[kU]) {
+#pragma unroll
+        for (int q = 0; q < kU; ++q) {
+            const int j = min(j0 + q * kSelThreads, n - 1);
+            pg[q] = v.P[j];
+            sg[q] = __float_as_uint(Sg[j]);
+        }
+    };
+    // a candidate's primary key from its fetched position and score bits
+    auto primary = [&](int j, int32_t p, uint32_t sbits) -> uint32_t {
+        return a.kind == KVC_POLICY_H2O ? float_order_bits(__uint_as_float(sbits))
+                                        : sel_primary(v, j, p);
+    };
+
     // classify, count candidates and drops, cache keys; the smallest
     // candidate key and the last dropped slot serve the one-eviction case
     int ncand = 0, ndrop = 0, dslot = -1, barg = -1;
     uint64_t best = ~0ull;
-    for (int j = tid; j < n; j += kSelThreads) {
-        const int32_t p = in_lds ? pos_s[j] : v.P[j];
-        const uint8_t k = sel_class(v, j, p);
-        if (in_lds) cls_s[j] = k;
+    auto classify = [&](int j, int32_t p, uint8_t k, uint32_t pr) {
         if (k == kCand) {
-            const uint32_t pr = h2o_keys ? prim_s[j] : sel_primary(v, j, p);
-            if (in_lds) prim_s[j] = pr;
             const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
             if (barg < 0 || key < best) {
                 best = key;
@@ -317,6 +334,32 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
         } else if (k == kDrop) {
             ++ndrop;
             dslot = j;
+        }
+    };
+    if (in_lds) {
+        for (int j = tid; j < n; j += kSelThreads) {
+            const int32_t p = pos_s[j];
+            const uint8_t k = sel_class(v, j, p);
+            cls_s[j] = k;
+            uint32_t pr = 0;
+            if (k == kCand) {
+                pr = h2o_keys ? prim_s[j] : sel_primary(v, j, p);
+                prim_s[j] = pr;
+            }
+            classify(j, p, k, pr);
+        }
+    } else {
+        for (int j0 = tid; j0 < n; j0 += kU * kSelThreads) {
+            int32_t pg[kU];
+            uint32_t sg[kU];
+            fetch(j0, pg, sg);
+#pragma unroll
+            for (int q = 0; q < kU; ++q) {
+                const int j = j0 + q * kSelThreads;
+                if (j >= n) break;
+                const uint8_t k = sel_class(v, j, pg[q]);
+                classify(j, pg[q], k, k == kCand ? primary(j, pg[q], sg[q]) : 0u);
+            }
         }
     }
     int tot;
@@ -349,20 +392,25 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
         for (int shift = 56; shift >= 0; shift -= 8) {
             for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
             __syncthreads();
-            for (int j = tid; j < n; j += kSelThreads) {
-                int32_t p;
-                uint8_t k;
-                if (in_lds) {
-                    k = cls_s[j];
-                    p = pos_s[j];
-                } else {
-                    p = v.P[j];
-                    k = sel_class(v, j, p);
-                }
-                if (k != kCand) continue;
-                const uint32_t pr = in_lds ? prim_s[j] : sel_primary(v, j, p);
+            auto count = [&](int32_t p, uint32_t pr) {
                 const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
                 if ((key & mask) == prefix) hist_add_wave(hist, (int)((key >> shift) & 255));
+            };
+            if (in_lds) {
+                for (int j = tid; j < n; j += kSelThreads)
+                    if (cls_s[j] == kCand) count(pos_s[j], prim_s[j]);
+            } else {
+                for (int j0 = tid; j0 < n; j0 += kU * kSelThreads) {
+                    int32_t pg[kU];
+                    uint32_t sg[kU];
+                    fetch(j0, pg, sg);
+#pragma unroll
+                    for (int q = 0; q < kU; ++q) {
+                        const int j = j0 + q * kSelThreads;
+                        if (j >= n) break;
+                        if (sel_class(v, j, pg[q]) == kCand) count(pg[q], primary(j, pg[q], sg[q]));
+                    }
+                }
             }
             __syncthreads();
             if (tid < 64) radix_pick_bin(hist, krem, sh_digit, sh_krem, sh_done);
@@ -377,34 +425,55 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
     }
 
     // keep flags -> ascending slot list: each thread owns a run of
-    // consecutive slots, so one scan orders the whole list
+    // consecutive slots, so one scan orders a whole run of the block
     int32_t *ks = a.keep_slots + (size_t)u * c.cap;
-    const int per = (n + kSelThreads - 1) / kSelThreads;
-    const int r0 = min(n, tid * per), r1 = min(n, r0 + per);
-    auto kept = [&](int j) -> bool {
-        int32_t p;
-        uint8_t k;
-        if (in_lds) {
-            k = cls_s[j];
-            p = pos_s[j];
-        } else {
-            p = v.P[j];
-            k = sel_class(v, j, p);
-        }
+    auto kept = [&](int j, int32_t p, uint8_t k, uint32_t pr) -> bool {
         if (k == kKeep) return true;
         if (k != kCand) return false;
         if (!rank) return true;
         if (keep_none) return false;
-        const uint32_t pr = in_lds ? prim_s[j] : sel_primary(v, j, p);
         const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
         return (key & mask) >= prefix;
     };
-    int mine = 0;
-    for (int j = r0; j < r1; ++j) mine += kept(j) ? 1 : 0;
-    int base;
-    int off = block_excl_scan(mine, red, &base);
-    for (int j = r0; j < r1; ++j)
-        if (kept(j)) ks[off++] = j;
+    int base = 0;
+    if (in_lds) {
+        const int per = (n + kSelThreads - 1) / kSelThreads;
+        const int r0 = min(n, tid * per), r1 = min(n, r0 + per);
+        int mine = 0;
+        for (int j = r0; j < r1; ++j) mine += kept(j, pos_s[j], cls_s[j], prim_s[j]) ? 1 : 0;
+        int off = block_excl_scan(mine, red, &base);
+        for (int j = r0; j < r1; ++j)
+            if (kept(j, pos_s[j], cls_s[j], prim_s[j])) ks[off++] = j;
+    } else {
+        // blocks of kU * kSelThreads slots, a run of kU per thread
+        for (int c0 = 0; c0 < n; c0 += kU * kSelThreads) {
+            const int r0 = c0 + tid * kU;
+            int32_t pg[kU];
+            uint32_t sg[kU];
+#pragma unroll
+            for (int q = 0; q < kU; ++q) {
+                const int j = min(r0 + q, n - 1);
+                pg[q] = v.P[j];
+                sg[q] = __float_as_uint(Sg[j]);
+            }
+            uint32_t flags = 0;
+#pragma unroll
+            for (int q = 0; q < kU; ++q) {
+                const int j = r0 + q;
+                if (j < n) {
+                    const uint8_t k = sel_class(v, j, pg[q]);
+                    if (kept(j, pg[q], k, k == kCand ? primary(j, pg[q], sg[q]) : 0u))
+                        flags |= 1u << q;
+                }
+            }
+            int t;
+            int off = block_excl_scan(__popc(flags), red, &t);
+#pragma unroll
+            for (int q = 0; q < kU; ++q)
+                if ((flags >> q) & 1u) ks[base + off++] = r0 + q;
+            base += t;
+        }
+    }
     if (tid == 0) a.n_out[u] = base;
     return -2;
 }
@@ -456,44 +525,7 @@ __device__ inline void compact_one(const CompactArgs &a, int u, int e) {
     if (tid == 0) c.n_slots[u] = src;
 }
 
-// Move one kept row from slot src to hole j (K, V, position, score).  With
-// BOTH, every load of the move goes out before its stores (rows of at most
-// 256 bytes: 2 x 16 sixteen-byte parts in registers); otherwise K then V.
-template <typename T, int D, bool BOTH>
-__device__ inline void move_row(const CacheDev &c, int b, int h, int j, int src, int32_t *P,
-                                float *S) {
-    constexpr int kParts = (int)(D * sizeof(T) / 16);
-    T *K = (T *)c.k;
-    T *V = (T *)c.v;
-    if constexpr (BOTH && kParts <= 16) {
-        uint4 kr[kParts], vr[kParts];
-        const uint4 *ksrc = reinterpret_cast<const uint4 *>(K + row_of(c, b, h, src) * D);
-        const uint4 *vsrc = reinterpret_cast<const uint4 *>(V + row_of(c, b, h, src) * D);
-#pragma unroll
-        for (int i = 0; i < kParts; ++i) {
-            kr[i] = ksrc[i];
-            vr[i] = vsrc[i];
-        }
-        const int32_t p = P[src];
-        const float sv = S ? S[src] : 0.f;
-        uint4 *kdst = reinterpret_cast<uint4 *>(K + row_of(c, b, h, j) * D);
-        uint4 *vdst = reinterpret_cast<uint4 *>(V + row_of(c, b, h, j) * D);
-#pragma unroll
-        for (int i = 0; i < kParts; ++i) {
-            kdst[i] = kr[i];
-            vdst[i] = vr[i];
-        }
-        P[j] = p;
-        if (S) S[j] = sv;
-    } else {
-        copy_row<T, D>(K + row_of(c, b, h, j) * D, K + row_of(c, b, h, src) * D);
-        copy_row<T, D>(V + row_of(c, b, h, j) * D, V + row_of(c, b, h, src) * D);
-        P[j] = P[src];
-        if (S) S[j] = S[src];
-    }
-}
-
-template <typename T, int D, bool BOTH = true>
+template <typename T, int D>
 __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
     const CacheDev &c = a.c;
     const int b = u / c.Hkv, h = u % c.Hkv;
@@ -536,7 +568,12 @@ __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
         const int idx = below + base + r;
         if (hole && idx < m) {
             const int src = ks[idx];
-            if (src >= m && src < n) move_row<T, D, BOTH>(c, b, h, j, src, P, S);
+            if (src >= m && src < n) {
+                copy_row<T, D>((T *)c.k + row_of(c, b, h, j) * D, (T *)c.k + row_of(c, b, h, src) * D);
+                copy_row<T, D>((T *)c.v + row_of(c, b, h, j) * D, (T *)c.v + row_of(c, b, h, src) * D);
+                P[j] = P[src];
+                if (S) S[j] = S[src];
+            }
         }
         base += t;
     }

@@ -139,6 +139,11 @@ def test_large_units_leave_the_lds_path():
         b, h = divmod(u, Hkv)
         want = _flags_to_slots(oracle.select_random(p, 1000, 2500, 5, b, h, 9))
         np.testing.assert_array_equal(got[u], want)
+    # dropped slots (no ranking) on the same path
+    got = _gpu_keep(cache, lambda k, m: kvc.evict_streaming(cache, 64, 3000, k, m))
+    for u, p in enumerate(units_pos):
+        want = _flags_to_slots(oracle.select_streaming(p, int(p.max()) + 1, 64, 3000))
+        np.testing.assert_array_equal(got[u], want)
 
 
 @pytest.mark.parametrize("dtype", [kvc.BF16, kvc.F32])
