@@ -77,11 +77,14 @@ int choose_nsplit(const kvc_cache *c, int hint) {
     const int T = (hint <= 0 || hint > c->capacity + 1) ? c->capacity + 1 : hint;
     const int units = units_of(c);
     if (kvc::mfma_tiles_ok(c->dtype, c->head_dim, c->block_size) && T > kvc::kFusedMaxT) {
-        // matrix-core splits: chunks of at most 512 slots (the 528-entry LDS
-        // instance, four workgroups per CU) and about 4,096 workgroups in
-        // all, but no chunk under 128 slots; at most 64 splits
-        int ns = (T + 511) / 512;
-        const int fill = (4096 + units - 1) / units, by_len = (T + 127) / 128;
+        // matrix-core splits: chunks of at most 528 slots (the 528-entry LDS
+        // instance, four workgroups per CU), and at least about 2,048
+        // workgroups in all (two per resident slot) while no chunk falls
+        // under 128 slots; at most 64 splits.  Longer chunks are cheaper per
+        // byte: at 256 units of 5,121 slots, 10 splits step in 121 us where
+        // 16 take 133 us and 20 take 148 us.
+        int ns = (T + 527) / 528;
+        const int fill = (2048 + units - 1) / units, by_len = (T + 127) / 128;
         const int want = fill < by_len ? fill : by_len;
         ns = ns > want ? ns : want;
         return ns > 64 ? 64 : ns;
