@@ -36,11 +36,11 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE reads 1,048,576 KiB (x 1.000).  Valid only for the kernel
 # sources whose digest is recorded; otherwise the bench reports null.
 PROFILED_TRAFFIC = {
-    "sources_digest": "6f19f1ab102882a6",
+    "sources_digest": "0a722629868ca454",
     "workload": "heavy_load_b512_l2048",
     "policy": "h2o",
-    "fetch_kib": 538433.07,
-    "write_kib": 26995.42,
+    "fetch_kib": 538442.06,
+    "write_kib": 26994.96,
     "fetch_scale": 1048576.0 / 524303.75,
     "write_scale": 1.0,
 }
