@@ -467,8 +467,10 @@ static hipError_t launch_split_tc(const AttnArgs &a, bool e5m2, hipStream_t s) {
 hipError_t launch_split(const AttnArgs &a, bool e5m2, int max_len, hipStream_t s) {
     const int chunk = split_chunk(max_len, a.nsplit);
     if (chunk <= kFusedSmallT) return launch_split_tc<kFusedSmallT>(a, e5m2, s);
-    if (chunk <= kFusedMaxT) return launch_split_tc<kFusedMaxT>(a, e5m2, s);
-    return hipErrorInvalidValue;
+    // chunks longer than the large instance holds (attended lengths above
+    // 64 splits of 1,024, the last slot of the largest capacity) take the
+    // generic routine inside its workgroups
+    return launch_split_tc<kFusedMaxT>(a, e5m2, s);
 }
 
 }  // namespace kvc

@@ -299,3 +299,35 @@ def test_paged_and_contiguous_give_identical_results():
         torch.cuda.synchronize()
         assert torch.equal(oa, op)
         _live_equal(a, p, sa, sp)
+
+
+def test_h2o_at_maximum_capacity():
+    # one unit at the library's capacity limit (65,536 slots: 64 splits of
+    # 1,024) beside a short one; the first step ranks 65,088 candidates from
+    # global memory, the second is a steady step
+    w = synth.workload("llama3_8b_h2o_b64")
+    _h2o_sync(w, [65535, 3000], capacity=65536, steps=2)
+
+
+@pytest.mark.parametrize("policy", ["h2o", "random", "streaming"])
+def test_whole_step_equals_three_calls_at_maximum_capacity(policy):
+    w = synth.workload("llama3_8b_h2o_b64", policy=policy, pinned=1024, n_keep=4096)
+    lengths, cap = [65535, 0], 65536
+    caches = [make_cache(w, lengths, cap), make_cache(w, lengths, cap)]
+    B = len(lengths)
+    h2o = policy == "h2o"
+    scs = [torch.zeros((B, w.kv_heads, cap), device="cuda") for _ in range(2)]
+    outs = [torch.empty((B, w.q_heads, w.head_dim), device="cuda") for _ in range(2)]
+    pol, _ = _policy_pair(w)
+    wss = [c.workspace(cap) for c in caches]
+    for t in range(1, 3):
+        q, kn, vn = synth.batch_step_inputs(w, t, B)
+        new_pos = torch.tensor([L + t - 1 for L in lengths], dtype=torch.int32, device="cuda")
+        args = (new_pos, dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype))
+        kvc.decode_step(caches[0], pol, t, *args, outs[0], scs[0] if h2o else None,
+                        max_len_hint=cap, workspace=wss[0])
+        _three_calls(caches[1], w, pol, t, *args, outs[1], scs[1] if h2o else None, wss[1], cap)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
+        _live_equal(caches[0], caches[1], scs[0] if h2o else None, scs[1] if h2o else None)
+    assert int(caches[0].flags.item()) == 0 and int(caches[1].flags.item()) == 0
