@@ -331,3 +331,33 @@ def test_whole_step_equals_three_calls_at_maximum_capacity(policy):
         assert torch.equal(outs[0], outs[1])
         _live_equal(caches[0], caches[1], scs[0] if h2o else None, scs[1] if h2o else None)
     assert int(caches[0].flags.item()) == 0 and int(caches[1].flags.item()) == 0
+
+
+@pytest.mark.parametrize("policy", ["h2o", "random"])
+def test_whole_step_on_a_full_cache_equals_three_calls(policy):
+    # every slot of the cache in use: the new token is attended but not stored
+    # (KVC_FLAG_FULL), and the one slot that leaves is chosen among the cached
+    # ones only; split path (capacity above the one-workgroup limit)
+    cap = 1100
+    w = synth.workload("llama3_8b_h2o_b64", policy=policy, n_heavy=8, n_recent=cap - 9,
+                       pinned=50, n_keep=cap - 51)
+    lengths = [cap, cap]
+    caches = [make_cache(w, lengths, cap), make_cache(w, lengths, cap)]
+    B = len(lengths)
+    h2o = policy == "h2o"
+    scs = [torch.zeros((B, w.kv_heads, cap), device="cuda") for _ in range(2)]
+    outs = [torch.empty((B, w.q_heads, w.head_dim), device="cuda") for _ in range(2)]
+    pol, _ = _policy_pair(w)
+    wss = [c.workspace(cap + 1) for c in caches]
+    q, kn, vn = synth.batch_step_inputs(w, 1, B)
+    new_pos = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    args = (new_pos, dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype))
+    kvc.decode_step(caches[0], pol, 1, *args, outs[0], scs[0] if h2o else None,
+                    max_len_hint=cap + 1, workspace=wss[0])
+    _three_calls(caches[1], w, pol, 1, *args, outs[1], scs[1] if h2o else None, wss[1], cap + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    _live_equal(caches[0], caches[1], scs[0] if h2o else None, scs[1] if h2o else None)
+    assert bool((caches[0].n_slots == cap - 1).all())
+    for c in caches:
+        assert int(c.flags.item()) & kvc.FLAG_FULL
