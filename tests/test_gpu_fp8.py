@@ -188,9 +188,10 @@ def test_streaming_trajectory_heavy_load_shape(capacity):
     _trajectory(w, [600, 512, 511, 40], capacity=capacity + 1, steps=3)
 
 
-def test_random_eviction_trajectory():
+@pytest.mark.parametrize("capacity", [200, 1104])
+def test_random_eviction_trajectory(capacity):
     w = _w("reasoning_random_b32", pinned=64, n_keep=96)
-    _trajectory(w, [150, 170, 64], capacity=200, steps=12)
+    _trajectory(w, [150, 170, 64], capacity=capacity, steps=12)
 
 
 def test_streaming_trajectory_paged():

@@ -112,6 +112,13 @@ def test_random_eviction_trajectory_reaches_steady_state(capacity):
     _trajectory(w, [150, 170, 64], capacity=capacity, steps=24)
 
 
+def test_random_eviction_on_paged_cache_split_path():
+    # paged blocks of 16 and a capacity above the one-workgroup limit: the
+    # split kernels rank their chunks' candidates through the block table
+    w = synth.workload("reasoning_random_b32", pinned=64, n_keep=96)
+    _trajectory(w, [150, 170, 64], capacity=1104, steps=12, paged=16)
+
+
 def test_random_eviction_three_call_path():
     w = synth.workload("reasoning_random_b32", pinned=64, n_keep=96)
     _trajectory(w, [150, 170], capacity=200, steps=6, fused=False)
