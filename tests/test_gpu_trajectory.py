@@ -368,3 +368,37 @@ def test_whole_step_on_a_full_cache_equals_three_calls(policy):
     assert bool((caches[0].n_slots == cap - 1).all())
     for c in caches:
         assert int(c.flags.item()) & kvc.FLAG_FULL
+
+
+@pytest.mark.parametrize("cap", [700, 1100])
+def test_h2o_ties_keep_the_lowest_positions(cap):
+    # q = 0: every attended slot gets probability 1 / (n + 1) from every head,
+    # so every candidate ties and the 64 heavy hitters are the lowest
+    # positions.  Slots hold shuffled positions, so a tie broken by slot
+    # instead of position would keep other tokens.  One-workgroup step
+    # (capacity 700) and the split path (1,100).
+    w = synth.workload("llama3_8b_h2o_b64", n_heavy=64, n_recent=448)
+    lengths = [cap - 1, 600]
+    cache = make_cache(w, lengths, cap)
+    rng = np.random.default_rng(5)
+    for b, L in enumerate(lengths):
+        perm = torch.from_numpy(rng.permutation(L).astype(np.int32)).cuda()
+        cache.pos[b, :, :L] = perm
+    B = len(lengths)
+    scores = torch.zeros((B, w.kv_heads, cap), device="cuda")
+    out = torch.empty((B, w.q_heads, w.head_dim), device="cuda")
+    _, kn, vn = synth.batch_step_inputs(w, 1, B)
+    q = torch.zeros((B, w.q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    new_pos = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    kvc.decode_step(cache, kvc.policy_h2o(64, 448), 1, new_pos, q, dev(kn, w.dtype),
+                    dev(vn, w.dtype), out, scores, max_len_hint=cap, workspace=cache.workspace(cap))
+    torch.cuda.synchronize()
+    n = cache.n_slots.cpu().numpy()
+    pos = cache.pos.cpu().numpy()
+    for b, L in enumerate(lengths):
+        seen = L + 1   # positions 0..L after the step
+        want = np.array(list(range(64)) + list(range(seen - 448, seen)), dtype=np.int32)
+        for h in range(w.kv_heads):
+            assert n[b, h] == 512
+            np.testing.assert_array_equal(np.sort(pos[b, h, :512]), want)
+    assert int(cache.flags.item()) == 0
