@@ -145,12 +145,13 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLdsT<STAGE> &C
     const bool can_store = n < c.cap;
     const int T_len = n + 1;
     const int chunk = split_chunk(T_len, ns);
+    const int nse = split_count(T_len, ns);   // the splits that hold entries
     const float *pp = a.part + (size_t)u * ns * G * (D + 2);
 
-    combine_load_ml<D>(pp, ns, G, CB);
+    combine_load_ml<D>(pp, nse, G, CB);
     __syncthreads();
-    combine_factors(ns, G, CB);
-    combine_output<D>(pp, ns, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
+    combine_factors(nse, G, CB);
+    combine_output<D>(pp, nse, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
     if (a.scores) {
         // p summed over the group for every attended slot (heads in order),
         // kJ slots per thread at a time; every logit load of a batch goes out
@@ -220,10 +221,11 @@ union FinishLdsT {
 // unit's candidate count and worst candidate from the splits' records
 // (wave 0).  Returns the slot that leaves, -1 when none does, or -2 when
 // more than one does (the full selection runs then).
-__device__ inline int presel_finish(const AttnArgs &a, const SelectArgs &sa, int u) {
+__device__ inline int presel_finish(const AttnArgs &a, const SelectArgs &sa, int u, int nse) {
     const int lane = threadIdx.x & 63;
-    const int nrec = a.nsplit * kPreselWaves;
-    const PreselRecord *R = reinterpret_cast<const PreselRecord *>(a.presel) + (size_t)u * nrec;
+    const int nrec = nse * kPreselWaves;   // the records of the splits that hold entries
+    const PreselRecord *R = reinterpret_cast<const PreselRecord *>(a.presel) +
+                            (size_t)u * a.nsplit * kPreselWaves;
     uint32_t cnt = 0;
     uint64_t best = ~0ull;
     int arg = -1;
@@ -269,12 +271,13 @@ __device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, in
     const float *pp = a.part + (size_t)u * ns * G * (D + 2);
 
     int n = c.n_slots[u];
-    combine_load_ml<D>(pp, ns, G, CB);
+    n = (n < 0) ? 0 : (n > c.cap ? c.cap : n);
+    const int nse = split_count(n + 1, ns);   // the splits that hold entries
+    combine_load_ml<D>(pp, nse, G, CB);
     if (tid < 64) {
-        const int e = presel_finish(a, sa, u);
+        const int e = presel_finish(a, sa, u, nse);
         if (tid == 0) sh_e = e;
     }
-    n = (n < 0) ? 0 : (n > c.cap ? c.cap : n);
     __syncthreads();
     const int e = sh_e;
     if (e == -2) return false;
@@ -294,8 +297,8 @@ __device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, in
         row = reinterpret_cast<const uint4 *>(X + row_of(c, b, h, src) * D)[tid % kParts];
     if (move && tid == 0) psrc = P[src];
 
-    combine_factors(ns, G, CB);
-    combine_output<D>(pp, ns, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
+    combine_factors(nse, G, CB);
+    combine_output<D>(pp, nse, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
     if (move && tid < 2 * kParts)
         reinterpret_cast<uint4 *>(X + row_of(c, b, h, e) * D)[tid % kParts] = row;
     if (move && tid == 0) P[e] = psrc;

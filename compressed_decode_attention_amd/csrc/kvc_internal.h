@@ -357,9 +357,21 @@ constexpr int kPreselWaves = 4;   // records per split: one per wave of the spli
 hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s);
 
 // Slots per split of a unit attending T entries over ns splits: equal shares
-// rounded up to whole 16-slot tiles (split s covers [s*chunk, (s+1)*chunk) of
-// the attended entries, clipped to T; trailing splits may be empty).
-__host__ __device__ inline int split_chunk(int T, int ns) { return ((T + ns - 1) / ns + 15) & ~15; }
+// rounded up to whole 16-slot tiles, and at least kMinChunk slots, so that a
+// unit much shorter than the launch's length bound fills only its first
+// split_count(T, ns) splits (split s covers [s*chunk, (s+1)*chunk) of the
+// attended entries, clipped to T; the later splits hold nothing, and the
+// matrix-core split kernel and every combine skip them).
+constexpr int kMinChunk = 128;
+__host__ __device__ inline int split_chunk(int T, int ns) {
+    const int c = ((T + ns - 1) / ns + 15) & ~15;
+    return c > kMinChunk ? c : kMinChunk;
+}
+__host__ __device__ inline int split_count(int T, int ns) {
+    const int c = split_chunk(T, ns);
+    const int k = (T + c - 1) / c;
+    return k < 1 ? 1 : (k > ns ? ns : k);
+}
 
 // Matrix-core split kernels (split.hip): bf16 or E5M2, head_dim 128, block
 // sizes 0 or a power of two >= 16; ns >= 2 splits of at most kFusedMaxT slots.

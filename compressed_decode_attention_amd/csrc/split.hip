@@ -160,6 +160,7 @@ void split_kernel(AttnArgs a) {
     const int n = __builtin_amdgcn_readfirstlane(load_count(c, u, s == 0 && tid == 0));
     const int T = n + 1;
     const int chunk = split_chunk(T, ns);
+    if (s >= split_count(T, ns)) return;   // past the unit's entries: nothing to attend
     if (chunk > TC) {   // longer than the launch promised: the generic routine
         using TK = typename std::conditional<F8, e5m2_t, uint16_t>::type;
         attn_unit_generic<TK, kHD>(a, u, s, *reinterpret_cast<AttnLds<kHD> *>(smem));
