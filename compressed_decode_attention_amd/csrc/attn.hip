@@ -144,8 +144,8 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLdsT<STAGE> &C
     const int n = load_count(c, u, false);
     const bool can_store = n < c.cap;
     const int T_len = n + 1;
-    const int chunk = split_chunk(T_len, ns);
-    const int nse = split_count(T_len, ns);   // the splits that hold entries
+    const int chunk = split_chunk(T_len, ns, a.max_len);
+    const int nse = split_count(T_len, ns, a.max_len);   // the splits that hold entries
     const float *pp = a.part + (size_t)u * ns * G * (D + 2);
 
     combine_load_ml<D>(pp, nse, G, CB);
@@ -272,7 +272,7 @@ __device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, in
 
     int n = c.n_slots[u];
     n = (n < 0) ? 0 : (n > c.cap ? c.cap : n);
-    const int nse = split_count(n + 1, ns);   // the splits that hold entries
+    const int nse = split_count(n + 1, ns, a.max_len);   // the splits that hold entries
     combine_load_ml<D>(pp, nse, G, CB);
     if (tid < 64) {
         const int e = presel_finish(a, sa, u, nse);

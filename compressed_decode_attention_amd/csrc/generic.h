@@ -42,7 +42,7 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
     const bool can_store = a.append && n < c.cap;
     if (a.append && !can_store && s == 0 && tid == 0) raise_flag(c, KVC_FLAG_FULL);
     const int T_len = n + 1;
-    const int chunk = split_chunk(T_len, a.nsplit);
+    const int chunk = split_chunk(T_len, a.nsplit, a.max_len);
     const int j0 = min(s * chunk, T_len), j1 = min(T_len, j0 + chunk);
 
     const TA *qp = (const TA *)a.q + ((size_t)b * c.Hq + (size_t)h * G) * D;

@@ -356,19 +356,22 @@ constexpr int kPreselWaves = 4;   // records per split: one per wave of the spli
 
 hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s);
 
-// Slots per split of a unit attending T entries over ns splits: equal shares
-// rounded up to whole 16-slot tiles, and at least kMinChunk slots, so that a
-// unit much shorter than the launch's length bound fills only its first
-// split_count(T, ns) splits (split s covers [s*chunk, (s+1)*chunk) of the
-// attended entries, clipped to T; the later splits hold nothing, and the
-// matrix-core split kernel and every combine skip them).
+// Slots per split of a launch over ns splits whose units attend at most
+// max_len entries: equal shares of max_len rounded up to whole 16-slot tiles,
+// at least kMinChunk.  Every unit of the launch uses the same chunk, so a unit
+// shorter than max_len fills only its first split_count splits (split s
+// covers [s*chunk, (s+1)*chunk) of the unit's T attended entries, clipped to
+// T; the later splits hold nothing, and the matrix-core split kernel and
+// every combine skip them).  A unit longer than the bound takes shares of its
+// own length, so ns splits still cover it.
 constexpr int kMinChunk = 128;
-__host__ __device__ inline int split_chunk(int T, int ns) {
-    const int c = ((T + ns - 1) / ns + 15) & ~15;
+__host__ __device__ inline int split_chunk(int T, int ns, int max_len) {
+    const int L = T > max_len ? T : max_len;
+    const int c = ((L + ns - 1) / ns + 15) & ~15;
     return c > kMinChunk ? c : kMinChunk;
 }
-__host__ __device__ inline int split_count(int T, int ns) {
-    const int c = split_chunk(T, ns);
+__host__ __device__ inline int split_count(int T, int ns, int max_len) {
+    const int c = split_chunk(T, ns, max_len);
     const int k = (T + c - 1) / c;
     return k < 1 ? 1 : (k > ns ? ns : k);
 }

@@ -159,8 +159,8 @@ void split_kernel(AttnArgs a) {
            col < G, r);
     const int n = __builtin_amdgcn_readfirstlane(load_count(c, u, s == 0 && tid == 0));
     const int T = n + 1;
-    const int chunk = split_chunk(T, ns);
-    if (s >= split_count(T, ns)) return;   // past the unit's entries: nothing to attend
+    const int chunk = split_chunk(T, ns, a.max_len);
+    if (s >= split_count(T, ns, a.max_len)) return;   // past the unit's entries: nothing to attend
     if (chunk > TC) {   // longer than the launch promised: the generic routine
         using TK = typename std::conditional<F8, e5m2_t, uint16_t>::type;
         attn_unit_generic<TK, kHD>(a, u, s, *reinterpret_cast<AttnLds<kHD> *>(smem));
@@ -466,7 +466,7 @@ static hipError_t launch_split_tc(const AttnArgs &a, bool e5m2, hipStream_t s) {
 }
 
 hipError_t launch_split(const AttnArgs &a, bool e5m2, int max_len, hipStream_t s) {
-    const int chunk = split_chunk(max_len, a.nsplit);
+    const int chunk = split_chunk(max_len, a.nsplit, max_len);
     if (chunk <= kFusedSmallT) return launch_split_tc<kFusedSmallT>(a, e5m2, s);
     // chunks longer than the large instance holds (attended lengths above
     // 64 splits of 1,024, the last slot of the largest capacity) take the
