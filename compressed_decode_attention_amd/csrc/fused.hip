@@ -50,6 +50,7 @@ struct FusedSmall {
     float l[kMaxGroup];      // softmax normalisers
     float il[kMaxGroup];     // 1 / l
     float wred[kFWaves][kMaxGroup];
+    float wmax[kFWaves][kMaxGroup];   // each wave's logit maxima, then its output factors
     int hist[256];
     int red[kFWaves * 2];
     int pmax[kFWaves];       // newest position seen by each wave
@@ -287,22 +288,16 @@ void fused_kernel(FusedArgs fa) {
         m = fmaxf(m, __shfl_xor(m, 4, 64));
         m = fmaxf(m, __shfl_xor(m, 2, 64));
         m = fmaxf(m, __shfl_xor(m, 1, 64));
-        if (col == 0 && 4 * r + i < G) sm.wred[w][4 * r + i] = m;
+        if (col == 0 && 4 * r + i < G) sm.wmax[w][4 * r + i] = m;
     }
     pmax = wave_max_i(pmax);
     if (lane == 0) sm.pmax[w] = pmax;
-    __syncthreads();
-    if (tid < G) {
-        float m = sm.wred[0][tid];
-        for (int v = 1; v < kFWaves; ++v) m = fmaxf(m, sm.wred[v][tid]);
-        sm.m[tid] = m;
-    }
-    if (tid == 64) {
-        int pm = sm.pmax[0];
-        for (int v = 1; v < kFWaves; ++v) pm = max(pm, sm.pmax[v]);
-        sm.posmax = pm;
-    }
-    __syncthreads();
+    // Each wave weighs its own tiles against its own maxima, so P.V starts
+    // without waiting for the other waves; the waves' sums are rescaled to
+    // the unit's maxima once P.V is done (the same exact softmax).  The
+    // maxima above were written by lanes of this wave: LDS operations of a
+    // wave complete in order.
+    __builtin_amdgcn_wave_barrier();
 
     // ---------------- P.V: MFMA 16x16x16 bf16 per 16-key tile.
     // A row (lane col) = query head ga; with G <= 8 rows 8..15 repeat heads
@@ -317,7 +312,7 @@ void fused_kernel(FusedArgs fa) {
     const int ga = pack2 ? (col & 7) : col;
     const bool arow = ga < G;
     const bool hi_lane = !pack2 || col < 8;
-    const float mrow = arow ? sm.m[ga] : 0.f;
+    const float mrow = arow ? sm.wmax[w][ga] : 0.f;
     float *lrow = lg + (arow ? ga : 0) * LD;
 #pragma unroll
     for (int i = 0; i < kNTW; ++i) {
@@ -369,10 +364,28 @@ void fused_kernel(FusedArgs fa) {
     if (lane < G) sm.wred[w][lane] = lsum;
     __syncthreads();   // weights in lg are final, partial row sums written
     if (tid < G) {
+        // the unit's maximum, each wave's factor exp(m_w - M), the
+        // normaliser; the factor over the normaliser then scales both the
+        // wave's weights (H2O) and its partial output
+        float M = -INFINITY;
+        for (int v = 0; v < kFWaves; ++v) M = fmaxf(M, sm.wmax[v][tid]);
         float l = 0.f;
-        for (int v = 0; v < kFWaves; ++v) l += sm.wred[v][tid];
+        float f[kFWaves];
+        for (int v = 0; v < kFWaves; ++v) {
+            const float mv = sm.wmax[v][tid];
+            f[v] = (mv == -INFINITY) ? 0.f : __expf(mv - M);
+            l += sm.wred[v][tid] * f[v];
+        }
+        const float il = 1.f / l;
+        for (int v = 0; v < kFWaves; ++v) sm.wmax[v][tid] = f[v] * il;
+        sm.m[tid] = M;
         sm.l[tid] = l;
-        sm.il[tid] = 1.f / l;
+        sm.il[tid] = il;
+    }
+    if (tid == 64) {
+        int pm = sm.pmax[0];
+        for (int v = 1; v < kFWaves; ++v) pm = max(pm, sm.pmax[v]);
+        sm.posmax = pm;
     }
     __syncthreads();
 
@@ -381,7 +394,8 @@ void fused_kernel(FusedArgs fa) {
         for (int j = tid; j < T; j += kFThreads) {
             float ps = 0.f;
             const int jc = lg_col(j);
-            for (int g = 0; g < G; ++g) ps += lg[g * LD + jc] * sm.il[g];
+            const int wj = (j >> 4) % kFWaves;   // the wave that weighed tile j / 16
+            for (int g = 0; g < G; ++g) ps += lg[g * LD + jc] * sm.wmax[wj][g];
             sc_s[j] = score_update((j < n) ? sc_s[j] : 0.f, ps, a.decay);
         }
     }
@@ -406,9 +420,9 @@ void fused_kernel(FusedArgs fa) {
         float *outp = a.out + ((size_t)b * c.Hq + (size_t)h * G) * kHD;
         for (int e = tid; e < G * kHD; e += kFThreads) {
             const int g = e / kHD;
-            float o = opart[e];
-            for (int v = 1; v < kFWaves; ++v) o += opart[(size_t)v * G * kHD + e];
-            outp[e] = o / sm.l[g];
+            float o = opart[e] * sm.wmax[0][g];
+            for (int v = 1; v < kFWaves; ++v) o += opart[(size_t)v * G * kHD + e] * sm.wmax[v][g];
+            outp[e] = o;
         }
     }
 
