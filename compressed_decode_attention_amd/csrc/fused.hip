@@ -296,8 +296,22 @@ void fused_kernel(FusedArgs fa) {
     // without waiting for the other waves; the waves' sums are rescaled to
     // the unit's maxima once P.V is done (the same exact softmax).  The
     // maxima above were written by lanes of this wave: LDS operations of a
-    // wave complete in order.
-    __builtin_amdgcn_wave_barrier();
+    // wave complete in order.  E5M2 caches only: the bf16 instances gain
+    // nothing measurable from it and the paged one would spill more, while
+    // both modes and both layouts of a dtype must compute alike (their
+    // results match bit for bit), so bf16 keeps one set of maxima per unit.
+    constexpr bool kWaveMax = F8;
+    if constexpr (kWaveMax) {
+        __builtin_amdgcn_wave_barrier();
+    } else {
+        __syncthreads();
+        if (tid < G) {
+            float m = sm.wmax[0][tid];
+            for (int v = 1; v < kFWaves; ++v) m = fmaxf(m, sm.wmax[v][tid]);
+            sm.m[tid] = m;
+        }
+        __syncthreads();
+    }
 
     // ---------------- P.V: MFMA 16x16x16 bf16 per 16-key tile.
     // A row (lane col) = query head ga; with G <= 8 rows 8..15 repeat heads
@@ -312,7 +326,7 @@ void fused_kernel(FusedArgs fa) {
     const int ga = pack2 ? (col & 7) : col;
     const bool arow = ga < G;
     const bool hi_lane = !pack2 || col < 8;
-    const float mrow = arow ? sm.wmax[w][ga] : 0.f;
+    const float mrow = arow ? (kWaveMax ? sm.wmax[w][ga] : sm.m[ga]) : 0.f;
     float *lrow = lg + (arow ? ga : 0) * LD;
 #pragma unroll
     for (int i = 0; i < kNTW; ++i) {
@@ -363,7 +377,16 @@ void fused_kernel(FusedArgs fa) {
     lsum += __shfl_xor(lsum, 32, 64);
     if (lane < G) sm.wred[w][lane] = lsum;
     __syncthreads();   // weights in lg are final, partial row sums written
-    if (tid < G) {
+    if (tid < G && !kWaveMax) {
+        // one maximum for the unit: every wave's factor is 1 / l
+        float l = 0.f;
+        for (int v = 0; v < kFWaves; ++v) l += sm.wred[v][tid];
+        const float il = 1.f / l;
+        for (int v = 0; v < kFWaves; ++v) sm.wmax[v][tid] = il;
+        sm.l[tid] = l;
+        sm.il[tid] = il;
+    }
+    if (tid < G && kWaveMax) {
         // the unit's maximum, each wave's factor exp(m_w - M), the
         // normaliser; the factor over the normaliser then scales both the
         // wave's weights (H2O) and its partial output
