@@ -229,6 +229,18 @@ def device_seed(*parts: int) -> int:
                & np.uint64(0x7FFFFFFFFFFFFFFF))
 
 
+def device_e5m2_truncated(x):
+    """The recipe of e5m2_truncated on a float32 device tensor: E5M2 codes
+    (torch.uint8) keeping sign, exponent and the top two mantissa bits."""
+    import torch
+    u = x.contiguous().view(torch.int32)
+    sign = (u >> 24) & 0x80
+    e = (u >> 23) & 0xFF
+    assert bool((e < 143).all()), "draw beyond the E5M2 range"
+    code = torch.where(e < 113, torch.zeros_like(u), ((e - 112) << 2) | ((u >> 21) & 3))
+    return (sign | code).to(torch.uint8)
+
+
 def device_normal(shape, *parts: int, device="cuda", dtype=None, scale_rows_frac: float = 0.0,
                   scale: float = 8.0):
     """N(0,1) draws on the device, rounded to `dtype` (bf16 by default); with

@@ -86,11 +86,11 @@ def _run(w, cache, lengths, pol, steps, hints, units, heavy_frac=0.0, seen0=None
         kn = synth.device_normal((B, cache.kv_heads, D), w.seed, w.wid, synth.T_KNEW, t,
                                  scale_rows_frac=heavy_frac)
         vn = synth.device_normal((B, cache.kv_heads, D), w.seed, w.wid, synth.T_VNEW, t)
-        pre = Snapshot(twin, "bf16", sc_t, units)
+        pre = Snapshot(twin, w.dtype, sc_t, units)
         kvc.decode_step(cache, pol, t, seen, q, kn, vn, out_f, sc_f, max_len_hint=hint,
                         workspace=ws)
         kvc.decode_attn(twin, seen, q, kn, vn, out_t, sc_t, max_len_hint=hint, workspace=ws2)
-        mid = Snapshot(twin, "bf16", sc_t, units)
+        mid = Snapshot(twin, w.dtype, sc_t, units)
         _policy_calls(pol, twin, sc_t, t, keep, nout)
         kk, mm = keep.cpu().numpy(), nout.cpu().numpy()
         if pol.kind != kvc.POLICY_FULL:
@@ -106,7 +106,7 @@ def _run(w, cache, lengths, pol, steps, hints, units, heavy_frac=0.0, seen0=None
         sn = seen.cpu().numpy()
         for (b, h) in units:
             u0, u1 = pre.unit(b, h), mid.unit(b, h)
-            ref, psum = oracle_unit_attend("bf16", qh[b, h * G:(h + 1) * G], u0, knh[b, h],
+            ref, psum = oracle_unit_attend(w.dtype, qh[b, h * G:(h + 1) * G], u0, knh[b, h],
                                            vnh[b, h], scale)
             err = np.abs(o[b, h * G:(h + 1) * G] - ref).max()
             assert err <= OUT_ATOL, (t, b, h, err)
@@ -134,21 +134,27 @@ def _run(w, cache, lengths, pol, steps, hints, units, heavy_frac=0.0, seen0=None
 
 def _prefill(w, B, cap, fill, heavy_frac=0.0, paged=0, lengths=None):
     lengths = [fill] * B if lengths is None else lengths
+    f8 = w.dtype == "e5m2"
+    dt = kvc.FP8_E5M2 if f8 else kvc.BF16
     if paged:
         max_blocks = cap // paged
         nblk = B * max_blocks
         perm = torch.from_numpy(synth.block_permutation(nblk, w.seed, w.wid).reshape(B, max_blocks).copy())
-        c = kvc.KvCache(B, w.q_heads, w.kv_heads, w.head_dim, cap, kvc.BF16, block_size=paged,
+        c = kvc.KvCache(B, w.q_heads, w.kv_heads, w.head_dim, cap, dt, block_size=paged,
                         num_blocks=nblk, block_table=perm)
     else:
-        c = kvc.KvCache(B, w.q_heads, w.kv_heads, w.head_dim, cap, kvc.BF16)
+        c = kvc.KvCache(B, w.q_heads, w.kv_heads, w.head_dim, cap, dt)
+    # E5M2 caches hold the float32 draws truncated to codes (the seeded recipe)
+    draw_dtype = torch.float32 if f8 else None
+    stored = synth.device_e5m2_truncated if f8 else (lambda x: x)
     chunk = 32
     for b0 in range(0, B, chunk):
         b1 = min(B, b0 + chunk)
         L = max(lengths[b0:b1])
-        k = synth.device_normal((b1 - b0, w.kv_heads, L, w.head_dim), w.seed, w.wid, synth.T_K, b0,
-                                scale_rows_frac=heavy_frac)
-        v = synth.device_normal((b1 - b0, w.kv_heads, L, w.head_dim), w.seed, w.wid, synth.T_V, b0)
+        k = stored(synth.device_normal((b1 - b0, w.kv_heads, L, w.head_dim), w.seed, w.wid,
+                                       synth.T_K, b0, dtype=draw_dtype, scale_rows_frac=heavy_frac))
+        v = stored(synth.device_normal((b1 - b0, w.kv_heads, L, w.head_dim), w.seed, w.wid,
+                                       synth.T_V, b0, dtype=draw_dtype))
         for i, b in enumerate(range(b0, b1)):
             Lb = lengths[b]
             if paged:
@@ -173,6 +179,17 @@ def test_heavy_load_b512_l2048_h2o_full_size():
     P = w.prompt_len
     cache = _prefill(w, w.batch, P + 1, P)
     units = [(b, h) for b in (0, 97, 255, 256, 511) for h in (0, 3, 7)]
+    _run(w, cache, [P] * w.batch, kvc.policy_h2o(64, 448), steps=3, hints=[P + 1, 513],
+         units=units)
+
+
+def test_heavy_load_b512_l2048_h2o_e5m2_full_size():
+    # the same layer with an E5M2 (8-bit float) cache: the first step trims on
+    # the split path, the others run the fused kernel's E5M2 instance
+    w = synth.workload("heavy_load_b512_l2048", dtype="e5m2")
+    P = w.prompt_len
+    cache = _prefill(w, w.batch, P + 1, P)
+    units = [(b, h) for b in (0, 200, 511) for h in (0, 6)]
     _run(w, cache, [P] * w.batch, kvc.policy_h2o(64, 448), steps=3, hints=[P + 1, 513],
          units=units)
 
