@@ -36,11 +36,11 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE reads 1,048,576 KiB (x 1.000).  Valid only for the fused kernel's
 # sources whose digest is recorded; otherwise the bench reports null.
 PROFILED_TRAFFIC = {
-    "sources_digest": "78493b9a35c93a3c",
+    "sources_digest": "6099f4ca4a8613ed",
     "workload": "heavy_load_b512_l2048",
     "policy": "h2o",
-    "fetch_kib": 538443.53,
-    "write_kib": 26995.26,
+    "fetch_kib": 538437.52,
+    "write_kib": 26995.25,
     "fetch_scale": 1048576.0 / 524303.75,
     "write_scale": 1.0,
 }
