@@ -29,21 +29,22 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 # HBM traffic of the fused step kernel at the heavy-load shape, from two
-# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
-# dispatch, mean over the steady-state dispatches), each scaled by what the
+# rocprofv3 --pmc runs of this script per case (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch, mean over the steady-state dispatches), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (--copy-probe-mb 1024):
-# FETCH_SIZE reads 524,302.9 KiB for 1,048,576 KiB copied (x 2.000),
-# WRITE_SIZE reads 1,048,576 KiB (x 1.000).  Valid only for the fused kernel's
-# sources whose digest is recorded; otherwise the bench reports null.
-PROFILED_TRAFFIC = {
-    "sources_digest": "6099f4ca4a8613ed",
-    "workload": "heavy_load_b512_l2048",
-    "policy": "h2o",
-    "fetch_kib": 538437.52,
-    "write_kib": 26995.25,
-    "fetch_scale": 1048576.0 / 524303.75,
-    "write_scale": 1.0,
-}
+# FETCH_SIZE reads 524,303.8 KiB for 1,048,576 KiB copied (x 2.000),
+# WRITE_SIZE reads 1,048,576 KiB (x 1.000).  A record is valid only for the
+# fused kernel's sources whose digest it holds; otherwise the bench reports null.
+FETCH_SCALE = 1048576.0 / 524303.75
+WRITE_SCALE = 1.0
+PROFILED_TRAFFIC = [
+    {"sources_digest": "6099f4ca4a8613ed", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "bf16", "fetch_kib": 538437.52, "write_kib": 26995.25},
+    {"sources_digest": "6099f4ca4a8613ed", "workload": "heavy_load_b512_l2048", "policy": "streaming",
+     "kv_dtype": "bf16", "fetch_kib": 534099.21, "write_kib": 18688.16},
+    {"sources_digest": "6099f4ca4a8613ed", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "e5m2", "fetch_kib": 276342.35, "write_kib": 25968.00},
+]
 
 
 # the translation unit of the fused step kernel: its source and every header it
@@ -65,11 +66,13 @@ def sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(workload: str, policy: str):
-    t = PROFILED_TRAFFIC
-    if t["workload"] != workload or t["policy"] != policy or sources_digest() != t["sources_digest"]:
-        return None
-    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+def profiled_traffic(workload: str, policy: str, kv_dtype: str):
+    digest = sources_digest()
+    for t in PROFILED_TRAFFIC:
+        if (t["workload"], t["policy"], t["kv_dtype"], t["sources_digest"]) == \
+                (workload, policy, kv_dtype, digest):
+            return (t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024.0
+    return None
 
 
 def log(msg):
@@ -744,7 +747,7 @@ def main():
     step_bytes = unit_bytes * B * Hkv
     achieved = step_bytes / (launch_ms * 1e-3) / 1e9
     steps_per_s = 1e3 / ms_per_step
-    traffic = None if f8 else profiled_traffic(w.name, policy)
+    traffic = profiled_traffic(w.name, policy, "e5m2" if f8 else "bf16")
 
     result = {
         "metric": f"decode steps/s and achieved HBM GB/s (% of peak), attn+evict, B={B} L={P}",
@@ -776,6 +779,8 @@ def main():
             "launch_ms": launch_ms,
             "attainable_read_gbs": attain["gbs"], "attainable_how": attain["how"],
             "frac_of_attainable": achieved / attain["gbs"],
+            # the counted bytes (traffic) over the same launch time
+            "counter_gbs": None if traffic is None else traffic / (launch_ms * 1e-3) / 1e9,
         },
     }
     if not args.no_cpu_baseline:
