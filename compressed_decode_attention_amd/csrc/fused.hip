@@ -284,13 +284,13 @@ void fused_kernel(FusedArgs fa) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float m = mx[i];
-        m = fmaxf(m, __shfl_xor(m, 8, 64));
-        m = fmaxf(m, __shfl_xor(m, 4, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, lane_xor_f<8>(m));
+        m = fmaxf(m, lane_xor_f<4>(m));
+        m = fmaxf(m, lane_xor_f<2>(m));
+        m = fmaxf(m, lane_xor_f<1>(m));
         if (col == 0 && 4 * r + i < G) sm.wmax[w][4 * r + i] = m;
     }
-    pmax = wave_max_i(pmax);
+    pmax = wave_max_iv(pmax);
     if (lane == 0) sm.pmax[w] = pmax;
     // Each wave weighs its own tiles against its own maxima, so P.V starts
     // without waiting for the other waves; the waves' sums are rescaled to
@@ -371,10 +371,10 @@ void fused_kernel(FusedArgs fa) {
 #pragma unroll
         for (int m8 = 0; m8 < 8; ++m8)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) oacc[m8][ii] += __shfl_xor(oacc[m8][ii], 32, 64);
+            for (int ii = 0; ii < 4; ++ii) oacc[m8][ii] = pair_sum32(oacc[m8][ii]);
     // lanes col, col+16, col+32, col+48 hold partial sums of A row col
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum = pair_sum16(lsum);
+    lsum = pair_sum32(lsum);
     if (lane < G) sm.wred[w][lane] = lsum;
     __syncthreads();   // weights in lg are final, partial row sums written
     if (tid < G && !kWaveMax) {
@@ -514,19 +514,25 @@ void fused_kernel(FusedArgs fa) {
         }
         flg_s[j] = k;
     }
-    ncand = wave_sum_i(ncand);
-    ndrop = wave_sum_i(ndrop);
-    dslot = wave_max_i(dslot);
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
-        const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
-        const int oa = __shfl_xor(barg, o, 64);
+    ncand = wave_sum_iv(ncand);
+    ndrop = wave_sum_iv(ndrop);
+    dslot = wave_max_iv(dslot);
+    auto arg_step = [&](uint32_t hi, uint32_t lo, int oa) {
         const uint64_t ob = ((uint64_t)hi << 32) | lo;
         if (ob < best || (ob == best && (unsigned)oa < (unsigned)barg)) {
             best = ob;
             barg = oa;
         }
-    }
+    };
+#define KVC_ARG_STEP(M) \
+    arg_step(lane_xor<M>((uint32_t)(best >> 32)), lane_xor<M>((uint32_t)best), (int)lane_xor<M>((uint32_t)barg))
+    KVC_ARG_STEP(32);
+    KVC_ARG_STEP(16);
+    KVC_ARG_STEP(8);
+    KVC_ARG_STEP(4);
+    KVC_ARG_STEP(2);
+    KVC_ARG_STEP(1);
+#undef KVC_ARG_STEP
     if (lane == 0) {
         sm.r_nc[w] = ncand;
         sm.r_nd[w] = ndrop;

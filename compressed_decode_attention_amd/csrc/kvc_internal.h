@@ -155,6 +155,76 @@ __device__ inline int wave_min_i(int x) {
     return x;
 }
 
+// The value of lane (lane ^ M) without a trip through the LDS unit: DPP
+// quad permutes for M = 1, 2; for M = 4 and 8 a row mirror (lane ^ 7, lane ^ 15)
+// composed with a quad permute or the half-row mirror; for M = 16 and 32 the
+// CDNA4 swaps of rows and of wave halves (v_permlane16/32_swap).  Every lane of
+// the wave must be active.  A butterfly step x op lane_xor<M>(x) gives every
+// lane the result the LDS shuffle gives (op commutative).
+template <int M>
+__device__ inline uint32_t lane_xor(uint32_t x) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane_xor mask");
+    const int v = (int)x;
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+    } else if constexpr (M == 4) {
+        const int h = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);     // lane ^ 7
+        return (uint32_t)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, false);   // then ^ 3
+    } else if constexpr (M == 8) {
+        const int h = __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);     // lane ^ 15
+        return (uint32_t)__builtin_amdgcn_mov_dpp(h, 0x141, 0xF, 0xF, false);  // then ^ 7
+    } else if constexpr (M == 16) {
+        // .x: the even row of each row pair, .y: the odd row
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (__lane_id() & 16) ? r[0] : r[1];
+    } else {
+        // .x: the lower half of the wave, .y: the upper half
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (__lane_id() & 32) ? r[0] : r[1];
+    }
+}
+template <int M>
+__device__ inline float lane_xor_f(float x) {
+    return __builtin_bit_cast(float, lane_xor<M>(__builtin_bit_cast(uint32_t, x)));
+}
+// x + (x of lane ^ 32) and x + (x of lane ^ 16), summed lower half (row) first
+// in every lane: the same value as the butterfly sum, without the lane select.
+// The two words are copied out of the result vector before the bit casts: a
+// bit cast applied to an element of it reads element 0 (hipcc 7.2).
+__device__ inline float pair_sum32(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+__device__ inline float pair_sum16(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t ev = r[0], od = r[1];
+    return __builtin_bit_cast(float, ev) + __builtin_bit_cast(float, od);
+}
+// whole-wave reductions through lane_xor (every lane active)
+__device__ inline int wave_sum_iv(int x) {
+    x += (int)lane_xor<32>((uint32_t)x);
+    x += (int)lane_xor<16>((uint32_t)x);
+    x += (int)lane_xor<8>((uint32_t)x);
+    x += (int)lane_xor<4>((uint32_t)x);
+    x += (int)lane_xor<2>((uint32_t)x);
+    x += (int)lane_xor<1>((uint32_t)x);
+    return x;
+}
+__device__ inline int wave_max_iv(int x) {
+    x = max(x, (int)lane_xor<32>((uint32_t)x));
+    x = max(x, (int)lane_xor<16>((uint32_t)x));
+    x = max(x, (int)lane_xor<8>((uint32_t)x));
+    x = max(x, (int)lane_xor<4>((uint32_t)x));
+    x = max(x, (int)lane_xor<2>((uint32_t)x));
+    x = max(x, (int)lane_xor<1>((uint32_t)x));
+    return x;
+}
+
 // Block-wide max of an int (blockDim.x a multiple of 64, <= 1024).
 __device__ inline int block_max_i(int x, int *red) {
     x = wave_max_i(x);
