@@ -91,17 +91,24 @@ __device__ inline void presel_add(const AttnArgs &a, int b, int h, int j, int32_
 // its output stores) to publish them.
 __device__ inline void presel_write(const AttnArgs &a, int u, int s, PreselAcc acc) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int o = 32; o > 0; o >>= 1) {
-        acc.cnt += __shfl_xor(acc.cnt, o, 64);
-        const uint32_t hi = __shfl_xor((uint32_t)(acc.best >> 32), o, 64);
-        const uint32_t lo = __shfl_xor((uint32_t)acc.best, o, 64);
-        const int oa = __shfl_xor(acc.arg, o, 64);
+    auto step = [&](uint32_t hi, uint32_t lo, int oa) {
         const uint64_t ok = ((uint64_t)hi << 32) | lo;
         if (ok < acc.best || (ok == acc.best && (unsigned)oa < (unsigned)acc.arg)) {
             acc.best = ok;
             acc.arg = oa;
         }
-    }
+    };
+    acc.cnt = wave_sum_iv(acc.cnt);
+#define KVC_PRESEL_STEP(M) \
+    step(lane_xor<M>((uint32_t)(acc.best >> 32)), lane_xor<M>((uint32_t)acc.best), \
+         (int)lane_xor<M>((uint32_t)acc.arg))
+    KVC_PRESEL_STEP(32);
+    KVC_PRESEL_STEP(16);
+    KVC_PRESEL_STEP(8);
+    KVC_PRESEL_STEP(4);
+    KVC_PRESEL_STEP(2);
+    KVC_PRESEL_STEP(1);
+#undef KVC_PRESEL_STEP
     if (lane == 0) {
         PreselRecord rec;
         rec.ncand = acc.cnt;
@@ -285,10 +292,10 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float m = mx[i];
-        m = fmaxf(m, __shfl_xor(m, 8, 64));
-        m = fmaxf(m, __shfl_xor(m, 4, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, lane_xor_f<8>(m));
+        m = fmaxf(m, lane_xor_f<4>(m));
+        m = fmaxf(m, lane_xor_f<2>(m));
+        m = fmaxf(m, lane_xor_f<1>(m));
         if (col == 0 && 4 * r + i < G) sm.wred[w][4 * r + i] = m;
     }
     __syncthreads();
@@ -354,9 +361,9 @@ void split_kernel(AttnArgs a) {
 #pragma unroll
         for (int m8 = 0; m8 < 8; ++m8)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) oacc[m8][ii] += __shfl_xor(oacc[m8][ii], 32, 64);
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+            for (int ii = 0; ii < 4; ++ii) oacc[m8][ii] = pair_sum32(oacc[m8][ii]);
+    lsum = pair_sum16(lsum);
+    lsum = pair_sum32(lsum);
     if (lane < G) sm.wred[w][lane] = lsum;
     __syncthreads();   // weights in lg are final, partial row sums written
 
