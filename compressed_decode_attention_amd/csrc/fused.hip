@@ -412,16 +412,96 @@ void fused_kernel(FusedArgs fa) {
     }
     __syncthreads();
 
-    // ---------------- H2O: accumulated attention with the final normaliser
+    // ---------------- H2O: accumulated attention with the final normaliser.
+    // Contiguous caches, step mode: the same pass classifies every entry for
+    // the selection and keeps the thread's counts and worst candidate in
+    // registers (the staging bytes, where the flags and keys would go, still
+    // hold the partial outputs); each wave's summary goes out before the
+    // output pass's barrier, so the usual single eviction needs no pass and
+    // no barrier of its own.  Paged caches classify after the output pass, as
+    // the registers held across it would spill there; both orders select the
+    // same entries.
+    constexpr bool kFold = MODE != kModeAttn && !PAGED;
+    const SelectArgs &sa = fa.sel;
+    const int L = sm.posmax + 1;
+    int ncand = 0, ndrop = 0, dslot = -1, barg = -1;
+    uint64_t best = ~0ull;
+    // the entry's class; a candidate's ranking key (smaller is evicted first)
+    auto classify = [&](int j, float sj, uint32_t &key) -> uint8_t {
+        const int32_t p = pos_s[j];
+        uint8_t k = kKeep;
+        if (sa.kind == KVC_POLICY_STREAMING)
+            k = (p < sa.n_sink || (int64_t)p >= (int64_t)L - sa.n_recent) ? kKeep : kDrop;
+        else if (sa.kind == KVC_POLICY_H2O)
+            k = ((int64_t)p >= (int64_t)L - sa.n_recent) ? kKeep : kCand;
+        else if (sa.kind == KVC_POLICY_RANDOM)
+            k = (p < sa.prompt_len) ? kKeep : kCand;
+        if (k == kCand)
+            key = (sa.kind == KVC_POLICY_H2O)
+                      ? float_order_bits(sj)
+                      : ~philox_word0((uint32_t)p, sa.step, (uint32_t)h, (uint32_t)b,
+                                      (uint32_t)(sa.seed & 0xFFFFFFFFu), (uint32_t)(sa.seed >> 32));
+        return k;
+    };
+    auto tally = [&](int j, float sj) {
+        uint32_t key = 0;
+        const uint8_t k = classify(j, sj, key);
+        if (k == kCand) {
+            ++ncand;
+            const uint64_t wd = rank_word(key, pos_s[j]);
+            if (barg < 0 || wd < best) {
+                best = wd;
+                barg = j;
+            }
+        } else if (k == kDrop) {
+            ++ndrop;
+            dslot = max(dslot, j);
+        }
+    };
     if (h2o) {
         for (int j = tid; j < T; j += kFThreads) {
             float ps = 0.f;
             const int jc = lg_col(j);
             const int wj = (j >> 4) % kFWaves;   // the wave that weighed tile j / 16
             for (int g = 0; g < G; ++g) ps += lg[g * LD + jc] * sm.wmax[wj][g];
-            sc_s[j] = score_update((j < n) ? sc_s[j] : 0.f, ps, a.decay);
+            const float sj = score_update((j < n) ? sc_s[j] : 0.f, ps, a.decay);
+            sc_s[j] = sj;
+            if constexpr (kFold) tally(j, sj);
         }
+    } else if constexpr (kFold) {
+        for (int j = tid; j < T; j += kFThreads) tally(j, sc_s[j]);
     }
+    // each wave's counts and worst candidate into the small LDS block
+    auto wave_summary = [&]() {
+        ncand = wave_sum_iv(ncand);
+        ndrop = wave_sum_iv(ndrop);
+        dslot = wave_max_iv(dslot);
+        auto arg_step = [&](uint32_t hi, uint32_t lo, int oa) {
+            const uint64_t ob = ((uint64_t)hi << 32) | lo;
+            if (ob < best || (ob == best && (unsigned)oa < (unsigned)barg)) {
+                best = ob;
+                barg = oa;
+            }
+        };
+#define KVC_ARG_STEP(M) \
+    arg_step(lane_xor<M>((uint32_t)(best >> 32)), lane_xor<M>((uint32_t)best), (int)lane_xor<M>((uint32_t)barg))
+        KVC_ARG_STEP(32);
+        KVC_ARG_STEP(16);
+        KVC_ARG_STEP(8);
+        KVC_ARG_STEP(4);
+        KVC_ARG_STEP(2);
+        KVC_ARG_STEP(1);
+#undef KVC_ARG_STEP
+        if (lane == 0) {
+            sm.r_nc[w] = ncand;
+            sm.r_nd[w] = ndrop;
+            sm.r_ds[w] = dslot;
+            sm.r_arg[w] = barg;
+            sm.mn_hi[w] = (uint32_t)(best >> 32);
+            sm.mn_lo[w] = (uint32_t)best;
+        }
+    };
+    if constexpr (kFold) wave_summary();
 
     // ---------------- output: sum the four waves' partial P.V, normalise.
     // The partials go to the staging bytes when they fit (G <= 8), else to
@@ -478,70 +558,30 @@ void fused_kernel(FusedArgs fa) {
         return;
     }
 
-    // ================= selection on the LDS copies =================
-    // One pass classifies every entry, draws the candidates' ranking keys and
-    // finds the worst candidate (smallest ranking word) and a dropped entry.
-    const SelectArgs &sa = fa.sel;
-    __syncthreads();   // the output pass is done with the staging bytes
-    const int L = sm.posmax + 1;
-    int ncand = 0, ndrop = 0, dslot = -1, barg = -1;
-    uint64_t best = ~0ull;
-    for (int j = tid; j < T; j += kFThreads) {
-        const int32_t p = pos_s[j];
-        uint8_t k = kKeep;
-        if (sa.kind == KVC_POLICY_STREAMING)
-            k = (p < sa.n_sink || (int64_t)p >= (int64_t)L - sa.n_recent) ? kKeep : kDrop;
-        else if (sa.kind == KVC_POLICY_H2O)
-            k = ((int64_t)p >= (int64_t)L - sa.n_recent) ? kKeep : kCand;
-        else if (sa.kind == KVC_POLICY_RANDOM)
-            k = (p < sa.prompt_len) ? kKeep : kCand;
-        if (k == kCand) {
-            const uint32_t key = (sa.kind == KVC_POLICY_H2O)
-                                     ? float_order_bits(sc_s[j])
-                                     : ~philox_word0((uint32_t)p, sa.step, (uint32_t)h, (uint32_t)b,
-                                                     (uint32_t)(sa.seed & 0xFFFFFFFFu),
-                                                     (uint32_t)(sa.seed >> 32));
-            key_s[j] = key;
-            ++ncand;
-            const uint64_t wd = rank_word(key, p);
-            if (barg < 0 || wd < best) {
-                best = wd;
-                barg = j;
+    // ================= selection =================
+    if constexpr (!kFold) {
+        __syncthreads();   // the output pass is done with the staging bytes
+        for (int j = tid; j < T; j += kFThreads) {
+            uint32_t key = 0;
+            const uint8_t k = classify(j, sc_s[j], key);
+            if (k == kCand) {
+                key_s[j] = key;
+                ++ncand;
+                const uint64_t wd = rank_word(key, pos_s[j]);
+                if (barg < 0 || wd < best) {
+                    best = wd;
+                    barg = j;
+                }
+            } else if (k == kDrop) {
+                ++ndrop;
+                dslot = max(dslot, j);
             }
-        } else if (k == kDrop) {
-            ++ndrop;
-            dslot = max(dslot, j);
+            flg_s[j] = k;
         }
-        flg_s[j] = k;
+        wave_summary();
+        __syncthreads();
     }
-    ncand = wave_sum_iv(ncand);
-    ndrop = wave_sum_iv(ndrop);
-    dslot = wave_max_iv(dslot);
-    auto arg_step = [&](uint32_t hi, uint32_t lo, int oa) {
-        const uint64_t ob = ((uint64_t)hi << 32) | lo;
-        if (ob < best || (ob == best && (unsigned)oa < (unsigned)barg)) {
-            best = ob;
-            barg = oa;
-        }
-    };
-#define KVC_ARG_STEP(M) \
-    arg_step(lane_xor<M>((uint32_t)(best >> 32)), lane_xor<M>((uint32_t)best), (int)lane_xor<M>((uint32_t)barg))
-    KVC_ARG_STEP(32);
-    KVC_ARG_STEP(16);
-    KVC_ARG_STEP(8);
-    KVC_ARG_STEP(4);
-    KVC_ARG_STEP(2);
-    KVC_ARG_STEP(1);
-#undef KVC_ARG_STEP
-    if (lane == 0) {
-        sm.r_nc[w] = ncand;
-        sm.r_nd[w] = ndrop;
-        sm.r_ds[w] = dslot;
-        sm.r_arg[w] = barg;
-        sm.mn_hi[w] = (uint32_t)(best >> 32);
-        sm.mn_lo[w] = (uint32_t)best;
-    }
-    __syncthreads();
+    // the waves' summaries
     ncand = 0;
     ndrop = 0;
     dslot = -1;
@@ -581,7 +621,19 @@ void fused_kernel(FusedArgs fa) {
         return;
     }
 
-    // ---- general case: finish the candidates' flags, then hole-fill
+    // ---- general case: flags and keys into the staging bytes (once every
+    // wave is done with them) when the tally did not write them; then finish
+    // the candidates' flags and hole-fill
+    if constexpr (kFold) {
+        __syncthreads();
+        for (int j = tid; j < T; j += kFThreads) {
+            uint32_t key = 0;
+            const uint8_t k = classify(j, sc_s[j], key);
+            if (k == kCand) key_s[j] = key;
+            flg_s[j] = k;
+        }
+        __syncthreads();
+    }
     if (extra > 0) {
         if (want <= 0) {
             for (int j = tid; j < T; j += kFThreads)
