@@ -521,11 +521,14 @@ void fused_kernel(FusedArgs fa) {
         }
         __syncthreads();
         float *outp = a.out + ((size_t)b * c.Hq + (size_t)h * G) * kHD;
-        for (int e = tid; e < G * kHD; e += kFThreads) {
+        // four consecutive elements of one head per thread (16-byte LDS
+        // reads and global stores; the partials' bases are 16-byte aligned)
+        for (int e = 4 * tid; e < G * kHD; e += 4 * kFThreads) {
             const int g = e / kHD;
-            float o = opart[e] * sm.wmax[0][g];
-            for (int v = 1; v < kFWaves; ++v) o += opart[(size_t)v * G * kHD + e] * sm.wmax[v][g];
-            outp[e] = o;
+            f32x4_t o = *reinterpret_cast<const f32x4_t *>(opart + e) * sm.wmax[0][g];
+            for (int v = 1; v < kFWaves; ++v)
+                o += *reinterpret_cast<const f32x4_t *>(opart + (size_t)v * G * kHD + e) * sm.wmax[v][g];
+            *reinterpret_cast<f32x4_t *>(outp + e) = o;
         }
     }
 
