@@ -463,7 +463,19 @@ void fused_kernel(FusedArgs fa) {
             float ps = 0.f;
             const int jc = lg_col(j);
             const int wj = (j >> 4) % kFWaves;   // the wave that weighed tile j / 16
-            for (int g = 0; g < G; ++g) ps += lg[g * LD + jc] * sm.wmax[wj][g];
+            if constexpr (PACK2) {
+                // G <= 8: every head's load in flight at once; heads past G
+                // leave the sum as it is (the same fused multiply-adds in the
+                // same order as the loop below)
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    const int gg = g < G ? g : 0;
+                    const float t = __builtin_fmaf(lg[gg * LD + jc], sm.wmax[wj][gg], ps);
+                    ps = g < G ? t : ps;
+                }
+            } else {
+                for (int g = 0; g < G; ++g) ps += lg[g * LD + jc] * sm.wmax[wj][g];
+            }
             const float sj = score_update((j < n) ? sc_s[j] : 0.f, ps, a.decay);
             sc_s[j] = sj;
             if constexpr (kFold) tally(j, sj);
