@@ -38,12 +38,12 @@ HBM_PEAK_GBS = 8000.0
 FETCH_SCALE = 1048576.0 / 524303.75
 WRITE_SCALE = 1.0
 PROFILED_TRAFFIC = [
-    {"sources_digest": "a52b22067e33f7fb", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "bf16", "fetch_kib": 538452.93, "write_kib": 26995.97},
-    {"sources_digest": "a52b22067e33f7fb", "workload": "heavy_load_b512_l2048", "policy": "streaming",
-     "kv_dtype": "bf16", "fetch_kib": 534097.58, "write_kib": 18688.17},
-    {"sources_digest": "a52b22067e33f7fb", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "e5m2", "fetch_kib": 276353.16, "write_kib": 25968.02},
+    {"sources_digest": "b70eef31641db5a0", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "bf16", "fetch_kib": 538454.28, "write_kib": 26996.20},
+    {"sources_digest": "b70eef31641db5a0", "workload": "heavy_load_b512_l2048", "policy": "streaming",
+     "kv_dtype": "bf16", "fetch_kib": 534103.07, "write_kib": 18688.10},
+    {"sources_digest": "b70eef31641db5a0", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "e5m2", "fetch_kib": 276358.52, "write_kib": 25968.01},
 ]
 
 
