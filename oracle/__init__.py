@@ -72,6 +72,16 @@ def lib():
         L.orc_select_random.argtypes = [ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
                                         ctypes.c_uint32, c_u8p]
+        L.orc_random_keys.restype = None
+        L.orc_random_keys.argtypes = [ctypes.c_int64, c_i32p, ctypes.c_uint64, ctypes.c_uint32,
+                                      ctypes.c_uint32, ctypes.c_uint32,
+                                      ctypes.POINTER(ctypes.c_uint32)]
+        L.orc_random_replay.restype = ctypes.c_int32
+        L.orc_random_replay.argtypes = [ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_uint32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint32,
+                                        ctypes.c_uint32, c_i32p, c_i32p, ctypes.c_int64, c_i32p,
+                                        c_i32p]
         L.orc_n_keep.restype = ctypes.c_int64
         L.orc_n_keep.argtypes = [ctypes.c_int64, ctypes.c_double]
         c_fp = ctypes.POINTER(ctypes.c_float)
@@ -136,6 +146,35 @@ def philox4x32_10(ctr, key) -> np.ndarray:
 
 def random_key(pos: int, seed: int, seq: int, head: int, step: int) -> int:
     return int(lib().orc_random_key(pos, seed, seq, head, step))
+
+
+def random_keys(pos, seed: int, seq: int, head: int, step: int) -> np.ndarray:
+    """Random-eviction key of every position in pos (uint32 array)."""
+    p = np.ascontiguousarray(pos, np.int32)
+    out = np.empty(p.size, np.uint32)
+    lib().orc_random_keys(p.size, _p(p, ctypes.c_int32), seed, seq, head, step,
+                          _p(out, ctypes.c_uint32))
+    return out.reshape(np.shape(pos))
+
+
+def random_replay(pos0, cap: int, steps: int, first_pos: int, first_step: int, prompt_len: int,
+                  n_keep: int, seed: int, seq: int, head: int):
+    """Positions-only replay of per-head random eviction over `steps` decode
+    steps of one unit (see orc_random_replay): returns (n_evicted [steps],
+    evicted positions in step order, final kept positions ascending)."""
+    p0 = np.ascontiguousarray(pos0, np.int32)
+    nev = np.zeros(steps, np.int32)
+    ev_cap = max(steps + p0.size, 1)
+    ev = np.empty(ev_cap, np.int32)
+    out = np.empty(max(cap, 1), np.int32)
+    n_out = np.zeros(1, np.int32)
+    rc = lib().orc_random_replay(p0.size, _p(p0, ctypes.c_int32), cap, steps, first_pos,
+                                 first_step, prompt_len, n_keep, seed, seq, head,
+                                 _p(nev, ctypes.c_int32), _p(ev, ctypes.c_int32), ev_cap,
+                                 _p(out, ctypes.c_int32), _p(n_out, ctypes.c_int32))
+    if rc != 0:
+        raise ValueError("random_replay: the kept set outgrew cap")
+    return nev, ev[:int(nev.sum())].copy(), out[:int(n_out[0])].copy()
 
 
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: Optional[float] = None,

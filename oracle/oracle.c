@@ -314,6 +314,88 @@ ORC_API void orc_select_random(int32_t n, const int32_t *pos, int32_t prompt_len
     free(c);
 }
 
+/* Random-eviction keys of n cached tokens of one unit: key[i] is
+ * orc_random_key(pos[i], seed, seq, head, step), one token at a time. */
+ORC_API void orc_random_keys(int64_t n, const int32_t *pos, uint64_t seed, uint32_t seq,
+                             uint32_t head, uint32_t step, uint32_t *key)
+{
+    for (int64_t i = 0; i < n; ++i)
+        key[i] = orc_random_key(pos[i], seed, seq, head, step);
+}
+
+/* Positions-only replay of per-head random eviction over a run of decode
+ * steps of one unit (sequence seq, kv head head): the kept set depends on
+ * positions and keys only, never on K, V or the queries, so a whole trace
+ * can be followed without attention.  The unit starts with the n0 positions
+ * pos0 (any order).  Step t = 0 .. steps-1 appends the token at position
+ * first_pos + t (a step attends first, then evicts), then keeps what
+ * orc_select_random keeps with step number first_step + t.  The positions
+ * it drops are appended to evicted[] (at most ev_cap in all) and their count
+ * goes to n_evicted[t].  The final kept positions, ascending, go to pos_out
+ * (room for cap) and their count to *n_out.  Returns 0, or -1 when the kept
+ * set would exceed cap or the drops ev_cap (nothing after that is valid).
+ * [P2] "scorers are overrated" (evict uniformly inside each head every
+ * time the cache is over budget), "six steps" (pin the prompt). */
+ORC_API int32_t orc_random_replay(int32_t n0, const int32_t *pos0, int32_t cap, int32_t steps,
+                                  int32_t first_pos, uint32_t first_step, int32_t prompt_len,
+                                  int32_t n_keep, uint64_t seed, uint32_t seq, uint32_t head,
+                                  int32_t *n_evicted, int32_t *evicted, int64_t ev_cap,
+                                  int32_t *pos_out, int32_t *n_out)
+{
+    int32_t *cur = (int32_t *)malloc(sizeof(int32_t) * (size_t)(cap + 1));
+    uint8_t *keep = (uint8_t *)malloc((size_t)(cap + 1));
+    int32_t n = 0;
+    int64_t ne = 0;
+    int32_t rc = 0;
+    if (n0 > cap) {
+        rc = -1;
+        goto done;
+    }
+    for (int32_t i = 0; i < n0; ++i)
+        cur[n++] = pos0[i];
+    for (int32_t t = 0; t < steps; ++t) {
+        cur[n++] = first_pos + t;                       /* the new token */
+        orc_select_random(n, cur, prompt_len, n_keep, seed, seq, head,
+                          first_step + (uint32_t)t, keep);
+        int32_t m = 0, dropped = 0;
+        for (int32_t j = 0; j < n; ++j) {
+            if (keep[j]) {
+                cur[m++] = cur[j];
+            } else {
+                if (ne >= ev_cap) {
+                    rc = -1;
+                    goto done;
+                }
+                evicted[ne++] = cur[j];
+                ++dropped;
+            }
+        }
+        n_evicted[t] = dropped;
+        n = m;
+        if (n > cap) {
+            rc = -1;
+            goto done;
+        }
+    }
+    /* ascending positions: insertion sort, plain and obviously correct */
+    for (int32_t i = 1; i < n; ++i) {
+        const int32_t x = cur[i];
+        int32_t j = i - 1;
+        while (j >= 0 && cur[j] > x) {
+            cur[j + 1] = cur[j];
+            --j;
+        }
+        cur[j + 1] = x;
+    }
+    for (int32_t i = 0; i < n; ++i)
+        pos_out[i] = cur[i];
+    *n_out = n;
+done:
+    free(cur);
+    free(keep);
+    return rc;
+}
+
 /* n_keep of the one-shot hook: max(1, int(N * keep_ratio)) with the product
  * taken in double and truncated, clamped to N (taking the first n_keep of a
  * permutation of N cannot give more than N); N <= 0 gives 0 (nothing to

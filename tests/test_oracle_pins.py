@@ -389,6 +389,68 @@ def test_random_keeps_the_smallest_keys():
     assert set(pos[kp]) == set(pos[keys <= thr])
 
 
+def test_random_equal_keys_go_to_the_lower_position():
+    # Word 0 of the generator is 32 bits: among 2^18 positions of one (seed,
+    # sequence, head, step) several pairs share a key.  With the pair at the
+    # edge of the kept set, the lower position is kept and the higher one
+    # evicted, whatever their slot order (a total order on (key, position)).
+    from key_ties import find_ties
+    seed, seq, head, step, prompt = 0x5EED, 3, 5, 41, 16
+    pos, keys, pairs = find_ties(seed, seq, head, step, prompt)
+    assert pairs, "a 2^18-position search holds a tied pair"
+    for W, lo, hi in pairs[:3]:
+        assert oracle.random_key(lo, seed, seq, head, step) == W
+        assert oracle.random_key(hi, seed, seq, head, step) == W and lo < hi
+        below = pos[keys < W][:40]
+        above = pos[keys > W][:7]
+        pinned = np.arange(prompt, dtype=np.int32)
+        for order in ("lo_first", "hi_first"):
+            pair = [lo, hi] if order == "lo_first" else [hi, lo]
+            cand = np.concatenate([pinned, above, pair, below]).astype(np.int32)
+            k = oracle.select_random(cand, prompt, below.size + 1, seed, seq, head, step)
+            kept = set(cand[k].tolist())
+            assert lo in kept and hi not in kept, (order, W, lo, hi)
+            assert set(pinned.tolist()) | set(below.tolist()) <= kept
+            assert not (set(above.tolist()) & kept)
+            # one more kept slot keeps both, one fewer keeps neither
+            k2 = oracle.select_random(cand, prompt, below.size + 2, seed, seq, head, step)
+            assert {lo, hi} <= set(cand[k2].tolist())
+            k0 = oracle.select_random(cand, prompt, below.size, seed, seq, head, step)
+            assert not ({lo, hi} & set(cand[k0].tolist()))
+
+
+def test_random_replay_schedule_and_survival():
+    # Positions-only replay of the long-trace schedule (prompt pinned, a fixed
+    # budget of n_keep generated tokens, one token per step): nothing leaves
+    # while the cache is under budget, then exactly one generated token per
+    # step, the one with the largest key of that step; the prompt never
+    # leaves.  Each steady step evicts one of n_keep + 1 candidates uniformly,
+    # so a token present at the start of the steady phase survives S more
+    # steps with probability (n_keep / (n_keep + 1))^S.
+    prompt, n_keep, grow, S = 32, 64, 64, 64
+    surv = []
+    for seed in range(60):
+        nev, ev, fin = oracle.random_replay(np.arange(prompt), prompt + n_keep + 1, grow + S,
+                                            prompt, 1, prompt, n_keep, seed, 2, 1)
+        assert nev[:grow].sum() == 0 and np.all(nev[grow:] == 1)
+        assert fin.size == prompt + n_keep and np.all(fin[:prompt] == np.arange(prompt))
+        assert np.all(ev >= prompt)
+        if seed < 3:
+            # the evicted token has the largest key of its step's candidates
+            kept = list(range(prompt + grow))
+            for t, e in zip(range(grow, grow + S), ev):
+                kept.append(prompt + t)
+                c = np.array([p for p in kept if p >= prompt], np.int32)
+                kk = oracle.random_keys(c, seed, 2, 1, t + 1).astype(np.int64)
+                assert int(c[kk == kk.max()].max()) == int(e)
+                kept.remove(int(e))
+            assert sorted(kept) == fin.tolist()
+        surv.append(int(((fin >= prompt) & (fin < prompt + grow)).sum()))
+    want = grow * (n_keep / (n_keep + 1)) ** S
+    sd = math.sqrt(grow * 0.37 * 0.63 / len(surv)) * 2   # loose: survivals are not independent
+    assert abs(np.mean(surv) - want) < 4 * sd, (np.mean(surv), want)
+
+
 def test_random_inclusion_frequency_is_uniform():
     # over many seeds each candidate survives with probability k / N
     N, k, trials = 40, 10, 2000
