@@ -167,6 +167,24 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _req(t: Optional[torch.Tensor], name: str, cache, dtype, numel: int,
+         optional: bool = False) -> Optional[int]:
+    """Pointer of a tensor argument after checking that it lives on the
+    cache's device with the expected dtype and element count (the library
+    reads and writes exactly that many elements through the pointer)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} must not be None")
+    if t.device != cache.device:
+        raise ValueError(f"{name} is on {t.device}, the cache on {cache.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return _ptr(t)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -209,6 +227,27 @@ class KvCache:
     @property
     def group(self) -> int:
         return self.q_heads // self.kv_heads
+
+    @property
+    def device(self) -> torch.device:
+        return self.k.device
+
+    def _step_ptrs(self, new_pos, q, k_new, v_new, out, scores):
+        """Checked pointers of a decode step's tensors."""
+        act = ACT_TORCH_DTYPE[self.dtype]
+        B, Hq, Hkv, D = self.batch, self.q_heads, self.kv_heads, self.head_dim
+        return (_req(new_pos, "new_pos", self, torch.int32, B),
+                _req(q, "q", self, act, B * Hq * D),
+                _req(k_new, "k_new", self, act, B * Hkv * D),
+                _req(v_new, "v_new", self, act, B * Hkv * D),
+                _req(out, "out", self, torch.float32, B * Hq * D),
+                _req(scores, "scores", self, torch.float32, B * Hkv * self.capacity,
+                     optional=True))
+
+    def _keep_ptrs(self, keep_slots, n_out):
+        B, H = self.batch, self.kv_heads
+        return (_req(keep_slots, "keep_slots", self, torch.int32, B * H * self.capacity),
+                _req(n_out, "n_out", self, torch.int32, B * H))
 
     def c(self) -> kvc_cache:
         if self._c is None:
@@ -275,9 +314,11 @@ def _scale(cache: KvCache, scale):
     return 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
 
 
-def _ws(workspace):
+def _ws(workspace, cache=None):
     if workspace is None:
         return None, 0
+    if cache is not None and workspace.device != cache.device:
+        raise ValueError(f"workspace is on {workspace.device}, the cache on {cache.device}")
     return _ptr(workspace), workspace.numel() * workspace.element_size()
 
 
@@ -287,10 +328,11 @@ def _ws(workspace):
 
 def decode_attn(cache: KvCache, new_pos, q, k_new, v_new, out, scores=None, scale=None,
                 max_len_hint: int = 0, workspace=None, stream=None, score_decay: float = 0.0):
-    wp, wn = _ws(workspace)
-    _check(_lib.kvc_decode_attn(ctypes.byref(cache.c()), _ptr(new_pos), _ptr(q), _ptr(k_new),
-                                _ptr(v_new), _ptr(out), _ptr(scores), _scale(cache, scale),
-                                score_decay, max_len_hint, wp, wn, _stream(stream)))
+    wp, wn = _ws(workspace, cache)
+    pp, qp, kp, vp, op, sp = cache._step_ptrs(new_pos, q, k_new, v_new, out, scores)
+    _check(_lib.kvc_decode_attn(ctypes.byref(cache.c()), pp, qp, kp, vp, op, sp,
+                                _scale(cache, scale), score_decay, max_len_hint, wp, wn,
+                                _stream(stream)))
 
 
 def h2o_accumulate(cache: KvCache, q_rows, m_rows: int, scores, q_pos=None, scale=None,
@@ -300,41 +342,54 @@ def h2o_accumulate(cache: KvCache, q_rows, m_rows: int, scores, q_pos=None, scal
     one fp32 log-sum-exp per row and head; it is allocated here if not given."""
     if workspace is None:
         workspace = cache.prompt_workspace(m_rows)
-    wp, wn = _ws(workspace)
-    _check(_lib.kvc_h2o_accumulate(ctypes.byref(cache.c()), _ptr(q_rows), m_rows, _ptr(q_pos),
-                                   _ptr(scores), _scale(cache, scale), wp, wn, _stream(stream)))
+    wp, wn = _ws(workspace, cache)
+    B, Hq, D = cache.batch, cache.q_heads, cache.head_dim
+    qr = _req(q_rows, "q_rows", cache, ACT_TORCH_DTYPE[cache.dtype], B * m_rows * Hq * D)
+    qpp = _req(q_pos, "q_pos", cache, torch.int32, B * m_rows, optional=True)
+    sp = _req(scores, "scores", cache, torch.float32, B * cache.kv_heads * cache.capacity)
+    _check(_lib.kvc_h2o_accumulate(ctypes.byref(cache.c()), qr, m_rows, qpp, sp,
+                                   _scale(cache, scale), wp, wn, _stream(stream)))
 
 
 def evict_streaming(cache: KvCache, n_sink: int, n_recent: int, keep_slots, n_out, stream=None):
-    _check(_lib.kvc_evict_streaming(ctypes.byref(cache.c()), n_sink, n_recent, _ptr(keep_slots),
-                                    _ptr(n_out), _stream(stream)))
+    kp, np_ = cache._keep_ptrs(keep_slots, n_out)
+    _check(_lib.kvc_evict_streaming(ctypes.byref(cache.c()), n_sink, n_recent, kp, np_,
+                                    _stream(stream)))
 
 
 def evict_h2o(cache: KvCache, scores, n_heavy: int, n_recent: int, keep_slots, n_out,
               stream=None):
-    _check(_lib.kvc_evict_h2o(ctypes.byref(cache.c()), _ptr(scores), n_heavy, n_recent,
-                              _ptr(keep_slots), _ptr(n_out), _stream(stream)))
+    kp, np_ = cache._keep_ptrs(keep_slots, n_out)
+    sp = _req(scores, "scores", cache, torch.float32,
+              cache.batch * cache.kv_heads * cache.capacity)
+    _check(_lib.kvc_evict_h2o(ctypes.byref(cache.c()), sp, n_heavy, n_recent, kp, np_,
+                              _stream(stream)))
 
 
 def evict_random(cache: KvCache, prompt_len: int, n_keep: int, seed: int, step: int, keep_slots,
                  n_out, stream=None):
-    _check(_lib.kvc_evict_random(ctypes.byref(cache.c()), prompt_len, n_keep, seed, step,
-                                 _ptr(keep_slots), _ptr(n_out), _stream(stream)))
+    kp, np_ = cache._keep_ptrs(keep_slots, n_out)
+    _check(_lib.kvc_evict_random(ctypes.byref(cache.c()), prompt_len, n_keep, seed, step, kp,
+                                 np_, _stream(stream)))
 
 
 def compact(cache: KvCache, keep_slots, n_out, scores=None, ordered_dst: Optional[KvCache] = None,
             stream=None):
     dst = ctypes.byref(ordered_dst.c()) if ordered_dst is not None else None
-    _check(_lib.kvc_compact(ctypes.byref(cache.c()), _ptr(keep_slots), _ptr(n_out), _ptr(scores),
-                            dst, _stream(stream)))
+    if ordered_dst is not None and ordered_dst.device != cache.device:
+        raise ValueError(f"ordered_dst is on {ordered_dst.device}, the cache on {cache.device}")
+    kp, np_ = cache._keep_ptrs(keep_slots, n_out)
+    sp = _req(scores, "scores", cache, torch.float32,
+              cache.batch * cache.kv_heads * cache.capacity, optional=True)
+    _check(_lib.kvc_compact(ctypes.byref(cache.c()), kp, np_, sp, dst, _stream(stream)))
 
 
 def decode_step(cache: KvCache, policy: kvc_policy, step: int, new_pos, q, k_new, v_new, out,
                 scores=None, scale=None, max_len_hint: int = 0, workspace=None, stream=None):
-    wp, wn = _ws(workspace)
-    _check(_lib.kvc_decode_step(ctypes.byref(cache.c()), ctypes.byref(policy), step,
-                                _ptr(new_pos), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
-                                _ptr(scores), _scale(cache, scale), max_len_hint, wp, wn,
+    wp, wn = _ws(workspace, cache)
+    pp, qp, kp, vp, op, sp = cache._step_ptrs(new_pos, q, k_new, v_new, out, scores)
+    _check(_lib.kvc_decode_step(ctypes.byref(cache.c()), ctypes.byref(policy), step, pp, qp, kp,
+                                vp, op, sp, _scale(cache, scale), max_len_hint, wp, wn,
                                 _stream(stream)))
 
 
@@ -379,6 +434,10 @@ class KiviCache:
     def group(self) -> int:
         return self.q_heads // self.kv_heads
 
+    @property
+    def device(self) -> torch.device:
+        return self.k_codes.device
+
     def c(self) -> kvc_kivi_cache:
         if self._c is None:
             c = kvc_kivi_cache()
@@ -401,15 +460,23 @@ class KiviCache:
 def kivi_prefill(cache: KiviCache, k, v, lengths, stream=None):
     """k, v [batch, kv_heads, max_len, head_dim] bf16; lengths [batch] int32 (device)."""
     max_len = k.shape[2]
-    _check(_lib.kvc_kivi_prefill(ctypes.byref(cache.c()), _ptr(k), _ptr(v), max_len,
-                                 _ptr(lengths), _stream(stream)))
+    n = cache.batch * cache.kv_heads * max_len * cache.head_dim
+    kp = _req(k, "k", cache, torch.bfloat16, n)
+    vp = _req(v, "v", cache, torch.bfloat16, n)
+    lp = _req(lengths, "lengths", cache, torch.int32, cache.batch)
+    _check(_lib.kvc_kivi_prefill(ctypes.byref(cache.c()), kp, vp, max_len, lp, _stream(stream)))
 
 
 def kivi_decode(cache: KiviCache, q, k_new, v_new, out, scale=None, max_quant_hint: int = 0,
                 workspace=None, stream=None):
     if workspace is None:
         workspace = cache.workspace(max_quant_hint)
-    wp, wn = _ws(workspace)
+    wp, wn = _ws(workspace, cache)
     sc = 1.0 / math.sqrt(cache.head_dim) if scale is None else float(scale)
-    _check(_lib.kvc_kivi_decode(ctypes.byref(cache.c()), _ptr(q), _ptr(k_new), _ptr(v_new),
-                                _ptr(out), sc, max_quant_hint, wp, wn, _stream(stream)))
+    B, Hq, Hkv, D = cache.batch, cache.q_heads, cache.kv_heads, cache.head_dim
+    qp = _req(q, "q", cache, torch.bfloat16, B * Hq * D)
+    kp = _req(k_new, "k_new", cache, torch.bfloat16, B * Hkv * D)
+    vp = _req(v_new, "v_new", cache, torch.bfloat16, B * Hkv * D)
+    op = _req(out, "out", cache, torch.float32, B * Hq * D)
+    _check(_lib.kvc_kivi_decode(ctypes.byref(cache.c()), qp, kp, vp, op, sc, max_quant_hint, wp,
+                                wn, _stream(stream)))

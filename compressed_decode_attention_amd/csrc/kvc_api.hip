@@ -238,6 +238,11 @@ kvc_status check_attn_args(const kvc_cache *c, const int32_t *new_pos, const voi
         return fail(KVC_ERR_INVALID_ARG, "%s: new_pos, q, k_new, v_new and out must not be NULL",
                     what);
     if (!isfinite(scale)) return fail(KVC_ERR_INVALID_ARG, "%s: scale is not finite", what);
+    // the matrix-core kernels read q, k_new and v_new and write out in
+    // 16-byte pieces
+    if ((uintptr_t)q % 16 || (uintptr_t)k_new % 16 || (uintptr_t)v_new % 16 || (uintptr_t)out % 16)
+        return fail(KVC_ERR_INVALID_ARG, "%s: q, k_new, v_new and out must be 16-byte aligned",
+                    what);
     return KVC_OK;
 }
 

@@ -190,6 +190,8 @@ size_t kvc_workspace_bytes(const kvc_cache *c, int32_t max_len_hint);
  *   q        [batch, q_heads, head_dim]  dtype
  *   k_new,v_new [batch, kv_heads, head_dim] dtype
  *   out      [batch, q_heads, head_dim] fp32
+ *            q, k_new, v_new and out must be 16-byte aligned (they are read
+ *            and written in 16-byte pieces); KVC_ERR_INVALID_ARG otherwise.
  *   score_decay  0 for the sums above; 0 < score_decay < 1 updates each score
  *            as s <- score_decay * s + (1 - score_decay) * sum_i p_i instead
  *            (decayed attention activity, see kvc_policy.decay); other values

@@ -110,6 +110,41 @@ def test_attention_argument_errors():
     assert need > 0
     assert _attn(_fake_cache(), ws=0x100000, nbytes=need - 1) == kvc.ERR_WORKSPACE
     assert _attn(_fake_cache(), ws=0x100010, nbytes=need) == kvc.ERR_WORKSPACE  # misaligned
+    # q, k_new, v_new and out are read and written in 16-byte pieces
+    for name, addr in (("q", 0x2008), ("k_new", 0x3004), ("v_new", 0x4002), ("out", 0x5004)):
+        assert _attn(_fake_cache(), ws=0x100000, nbytes=need, **{name: addr}) == \
+            kvc.ERR_INVALID_ARG, name
+        assert b"16-byte aligned" in kvc.library().kvc_last_error()
+
+
+def test_binding_checks_tensor_dtype_and_size_before_the_call():
+    # host tensors stand in for device ones: the checks run before any call
+    c = kvc.KvCache(2, 8, 2, 128, 16, kvc.BF16, device="cpu")
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    pos = torch.zeros(B, dtype=torch.int32)
+    q = torch.zeros((B, Hq, D), dtype=torch.bfloat16)
+    kn = torch.zeros((B, Hkv, D), dtype=torch.bfloat16)
+    out = torch.zeros((B, Hq, D), dtype=torch.float32)
+    bad = [
+        dict(q=q.float()),                                    # wrong dtype
+        dict(q=q[:1]),                                        # too few elements
+        dict(out=out.to(torch.bfloat16)),                     # a bf16 out would be overrun
+        dict(new_pos=pos.long()),
+        dict(k_new=torch.zeros((B, Hkv, D + 8), dtype=torch.bfloat16)),
+        dict(scores=torch.zeros((B, Hkv, 8))),                # shorter than the capacity
+    ]
+    for change in bad:
+        args = dict(new_pos=pos, q=q, k_new=kn, v_new=kn, out=out, scores=None)
+        args.update(change)
+        with pytest.raises(ValueError):
+            kvc.decode_step(c, kvc.policy_streaming(), 1, args["new_pos"], args["q"],
+                            args["k_new"], args["v_new"], args["out"], args["scores"])
+    keep = torch.zeros((B, Hkv, 16), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        kvc.evict_streaming(c, 4, 4, keep, torch.zeros((B, Hkv), dtype=torch.int64))
+    with pytest.raises(ValueError):
+        kvc.evict_streaming(c, 4, 4, keep[:, :, :8].contiguous(), torch.zeros((B, Hkv),
+                                                                               dtype=torch.int32))
 
 
 @no_gpu
