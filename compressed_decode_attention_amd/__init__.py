@@ -38,7 +38,7 @@ EXPORTED = (
     "kvc_workspace_bytes", "kvc_decode_attn", "kvc_h2o_accumulate", "kvc_evict_streaming",
     "kvc_evict_h2o", "kvc_evict_random", "kvc_compact", "kvc_decode_step", "kvc_stream_read",
     "kvc_h2o_accumulate_workspace_bytes", "kvc_kivi_workspace_bytes", "kvc_kivi_prefill",
-    "kvc_kivi_decode",
+    "kvc_kivi_decode", "kvc_decode_step_noalloc",
 )
 
 
@@ -107,6 +107,9 @@ _lib.kvc_decode_step.restype = ctypes.c_int
 _lib.kvc_decode_step.argtypes = [_CP, ctypes.POINTER(kvc_policy), ctypes.c_uint32, _P, _P, _P,
                                  _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P,
                                  ctypes.c_size_t, _P]
+_lib.kvc_decode_step_noalloc.restype = ctypes.c_int
+_lib.kvc_decode_step_noalloc.argtypes = [_CP, ctypes.POINTER(kvc_policy), ctypes.c_uint32, _P,
+                                         _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int32, _P]
 _lib.kvc_stream_read.restype = ctypes.c_int
 _lib.kvc_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
 _lib.kvc_kivi_workspace_bytes.restype = ctypes.c_size_t
@@ -391,6 +394,19 @@ def decode_step(cache: KvCache, policy: kvc_policy, step: int, new_pos, q, k_new
     _check(_lib.kvc_decode_step(ctypes.byref(cache.c()), ctypes.byref(policy), step, pp, qp, kp,
                                 vp, op, sp, _scale(cache, scale), max_len_hint, wp, wn,
                                 _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # KVC_NOALLOC_SCRATCH_BYTES of kvc.h
+
+
+def decode_step_noalloc(cache: KvCache, policy: kvc_policy, step: int, new_pos, q, k_new, v_new,
+                        out, scores=None, scale=None, max_len_hint: int = 0, stream=None):
+    """decode_step without a workspace: the library's static per-GPU scratch
+    (calls that overlap on one GPU race)."""
+    pp, qp, kp, vp, op, sp = cache._step_ptrs(new_pos, q, k_new, v_new, out, scores)
+    _check(_lib.kvc_decode_step_noalloc(ctypes.byref(cache.c()), ctypes.byref(policy), step, pp,
+                                        qp, kp, vp, op, sp, _scale(cache, scale), max_len_hint,
+                                        _stream(stream)))
 
 
 def stream_read(buf, sink, nbytes: Optional[int] = None, stream=None):

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvc_internal.h"
 
 #define KVC_EXPORT extern "C" __attribute__((visibility("default")))
@@ -445,12 +447,11 @@ KVC_EXPORT kvc_status kvc_compact(const kvc_cache *c, const int32_t *keep_slots,
     return hip_status(kvc::launch_compact(a, c->dtype, (hipStream_t)stream), what);
 }
 
-KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *policy, uint32_t step,
-                                      const int32_t *new_pos, const void *q, const void *k_new,
-                                      const void *v_new, float *out, float *h2o_scores,
-                                      float scale, int32_t max_len_hint, void *workspace,
-                                      size_t workspace_bytes, void *stream) {
-    const char *what = "kvc_decode_step";
+static kvc_status decode_step(const char *what, const kvc_cache *c, const kvc_policy *policy,
+                              uint32_t step, const int32_t *new_pos, const void *q,
+                              const void *k_new, const void *v_new, float *out,
+                              float *h2o_scores, float scale, int32_t max_len_hint,
+                              void *workspace, size_t workspace_bytes, void *stream) {
     kvc_status s = check_attn_args(c, new_pos, q, k_new, v_new, out, scale, what);
     if (s != KVC_OK) return s;
     if ((s = check_policy(policy, h2o_scores, what)) != KVC_OK) return s;
@@ -492,6 +493,76 @@ KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *poli
         a.presel_seed = policy->seed;
     }
     return hip_status(kvc::launch_step_split(a, sa, ca, c->dtype, st), what);
+}
+
+KVC_EXPORT kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *policy, uint32_t step,
+                                      const int32_t *new_pos, const void *q, const void *k_new,
+                                      const void *v_new, float *out, float *h2o_scores,
+                                      float scale, int32_t max_len_hint, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    return decode_step("kvc_decode_step", c, policy, step, new_pos, q, k_new, v_new, out,
+                       h2o_scores, scale, max_len_hint, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// kvc_decode_step without a caller workspace: the same kernels take their
+// scratch (split partials, fallback logits, keep lists) from one static
+// device array of KVC_NOALLOC_SCRATCH_BYTES.  Host code never passes the
+// array's name to a kernel (in host code it names a host-side stand-in): the
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is used.  Nothing in the scratch has to start at zero (every
+// region is written before it is read within a call), so no clearing is
+// enqueued.  Calls on one device share the array: calls that overlap on one
+// GPU race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch's device address on the current device (looked up once).
+kvc_status scratch_of_current_device(void **ptr, const char *what) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVC_ERR_HIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: device %d beyond %d", what, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KVC_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", what,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return KVC_OK;
+}
+}  // namespace
+
+KVC_EXPORT kvc_status kvc_decode_step_noalloc(const kvc_cache *c, const kvc_policy *policy,
+                                              uint32_t step, const int32_t *new_pos,
+                                              const void *q, const void *k_new,
+                                              const void *v_new, float *out, float *h2o_scores,
+                                              float scale, int32_t max_len_hint, void *stream) {
+    const char *what = "kvc_decode_step_noalloc";
+    // every argument and the scratch size are checked before the device is touched
+    kvc_status s = check_attn_args(c, new_pos, q, k_new, v_new, out, scale, what);
+    if (s != KVC_OK) return s;
+    if ((s = check_policy(policy, h2o_scores, what)) != KVC_OK) return s;
+    const size_t need = layout(c, max_len_hint).total;
+    if (need > (size_t)KVC_NOALLOC_SCRATCH_BYTES)
+        return fail(KVC_ERR_WORKSPACE,
+                    "%s: this cache and length hint need %zu bytes of scratch; the static "
+                    "scratch holds %zu (use kvc_decode_step with a workspace)",
+                    what, need, (size_t)KVC_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((s = scratch_of_current_device(&ws, what)) != KVC_OK) return s;
+    return decode_step(what, c, policy, step, new_pos, q, k_new, v_new, out, h2o_scores, scale,
+                       max_len_hint, ws, (size_t)KVC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 KVC_EXPORT kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink,

@@ -301,6 +301,25 @@ kvc_status kvc_decode_step(const kvc_cache *c, const kvc_policy *policy,
                            size_t workspace_bytes, void *stream);
 
 /*
+ * kvc_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as kvc_decode_step without the workspace: its
+ * scratch is one static device array of KVC_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends.  The call
+ * allocates nothing.  A cache and length hint whose workspace
+ * (kvc_workspace_bytes) exceeds the array are rejected with
+ * KVC_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares its array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ */
+#define KVC_NOALLOC_SCRATCH_BYTES (128u << 20)
+kvc_status kvc_decode_step_noalloc(const kvc_cache *c, const kvc_policy *policy,
+                                   uint32_t step, const int32_t *new_pos, const void *q,
+                                   const void *k_new, const void *v_new, float *out,
+                                   float *h2o_scores, float scale, int32_t max_len_hint,
+                                   void *stream);
+
+/*
  * Measurement helper, not part of a decode step: reads `bytes` bytes of
  * device memory at `src` once, with fully coalesced 16-byte loads spread over
  * the whole GPU, and writes `sink` (one uint32_t of device memory) only if the

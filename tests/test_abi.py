@@ -117,6 +117,28 @@ def test_attention_argument_errors():
         assert b"16-byte aligned" in kvc.library().kvc_last_error()
 
 
+@no_gpu
+def test_noalloc_step_rejects_caches_beyond_its_static_scratch():
+    lib = kvc.library()
+    pol = kvc.policy_streaming()
+    # batch 512 x 8 kv heads at capacity 65,536: gigabytes of fallback scratch
+    big = _fake_cache(batch=512, q_heads=64, kv_heads=8, capacity=65536)
+    need = lib.kvc_workspace_bytes(ctypes.byref(big), 0)
+    assert need > kvc.NOALLOC_SCRATCH_BYTES
+    assert lib.kvc_decode_step_noalloc(ctypes.byref(big), ctypes.byref(pol), 1, 0x1000, 0x2000,
+                                       0x3000, 0x4000, 0x5000, None, 0.1, 0, None) == \
+        kvc.ERR_WORKSPACE
+    assert b"static scratch" in lib.kvc_last_error()
+    # argument errors come first, as for kvc_decode_step
+    assert lib.kvc_decode_step_noalloc(ctypes.byref(_fake_cache()), ctypes.byref(pol), 1, 0x1000,
+                                       None, 0x3000, 0x4000, 0x5000, None, 0.1, 0, None) == \
+        kvc.ERR_INVALID_ARG
+    h2o = kvc.policy_h2o()
+    assert lib.kvc_decode_step_noalloc(ctypes.byref(_fake_cache()), ctypes.byref(h2o), 1, 0x1000,
+                                       0x2000, 0x3000, 0x4000, 0x5000, None, 0.1, 0, None) == \
+        kvc.ERR_INVALID_ARG
+
+
 def test_binding_checks_tensor_dtype_and_size_before_the_call():
     # host tensors stand in for device ones: the checks run before any call
     c = kvc.KvCache(2, 8, 2, 128, 16, kvc.BF16, device="cpu")
