@@ -38,20 +38,14 @@
 namespace kvc {
 
 constexpr int kKivRow = kHD / 2;                     // bytes of one token's 4-bit codes
-#ifndef KVC_KIV_WAVES
-#define KVC_KIV_WAVES 3
-#endif
+constexpr int kKivWavesPerEU = 3;                    // waves per SIMD of the quantized kernel
 constexpr int kKivVG = kHD / 32;                     // V grids per token
 
 // codes and grids are read once per step: non-temporal loads
-#ifndef KVC_KIV_NT
-#define KVC_KIV_NT 1
-#endif
 template <typename T>
 __device__ inline T kiv_load(const T *p) {
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-    if constexpr (!KVC_KIV_NT) return *p;
-    else if constexpr (sizeof(T) == 16)
+    if constexpr (sizeof(T) == 16)
         return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p)));
     else return __builtin_nontemporal_load(p);
 }
@@ -222,7 +216,7 @@ __device__ inline float bf16_hi_half(uint32_t p) { return __uint_as_float(p & 0x
 // wave stages the group's grids in its own LDS, builds the scaled query
 // operand there, runs the K products, the softmax update and the P.V
 // products; LDS traffic of one wave needs no workgroup barrier.
-__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(KVC_KIV_WAVES)))
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kKivWavesPerEU)))
 void kivi_qattn_kernel(KiviArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int ns = a.nsq;

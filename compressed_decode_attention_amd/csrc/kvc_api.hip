@@ -617,11 +617,9 @@ int kivi_nsq(const kvc_kivi_cache *c, int hint) {
     const int groups = mq / kvc::kKivGroup;
     if (c->max_quant == 0) return 0;
     if (groups == 0) return 1;
-#ifndef KVC_KIV_SPLIT_GROUPS
-#define KVC_KIV_SPLIT_GROUPS 64
-#endif
+constexpr int kKivSplitGroups = 64;   // quantized groups per workgroup of the KIVI attention
     const int units = c->batch * c->kv_heads;
-    int ns = (groups + KVC_KIV_SPLIT_GROUPS - 1) / KVC_KIV_SPLIT_GROUPS;
+    int ns = (groups + kKivSplitGroups - 1) / kKivSplitGroups;
     const int fill = (4096 + units - 1) / units, by_len = (groups + 3) / 4;
     const int want = fill < by_len ? fill : by_len;
     ns = ns > want ? ns : want;

@@ -541,10 +541,7 @@ hipError_t launch_step_split(const AttnArgs &a, const SelectArgs &sa, const Comp
 // (decode_attn) or the whole step (decode_step)
 enum { kModeAttn = 0, kModeStep = 1 };
 constexpr int kFusedMaxT = 1024;   // largest attended length of the LDS fast path
-#ifndef KVC_FUSED_SMALL_T
-#define KVC_FUSED_SMALL_T 528
-#endif
-constexpr int kFusedSmallT = KVC_FUSED_SMALL_T;  // LDS capacity used up to a 512 budget + 1
+constexpr int kFusedSmallT = 528;  // LDS capacity used up to a 512 budget + 1
 
 struct FusedArgs {
     AttnArgs attn;      // nsplit must be 1; logits = global scratch of the fallback

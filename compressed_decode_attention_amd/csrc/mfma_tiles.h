@@ -16,26 +16,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kHD = 128;   // head_dim of the fast path
-#ifndef KVC_DK
-#define KVC_DK 3
-#endif
-#ifndef KVC_DV
-#define KVC_DV 2
-#endif
-#ifndef KVC_DK8
-#define KVC_DK8 4
-#endif
-#ifndef KVC_DV8
-#define KVC_DV8 3
-#endif
-constexpr int kDK = KVC_DK;   // K tiles (16 keys x 256 B) in flight per wave
-constexpr int kDV = KVC_DV;   // V tiles (16 keys x 256 B) in flight per wave
-constexpr int kDK8 = KVC_DK8;   // the same for E5M2 rows (16 keys x 128 B)
-constexpr int kDV8 = KVC_DV8;
-#ifndef KVC_WAVES_PER_EU
-#define KVC_WAVES_PER_EU 4
-#endif
-constexpr int kWavesPerEU = KVC_WAVES_PER_EU;   // 4 workgroups of 4 waves per CU
+constexpr int kDK = 3;    // K tiles (16 keys x 256 B) in flight per wave
+constexpr int kDV = 2;    // V tiles (16 keys x 256 B) in flight per wave
+constexpr int kDK8 = 4;   // the same for E5M2 rows (16 keys x 128 B)
+constexpr int kDV8 = 3;
+constexpr int kWavesPerEU = 4;   // 4 workgroups of 4 waves per CU
 
 __device__ inline bf16x8_t as_bf16x8(u16x8_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
@@ -97,15 +82,11 @@ __device__ inline void load_q(u16x8_t (&qa)[4], const uint16_t *qp, bool valid, 
 // what the caches hold for others: about 10% faster for the whole step than
 // the default policy.  From a block-paged pool the default policy is about 12%
 // faster, so the policy follows the layout.
-#ifndef KVC_LOAD_POLICY
-#define KVC_LOAD_POLICY 2
-#endif
-#ifndef KVC_LOAD_POLICY_PAGED
-#define KVC_LOAD_POLICY_PAGED 0
-#endif
+constexpr int kLoadPolicy = 2;        // cache policy bits of the buffer loads: non-temporal
+constexpr int kLoadPolicyPaged = 0;   // the default policy
 template <bool F8, bool PAGED>
 __device__ inline typename KvRow<F8>::type buffer_row(__amdgpu_buffer_rsrc_t rs, int voff) {
-    constexpr int pol = PAGED ? KVC_LOAD_POLICY_PAGED : KVC_LOAD_POLICY;
+    constexpr int pol = PAGED ? kLoadPolicyPaged : kLoadPolicy;
     if constexpr (F8)
         return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, pol));
     else

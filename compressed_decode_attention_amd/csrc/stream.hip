@@ -10,9 +10,6 @@ namespace kvc {
 
 // non-temporal loads: the policy the step kernels read K and V with, and
 // the faster one for a read-once stream
-#ifndef KVC_STREAM_NT
-#define KVC_STREAM_NT 1
-#endif
 constexpr int kStreamThreads = 256;
 constexpr int kStreamBlocks = 4096;   // 16 workgroups per compute unit
 constexpr uint32_t kStreamMarker = 0x9E3779B9u;
@@ -22,12 +19,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint4
     uint32_t acc = 0;
     const size_t stride = (size_t)gridDim.x * kStreamThreads;
     for (size_t i = (size_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n16; i += stride) {
-#if KVC_STREAM_NT
         typedef uint32_t v4u __attribute__((ext_vector_type(4)));
         const uint4 v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p + i)));
-#else
-        const uint4 v = p[i];
-#endif
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     if (acc == kStreamMarker) *sink = acc;
