@@ -14,25 +14,31 @@
 //  1. statistics: one workgroup per 128 rows of a unit.  K tiles of 64 slots
 //     are staged in LDS (XOR swizzle, conflict-free reads) and enter
 //     v_mfma_f32_16x16x32_bf16 as the A operand; the rows are the B operand,
-//     held in registers.  Each lane keeps a running max / sum over its four
-//     slots of every 16-slot tile; four lanes merge into the row's
-//     log-sum-exp, written to the workspace.
+//     held in registers.  Each lane keeps a running maximum of the raw dot
+//     products (the scale is positive, so the order is the same) and a sum
+//     of exp2(c2 * (dot - maximum)), rescaled once per two 16-slot tiles;
+//     four lanes merge into the row's log-sum-exp, written to the workspace.
 //  2. scores: one workgroup per 128 slots of a unit.  The slots are the B
 //     operand, held in registers; 64-row query tiles are staged in LDS.  Each
-//     lane sums exp(z - lse) over its four rows of every tile into fp64 column
-//     sums (a fixed order: the scores are deterministic), and one lane per
-//     slot adds the total to the score.
+//     lane sums exp2(c2 * dot - lse) over its 16 rows of a tile in fp32,
+//     adds that to an fp64 column sum (a fixed order: the scores are
+//     deterministic), and one lane per slot adds the total to the score.
 // Tiles that no row of a block can see (from the positions alone) are
 // skipped, which halves the work of a causal prompt; tiles that every row sees
-// whole (most of a causal triangle) run without the per-element mask.  The
-// softmax runs in base 2 (scale * log2(e) folded into one factor, the row
-// statistic a base-2 log-sum-exp), so an element costs one multiply-add and
-// one v_exp_f32.  All blocks of one unit
-// run on one XCD (workgroups are dealt round-robin over the eight XCDs), so
-// the K (pass 1) or Q (pass 2) rows they share are read from that XCD's L2.
+// whole (most of a causal triangle) run a mask-free variant of the tile's
+// straight-line code (the choice is uniform per tile, so neither variant
+// branches inside).  The softmax runs in base 2 (scale * log2(e) folded into
+// one factor c2, the row statistic a base-2 log-sum-exp), so an element costs
+// one multiply-add and one v_exp_f32.  Each slot tile's smallest and largest
+// position come from a wave reduction (a wave's 64 lanes hold one tile).  All
+// blocks of one unit run on one XCD (workgroups are dealt round-robin over the
+// eight XCDs), so the K (pass 1) or Q (pass 2) rows they share are read from
+// that XCD's L2.
 #include "kvc_internal.h"
 
 #include <limits.h>
+
+#include <type_traits>
 
 namespace kvc {
 
@@ -48,6 +54,7 @@ constexpr int kStatRows = 128;    // rows per workgroup, pass 1 (32 per wave)
 constexpr int kScoreSlots = 128;  // slots per workgroup, pass 2 (32 per wave)
 constexpr int kTile = 64;         // slots (pass 1) or rows (pass 2) staged per step
 constexpr int kMaxRowTilesLds = 4096;   // pass 2: row tiles whose largest position fits in LDS
+constexpr int kSG = 2;            // pass 1: 16-slot tiles per maximum and rescale
 
 __device__ inline bf16x8_p as_bf(u16x8_p x) { return __builtin_bit_cast(bf16x8_p, x); }
 
@@ -145,17 +152,20 @@ void prompt_stats_kernel(PromptArgs a) {
         qmax = max(qmax, qp[t]);
     }
     // smallest and largest position of every slot tile
-    for (int i = tid; i < ntile; i += kPThreads) {
-        tmin_s[i] = INT_MAX;
-        tmax_s[i] = INT_MIN;
+    // (a wave's 64 lanes cover exactly one 64-slot tile: lanes past n
+    // contribute nothing)
+    static_assert(kTile == 64, "one wave per slot tile");
+    for (int kt = w; kt < ntile; kt += kPThreads / 64) {
+        const int j = kt * kTile + lane;
+        const int p = j < n ? P[j] : INT_MAX;
+        const int lo = wave_min_i(p);
+        const int hi = wave_max_i(j < n ? p : INT_MIN);
+        if (lane == 0) {
+            tmin_s[kt] = lo;
+            tmax_s[kt] = hi;
+        }
     }
-    qmax = block_max(qmax, red);   // (its barriers also publish the initial values)
-    for (int j = tid; j < n; j += kPThreads) {
-        const int p = P[j];
-        atomicMin(&tmin_s[j / kTile], p);
-        atomicMax(&tmax_s[j / kTile], p);
-    }
-    __syncthreads();
+    qmax = block_max(qmax, red);   // (its barriers also publish the tile bounds)
     // smallest position of each 16-row tile of the wave, and whether the tile
     // holds no padding row (only such tiles may skip the mask)
     int qmin[2];
@@ -188,6 +198,8 @@ void prompt_stats_kernel(PromptArgs a) {
         ppos = (j0 + (tid & (kTile - 1)) < n) ? p : INT_MAX;
     };
 
+    // running maximum of the raw dot products (c2 > 0 keeps the order) and
+    // the sum of exp2(c2 * (dot - maximum)), per lane and row tile
     float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};
     int cur = next_active(0);
     if (cur < ntile) fetch(cur);
@@ -209,49 +221,71 @@ void prompt_stats_kernel(PromptArgs a) {
         bool inner[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) inner[t] = slots_full && rows_full[t] && kmax <= qmin[t];
+        // two 16-slot tiles' dot products at a time (8 per lane and row
+        // tile), then one maximum and one rescale per row tile.  The mask
+        // decision is uniform per tile, so each variant is straight-line code.
+        auto tile_body = [&](auto masked_c) {
+            constexpr bool kMasked = decltype(masked_c)::value;
 #pragma unroll
-        for (int s = 0; s < kTile / 16; ++s) {
-            // A operand: lane (col, r) holds dims 32c + 8r.. of slot 16s + col
-            const int q = 16 * s + col;
-            u16x8_p ka[4];
+            for (int s0 = 0; s0 < kTile / 16; s0 += kSG) {
+                f32x4_p acc[2][kSG];
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4)
-                ka[c4] = *reinterpret_cast<const u16x8_p *>(ktile[buf] + tile_off(q, 4 * c4 + r));
-            // C[slot 4r + i][row col]
-            int kp[4];
-            bool kv[4];
+                for (int s = 0; s < kSG; ++s) {
+                    // A operand: lane (col, r) holds dims 32c + 8r.. of slot 16(s0+s) + col
+                    const int q = 16 * (s0 + s) + col;
+                    u16x8_p ka[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kp[i] = kpos[buf][16 * s + 4 * r + i];
-                kv[i] = j0 + 16 * s + 4 * r + i < n;
-            }
+                    for (int c4 = 0; c4 < 4; ++c4)
+                        ka[c4] = *reinterpret_cast<const u16x8_p *>(ktile[buf] + tile_off(q, 4 * c4 + r));
+                    // C[slot 4r + i][row col]
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int t = 0; t < 2; ++t) {
+                        acc[t][s] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ka[c4]), as_bf(qb[t][c4]), acc,
-                                                                  0, 0, 0);
-                // base-2 logits (scale * log2 e folded in)
-                float z[4];
-                if (inner[t]) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) z[i] = acc[i] * c2;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        z[i] = (kv[i] && kp[i] <= qp[t]) ? acc[i] * c2 : -INFINITY;
+                        for (int c4 = 0; c4 < 4; ++c4)
+                            acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf(ka[c4]), as_bf(qb[t][c4]), acc[t][s], 0, 0, 0);
+                    }
                 }
-                const float zmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-                const float mnew = fmaxf(mm[t], zmax);
-                if (mnew != -INFINITY) {
-                    const float sum = (exp2_hw(z[0] - mnew) + exp2_hw(z[1] - mnew)) +
-                                      (exp2_hw(z[2] - mnew) + exp2_hw(z[3] - mnew));
-                    ll[t] = ll[t] * exp2_hw(mm[t] - mnew) + sum;
-                    mm[t] = mnew;
+                if constexpr (kMasked) {
+                    // slots a row does not see (or past n) weigh nothing
+#pragma unroll
+                    for (int s = 0; s < kSG; ++s)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int jj = 16 * (s0 + s) + 4 * r + i;
+                            const int kp = kpos[buf][jj];
+                            const bool live = j0 + jj < n;
+#pragma unroll
+                            for (int t = 0; t < 2; ++t)
+                                acc[t][s][i] = (live && kp <= qp[t]) ? acc[t][s][i] : -INFINITY;
+                        }
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    float mx = mm[t];
+#pragma unroll
+                    for (int s = 0; s < kSG; ++s)
+                        mx = fmaxf(mx, fmaxf(fmaxf(acc[t][s][0], acc[t][s][1]),
+                                             fmaxf(acc[t][s][2], acc[t][s][3])));
+                    // base-2 weights exp2(c2 * (dot - max)) (scale * log2 e in
+                    // c2); a row with nothing seen yet keeps a zero sum
+                    const float ms = (mx == -INFINITY) ? 0.f : mx;
+                    const float nb = -ms * c2;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int s = 0; s < kSG; ++s)
+                        sum += (exp2_hw(fmaf(acc[t][s][0], c2, nb)) + exp2_hw(fmaf(acc[t][s][1], c2, nb))) +
+                               (exp2_hw(fmaf(acc[t][s][2], c2, nb)) + exp2_hw(fmaf(acc[t][s][3], c2, nb)));
+                    ll[t] = ll[t] * exp2_hw(fmaf(mm[t], c2, nb)) + sum;
+                    mm[t] = mx;
                 }
             }
-        }
+        };
+        if (inner[0] && inner[1])
+            tile_body(std::integral_constant<bool, false>());
+        else
+            tile_body(std::integral_constant<bool, true>());
         buf ^= 1;
         cur = nxt;
     }
@@ -264,13 +298,13 @@ void prompt_stats_kernel(PromptArgs a) {
             const float mo = __shfl_xor(m, off, 64), lo = __shfl_xor(l, off, 64);
             const float mn = fmaxf(m, mo);
             if (mn != -INFINITY) {
-                l = l * exp2_hw(m - mn) + lo * exp2_hw(mo - mn);
+                l = l * exp2_hw((m - mn) * c2) + lo * exp2_hw((mo - mn) * c2);
                 m = mn;
             }
         }
-        // base-2 log-sum-exp of the row
+        // base-2 log-sum-exp of the row's base-2 logits c2 * dot
         if (r == 0 && Rw[t] < nrows)
-            a.lse[(size_t)u * nrows + Rw[t]] = (l > 0.f) ? m + log2f(l) : -INFINITY;
+            a.lse[(size_t)u * nrows + Rw[t]] = (l > 0.f) ? m * c2 + log2f(l) : -INFINITY;
     }
 }
 
@@ -282,7 +316,8 @@ void prompt_stats_kernel(PromptArgs a) {
 // number of row tiles fits the LDS table; otherwise every tile is visited and
 // the masks alone decide): the next active tile's rows load into registers
 // while the MFMAs run on the current LDS buffer.
-__global__ __launch_bounds__(kPThreads) void prompt_scores_kernel(PromptArgs a) {
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void prompt_scores_kernel(PromptArgs a) {
     __shared__ __align__(16) unsigned char qtile[2][kTile * 256];
     __shared__ int rpos[2][kTile];
     __shared__ float rlse[2][kTile];
@@ -392,41 +427,51 @@ __global__ __launch_bounds__(kPThreads) void prompt_scores_kernel(PromptArgs a) 
         bool inner[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) inner[t] = slots_full[t] && rows_full && kmaxw[t] <= tmin;
+        // the tile's probabilities are summed in fp32 per lane (16 rows per
+        // slot and lane, in a fixed order), then added to the fp64 total.
+        // The mask decision is uniform per tile: straight-line variants.
+        float ts[2] = {0.f, 0.f};
+        auto tile_body = [&](auto masked_c) {
+            constexpr bool kMasked = decltype(masked_c)::value;
 #pragma unroll
-        for (int s = 0; s < kTile / 16; ++s) {
-            // A operand: lane (col, r) holds dims 32c + 8r.. of row 16s + col
-            const int q = 16 * s + col;
-            u16x8_p qa[4];
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4)
-                qa[c4] = *reinterpret_cast<const u16x8_p *>(qtile[buf] + tile_off(q, 4 * c4 + r));
-            // C[row 4r + i][slot col]
-            int rp[4];
-            float rl[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                rp[i] = rpos[buf][16 * s + 4 * r + i];
-                rl[i] = rlse[buf][16 * s + 4 * r + i];   // base 2
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < kTile / 16; ++s) {
+                // A operand: lane (col, r) holds dims 32c + 8r.. of row 16s + col
+                const int q = 16 * s + col;
+                u16x8_p qa[4];
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(qa[c4]), as_bf(kb[t][c4]), acc,
-                                                                  0, 0, 0);
-                float e[4];
-                if (inner[t]) {
+                    qa[c4] = *reinterpret_cast<const u16x8_p *>(qtile[buf] + tile_off(q, 4 * c4 + r));
+                // C[row 4r + i][slot col]
+                float rl[4];
+                int rp[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) e[i] = exp2_hw(fmaf(acc[i], c2, -rl[i]));
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        e[i] = (kv[t] && kp[t] <= rp[i]) ? exp2_hw(fmaf(acc[i], c2, -rl[i])) : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    rl[i] = rlse[buf][16 * s + 4 * r + i];   // base 2
+                    if constexpr (kMasked) rp[i] = rpos[buf][16 * s + 4 * r + i];
                 }
-                cs[t] += (double)((e[0] + e[1]) + (e[2] + e[3]));
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(qa[c4]), as_bf(kb[t][c4]),
+                                                                      acc, 0, 0, 0);
+                    float e[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        e[i] = exp2_hw(fmaf(acc[i], c2, -rl[i]));
+                        if constexpr (kMasked) e[i] = (kv[t] && kp[t] <= rp[i]) ? e[i] : 0.f;
+                    }
+                    ts[t] += (e[0] + e[1]) + (e[2] + e[3]);
+                }
             }
-        }
+        };
+        if (inner[0] && inner[1])
+            tile_body(std::integral_constant<bool, false>());
+        else
+            tile_body(std::integral_constant<bool, true>());
+#pragma unroll
+        for (int t = 0; t < 2; ++t) cs[t] += (double)ts[t];
         buf ^= 1;
         cur = nxt;
     }
