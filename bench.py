@@ -67,12 +67,18 @@ def sources_digest() -> str:
 
 
 def profiled_traffic(workload: str, policy: str, kv_dtype: str):
+    """(bytes per launch, where the figure comes from): a stored counter
+    record for these exact fused-kernel sources, or (None, why not)."""
     digest = sources_digest()
     for t in PROFILED_TRAFFIC:
         if (t["workload"], t["policy"], t["kv_dtype"], t["sources_digest"]) == \
                 (workload, policy, kv_dtype, digest):
-            return (t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024.0
-    return None
+            return ((t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024.0,
+                    f"stored record, not measured in this run: rocprofv3 --pmc FETCH_SIZE and "
+                    f"WRITE_SIZE of this script at this workload, policy and cache dtype, "
+                    f"calibrated on a 1 GiB copy, for fused-kernel sources digest {digest}")
+    return None, (f"none: no counter record for the current fused-kernel sources "
+                  f"(digest {digest}) at this workload, policy and cache dtype")
 
 
 def log(msg):
@@ -142,9 +148,21 @@ def cpu_baseline(w, n_cached: int, budget_s: float = 12.0, decay: float = 0.0,
         "sample": (f"{steps} whole-batch {policy} steps ({w.batch} sequences x {w.kv_heads} kv heads, "
                    f"{n_cached} cached + 1 new per unit, fp64, one thread), "
                    f"{t_work:.1f} s of timed work"),
-        "host_cpu": platform.processor() or platform.machine(),
+        "host_cpu": host_cpu_model(),
         "host_nproc": os.cpu_count(),
     }
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name as /proc/cpuinfo reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def copy_probe(torch, mib: int, reps: int = 5):
@@ -554,13 +572,179 @@ def paged_bench(torch, kvc, synth, args, w):
     }), flush=True)
 
 
+def whole_run(torch, kvc, synth, args):
+    """Per-head random eviction over the reasoning trace's whole schedule:
+    the pinned prompt, then one decode step per generated token; the cache
+    grows from the prompt to the budget (pinned + n_keep, no eviction), then
+    every step evicts one generated token per head.  Every step is one
+    kvc_decode_step; the two phases are timed with events on the launch
+    stream and the run's average is the value."""
+    w = synth.workload(args.workload)
+    assert w.policy == "random", "--whole-run follows a random-eviction workload's schedule"
+    B, Hq, Hkv, D, P = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.pinned
+    G = Hq // Hkv
+    steps = w.steps
+    cap = w.pinned + w.n_keep + 1
+    dev = torch.device("cuda", 0)
+    cache = kvc.KvCache(B, Hq, Hkv, D, cap, kvc.BF16, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    cache.k[:, :, :P] = torch.randn(cache.k[:, :, :P].shape, generator=gen, device=dev).to(torch.bfloat16)
+    cache.v[:, :, :P] = torch.randn(cache.v[:, :, :P].shape, generator=gen, device=dev).to(torch.bfloat16)
+    cache.pos[:, :, :P] = torch.arange(P, dtype=torch.int32, device=dev)
+    cache.n_slots.fill_(P)
+    pool = [(torch.randn((B, Hq, D), generator=gen, device=dev).to(torch.bfloat16),
+             torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16),
+             torch.randn((B, Hkv, D), generator=gen, device=dev).to(torch.bfloat16))
+            for _ in range(4)]
+    new_pos = (P + torch.arange(steps, dtype=torch.int32, device=dev)).view(-1, 1).expand(
+        steps, B).contiguous()
+    out = torch.empty((B, Hq, D), device=dev)
+    pol = kvc.policy_random(w.pinned, w.n_keep, w.seed)
+    ws = cache.workspace(cap)
+    stream = torch.cuda.current_stream()
+    warm_first_step(torch, kvc, cache, pol, False)
+    grow = w.n_keep   # steps 1 .. n_keep fill the budget; later steps evict one
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for t in range(1, steps + 1):
+        if t == grow + 1:
+            ev[1].record(stream)
+        q, kn, vn = pool[t % 4]
+        kvc.decode_step(cache, pol, t, new_pos[t - 1], q, kn, vn, out, max_len_hint=cap,
+                        workspace=ws, stream=stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    assert int(cache.flags.item()) == 0, "device contract flag raised"
+    assert bool((cache.n_slots == cap - 1).all())
+    grow_ms, steady_ms = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    total_ms = grow_ms + steady_ms
+    # algorithmic bytes: every step attends its n cached slots + the new token
+    n_of = lambda t: min(P + t - 1, cap - 1)
+    grow_bytes = sum(per_unit_bytes(n_of(t), G, D, 2, "random") for t in range(1, grow + 1)) * B * Hkv
+    steady_bytes = per_unit_bytes(cap - 1, G, D, 2, "random") * (steps - grow) * B * Hkv
+    run_gbs = (grow_bytes + steady_bytes) / (total_ms * 1e-3) / 1e9
+    log(f"{w.name} whole run: {steps} steps in {total_ms:.1f} ms (growth {grow} steps "
+        f"{grow_ms:.1f} ms, steady {steps - grow} steps {steady_ms:.1f} ms), {run_gbs:.0f} GB/s")
+    print(json.dumps({
+        "metric": f"decode steps/s over the whole random-eviction run, B={B}",
+        "value": steps / (total_ms * 1e-3), "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": 0, "ms_per_step": total_ms / steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "pinned": P, "n_keep": w.n_keep, "policy": "random",
+                   "growth_steps": grow, "growth_us_per_step": grow_ms * 1e3 / grow,
+                   "steady_steps": steps - grow,
+                   "steady_us_per_step": steady_ms * 1e3 / (steps - grow),
+                   "tokens_per_s": B * steps / (total_ms * 1e-3)},
+        "roofline": {"bound": "hbm", "achieved": run_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": run_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "traffic_source": "none: not profiled for this run",
+                     "kernel": "kvc_decode_step (split path: split_kernel + finish_kernel)",
+                     "bytes_per_run": grow_bytes + steady_bytes},
+    }), flush=True)
+
+
+def cpu_baselines(args):
+    """The oracle (one host thread, fp64, unmodified) on every workload's
+    whole batch, a few steps each, in the phases the workload runs: one JSON
+    line per (workload, phase).  No GPU is used."""
+    import numpy as np
+    import oracle
+    import synth
+
+    def timed(w, pol, loads, steps, first_step=1):
+        orc = oracle.Oracle(w.q_heads, w.kv_heads, w.head_dim, w.dtype)
+        t0 = time.perf_counter()
+        for b, (n, pos, seen) in enumerate(loads):
+            k, v = synth.prefill_kv(w, b, n)
+            orc.load(b, k, v, seen=seen, pos=None if pos is None else [pos] * w.kv_heads)
+        load_s = time.perf_counter() - t0
+        work = 0.0
+        for t in range(first_step, first_step + steps):
+            inputs = [synth.step_inputs(w, b, t) for b in range(len(loads))]
+            t1 = time.perf_counter()
+            for b in range(len(loads)):
+                orc.step(b, *inputs[b], pol, step=t)
+            work += time.perf_counter() - t1
+        return work, load_s
+
+    def report(w, phase, pol_name, steps, work, cached):
+        units = w.batch * w.kv_heads
+        print(json.dumps({
+            "cpu_oracle": w.name, "phase": phase, "policy": pol_name, "batch": w.batch,
+            "units": units, "cached_per_unit": cached, "steps_timed": steps,
+            "seconds": work, "steps_per_s": steps / work, "tokens_per_s": w.batch * steps / work,
+            "cores": 1, "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count(),
+            "numpy": np.__version__}), flush=True)
+        log(f"{w.name} {phase}: {steps / work:.4f} steps/s over {steps} steps ({work:.1f} s)")
+
+    # tiny StreamingLLM layer: all 16 steps from 1,024 cached tokens (step 1 trims to 512)
+    w = synth.workload("tiny_mha_streaming_f32")
+    pol = oracle.Policy.streaming(w.n_sink, w.n_recent)
+    work, _ = timed(w, pol, [(w.prompt_len, None, w.prompt_len)], w.steps)
+    report(w, "all 16 steps", "streaming", w.steps, work, "1024 -> 512")
+
+    def steady_pos(w):
+        keep = 512 - w.n_recent
+        return np.concatenate([np.arange(keep), np.arange(w.prompt_len - w.n_recent, w.prompt_len)])
+
+    # H2O layers: the over-budget first step, then steady steps at 512 + 1
+    for name, steady in (("llama3_8b_h2o_b64", 3), ("heavy_load_b512_l2048", 3)):
+        w = synth.workload(name)
+        pol = oracle.Policy.h2o(w.n_heavy, w.n_recent)
+        work, _ = timed(w, pol, [(w.prompt_len, None, w.prompt_len)] * w.batch, 1)
+        report(w, "step 1 (trim 2,049 -> 512)", "h2o", 1, work, w.prompt_len)
+        work, _ = timed(w, pol, [(512, steady_pos(w), w.prompt_len)] * w.batch, steady, 2)
+        report(w, "steady", "h2o", steady, work, 512)
+
+    # reasoning trace, random eviction: a growth step and steady steps
+    w = synth.workload("reasoning_random_b32")
+    pol = oracle.Policy.random(w.pinned, w.n_keep, w.seed)
+    work, _ = timed(w, pol, [(w.pinned, None, w.pinned)] * w.batch, 3)
+    report(w, "growth (first steps after the 1,024-token prompt)", "random", 3, work, w.pinned)
+    fill = w.pinned + w.n_keep
+    work, _ = timed(w, pol, [(fill, None, fill)] * w.batch, 3, w.n_keep + 1)
+    report(w, "steady (5,120 cached, one eviction per head)", "random", 3, work, fill)
+
+    # mixed-length batch: the first step over every prompt, then steady steps
+    w = synth.workload("mixed_paged_h2o_b128")
+    lengths = [int(x) for x in synth.mixed_lengths(w)]
+    pol = oracle.Policy.h2o(w.n_heavy, w.n_recent)
+    work, _ = timed(w, pol, [(L, None, L) for L in lengths], 1)
+    report(w, "step 1 (every prompt, trim to 512)", "h2o", 1, work,
+           f"log-uniform 512..32768, mean {sum(lengths) / len(lengths):.0f}")
+    loads = []
+    for L in lengths:
+        keep = 512 - w.n_recent
+        loads.append((512, np.concatenate([np.arange(keep), np.arange(L - w.n_recent, L)]), L))
+    work, _ = timed(w, pol, loads, 3, 2)
+    report(w, "steady", "h2o", 3, work, 512)
+
+
 def sweep(torch, kvc, synth, args):
     """Where eviction pays: full vs StreamingLLM-512 vs H2O-512 (and H2O with an
     unfused score pass) over batch and prompt length.  One JSON line per point."""
+    Hq, Hkv, D = 64, 8, 128
+    G = Hq // Hkv
     for B, P in SWEEP_POINTS:
+        fused_us = None
         for policy, unfused in (("full", False), ("streaming", False), ("h2o", False),
                                 ("h2o", True)):
             r = sweep_point(torch, kvc, synth, B, P, policy, args.steps, args.warmup, unfused)
+            if policy == "h2o" and not unfused:
+                fused_us = r["us_per_step"]
+            if unfused and fused_us is not None:
+                # what the unfused step would take if its second pass were
+                # bandwidth-bound like the fused step: that pass's algorithmic
+                # bytes (K of the 513 attended slots once, the query, the
+                # scores read and written) at the fused step's achieved rate
+                n = 513
+                second = n * D * 2 + G * D * 2 + 8 * n
+                ideal = fused_us * (1.0 + second / per_unit_bytes(512, G, D, 2, "h2o"))
+                r["unfused_ideal_us_per_step"] = ideal
+                r["fusion_gain_vs_measured_unfused"] = r["us_per_step"] / fused_us
+                r["fusion_gain_vs_ideal_unfused"] = ideal / fused_us
             log(f"B={B} P={P} {r['policy']}: {r['us_per_step']:.1f} us/step, "
                 f"{r['algorithmic_gbs']:.0f} GB/s")
             print(json.dumps(r), flush=True)
@@ -590,6 +774,13 @@ def main():
                          "length; one JSON line per point")
     ap.add_argument("--kivi", action="store_true",
                     help="KIVI-4 quantized-cache decode steps at the workload's shape")
+    ap.add_argument("--whole-run", action="store_true",
+                    help="random eviction over the workload's whole schedule (growth to the "
+                         "budget, then one eviction per head per step; --workload "
+                         "reasoning_random_b32): run-average steps/s")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="only time the CPU oracle (one thread) on every workload's phases; "
+                         "no GPU")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -599,6 +790,10 @@ def main():
                                    "Units (sequence, kv head) are independent, so the path "
                                    "shards by sequences or kv heads with no exchange."}))
         sys.exit(2)
+
+    if args.cpu_baselines:
+        cpu_baselines(args)
+        return
 
     import torch
 
@@ -617,6 +812,9 @@ def main():
         return
     if args.kivi:
         kivi_bench(torch, kvc, synth, args)
+        return
+    if args.whole_run:
+        whole_run(torch, kvc, synth, args)
         return
 
     f8 = args.kv_dtype == "fp8"
@@ -747,7 +945,7 @@ def main():
     step_bytes = unit_bytes * B * Hkv
     achieved = step_bytes / (launch_ms * 1e-3) / 1e9
     steps_per_s = 1e3 / ms_per_step
-    traffic = profiled_traffic(w.name, policy, "e5m2" if f8 else "bf16")
+    traffic, traffic_source = profiled_traffic(w.name, policy, "e5m2" if f8 else "bf16")
 
     result = {
         "metric": f"decode steps/s and achieved HBM GB/s (% of peak), attn+evict, B={B} L={P}",
@@ -774,6 +972,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "traffic_source": traffic_source,
             "kernel": "kvc_decode_step (whole step)",
             "bytes_per_unit": unit_bytes, "units_per_launch": B * Hkv,
             "launch_ms": launch_ms,

@@ -285,8 +285,8 @@ KVC_EXPORT int64_t kvc_n_keep(int64_t n_candidates, double keep_ratio) {
     return k;
 }
 
-KVC_EXPORT const char *kvc_status_string(kvc_status s) {
-    switch (s) {
+KVC_EXPORT const char *kvc_status_string(int status) {
+    switch (status) {
         case KVC_OK: return "ok";
         case KVC_ERR_INVALID_ARG: return "invalid argument";
         case KVC_ERR_UNSUPPORTED: return "unsupported shape or dtype";

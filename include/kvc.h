@@ -154,8 +154,9 @@ size_t kvc_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
  * implementation"]. */
 int64_t kvc_n_keep(int64_t n_candidates, double keep_ratio);
 
-/* Static, never-freed description of a status code. */
-const char *kvc_status_string(kvc_status s);
+/* Static, never-freed description of a status code (a kvc_status value;
+ * any other int gives "unknown status"). */
+const char *kvc_status_string(int status);
 
 /* Detail of the last error returned on the calling thread ("" if none). */
 const char *kvc_last_error(void);

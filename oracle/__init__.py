@@ -22,7 +22,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c to load (the sanitizer test
+# runs the pins against an AddressSanitizer / UndefinedBehaviorSanitizer build)
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 
 def build() -> str:
@@ -40,7 +42,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if "ORACLE_LIB" not in os.environ and (
+                not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         L = ctypes.CDLL(_LIB)
         c_i32p = ctypes.POINTER(ctypes.c_int32)
