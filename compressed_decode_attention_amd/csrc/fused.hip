@@ -76,22 +76,76 @@ __device__ inline uint64_t rank_word(uint32_t primary, int32_t pos) {
     return ((uint64_t)primary << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
 }
 
+// What the step kernel reads from its arguments: one copy of the cache's
+// description and the policy, nothing twice (the kernel's scalar registers
+// hold what it keeps live; a duplicate would cost registers or spills).
+struct FusedParams {
+    CacheDev c;
+    const int32_t *new_pos;
+    const void *q, *k_new, *v_new;
+    float *out;
+    float *scores;        // may be null
+    float *logits;        // scratch of the fallback routines
+    int32_t *keep_slots, *n_out;
+    float scale, decay;
+    int kind, n_sink, n_heavy, n_recent, prompt_len, n_keep;
+    uint32_t step;
+    uint64_t seed;
+};
+
+// Units longer than the launch's LDS capacity (or a full cache): the generic
+// per-unit routines, with their arguments rebuilt from the kernel's.
 template <int MODE, bool F8>
-__device__ void fused_generic(const FusedArgs &fa, int u, unsigned char *smem) {
+__device__ void fused_generic(const FusedParams &p, int u, unsigned char *smem) {
     using TK = typename std::conditional<F8, e5m2_t, uint16_t>::type;
-    attn_unit_generic<TK, kHD>(fa.attn, u, 0, *reinterpret_cast<AttnLds<kHD> *>(smem));
+    AttnArgs a{};
+    a.c = p.c;
+    a.new_pos = p.new_pos;
+    a.q = p.q;
+    a.k_new = p.k_new;
+    a.v_new = p.v_new;
+    a.out = p.out;
+    a.scores = p.scores;
+    a.scale = p.scale;
+    a.decay = p.decay;
+    a.nsplit = 1;
+    a.max_len = p.c.cap + 1;
+    a.append = true;
+    a.part = nullptr;
+    a.logits = p.logits;
+    attn_unit_generic<TK, kHD>(a, u, 0, *reinterpret_cast<AttnLds<kHD> *>(smem));
     if (MODE == kModeAttn) return;
     __syncthreads();
-    select_unit<1>(fa.sel, u, *reinterpret_cast<SelLds<1> *>(smem));
+    SelectArgs sa{};
+    sa.c = p.c;
+    sa.kind = p.kind;
+    sa.n_sink = p.n_sink;
+    sa.n_heavy = p.n_heavy;
+    sa.n_recent = p.n_recent;
+    sa.prompt_len = p.prompt_len;
+    sa.n_keep = p.n_keep;
+    sa.seed = p.seed;
+    sa.step = p.step;
+    sa.scores = p.scores;
+    sa.keep_slots = p.keep_slots;
+    sa.n_out = p.n_out;
+    select_unit<1>(sa, u, *reinterpret_cast<SelLds<1> *>(smem));
     __syncthreads();
-    compact_unit<TK, kHD>(fa.comp, u, *reinterpret_cast<CompLds *>(smem));
+    CompactArgs ca{};
+    ca.c = p.c;
+    ca.keep_slots = p.keep_slots;
+    ca.n_out = p.n_out;
+    ca.scores = p.scores;
+    ca.ordered = false;
+    ca.dst = p.c;
+    compact_unit<TK, kHD>(ca, u, *reinterpret_cast<CompLds *>(smem));
 }
 
 // PACK2: G <= 8, so one P.V MFMA carries both bf16 parts of p (rows 0..7 and
 // 8..15); otherwise each tile takes two MFMAs per dim block.  F8: E5M2 cache.
 template <int MODE, bool PAGED, int TC, bool PACK2, bool F8>
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU)))
-void fused_kernel(FusedArgs fa) {
+void fused_kernel(FusedParams fp) {
     using Row = typename KvRow<F8>::type;
     constexpr int RB = F8 ? kHD : 2 * kHD;   // bytes of one cached K or V row
     constexpr int NP = RB / 16;                // its 16-byte parts
@@ -101,8 +155,8 @@ void fused_kernel(FusedArgs fa) {
     // loops unroll into straight-line code with exact load/wait pairing
     constexpr int kNTW = (TC / 16 + kFWaves - 1) / kFWaves;
     extern __shared__ __align__(16) unsigned char smem[];
-    const AttnArgs &a = fa.attn;
-    const CacheDev &c = a.c;
+    const FusedParams &a = fp;
+    const CacheDev &c = fp.c;
     const int u = blockIdx.x;
     const int b = u / c.Hkv, h = u % c.Hkv;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -117,7 +171,7 @@ void fused_kernel(FusedArgs fa) {
     const int n = __builtin_amdgcn_readfirstlane(load_count(c, u, tid == 0));
     const int T = n + 1;
     if (T > TC || n >= c.cap) {
-        fused_generic<MODE, F8>(fa, u, smem);
+        fused_generic<MODE, F8>(fp, u, smem);
         return;
     }
 
@@ -194,6 +248,10 @@ void fused_kernel(FusedArgs fa) {
         return buffer_row<F8, PAGED>(rs, lane_off + toff + 4 * RB * k);
     };
     const int tn = n >> 4, qn = n & 15;   // tile and row of the new token
+    // the scale as a vector register: held across the K loop, it would
+    // otherwise pin a scalar register group that the loop keeps reloading
+    float scale;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(scale) : "s"(a.scale));
     int pmax = -1;
     {
         Row kb[DK][4];
@@ -248,14 +306,18 @@ void fused_kernel(FusedArgs fa) {
             for (int c4 = 0; c4 < 4; ++c4)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kop[c4]),
                                                               acc, 0, 0, 0);
-            const int j = 16 * t + col;
-            const int jc = 16 * t + (((col & 3) << 2) | (col >> 2));   // lg_col(j)
+            // tiles past the unit hold no key (uniform test); inside the
+            // last tile, keys past T get -inf, so the softmax weighs them 0
+            if (t < ntiles) {
+                const int j = 16 * t + col;
+                const int jc = 16 * t + (((col & 3) << 2) | (col >> 2));   // lg_col(j)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int g = 4 * r + ii;
-                const float z = (j < T) ? acc[ii] * a.scale : -INFINITY;
-                if (g < G && j < T) lg[g * LD + jc] = z;
-                mx[ii] = fmaxf(mx[ii], z);
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int g = 4 * r + ii;
+                    const float z = (j < T) ? acc[ii] * scale : -INFINITY;
+                    if (g < G) lg[g * LD + jc] = z;
+                    mx[ii] = fmaxf(mx[ii], z);
+                }
             }
         }
     }
@@ -332,26 +394,34 @@ void fused_kernel(FusedArgs fa) {
     for (int i = 0; i < kNTW; ++i) {
         const int t = w + kFWaves * i;
         const int c0 = 16 * t + 4 * r;         // lg_col of key 16t + r
-        const f32x4_t z = *reinterpret_cast<const f32x4_t *>(lrow + (c0 < LD - 3 ? c0 : 0));
-        f32x4_t p;
+        // logits of keys past T are -inf (weight 0); tiles past the unit
+        // (uniform test) and the padding rows of A weigh nothing
+        f32x4_t p = {0.f, 0.f, 0.f, 0.f};
+        if (t < ntiles) {
+            const f32x4_t z = *reinterpret_cast<const f32x4_t *>(lrow + c0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = arow ? __expf(z[e] - mrow) : 0.f;
+        }
         s16x4_t ahi, alo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool live = arow && (16 * t + 4 * e + r) < T;
-            p[e] = live ? __expf(z[e] - mrow) : 0.f;
             ahi[e] = bf16_bits(p[e]);
             alo[e] = bf16_bits(p[e] - bf16_value(ahi[e]));
         }
         if (hi_lane) {
             lsum += (p[0] + p[1]) + (p[2] + p[3]);
-            if (arow && t < ntiles) *reinterpret_cast<f32x4_t *>(lrow + c0) = p;
+            if (t < ntiles && arow) *reinterpret_cast<f32x4_t *>(lrow + c0) = p;
         }
         const s16x4_t a0 = (pack2 && !hi_lane) ? alo : ahi;
-        // B operand of MFMA m: element m of the four rows this lane loaded
+        // B operand of MFMA m: element m of the four rows this lane loaded;
+        // row n (read as zeros) is the new token's, in tile tn only
         u16x8_t vr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            vr[e] = (16 * t + 4 * e + r == n) ? vnc : as_bf16_row(vb[i % DV][e]);
+        for (int e = 0; e < 4; ++e) vr[e] = as_bf16_row(vb[i % DV][e]);
+        if (t == tn)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * e + r == qn) vr[e] = vnc;
         s16x4_t bop[8];
 #pragma unroll
         for (int m8 = 0; m8 < 8; ++m8)
@@ -422,7 +492,7 @@ void fused_kernel(FusedArgs fa) {
     // the registers held across it would spill there; both orders select the
     // same entries.
     constexpr bool kFold = MODE != kModeAttn && !PAGED;
-    const SelectArgs &sa = fa.sel;
+    const FusedParams &sa = fp;
     const int L = sm.posmax + 1;
     int ncand = 0, ndrop = 0, dslot = -1, barg = -1;
     uint64_t best = ~0ull;
@@ -745,13 +815,39 @@ size_t fused_smem_bytes(int G, int tcap) {
     return fast > gen ? fast : gen;
 }
 
+static FusedParams params_of(const FusedArgs &fa) {
+    FusedParams p{};
+    p.c = fa.attn.c;
+    p.new_pos = fa.attn.new_pos;
+    p.q = fa.attn.q;
+    p.k_new = fa.attn.k_new;
+    p.v_new = fa.attn.v_new;
+    p.out = fa.attn.out;
+    p.scores = fa.attn.scores;
+    p.logits = fa.attn.logits;
+    p.keep_slots = fa.sel.keep_slots;
+    p.n_out = fa.sel.n_out;
+    p.scale = fa.attn.scale;
+    p.decay = fa.attn.decay;
+    p.kind = fa.sel.kind;
+    p.n_sink = fa.sel.n_sink;
+    p.n_heavy = fa.sel.n_heavy;
+    p.n_recent = fa.sel.n_recent;
+    p.prompt_len = fa.sel.prompt_len;
+    p.n_keep = fa.sel.n_keep;
+    p.step = fa.sel.step;
+    p.seed = fa.sel.seed;
+    return p;
+}
+
 template <int MODE, bool PAGED, int TC, bool F8>
 static void launch_pk(const FusedArgs &fa, bool pack2, size_t smem, hipStream_t s) {
     const dim3 grid(fa.attn.c.B * fa.attn.c.Hkv), block(kFThreads);
+    const FusedParams p = params_of(fa);
     if (pack2)
-        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, true, F8>), grid, block, smem, s, fa);
+        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, true, F8>), grid, block, smem, s, p);
     else
-        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, false, F8>), grid, block, smem, s, fa);
+        hipLaunchKernelGGL((fused_kernel<MODE, PAGED, TC, false, F8>), grid, block, smem, s, p);
 }
 
 // every instantiation of one LDS capacity may use its largest LDS size
