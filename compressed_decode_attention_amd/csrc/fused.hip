@@ -252,6 +252,19 @@ void fused_kernel(FusedParams fp) {
     // otherwise pin a scalar register group that the loop keeps reloading
     float scale;
     asm volatile("v_mov_b32 %0, %1" : "=v"(scale) : "s"(a.scale));
+    // where this lane stores logit row 4r + ii of tile t: lgp[ii] + 16 t.  The
+    // padding rows (4r + ii >= G) store into this wave's own staging tile
+    // instead, every such lane to the same word (free at that point: LDS
+    // operations of a wave complete in order; 16 t + ii < 1,024 words), so the
+    // stores need no mask
+    static_assert(16 * (TC / 16) * 4 <= (int)kStageBytes, "dummy logit stores stay in the wave's tile");
+    float *lgp[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int g = 4 * r + ii;
+        lgp[ii] = (g < G) ? lg + g * LD + (((col & 3) << 2) | (col >> 2))
+                          : reinterpret_cast<float *>(stage) + ii;
+    }
     int pmax = -1;
     {
         Row kb[DK][4];
@@ -310,13 +323,11 @@ void fused_kernel(FusedParams fp) {
             // last tile, keys past T get -inf, so the softmax weighs them 0
             if (t < ntiles) {
                 const int j = 16 * t + col;
-                const int jc = 16 * t + (((col & 3) << 2) | (col >> 2));   // lg_col(j)
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
-                    const int g = 4 * r + ii;
                     const float z = (j < T) ? acc[ii] * scale : -INFINITY;
-                    if (g < G) lg[g * LD + jc] = z;
-                    mx[ii] = fmaxf(mx[ii], z);
+                    lgp[ii][16 * t] = z;
+                    mx[ii] = z > mx[ii] ? z : mx[ii];
                 }
             }
         }
