@@ -223,6 +223,22 @@ void split_kernel(AttnArgs a) {
     };
     // the new token's tile and row inside the chunk (none when n is outside)
     const int tn = (j0 <= n && n < j1) ? (n - j0) >> 4 : -1, qn = n & 15;
+    // the scale as a vector register: held across the K loop, it would
+    // otherwise pin a scalar register group that the loop keeps reloading
+    float scale;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(scale) : "s"(a.scale));
+    // where this lane stores logit row 4r + ii of tile t: lgp[ii] + 16 t.  The
+    // padding rows (4r + ii >= G) store into this wave's own staging tile
+    // instead, every such lane to the same word (free at that point: LDS
+    // operations of a wave complete in order), so the stores need no mask
+    static_assert(16 * (TC / 16) * 4 <= (int)kStageBytes, "dummy logit stores stay in the wave's tile");
+    float *lgp[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int g = 4 * r + ii;
+        lgp[ii] = (g < G) ? lg + g * LD + (((col & 3) << 2) | (col >> 2))
+                          : reinterpret_cast<float *>(stage) + ii;
+    }
     {
         Row kb[DK][4];
 #pragma unroll
@@ -258,15 +274,17 @@ void split_kernel(AttnArgs a) {
             for (int c4 = 0; c4 < 4; ++c4)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kop[c4]),
                                                               acc, 0, 0, 0);
-            const int jr = 16 * t + col;   // slot j0 + jr
-            const int jc = 16 * t + (((col & 3) << 2) | (col >> 2));   // lg_col(jr)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int g = 4 * r + ii;
+            // tiles past the chunk hold no key (uniform test); inside the
+            // last tile, keys past j1 get -inf, so they weigh 0
+            if (t < ntiles) {
+                const int jr = 16 * t + col;   // slot j0 + jr
                 const bool live = j0 + jr < j1;
-                const float z = live ? acc[ii] * a.scale : -INFINITY;
-                if (g < G && live) lg[g * LD + jc] = z;
-                mx[ii] = fmaxf(mx[ii], z);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float z = live ? acc[ii] * scale : -INFINITY;
+                    lgp[ii][16 * t] = z;
+                    mx[ii] = z > mx[ii] ? z : mx[ii];
+                }
             }
         }
     }
@@ -323,25 +341,33 @@ void split_kernel(AttnArgs a) {
     for (int i = 0; i < kNTW; ++i) {
         const int t = w + kFWaves * i;
         const int c0 = 16 * t + 4 * r;
-        const f32x4_t z = *reinterpret_cast<const f32x4_t *>(lrow + (c0 < LD - 3 ? c0 : 0));
-        f32x4_t p;
+        // logits past j1 are -inf (weight 0); tiles past the chunk (uniform
+        // test), the padding rows of A and an empty chunk weigh nothing
+        f32x4_t p = {0.f, 0.f, 0.f, 0.f};
+        if (t < ntiles) {
+            const f32x4_t z = *reinterpret_cast<const f32x4_t *>(lrow + c0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = (arow && any) ? __expf(z[e] - mrow) : 0.f;
+        }
         s16x4_t ahi, alo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool live = arow && any && (j0 + 16 * t + 4 * e + r) < j1;
-            p[e] = live ? __expf(z[e] - mrow) : 0.f;
             ahi[e] = bf16_bits(p[e]);
             alo[e] = bf16_bits(p[e] - bf16_value(ahi[e]));
         }
         if (hi_lane) {
             lsum += (p[0] + p[1]) + (p[2] + p[3]);
-            if (arow && t < ntiles) *reinterpret_cast<f32x4_t *>(lrow + c0) = p;
+            if (t < ntiles && arow) *reinterpret_cast<f32x4_t *>(lrow + c0) = p;
         }
         const s16x4_t a0 = (pack2 && !hi_lane) ? alo : ahi;
+        // row n (read as zeros) is the new token's, in tile tn only
         u16x8_t vr[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            vr[e] = (j0 + 16 * t + 4 * e + r == n) ? vnc : as_bf16_row(vb[i % DV][e]);
+        for (int e = 0; e < 4; ++e) vr[e] = as_bf16_row(vb[i % DV][e]);
+        if (t == tn)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * e + r == qn) vr[e] = vnc;
         s16x4_t bop[8];
 #pragma unroll
         for (int m8 = 0; m8 < 8; ++m8)
