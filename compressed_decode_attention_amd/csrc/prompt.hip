@@ -19,9 +19,10 @@
 //     of exp2(c2 * (dot - maximum)), rescaled once per two 16-slot tiles;
 //     four lanes merge into the row's log-sum-exp, written to the workspace.
 //  2. scores: one workgroup per 128 slots of a unit.  The slots are the B
-//     operand, held in registers; 64-row query tiles are staged in LDS.  Each
-//     lane sums exp2(c2 * dot - lse) over its 16 rows of a tile in fp32,
-//     adds that to an fp64 column sum (a fixed order: the scores are
+//     operand, held in registers; query tiles (64 consecutive positions of
+//     one head, so a tile's rows share one stride through q) are staged in
+//     LDS.  Each lane sums exp2(c2 * dot - lse) over its 16 rows of a tile in
+//     fp32, adds that to an fp64 column sum (a fixed order: the scores are
 //     deterministic), and one lane per slot adds the total to the score.
 // Tiles that no row of a block can see (from the positions alone) are
 // skipped, which halves the work of a causal prompt; tiles that every row sees
@@ -53,7 +54,7 @@ constexpr int kPD = 128;          // head_dim of this path
 constexpr int kStatRows = 128;    // rows per workgroup, pass 1 (32 per wave)
 constexpr int kScoreSlots = 128;  // slots per workgroup, pass 2 (32 per wave)
 constexpr int kTile = 64;         // slots (pass 1) or rows (pass 2) staged per step
-constexpr int kMaxRowTilesLds = 4096;   // pass 2: row tiles whose largest position fits in LDS
+constexpr int kMaxRowTilesLds = 4096;   // pass 2: position tiles whose largest position fits in LDS
 constexpr int kSG = 2;            // pass 1: 16-slot tiles per maximum and rescale
 
 __device__ inline bf16x8_p as_bf(u16x8_p x) { return __builtin_bit_cast(bf16x8_p, x); }
@@ -132,6 +133,8 @@ void prompt_stats_kernel(PromptArgs a) {
     const int32_t *P = c.pos + (size_t)u * c.cap;
     const int ntile = (n + kTile - 1) / kTile;
     int *tmin_s = tile_pos, *tmax_s = tile_pos + (c.cap + kTile - 1) / kTile;
+    // contiguous caches: the unit's first row; slot j is row j after it
+    const uint16_t *Ku = c.bs == 0 ? K + (size_t)u * c.cap * kPD : nullptr;
 
     // B operands: two 16-row tiles per wave; lane (col, r) holds dims
     // 32c + 8r .. 32c + 8r + 7 of row col
@@ -190,8 +193,8 @@ void prompt_stats_kernel(PromptArgs a) {
 #pragma unroll
         for (int pass = 0; pass < kTile / 16; ++pass) {
             const int j = min(j0 + 16 * pass + (tid >> 4), n - 1);
-            pre[pass] = *reinterpret_cast<const u16x8_p *>(K + row_of(c, b, h, j) * kPD +
-                                                           8 * (tid & 15));
+            const size_t row = Ku ? (size_t)j : row_of(c, b, h, j);
+            pre[pass] = *reinterpret_cast<const u16x8_p *>((Ku ? Ku : K) + row * kPD + 8 * (tid & 15));
         }
         const int jp = min(j0 + (tid & (kTile - 1)), n - 1);
         const int p = P[jp];
@@ -311,18 +314,19 @@ void prompt_stats_kernel(PromptArgs a) {
 // ---------------------------------------------------------------------------
 // pass 2: every slot's score receives the probabilities of all rows
 // ---------------------------------------------------------------------------
-// Software pipeline over the 64-row query tiles that see some slot of the
-// block (from each row tile's largest position, found up front when the
-// number of row tiles fits the LDS table; otherwise every tile is visited and
-// the masks alone decide): the next active tile's rows load into registers
-// while the MFMAs run on the current LDS buffer.
+// Software pipeline over the query tiles that see some slot of the block
+// (from the largest position of each 64-position tile, found up front when
+// the number of such tiles fits the LDS table; otherwise every tile is
+// visited and the masks alone decide; a position tile that sees nothing is
+// skipped for all heads of the group at once): the next active tile's rows
+// load into registers while the MFMAs run on the current LDS buffer.
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void prompt_scores_kernel(PromptArgs a) {
     __shared__ __align__(16) unsigned char qtile[2][kTile * 256];
     __shared__ int rpos[2][kTile];
     __shared__ float rlse[2][kTile];
     __shared__ int red[kPThreads / 64];
-    extern __shared__ int rtile_max[];   // [row tiles] largest position, when tracked
+    extern __shared__ int rtile_max[];   // [position tiles] largest position, when tracked
     const CacheDev &c = a.c;
     const int nrows = a.m_rows * c.G;
     const int nblk = (c.cap + kScoreSlots - 1) / kScoreSlots;
@@ -335,8 +339,13 @@ void prompt_scores_kernel(PromptArgs a) {
     if (blk * kScoreSlots >= n) return;   // the whole block is past the filled slots
     const uint16_t *K = static_cast<const uint16_t *>(c.k);
     const int32_t *P = c.pos + (size_t)u * c.cap;
-    const int nrt = (nrows + kTile - 1) / kTile;
-    const bool track = nrt <= a.row_tiles_lds;
+    // row tiles: 64 consecutive positions of one head, head-minor (tile rt
+    // holds positions 64 (rt / G) .. + 63 of head rt % G), so a tile's rows
+    // are consecutive query rows of one head
+    const int G = c.G;
+    const int nrt_g = (a.m_rows + kTile - 1) / kTile;   // position tiles
+    const int nrt = nrt_g * G;
+    const bool track = nrt_g <= a.row_tiles_lds;
 
     // B operands: two 16-slot tiles per wave; lane (col, r) holds dims
     // 32c + 8r .. of slot col
@@ -357,18 +366,16 @@ void prompt_scores_kernel(PromptArgs a) {
         kp[t] = kv[t] ? P[j] : INT_MAX;
         kmin = min(kmin, kp[t]);
     }
+    // largest position of every position tile (a wave's 64 lanes hold one)
     if (track)
-        for (int i = tid; i < nrt; i += kPThreads) rtile_max[i] = INT_MIN;
-    kmin = block_min(kmin, red);   // (its barriers also publish the initial values)
-    if (track) {
-        for (int rr = tid; rr < a.m_rows; rr += kPThreads) {
-            const int p = a.q_pos ? a.q_pos[(size_t)b * a.m_rows + rr] : INT_MAX;
-            const int t0 = rr * c.G / kTile, t1 = (rr * c.G + c.G - 1) / kTile;
-            atomicMax(&rtile_max[t0], p);
-            if (t1 != t0) atomicMax(&rtile_max[t1], p);
+        for (int k = w; k < nrt_g; k += kPThreads / 64) {
+            const int rr = kTile * k + lane;
+            const int p = rr < a.m_rows ? (a.q_pos ? a.q_pos[(size_t)b * a.m_rows + rr] : INT_MAX)
+                                        : INT_MIN;
+            const int hi = wave_max_i(p);
+            if (lane == 0) rtile_max[k] = hi;
         }
-        __syncthreads();
-    }
+    kmin = block_min(kmin, red);   // (its barriers also publish the tile bounds)
     // largest position of each 16-slot tile of the wave, and whether all its
     // slots are filled (only such tiles may skip the mask)
     int kmaxw[2];
@@ -381,7 +388,11 @@ void prompt_scores_kernel(PromptArgs a) {
     const float c2 = a.scale * kLog2e;
     auto next_active = [&](int rt) {
         if (track)
-            while (rt < nrt && rtile_max[rt] < kmin) ++rt;
+            while (rt < nrt) {
+                const int k = rt / G;
+                if (rtile_max[k] >= kmin) break;
+                rt = (k + 1) * G;   // no row of this position tile sees the block
+            }
         return rt;
     };
     // the tile's query rows, positions and base-2 log-sum-exps into registers;
@@ -390,18 +401,24 @@ void prompt_scores_kernel(PromptArgs a) {
     u16x8_p pre[kTile / 16];
     int ppos = 0;
     float plse = 0.f;
+    // position rr of head g (of this kv head's group) is query row
+    // (b m + rr) Hq + h G + g of q_rows, and statistic rr G + g of the unit
+    const uint16_t *qbase = static_cast<const uint16_t *>(a.q_rows) +
+                            ((size_t)b * a.m_rows * c.Hq + (size_t)h * G) * kPD;
     auto fetch = [&](int rt) {
-        const int R0 = rt * kTile;
+        const int k = rt / G, g = rt - k * G;
+        const int rr0 = kTile * k;
 #pragma unroll
         for (int pass = 0; pass < kTile / 16; ++pass) {
-            const int R = min(R0 + 16 * pass + (tid >> 4), nrows - 1);
-            pre[pass] = *reinterpret_cast<const u16x8_p *>(q_row(a, b, h, R) + 8 * (tid & 15));
+            const int rr = min(rr0 + 16 * pass + (tid >> 4), a.m_rows - 1);
+            pre[pass] = *reinterpret_cast<const u16x8_p *>(
+                qbase + ((size_t)rr * c.Hq + g) * kPD + 8 * (tid & 15));
         }
-        const int R = R0 + (tid & (kTile - 1)), Rc = min(R, nrows - 1);
-        const int p = row_pos(a, b, Rc);
-        const float l = a.lse[(size_t)u * nrows + Rc];
-        ppos = R < nrows ? p : INT_MIN;
-        plse = R < nrows ? l : -INFINITY;
+        const int rr = rr0 + (tid & (kTile - 1)), rc = min(rr, a.m_rows - 1);
+        const int p = a.q_pos ? a.q_pos[(size_t)b * a.m_rows + rc] : INT_MAX;
+        const float l = a.lse[(size_t)u * nrows + (size_t)rc * G + g];
+        ppos = rr < a.m_rows ? p : INT_MIN;
+        plse = rr < a.m_rows ? l : -INFINITY;
     };
 
     double cs[2] = {0.0, 0.0};
@@ -409,7 +426,6 @@ void prompt_scores_kernel(PromptArgs a) {
     if (cur < nrt) fetch(cur);
     int buf = 0;
     while (cur < nrt) {
-        const int R0 = cur * kTile;
 #pragma unroll
         for (int pass = 0; pass < kTile / 16; ++pass)
             *reinterpret_cast<u16x8_p *>(qtile[buf] + tile_off(16 * pass + (tid >> 4), tid & 15)) =
@@ -423,7 +439,7 @@ void prompt_scores_kernel(PromptArgs a) {
         if (nxt < nrt) fetch(nxt);   // lands while this tile computes
         // every row of a filled 64-row tile sees the wave's whole 16-slot tile
         const int tmin = __builtin_amdgcn_readfirstlane(wave_min_i(rpos[buf][lane]));
-        const bool rows_full = R0 + kTile <= nrows;
+        const bool rows_full = kTile * (cur / G) + kTile <= a.m_rows;
         bool inner[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) inner[t] = slots_full[t] && rows_full && kmaxw[t] <= tmin;
@@ -499,10 +515,10 @@ hipError_t launch_prompt_scores(const PromptArgs &a, hipStream_t s) {
     const size_t tile_bytes = 2 * (size_t)((a.c.cap + kTile - 1) / kTile) * sizeof(int);
     hipLaunchKernelGGL(prompt_stats_kernel, dim3(groups * 8 * nb1), dim3(kPThreads), tile_bytes, s,
                        a);
-    // row tiles whose largest position is tracked in LDS (up to 16 KB)
+    // position tiles whose largest position is tracked in LDS (up to 16 KB)
     PromptArgs a2 = a;
-    const int nrt = (nrows + kTile - 1) / kTile;
-    a2.row_tiles_lds = nrt <= kMaxRowTilesLds ? nrt : 0;
+    const int nrt_g = (a.m_rows + kTile - 1) / kTile;
+    a2.row_tiles_lds = nrt_g <= kMaxRowTilesLds ? nrt_g : 0;
     hipLaunchKernelGGL(prompt_scores_kernel, dim3(groups * 8 * nb2), dim3(kPThreads),
                        (size_t)a2.row_tiles_lds * sizeof(int), s, a2);
     return hipGetLastError();
