@@ -11,15 +11,16 @@
 // nothing.
 //
 // Two passes, both exact (no approximation of the softmax):
-//  1. statistics: one workgroup per 128 rows of a unit.  K tiles of 64 slots
+//  1. statistics: one workgroup per 256 rows of a unit.  K tiles of 64 slots
 //     are staged in LDS (XOR swizzle, conflict-free reads) and enter
 //     v_mfma_f32_16x16x32_bf16 as the A operand; the rows are the B operand,
-//     held in registers.  Each lane keeps a running maximum of the raw dot
+//     held in registers (64 rows per wave, so each A operand read from LDS
+//     feeds four row tiles).  Each lane keeps a running maximum of the raw dot
 //     products (the scale is positive, so the order is the same) and a sum
 //     of exp2(c2 * (dot - maximum)), rescaled once per two 16-slot tiles;
 //     four lanes merge into the row's log-sum-exp, written to the workspace.
-//  2. scores: one workgroup per 128 slots of a unit.  The slots are the B
-//     operand, held in registers; query tiles (64 consecutive positions of
+//  2. scores: one workgroup per 256 slots of a unit.  The slots are the B
+//     operand, held in registers (64 slots per wave); query tiles (64 consecutive positions of
 //     one head, so a tile's rows share one stride through q) are staged in
 //     LDS.  Each lane sums exp2(c2 * dot - lse) over its 16 rows of a tile in
 //     fp32, adds that to an fp64 column sum (a fixed order: the scores are
@@ -34,7 +35,9 @@
 // position come from a wave reduction (a wave's 64 lanes hold one tile).  All
 // blocks of one unit run on one XCD (workgroups are dealt round-robin over the
 // eight XCDs), so the K (pass 1) or Q (pass 2) rows they share are read from
-// that XCD's L2.
+// that XCD's L2.  Both kernels run three waves per SIMD: the larger register
+// tiles halve the LDS reads and the per-tile fixed work (staging, barrier,
+// next-tile search) per product, which pays more than a fourth wave.
 #include "kvc_internal.h"
 
 #include <limits.h>
@@ -51,8 +54,10 @@ typedef uint16_t u16x8_p __attribute__((ext_vector_type(8)));
 
 constexpr int kPThreads = 256;
 constexpr int kPD = 128;          // head_dim of this path
-constexpr int kStatRows = 128;    // rows per workgroup, pass 1 (32 per wave)
-constexpr int kScoreSlots = 128;  // slots per workgroup, pass 2 (32 per wave)
+constexpr int kRT = 4;            // pass 1: 16-row tiles per wave (B operands in registers)
+constexpr int kStatRows = 64 * kRT;     // rows per workgroup, pass 1
+constexpr int kST = 4;            // pass 2: 16-slot tiles per wave (B operands in registers)
+constexpr int kScoreSlots = 64 * kST;   // slots per workgroup, pass 2
 constexpr int kTile = 64;         // slots (pass 1) or rows (pass 2) staged per step
 constexpr int kMaxRowTilesLds = 4096;   // pass 2: position tiles whose largest position fits in LDS
 constexpr int kSG = 2;            // pass 1: 16-slot tiles per maximum and rescale
@@ -114,7 +119,7 @@ __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }  
 // (found up front from each tile's smallest position): while the MFMAs run on
 // one LDS buffer, the next active tile's K rows are already in registers on
 // their way; one barrier per tile.
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void prompt_stats_kernel(PromptArgs a) {
     __shared__ __align__(16) unsigned char ktile[2][kTile * 256];
     __shared__ int kpos[2][kTile];
@@ -136,14 +141,14 @@ void prompt_stats_kernel(PromptArgs a) {
     // contiguous caches: the unit's first row; slot j is row j after it
     const uint16_t *Ku = c.bs == 0 ? K + (size_t)u * c.cap * kPD : nullptr;
 
-    // B operands: two 16-row tiles per wave; lane (col, r) holds dims
+    // B operands: kRT 16-row tiles per wave; lane (col, r) holds dims
     // 32c + 8r .. 32c + 8r + 7 of row col
-    u16x8_p qb[2][4];
-    int qp[2], Rw[2];
+    u16x8_p qb[kRT][4];
+    int qp[kRT], Rw[kRT];
     int qmax = INT_MIN;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int R = blk * kStatRows + 32 * w + 16 * t + col;
+    for (int t = 0; t < kRT; ++t) {
+        const int R = blk * kStatRows + 16 * kRT * w + 16 * t + col;
         Rw[t] = R;
         const bool ok = R < nrows;
         const uint16_t *qr = q_row(a, b, h, ok ? R : 0);
@@ -171,12 +176,12 @@ void prompt_stats_kernel(PromptArgs a) {
     qmax = block_max(qmax, red);   // (its barriers also publish the tile bounds)
     // smallest position of each 16-row tile of the wave, and whether the tile
     // holds no padding row (only such tiles may skip the mask)
-    int qmin[2];
-    bool rows_full[2];
+    int qmin[kRT];
+    bool rows_full[kRT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kRT; ++t) {
         qmin[t] = __builtin_amdgcn_readfirstlane(wave_min_i(qp[t]));
-        rows_full[t] = blk * kStatRows + 32 * w + 16 * t + 15 < nrows;
+        rows_full[t] = blk * kStatRows + 16 * kRT * w + 16 * t + 15 < nrows;
     }
     const float c2 = a.scale * kLog2e;
     // next tile (from kt on) that some row of the block sees (uniform)
@@ -203,7 +208,9 @@ void prompt_stats_kernel(PromptArgs a) {
 
     // running maximum of the raw dot products (c2 > 0 keeps the order) and
     // the sum of exp2(c2 * (dot - maximum)), per lane and row tile
-    float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};
+    float mm[kRT], ll[kRT];
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) { mm[t] = -INFINITY; ll[t] = 0.f; }
     int cur = next_active(0);
     if (cur < ntile) fetch(cur);
     int buf = 0;
@@ -221,17 +228,18 @@ void prompt_stats_kernel(PromptArgs a) {
         // no mask (positions alone cannot tell padding, so fullness is checked)
         const bool slots_full = j0 + kTile <= n;
         const int kmax = tmax_s[cur];
-        bool inner[2];
+        bool inner[kRT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) inner[t] = slots_full && rows_full[t] && kmax <= qmin[t];
+        for (int t = 0; t < kRT; ++t) inner[t] = slots_full && rows_full[t] && kmax <= qmin[t];
         // two 16-slot tiles' dot products at a time (8 per lane and row
-        // tile), then one maximum and one rescale per row tile.  The mask
+        // tile, for each of the wave's row tiles), then one maximum and one
+        // rescale per row tile.  The mask
         // decision is uniform per tile, so each variant is straight-line code.
         auto tile_body = [&](auto masked_c) {
             constexpr bool kMasked = decltype(masked_c)::value;
 #pragma unroll
             for (int s0 = 0; s0 < kTile / 16; s0 += kSG) {
-                f32x4_p acc[2][kSG];
+                f32x4_p acc[kRT][kSG];
 #pragma unroll
                 for (int s = 0; s < kSG; ++s) {
                     // A operand: lane (col, r) holds dims 32c + 8r.. of slot 16(s0+s) + col
@@ -242,7 +250,7 @@ void prompt_stats_kernel(PromptArgs a) {
                         ka[c4] = *reinterpret_cast<const u16x8_p *>(ktile[buf] + tile_off(q, 4 * c4 + r));
                     // C[slot 4r + i][row col]
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < kRT; ++t) {
                         acc[t][s] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int c4 = 0; c4 < 4; ++c4)
@@ -260,12 +268,12 @@ void prompt_stats_kernel(PromptArgs a) {
                             const int kp = kpos[buf][jj];
                             const bool live = j0 + jj < n;
 #pragma unroll
-                            for (int t = 0; t < 2; ++t)
+                            for (int t = 0; t < kRT; ++t)
                                 acc[t][s][i] = (live && kp <= qp[t]) ? acc[t][s][i] : -INFINITY;
                         }
                 }
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < kRT; ++t) {
                     float mx = mm[t];
 #pragma unroll
                     for (int s = 0; s < kSG; ++s)
@@ -285,7 +293,10 @@ void prompt_stats_kernel(PromptArgs a) {
                 }
             }
         };
-        if (inner[0] && inner[1])
+        bool all_inner = true;
+#pragma unroll
+        for (int t = 0; t < kRT; ++t) all_inner = all_inner && inner[t];
+        if (all_inner)
             tile_body(std::integral_constant<bool, false>());
         else
             tile_body(std::integral_constant<bool, true>());
@@ -294,7 +305,7 @@ void prompt_stats_kernel(PromptArgs a) {
     }
     // merge the four lanes of each row, then log-sum-exp
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kRT; ++t) {
         float m = mm[t], l = ll[t];
 #pragma unroll
         for (int off = 16; off <= 32; off <<= 1) {
@@ -320,7 +331,7 @@ void prompt_stats_kernel(PromptArgs a) {
 // visited and the masks alone decide; a position tile that sees nothing is
 // skipped for all heads of the group at once): the next active tile's rows
 // load into registers while the MFMAs run on the current LDS buffer.
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void prompt_scores_kernel(PromptArgs a) {
     __shared__ __align__(16) unsigned char qtile[2][kTile * 256];
     __shared__ int rpos[2][kTile];
@@ -347,15 +358,15 @@ void prompt_scores_kernel(PromptArgs a) {
     const int nrt = nrt_g * G;
     const bool track = nrt_g <= a.row_tiles_lds;
 
-    // B operands: two 16-slot tiles per wave; lane (col, r) holds dims
+    // B operands: kST 16-slot tiles per wave; lane (col, r) holds dims
     // 32c + 8r .. of slot col
-    u16x8_p kb[2][4];
-    int kp[2], jw[2];
-    bool kv[2];
+    u16x8_p kb[kST][4];
+    int kp[kST], jw[kST];
+    bool kv[kST];
     int kmin = INT_MAX;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int j = blk * kScoreSlots + 32 * w + 16 * t + col;
+    for (int t = 0; t < kST; ++t) {
+        const int j = blk * kScoreSlots + 16 * kST * w + 16 * t + col;
         jw[t] = j;
         kv[t] = j < n;
         const size_t row = row_of(c, b, h, kv[t] ? j : 0);
@@ -378,12 +389,12 @@ void prompt_scores_kernel(PromptArgs a) {
     kmin = block_min(kmin, red);   // (its barriers also publish the tile bounds)
     // largest position of each 16-slot tile of the wave, and whether all its
     // slots are filled (only such tiles may skip the mask)
-    int kmaxw[2];
-    bool slots_full[2];
+    int kmaxw[kST];
+    bool slots_full[kST];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kST; ++t) {
         kmaxw[t] = __builtin_amdgcn_readfirstlane(wave_max_i(kp[t]));
-        slots_full[t] = blk * kScoreSlots + 32 * w + 16 * t + 15 < n;
+        slots_full[t] = blk * kScoreSlots + 16 * kST * w + 16 * t + 15 < n;
     }
     const float c2 = a.scale * kLog2e;
     auto next_active = [&](int rt) {
@@ -421,7 +432,9 @@ void prompt_scores_kernel(PromptArgs a) {
         plse = rr < a.m_rows ? l : -INFINITY;
     };
 
-    double cs[2] = {0.0, 0.0};
+    double cs[kST];
+#pragma unroll
+    for (int t = 0; t < kST; ++t) cs[t] = 0.0;
     int cur = next_active(0);
     if (cur < nrt) fetch(cur);
     int buf = 0;
@@ -440,13 +453,15 @@ void prompt_scores_kernel(PromptArgs a) {
         // every row of a filled 64-row tile sees the wave's whole 16-slot tile
         const int tmin = __builtin_amdgcn_readfirstlane(wave_min_i(rpos[buf][lane]));
         const bool rows_full = kTile * (cur / G) + kTile <= a.m_rows;
-        bool inner[2];
+        bool inner[kST];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) inner[t] = slots_full[t] && rows_full && kmaxw[t] <= tmin;
+        for (int t = 0; t < kST; ++t) inner[t] = slots_full[t] && rows_full && kmaxw[t] <= tmin;
         // the tile's probabilities are summed in fp32 per lane (16 rows per
         // slot and lane, in a fixed order), then added to the fp64 total.
         // The mask decision is uniform per tile: straight-line variants.
-        float ts[2] = {0.f, 0.f};
+        float ts[kST];
+#pragma unroll
+        for (int t = 0; t < kST; ++t) ts[t] = 0.f;
         auto tile_body = [&](auto masked_c) {
             constexpr bool kMasked = decltype(masked_c)::value;
 #pragma unroll
@@ -466,7 +481,7 @@ void prompt_scores_kernel(PromptArgs a) {
                     if constexpr (kMasked) rp[i] = rpos[buf][16 * s + 4 * r + i];
                 }
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < kST; ++t) {
                     f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int c4 = 0; c4 < 4; ++c4)
@@ -482,18 +497,21 @@ void prompt_scores_kernel(PromptArgs a) {
                 }
             }
         };
-        if (inner[0] && inner[1])
+        bool all_inner = true;
+#pragma unroll
+        for (int t = 0; t < kST; ++t) all_inner = all_inner && inner[t];
+        if (all_inner)
             tile_body(std::integral_constant<bool, false>());
         else
             tile_body(std::integral_constant<bool, true>());
 #pragma unroll
-        for (int t = 0; t < 2; ++t) cs[t] += (double)ts[t];
+        for (int t = 0; t < kST; ++t) cs[t] += (double)ts[t];
         buf ^= 1;
         cur = nxt;
     }
     // the four lanes of a slot hold different rows: add them, then the score
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kST; ++t) {
         double v = cs[t];
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
