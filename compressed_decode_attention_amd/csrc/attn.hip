@@ -39,9 +39,9 @@ struct CombLdsT {
 using CombLds = CombLdsT<kCombStage>;
 
 // The splits' (m, l) of one unit into LDS (the caller syncs).
-template <int D, typename CL>
+template <int D, int NT = kAttnThreads, typename CL>
 __device__ inline void combine_load_ml(const float *pp, int ns, int G, CL &CB) {
-    for (int i = threadIdx.x; i < ns * G; i += kAttnThreads) {
+    for (int i = threadIdx.x; i < ns * G; i += NT) {
         const int s = i / G, g = i % G;
         CB.ms[s][g] = pp[(s * G + g) * (D + 2) + D];
         CB.ls[s][g] = pp[(s * G + g) * (D + 2) + D + 1];
@@ -50,7 +50,7 @@ __device__ inline void combine_load_ml(const float *pp, int ns, int G, CL &CB) {
 
 // Global max M and normaliser L per head, then the factor of each split,
 // exp(m_s - M) / L (0 for an empty split); L sums the splits in order.
-template <typename CL>
+template <int NT = kAttnThreads, typename CL>
 __device__ inline void combine_factors(int ns, int G, CL &CB) {
     const int tid = threadIdx.x;
     if (tid < G) {
@@ -60,7 +60,7 @@ __device__ inline void combine_factors(int ns, int G, CL &CB) {
         CB.Mg[tid] = M;
     }
     __syncthreads();
-    for (int i = tid; i < ns * G; i += kAttnThreads) {
+    for (int i = tid; i < ns * G; i += NT) {
         const int s = i / G, g = i % G;
         const float ms = CB.ms[s][g];
         CB.fac[s][g] = (ms == -INFINITY) ? 0.f : __expf(ms - CB.Mg[g]);
@@ -73,7 +73,7 @@ __device__ inline void combine_factors(int ns, int G, CL &CB) {
         CB.Lg[tid] = L;
     }
     __syncthreads();
-    for (int i = tid; i < ns * G; i += kAttnThreads) {
+    for (int i = tid; i < ns * G; i += NT) {
         const int s = i / G, g = i % G;
         CB.fac[s][g] = CB.fac[s][g] / CB.Lg[g];
     }
@@ -86,7 +86,7 @@ __device__ inline void combine_factors(int ns, int G, CL &CB) {
 // the unit's partials returns zeros past its end), so all of a thread's loads
 // of a pass are in flight at once.  Lanes past the live elements compute on
 // padding and store nothing.
-template <int D, int STAGE>
+template <int D, int STAGE, int NT = kAttnThreads>
 __device__ inline void combine_output(const float *pp, int ns, int G, CombLdsT<STAGE> &CB,
                                       float *out_row) {
     const int tid = threadIdx.x;
@@ -94,8 +94,8 @@ __device__ inline void combine_output(const float *pp, int ns, int G, CombLdsT<S
     const int sb_max = STAGE / GD;
     const uint32_t bytes = (uint32_t)(ns * G * (D + 2)) * 4u;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(pp, bytes);
-    constexpr int kE = (kMaxGroup * D + kAttnThreads - 1) / kAttnThreads;
-    constexpr int kL = STAGE / 2 / kAttnThreads;   // float2 loads per thread and pass
+    constexpr int kE = (kMaxGroup * D + NT - 1) / NT;
+    constexpr int kL = STAGE / 2 / NT;   // float2 loads per thread and pass
     float o[kE];
 #pragma unroll
     for (int k = 0; k < kE; ++k) o[k] = 0.f;
@@ -105,20 +105,20 @@ __device__ inline void combine_output(const float *pp, int ns, int G, CombLdsT<S
         u32x2_t r[kL];
 #pragma unroll
         for (int k = 0; k < kL; ++k) {
-            const int i = tid + k * kAttnThreads;   // float2 index within the block
+            const int i = tid + k * NT;   // float2 index within the block
             const int s = s0 + i / GD2, e2 = 2 * (i % GD2);
             const uint32_t off = (i < n2) ? (uint32_t)((s * G + e2 / D) * (D + 2) + e2 % D) * 4u : bytes;
             r[k] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
         }
 #pragma unroll
         for (int k = 0; k < kL; ++k)
-            reinterpret_cast<u32x2_t *>(CB.stage)[tid + k * kAttnThreads] = r[k];
+            reinterpret_cast<u32x2_t *>(CB.stage)[tid + k * NT] = r[k];
         __syncthreads();
         for (int s = 0; s < sb; ++s) {
             const float *st = CB.stage + s * GD;
 #pragma unroll
             for (int k = 0; k < kE; ++k) {
-                const int el = tid + k * kAttnThreads;
+                const int el = tid + k * NT;
                 o[k] += st[el] * CB.fac[s0 + s][el / D];
             }
         }
@@ -126,14 +126,14 @@ __device__ inline void combine_output(const float *pp, int ns, int G, CombLdsT<S
     }
 #pragma unroll
     for (int k = 0; k < kE; ++k) {
-        const int el = tid + k * kAttnThreads;
+        const int el = tid + k * NT;
         if (el < GD) out_row[el] = o[k];
     }
 }
 
 // Combine the splits of one unit: rescale partial sums to the global max,
 // normalise, update scores and the slot count.
-template <int D, int STAGE>
+template <int D, int STAGE, int NT = kAttnThreads>
 __device__ inline void combine_unit(const AttnArgs &a, int u, CombLdsT<STAGE> &CB) {
     const CacheDev &c = a.c;
     const int G = c.G, ns = a.nsplit;
@@ -148,10 +148,10 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLdsT<STAGE> &C
     const int nse = split_count(T_len, ns, a.max_len);   // the splits that hold entries
     const float *pp = a.part + (size_t)u * ns * G * (D + 2);
 
-    combine_load_ml<D>(pp, nse, G, CB);
+    combine_load_ml<D, NT>(pp, nse, G, CB);
     __syncthreads();
-    combine_factors(nse, G, CB);
-    combine_output<D>(pp, nse, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
+    combine_factors<NT>(nse, G, CB);
+    combine_output<D, STAGE, NT>(pp, nse, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
     if (a.scores) {
         // p summed over the group for every attended slot (heads in order),
         // kJ slots per thread at a time; every logit load of a batch goes out
@@ -163,12 +163,12 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLdsT<STAGE> &C
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(lg, lbytes);
         float *sc = a.scores + (size_t)u * c.cap;
         constexpr int kJ = (STAGE == kCombStage) ? 4 : 2;
-        for (int j0 = tid; j0 < T_len; j0 += kJ * kAttnThreads) {
+        for (int j0 = tid; j0 < T_len; j0 += kJ * NT) {
             int jj[kJ], sj[kJ];
             float ps[kJ], old[kJ], lv[kMaxGroup][kJ];
 #pragma unroll
             for (int q = 0; q < kJ; ++q) {
-                const int j = j0 + q * kAttnThreads;
+                const int j = j0 + q * NT;
                 jj[q] = j < T_len ? j : T_len - 1;
                 sj[q] = jj[q] / chunk;
                 ps[q] = 0.f;
@@ -188,7 +188,7 @@ __device__ inline void combine_unit(const AttnArgs &a, int u, CombLdsT<STAGE> &C
                     for (int q = 0; q < kJ; ++q) ps[q] += lv[g][q] * fac[sj[q]][g];
 #pragma unroll
             for (int q = 0; q < kJ; ++q) {
-                const int j = j0 + q * kAttnThreads;
+                const int j = j0 + q * NT;
                 if (j < n) sc[j] = score_update(old[q], ps[q], a.decay);
                 else if (j == n && can_store) sc[n] = score_update(0.f, ps[q], a.decay);
             }
@@ -261,8 +261,8 @@ __device__ inline int presel_finish(const AttnArgs &a, const SelectArgs &sa, int
 // dependent memory round trips (the first loads go out together, and the
 // moved row is copied while the output is combined).  Returns false, having
 // written nothing, when more than one slot leaves.
-template <typename T, int D, typename CL>
-__device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, int u, CL &CB,
+template <typename T, int D, int NT, int STAGE>
+__device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, int u, CombLdsT<STAGE> &CB,
                                      int &sh_e) {
     const CacheDev &c = a.c;
     const int G = c.G, ns = a.nsplit;
@@ -273,7 +273,7 @@ __device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, in
     int n = c.n_slots[u];
     n = (n < 0) ? 0 : (n > c.cap ? c.cap : n);
     const int nse = split_count(n + 1, ns, a.max_len);   // the splits that hold entries
-    combine_load_ml<D>(pp, nse, G, CB);
+    combine_load_ml<D, NT>(pp, nse, G, CB);
     if (tid < 64) {
         const int e = presel_finish(a, sa, u, nse);
         if (tid == 0) sh_e = e;
@@ -297,8 +297,8 @@ __device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, in
         row = reinterpret_cast<const uint4 *>(X + row_of(c, b, h, src) * D)[tid % kParts];
     if (move && tid == 0) psrc = P[src];
 
-    combine_factors(nse, G, CB);
-    combine_output<D>(pp, nse, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
+    combine_factors<NT>(nse, G, CB);
+    combine_output<D, STAGE, NT>(pp, nse, G, CB, a.out + ((size_t)b * c.Hq + (size_t)h * G) * D);
     if (move && tid < 2 * kParts)
         reinterpret_cast<uint4 *>(X + row_of(c, b, h, e) * D)[tid % kParts] = row;
     if (move && tid == 0) P[e] = psrc;
@@ -306,26 +306,40 @@ __device__ inline bool finish_presel(const AttnArgs &a, const SelectArgs &sa, in
     return true;
 }
 
-template <typename T, int D, bool SMALL>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(SMALL ? 4 : 1)))
+// Three instances: SMALL (up to kSelLdsSmall attended slots, 256 threads,
+// four workgroups per CU), MID (up to kSelLdsSlots, 256 threads, two per CU)
+// and LONG (longer units: 512 threads, still two per CU, so that the score
+// update and the selection passes over tens of thousands of slots, one unit's
+// critical path, have twice the threads and loads in flight; 1,024 threads
+// would leave one workgroup per CU for the batch's many shorter units).
+enum FinishSize { kFinishSmall, kFinishMid, kFinishLong };
+template <int SZ>
+struct FinishCfg {
+    static constexpr int SEL = SZ == kFinishSmall ? kSelLdsSmall : kSelLdsSlots;
+    static constexpr int STAGE = SZ == kFinishSmall ? kCombStageSmall : kCombStage;
+    static constexpr int NT = SZ == kFinishLong ? 512 : kAttnThreads;
+    static constexpr int WPE = SZ == kFinishMid ? 1 : 4;
+};
+
+template <typename T, int D, int SZ>
+__global__ __launch_bounds__(FinishCfg<SZ>::NT) __attribute__((amdgpu_waves_per_eu(FinishCfg<SZ>::WPE)))
 void finish_kernel(AttnArgs a, SelectArgs sa, CompactArgs ca) {
-    constexpr int SEL = SMALL ? kSelLdsSmall : kSelLdsSlots;
-    constexpr int STAGE = SMALL ? kCombStageSmall : kCombStage;
-    __shared__ FinishLdsT<SEL, STAGE> F;
+    using Cfg = FinishCfg<SZ>;
+    __shared__ FinishLdsT<Cfg::SEL, Cfg::STAGE> F;
     __shared__ int sh_e;
     const int u = blockIdx.x;
     if (a.presel && !a.scores && a.nsplit > 1) {
-        if (finish_presel<T, D>(a, sa, u, F.comb, sh_e)) return;
+        if (finish_presel<T, D, Cfg::NT, Cfg::STAGE>(a, sa, u, F.comb, sh_e)) return;
         __syncthreads();
     }
     if (a.nsplit > 1) {
-        combine_unit<D>(a, u, F.comb);
+        combine_unit<D, Cfg::STAGE, Cfg::NT>(a, u, F.comb);
         __syncthreads();
     }
-    const int e = select_unit<SEL>(sa, u, F.sel);
+    const int e = select_unit<Cfg::SEL, Cfg::NT>(sa, u, F.sel);
     __syncthreads();
     if (e >= -1) compact_one<T, D>(ca, u, e);
-    else compact_unit<T, D>(ca, u, F.comp);
+    else compact_unit<T, D, Cfg::NT>(ca, u, F.comp);
 }
 
 template <typename T, int D>
@@ -367,11 +381,15 @@ hipError_t launch_attn(const AttnArgs &a, int dtype, hipStream_t s) {
 template <typename T, int D>
 static void launch_finish_typed(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,
                                 hipStream_t s) {
+    const dim3 grid(a.c.B * a.c.Hkv);
     if (a.max_len <= kSelLdsSmall)
-        hipLaunchKernelGGL((finish_kernel<T, D, true>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0,
+        hipLaunchKernelGGL((finish_kernel<T, D, kFinishSmall>), grid, dim3(FinishCfg<kFinishSmall>::NT), 0,
                            s, a, sa, ca);
+    else if (a.max_len <= kSelLdsSlots)
+        hipLaunchKernelGGL((finish_kernel<T, D, kFinishMid>), grid, dim3(FinishCfg<kFinishMid>::NT), 0, s,
+                           a, sa, ca);
     else
-        hipLaunchKernelGGL((finish_kernel<T, D, false>), dim3(a.c.B * a.c.Hkv), dim3(kAttnThreads), 0,
+        hipLaunchKernelGGL((finish_kernel<T, D, kFinishLong>), grid, dim3(FinishCfg<kFinishLong>::NT), 0,
                            s, a, sa, ca);
 }
 

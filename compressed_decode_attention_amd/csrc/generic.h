@@ -203,6 +203,7 @@ __device__ inline void attn_unit_generic(const AttnArgs &a, int u, int s, AttnLd
 enum : uint8_t { kDrop = 0, kKeep = 1, kCand = 2 };
 
 constexpr int kSelThreads = 256;
+constexpr int kMaxBlockWaves = 16;   // the block helpers' scratch: up to 1,024 threads
 
 struct SelView {
     int kind, n_sink, n_recent, prompt_len;
@@ -242,15 +243,15 @@ struct SelLds {
     int32_t pos_s[kSelLds];
     uint8_t cls_s[kSelLds];
     int hist[256];
-    int red[kSelThreads / 64];
-    uint32_t red3[3 * (kSelThreads / 64)];
+    int red[kMaxBlockWaves];
+    uint32_t red3[3 * kMaxBlockWaves];
     int sh_digit, sh_krem, sh_done;
 };
 
 // Units of up to kSelLds slots keep their ranking keys in LDS; longer units
 // recompute them from global memory on every pass.  Returns the evicted slot
 // when at most one slot leaves (-1: none leaves), else -2.
-template <int kSelLds>
+template <int kSelLds, int NT = kSelThreads>
 __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S) {
     const CacheDev &c = a.c;
     const int tid = threadIdx.x;
@@ -285,7 +286,7 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
     int mx = -1;
     if (in_lds) {
 #pragma unroll 4
-        for (int j = tid; j < n; j += kSelThreads) {
+        for (int j = tid; j < n; j += NT) {
             const int32_t p = v.P[j];
             pos_s[j] = p;
             if (h2o_keys) prim_s[j] = float_order_bits(v.S[j]);
@@ -293,12 +294,12 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
         }
     } else {
 #pragma unroll 4
-        for (int j = tid; j < n; j += kSelThreads) mx = max(mx, v.P[j]);
+        for (int j = tid; j < n; j += NT) mx = max(mx, v.P[j]);
     }
     v.L = block_max_i(mx, red) + 1;   // (its barriers publish the LDS copies)
 
     // Units longer than the LDS copy are read from global memory kU slots per
-    // thread at a time (slots j0 + q * kSelThreads, the same order as one at
+    // thread at a time (slots j0 + q * NT, the same order as one at
     // a time), every load of a group issued before any is used; scores are
     // fetched for every policy (positions stand in when there are none).  A
     // caller with no LDS copy (a fallback inside another kernel) takes one
@@ -308,7 +309,7 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
     auto fetch = [&](int j0, int32_t (&pg)[kU], uint32_t (&sg)[kU]) {
 #pragma unroll
         for (int q = 0; q < kU; ++q) {
-            const int j = min(j0 + q * kSelThreads, n - 1);
+            const int j = min(j0 + q * NT, n - 1);
             pg[q] = v.P[j];
             sg[q] = __float_as_uint(Sg[j]);
         }
@@ -337,7 +338,7 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
         }
     };
     if (in_lds) {
-        for (int j = tid; j < n; j += kSelThreads) {
+        for (int j = tid; j < n; j += NT) {
             const int32_t p = pos_s[j];
             const uint8_t k = sel_class(v, j, p);
             cls_s[j] = k;
@@ -349,13 +350,13 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
             classify(j, p, k, pr);
         }
     } else {
-        for (int j0 = tid; j0 < n; j0 += kU * kSelThreads) {
+        for (int j0 = tid; j0 < n; j0 += kU * NT) {
             int32_t pg[kU];
             uint32_t sg[kU];
             fetch(j0, pg, sg);
 #pragma unroll
             for (int q = 0; q < kU; ++q) {
-                const int j = j0 + q * kSelThreads;
+                const int j = j0 + q * NT;
                 if (j >= n) break;
                 const uint8_t k = sel_class(v, j, pg[q]);
                 classify(j, pg[q], k, k == kCand ? primary(j, pg[q], sg[q]) : 0u);
@@ -377,7 +378,7 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
         dslot = block_max_i(dslot, red);
         const int e = (extra == 1) ? barg : (ndrop == 1 ? dslot : -1);
         int32_t *ks = a.keep_slots + (size_t)u * c.cap;
-        for (int j = tid; j < n; j += kSelThreads)
+        for (int j = tid; j < n; j += NT)
             if (j != e) ks[(e >= 0 && j > e) ? j - 1 : j] = j;
         if (tid == 0) a.n_out[u] = (e >= 0) ? n - 1 : n;
         return e;
@@ -390,23 +391,23 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
     if (rank && want > 0) {
         int krem = want;
         for (int shift = 56; shift >= 0; shift -= 8) {
-            for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+            for (int i = tid; i < 256; i += NT) hist[i] = 0;
             __syncthreads();
             auto count = [&](int32_t p, uint32_t pr) {
                 const uint64_t key = ((uint64_t)pr << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
                 if ((key & mask) == prefix) hist_add_wave(hist, (int)((key >> shift) & 255));
             };
             if (in_lds) {
-                for (int j = tid; j < n; j += kSelThreads)
+                for (int j = tid; j < n; j += NT)
                     if (cls_s[j] == kCand) count(pos_s[j], prim_s[j]);
             } else {
-                for (int j0 = tid; j0 < n; j0 += kU * kSelThreads) {
+                for (int j0 = tid; j0 < n; j0 += kU * NT) {
                     int32_t pg[kU];
                     uint32_t sg[kU];
                     fetch(j0, pg, sg);
 #pragma unroll
                     for (int q = 0; q < kU; ++q) {
-                        const int j = j0 + q * kSelThreads;
+                        const int j = j0 + q * NT;
                         if (j >= n) break;
                         if (sel_class(v, j, pg[q]) == kCand) count(pg[q], primary(j, pg[q], sg[q]));
                     }
@@ -437,7 +438,7 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
     };
     int base = 0;
     if (in_lds) {
-        const int per = (n + kSelThreads - 1) / kSelThreads;
+        const int per = (n + NT - 1) / NT;
         const int r0 = min(n, tid * per), r1 = min(n, r0 + per);
         int mine = 0;
         for (int j = r0; j < r1; ++j) mine += kept(j, pos_s[j], cls_s[j], prim_s[j]) ? 1 : 0;
@@ -445,8 +446,8 @@ __device__ inline int select_unit(const SelectArgs &a, int u, SelLds<kSelLds> &S
         for (int j = r0; j < r1; ++j)
             if (kept(j, pos_s[j], cls_s[j], prim_s[j])) ks[off++] = j;
     } else {
-        // blocks of kU * kSelThreads slots, a run of kU per thread
-        for (int c0 = 0; c0 < n; c0 += kU * kSelThreads) {
+        // blocks of kU * NT slots, a run of kU per thread
+        for (int c0 = 0; c0 < n; c0 += kU * NT) {
             const int r0 = c0 + tid * kU;
             int32_t pg[kU];
             uint32_t sg[kU];
@@ -495,7 +496,7 @@ __device__ inline void copy_row(T *dst, const T *src) {
 
 struct CompLds {
     uint32_t kept_bits[kMaxCapacity / 32];
-    int red[kCompThreads / 64];
+    int red[kMaxBlockWaves];
 };
 
 // Compaction when slot e alone leaves a unit of n slots (e < 0: none): the
@@ -525,7 +526,7 @@ __device__ inline void compact_one(const CompactArgs &a, int u, int e) {
     if (tid == 0) c.n_slots[u] = src;
 }
 
-template <typename T, int D>
+template <typename T, int D, int NT = kCompThreads>
 __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
     const CacheDev &c = a.c;
     const int b = u / c.Hkv, h = u % c.Hkv;
@@ -542,10 +543,10 @@ __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
     const int32_t *ks = a.keep_slots + (size_t)u * c.cap;
     const int words = (m + 31) / 32;
     // kept slots below m form a prefix of the ascending list; mark them
-    for (int w = tid; w < words; w += kCompThreads) kept_bits[w] = 0;
+    for (int w = tid; w < words; w += NT) kept_bits[w] = 0;
     __syncthreads();
     int below = 0;
-    for (int i = tid; i < m; i += kCompThreads) {
+    for (int i = tid; i < m; i += NT) {
         const int j = ks[i];
         if (j >= 0 && j < m) {
             atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
@@ -560,7 +561,7 @@ __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
     int32_t *P = c.pos + (size_t)u * c.cap;
     float *S = a.scores ? a.scores + (size_t)u * c.cap : nullptr;
     int base = 0;
-    for (int j0 = 0; j0 < m; j0 += kCompThreads) {
+    for (int j0 = 0; j0 < m; j0 += NT) {
         const int j = j0 + tid;
         const int hole = (j < m) && !((kept_bits[j >> 5] >> (j & 31)) & 1u);
         int t;
