@@ -101,6 +101,19 @@ def test_shuffled_slots_and_arbitrary_positions():
     _check(w, cache, _rows(w, B, m), q_pos)
 
 
+def test_several_blocks_ragged_tails_and_unsorted_rows():
+    # more slots than one workgroup's block (256) with a ragged last block,
+    # rows in ragged 64-position tiles: sequence 0 at every other position
+    # (a row tile sees slots of several blocks), sequence 1 at unsorted
+    # positions, some past every slot (whole position tiles of mixed rows)
+    w = W_G5
+    lengths, m = [600, 517], 333
+    cache = make_cache(w, lengths, capacity=600)
+    rng = np.random.default_rng(9)
+    q_pos = [np.arange(m) * 2, rng.permutation(700)[:m]]
+    _check(w, cache, _rows(w, len(lengths), m), q_pos)
+
+
 def test_paged_cache_matches_contiguous_bit_for_bit():
     w = W_G8
     lengths, m = [200, 33, 129], 160
