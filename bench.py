@@ -35,15 +35,15 @@ HBM_PEAK_GBS = 8000.0
 # FETCH_SIZE reads 524,302.7 KiB for 1,048,576 KiB copied (x 2.000),
 # WRITE_SIZE reads 1,048,576 KiB (x 1.000).  A record is valid only for the
 # fused kernel's sources whose digest it holds; otherwise the bench reports null.
-FETCH_SCALE = 1048576.0 / 524302.66
+FETCH_SCALE = 1048576.0 / 524302.68
 WRITE_SCALE = 1.0
 PROFILED_TRAFFIC = [
-    {"sources_digest": "1cf12582e2a9c01e", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "bf16", "fetch_kib": 538445.92, "write_kib": 26996.14},
-    {"sources_digest": "1cf12582e2a9c01e", "workload": "heavy_load_b512_l2048", "policy": "streaming",
-     "kv_dtype": "bf16", "fetch_kib": 534096.68, "write_kib": 18688.17},
-    {"sources_digest": "1cf12582e2a9c01e", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "e5m2", "fetch_kib": 276352.19, "write_kib": 25968.01},
+    {"sources_digest": "0712211bcd635318", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "bf16", "fetch_kib": 538439.79, "write_kib": 26995.71},
+    {"sources_digest": "0712211bcd635318", "workload": "heavy_load_b512_l2048", "policy": "streaming",
+     "kv_dtype": "bf16", "fetch_kib": 534090.55, "write_kib": 18688.11},
+    {"sources_digest": "0712211bcd635318", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "e5m2", "fetch_kib": 276352.17, "write_kib": 25968.02},
 ]
 
 
