@@ -108,6 +108,16 @@ __device__ inline int row_pos(const PromptArgs &a, int b, int R) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Maximum of three floats in one v_max3_f32.  The operands here are dot
+// products of finite values or -inf, never NaN, so the quieting the compiler
+// puts before an IEEE maximum of each MFMA result (one more instruction per
+// operand) is not needed.
+__device__ inline float max3_f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }   // v_exp_f32
 
 }  // namespace
@@ -276,12 +286,14 @@ void prompt_stats_kernel(PromptArgs a) {
                 for (int t = 0; t < kRT; ++t) {
                     float mx = mm[t];
 #pragma unroll
-                    for (int s = 0; s < kSG; ++s)
-                        mx = fmaxf(mx, fmaxf(fmaxf(acc[t][s][0], acc[t][s][1]),
-                                             fmaxf(acc[t][s][2], acc[t][s][3])));
+                    for (int s = 0; s < kSG; ++s) {
+                        mx = max3_f(mx, acc[t][s][0], acc[t][s][1]);
+                        mx = max3_f(mx, acc[t][s][2], acc[t][s][3]);
+                    }
                     // base-2 weights exp2(c2 * (dot - max)) (scale * log2 e in
-                    // c2); a row with nothing seen yet keeps a zero sum
-                    const float ms = (mx == -INFINITY) ? 0.f : mx;
+                    // c2); a row with nothing seen yet keeps a zero sum (a
+                    // mask-free tile gives every row a finite maximum)
+                    const float ms = (!kMasked || mx != -INFINITY) ? mx : 0.f;
                     const float nb = -ms * c2;
                     float sum = 0.f;
 #pragma unroll
