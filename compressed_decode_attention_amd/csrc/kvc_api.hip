@@ -31,6 +31,7 @@ kvc_status ok() {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxUnits = 1 << 24;   // sequences x kv heads in one call
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 kvc_status check_cache(const kvc_cache *c, const char *what) {
@@ -52,6 +53,11 @@ kvc_status check_cache(const kvc_cache *c, const char *what) {
     if (c->capacity > kvc::kMaxCapacity)
         return fail(KVC_ERR_UNSUPPORTED, "%s: capacity %d > %d", what, c->capacity,
                     kvc::kMaxCapacity);
+    // launches are one workgroup per unit times at most 64 splits: the grid
+    // stays below 2^31 workgroups
+    if ((int64_t)c->batch * c->kv_heads > kMaxUnits)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: batch x kv_heads = %lld units > %d", what,
+                    (long long)c->batch * c->kv_heads, kMaxUnits);
     if (!c->k || !c->v || !c->pos || !c->n_slots)
         return fail(KVC_ERR_INVALID_ARG, "%s: k, v, pos and n_slots must not be NULL", what);
     if ((uintptr_t)c->k % 16 || (uintptr_t)c->v % 16)
@@ -594,6 +600,9 @@ kvc_status check_kivi(const kvc_kivi_cache *c, const char *what) {
     if (c->head_dim != 128)
         return fail(KVC_ERR_UNSUPPORTED, "%s: head_dim %d (built: 128)", what, c->head_dim);
     if (c->bits != 4) return fail(KVC_ERR_UNSUPPORTED, "%s: bits %d (built: 4)", what, c->bits);
+    if ((int64_t)c->batch * c->kv_heads > kMaxUnits)
+        return fail(KVC_ERR_UNSUPPORTED, "%s: batch x kv_heads = %lld units > %d", what,
+                    (long long)c->batch * c->kv_heads, kMaxUnits);
     if (c->max_quant % kvc::kKivGroup != 0)
         return fail(KVC_ERR_SHAPE, "%s: max_quant %d is not a multiple of %d", what, c->max_quant,
                     kvc::kKivGroup);

@@ -80,6 +80,8 @@ typedef enum kvc_dtype {
  * (attention is permutation invariant because keys already carry their
  * position encoding [BLOG "reference implementation", note on sort()]), and
  * pos[] maps each slot to the token's original position [EMP 4.2].
+ * Limits: capacity <= 65,536 slots, q_heads / kv_heads <= 16 and
+ * batch * kv_heads <= 16,777,216 units (KVC_ERR_UNSUPPORTED beyond).
  *
  * Contiguous layout (block_size == 0):
  *   k, v       [batch, kv_heads, capacity, head_dim] of dtype
@@ -374,7 +376,8 @@ kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink, void *
  * two codes with two ALU instructions.
  * ========================================================================== */
 typedef struct kvc_kivi_cache {
-    int32_t batch, q_heads, kv_heads, head_dim;  /* head_dim 128; q_heads / kv_heads <= 8 */
+    int32_t batch, q_heads, kv_heads, head_dim;  /* head_dim 128; q_heads / kv_heads <= 8;
+                                                    batch * kv_heads <= 16,777,216 */
     int32_t max_quant;                           /* T: quantised tokens per unit, a multiple of 32 */
     int32_t bits;                                /* 4 */
     uint8_t *k_codes, *v_codes;

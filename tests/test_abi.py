@@ -86,6 +86,7 @@ def _attn(c, ws=None, nbytes=0, **kw):
     (dict(dtype=7), kvc.ERR_UNSUPPORTED),
     (dict(capacity=0), kvc.ERR_INVALID_ARG),
     (dict(capacity=70000), kvc.ERR_UNSUPPORTED),
+    (dict(batch=1 << 23, kv_heads=4, q_heads=8), kvc.ERR_UNSUPPORTED),   # 2^25 units
     (dict(k=None), kvc.ERR_INVALID_ARG),
     (dict(k=0x10008), kvc.ERR_INVALID_ARG),          # misaligned
     (dict(block_size=16, block_table=0x50000, max_blocks=3, num_blocks=10), kvc.ERR_SHAPE),
@@ -255,6 +256,7 @@ def _fake_kivi(**kw):
     (dict(max_quant=-32), kvc.ERR_INVALID_ARG),
     (dict(k_res=None), kvc.ERR_INVALID_ARG),
     (dict(v_codes=0x100008), kvc.ERR_INVALID_ARG),  # misaligned
+    (dict(batch=1 << 23, kv_heads=4, q_heads=8), kvc.ERR_UNSUPPORTED),   # 2^25 units
 ])
 def test_kivi_cache_validation(change, status):
     lib = kvc.library()
