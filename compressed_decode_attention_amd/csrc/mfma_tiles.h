@@ -80,13 +80,15 @@ __device__ inline void load_q(u16x8_t (&qa)[4], const uint16_t *qp, bool valid, 
 // K and V rows are read once per step.  From a contiguous cache,
 // non-temporal loads (the "nt" cache policy bit) keep them from displacing
 // what the caches hold for others: about 10% faster for the whole step than
-// the default policy.  From a block-paged pool the default policy is about 12%
-// faster, so the policy follows the layout.
+// the default policy.  From a block-paged pool the one-workgroup step is
+// faster with the default policy (1-2% at the mixed-length batch), while the
+// split kernel, which streams long units chunk by chunk, is about 5% faster
+// with non-temporal loads (PAGED_NT).
 constexpr int kLoadPolicy = 2;        // cache policy bits of the buffer loads: non-temporal
 constexpr int kLoadPolicyPaged = 0;   // the default policy
-template <bool F8, bool PAGED>
+template <bool F8, bool PAGED, bool PAGED_NT = false>
 __device__ inline typename KvRow<F8>::type buffer_row(__amdgpu_buffer_rsrc_t rs, int voff) {
-    constexpr int pol = PAGED ? kLoadPolicyPaged : kLoadPolicy;
+    constexpr int pol = (PAGED && !PAGED_NT) ? kLoadPolicyPaged : kLoadPolicy;
     if constexpr (F8)
         return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, pol));
     else

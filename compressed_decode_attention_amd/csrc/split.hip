@@ -219,7 +219,7 @@ void split_kernel(AttnArgs a) {
         __amdgpu_buffer_rsrc_t rs;
         int toff;
         src.tile(t, false, rs, toff);
-        return buffer_row<F8, PAGED>(rs, lane_off + toff + 4 * RB * k);
+        return buffer_row<F8, PAGED, true>(rs, lane_off + toff + 4 * RB * k);
     };
     // the new token's tile and row inside the chunk (none when n is outside)
     const int tn = (j0 <= n && n < j1) ? (n - j0) >> 4 : -1, qn = n & 15;
@@ -293,7 +293,7 @@ void split_kernel(AttnArgs a) {
         __amdgpu_buffer_rsrc_t rs;
         int toff;
         src.tile(t, true, rs, toff);
-        return buffer_row<F8, PAGED>(rs, lane_off + toff + 4 * RB * k);
+        return buffer_row<F8, PAGED, true>(rs, lane_off + toff + 4 * RB * k);
     };
     u16x8_t vnc = *reinterpret_cast<const u16x8_t *>(vn + 8 * col);
     if constexpr (F8) vnc = e5m2x8_to_bf16(e5m2x8_encode(vnc));
