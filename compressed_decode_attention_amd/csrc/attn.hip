@@ -321,13 +321,40 @@ struct FinishCfg {
     static constexpr int WPE = SZ == kFinishMid ? 1 : 4;
 };
 
+// The order in which the long-unit finish pass takes the units: longest
+// first (ties: lower unit), so that the longest units, each one workgroup's
+// critical path, start in the first round of workgroup slots and the shorter
+// ones fill in around them.  One workgroup sorts the units' slot counts in
+// LDS (bitonic); every unit appears once, so the pass computes exactly what
+// it computes in unit order.
+constexpr int kOrderMax = 4096;   // units a launch can order
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void unit_order_kernel(CacheDev c, int32_t *order) {
+    __shared__ uint64_t key[kOrderMax];
+    const int units = c.B * c.Hkv;
+    int len = 1;
+    while (len < units) len <<= 1;
+    for (int i = threadIdx.x; i < len; i += kOrderThreads) {
+        uint64_t k = ~0ull;
+        if (i < units) {
+            int n = c.n_slots[i];
+            n = n < 0 ? 0 : (n > c.cap ? c.cap : n);
+            k = ((uint64_t)(uint32_t)(c.cap - n) << 32) | (uint32_t)i;
+        }
+        key[i] = k;
+    }
+    __syncthreads();
+    bitonic_sort(key, len);
+    for (int i = threadIdx.x; i < units; i += kOrderThreads) order[i] = (int32_t)(uint32_t)key[i];
+}
+
 template <typename T, int D, int SZ>
 __global__ __launch_bounds__(FinishCfg<SZ>::NT) __attribute__((amdgpu_waves_per_eu(FinishCfg<SZ>::WPE)))
 void finish_kernel(AttnArgs a, SelectArgs sa, CompactArgs ca) {
     using Cfg = FinishCfg<SZ>;
     __shared__ FinishLdsT<Cfg::SEL, Cfg::STAGE> F;
     __shared__ int sh_e;
-    const int u = blockIdx.x;
+    const int u = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
     if (a.presel && !a.scores && a.nsplit > 1) {
         if (finish_presel<T, D, Cfg::NT, Cfg::STAGE>(a, sa, u, F.comb, sh_e)) return;
         __syncthreads();
@@ -382,15 +409,25 @@ template <typename T, int D>
 static void launch_finish_typed(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,
                                 hipStream_t s) {
     const dim3 grid(a.c.B * a.c.Hkv);
+    AttnArgs au = a;   // the shorter instances take the units in order
+    au.order = nullptr;
     if (a.max_len <= kSelLdsSmall)
         hipLaunchKernelGGL((finish_kernel<T, D, kFinishSmall>), grid, dim3(FinishCfg<kFinishSmall>::NT), 0,
-                           s, a, sa, ca);
+                           s, au, sa, ca);
     else if (a.max_len <= kSelLdsSlots)
         hipLaunchKernelGGL((finish_kernel<T, D, kFinishMid>), grid, dim3(FinishCfg<kFinishMid>::NT), 0, s,
-                           a, sa, ca);
-    else
+                           au, sa, ca);
+    else {
+        // longest units first, when the launch has few enough units to sort
+        AttnArgs ao = a;
+        const int units = a.c.B * a.c.Hkv;
+        if (a.order && units <= kOrderMax)
+            hipLaunchKernelGGL(unit_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a.c, a.order);
+        else
+            ao.order = nullptr;
         hipLaunchKernelGGL((finish_kernel<T, D, kFinishLong>), grid, dim3(FinishCfg<kFinishLong>::NT), 0,
-                           s, a, sa, ca);
+                           s, ao, sa, ca);
+    }
 }
 
 hipError_t launch_step_split(const AttnArgs &a, const SelectArgs &sa, const CompactArgs &ca,

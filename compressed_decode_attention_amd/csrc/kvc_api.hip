@@ -129,6 +129,7 @@ struct Workspace {
     size_t keep_off, keep_bytes;
     size_t nout_off, nout_bytes;
     size_t presel_off, presel_bytes;
+    size_t order_off, order_bytes;
     size_t total;
     int nsplit;
     int max_len;   // attended length bound of every unit
@@ -157,6 +158,9 @@ Workspace layout(const kvc_cache *c, int hint) {
     off += align_up(w.nout_bytes);
     w.presel_off = off;
     off += align_up(w.presel_bytes);
+    w.order_bytes = w.nsplit > 1 ? units * sizeof(int32_t) : 0;
+    w.order_off = off;
+    off += align_up(w.order_bytes);
     w.total = off;
     return w;
 }
@@ -220,6 +224,7 @@ kvc::AttnArgs attn_args(const kvc_cache *c, const int32_t *new_pos, const void *
     a.append = true;
     a.part = w.part_bytes ? (float *)((char *)ws + w.part_off) : nullptr;
     a.logits = (float *)((char *)ws + w.logit_off);
+    a.order = w.order_bytes ? (int32_t *)((char *)ws + w.order_off) : nullptr;
     return a;
 }
 

@@ -412,6 +412,9 @@ struct AttnArgs {
     int32_t presel_prompt_len = 0;
     uint32_t presel_step = 0;
     uint64_t presel_seed = 0;
+    // Finish pass over long units: scratch for the order in which its
+    // workgroups take the units ([units] int32, longest first).
+    int32_t *order = nullptr;
 };
 
 // One wave's share of a split's random-eviction ranking: the number of
