@@ -32,18 +32,18 @@ HBM_PEAK_GBS = 8000.0
 # rocprofv3 --pmc runs of this script per case (FETCH_SIZE, then WRITE_SIZE, KiB
 # per dispatch, mean over the steady-state dispatches), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (--copy-probe-mb 1024):
-# FETCH_SIZE reads 524,302.6 KiB for 1,048,576 KiB copied (x 2.000),
+# FETCH_SIZE reads 524,301.2 KiB for 1,048,576 KiB copied (x 2.000),
 # WRITE_SIZE reads 1,048,576 KiB (x 1.000).  A record is valid only for the
 # fused kernel's sources whose digest it holds; otherwise the bench reports null.
-FETCH_SCALE = 1048576.0 / 524302.61
+FETCH_SCALE = 1048576.0 / 524301.22
 WRITE_SCALE = 1.0
 PROFILED_TRAFFIC = [
-    {"sources_digest": "17b684c9464cdd1d", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "bf16", "fetch_kib": 538445.90, "write_kib": 26995.85},
-    {"sources_digest": "17b684c9464cdd1d", "workload": "heavy_load_b512_l2048", "policy": "streaming",
-     "kv_dtype": "bf16", "fetch_kib": 534096.68, "write_kib": 18688.11},
-    {"sources_digest": "17b684c9464cdd1d", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "e5m2", "fetch_kib": 276352.22, "write_kib": 25968.01},
+    {"sources_digest": "e830e21427665ab7", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "bf16", "fetch_kib": 538445.94, "write_kib": 26995.90},
+    {"sources_digest": "e830e21427665ab7", "workload": "heavy_load_b512_l2048", "policy": "streaming",
+     "kv_dtype": "bf16", "fetch_kib": 534096.69, "write_kib": 18688.16},
+    {"sources_digest": "e830e21427665ab7", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "e5m2", "fetch_kib": 276352.18, "write_kib": 25968.02},
 ]
 
 
