@@ -168,6 +168,27 @@ void fused_kernel(FusedParams fp) {
     u16x8_t qa[4];
     load_q(qa, static_cast<const uint16_t *>(a.q) + ((size_t)b * c.Hq + (size_t)h * G + col) * kHD,
            col < G, r);
+    // contiguous caches: the wave's first K tile goes out before the slot
+    // count is known, through a resource over the whole capacity (rows at or
+    // past n may hold old data: their logits are replaced by -inf, the new
+    // token's row is overwritten in staging, and rows past the capacity read
+    // zeros); a second early tile would spill
+    using RowT = typename KvRow<F8>::type;
+    constexpr int RBk = F8 ? kHD : 2 * kHD;
+    constexpr int DK0 = 1;
+    RowT kb0[DK0][4];
+    if constexpr (!PAGED) {
+        const TileSrc<false, RBk> src0(c, b, h, c.cap, nullptr);
+        const int lane_off0 = (lane >> 4) * RBk + KvRow<F8>::kBytes * (lane & 15);
+#pragma unroll
+        for (int d = 0; d < DK0; ++d) {
+            __amdgpu_buffer_rsrc_t rs;
+            int toff;
+            src0.tile(w + kFWaves * d, false, rs, toff);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) kb0[d][k] = buffer_row<F8, false>(rs, lane_off0 + toff + 4 * RBk * k);
+        }
+    }
     const int n = __builtin_amdgcn_readfirstlane(load_count(c, u, tid == 0));
     const int T = n + 1;
     if (T > TC || n >= c.cap) {
@@ -271,7 +292,7 @@ void fused_kernel(FusedParams fp) {
 #pragma unroll
         for (int d = 0; d < DK; ++d)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) kb[d][k] = kload(w + kFWaves * d, k);
+            for (int k = 0; k < 4; ++k) kb[d][k] = (!PAGED && d < DK0) ? kb0[d < DK0 ? d : 0][k] : kload(w + kFWaves * d, k);
         // the staged values land in LDS while the first K tiles are in flight.
         // No branch: every index at or past n writes slot n with the new
         // token's position and a zero score, the values slot n takes anyway.
