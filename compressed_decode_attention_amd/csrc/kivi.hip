@@ -188,16 +188,23 @@ __global__ __launch_bounds__(256) void kivi_prefill_kernel(KiviArgs a) {
 // attention over the quantized tokens
 // ---------------------------------------------------------------------------
 struct KivSmall {
-    float m[kFWaves][8];             // each wave's running max per head
+    float m[kFWaves][8];             // each wave's reference maximum per head (base-2 logits)
     float l[kFWaves][8];             // each wave's running sum per head
     float corr[kFWaves][8][kKivVG];
 };
-constexpr int kKivAS = kHD + 8;      // bf16 row stride of a wave's A tile (padded against bank clashes)
+// A tile: one row per head, the high parts of its 128 (scaled) query values in
+// columns 0..127 and their low parts in 128..255 (padded against bank clashes)
+constexpr int kKivAS = 2 * kHD + 8;
 constexpr int kKivPL = 2 * 16 + 4;   // fp32 row stride of a wave's P tile (32 keys)
-// one wave's LDS: A tile [16][kKivAS] bf16, K grids [128 s | lo][128], V grids
-// [32 tokens][4 x 128 s, 4 x lo], P tile [8][kKivPL], alpha [8]
-constexpr size_t kKivWaveLds = 16 * kKivAS * 2 + 2 * kHD * 4 + kKivGroup * 2 * kKivVG * 4 +
-                               8 * kKivPL * 4 + 8 * 4;
+// one wave's LDS: A tile [8][kKivAS] bf16, K grids [128 s | lo][128], V grids
+// [32 tokens][4 x 128 s, 4 x lo], P tile [8][kKivPL], alpha [8], logit constants [8]
+constexpr size_t kKivWaveLds = 8 * kKivAS * 2 + 2 * kHD * 4 + kKivGroup * 2 * kKivVG * 4 +
+                               8 * kKivPL * 4 + 8 * 4 + 8 * 4;
+// A wave keeps a reference maximum per head and rescales its sums only when a
+// group's logit exceeds it by more than this (base-2 units): the weights stay
+// at most 2^8, far inside fp32 and the bf16 pairs' exponent range.
+constexpr float kKivLazy = 8.f;
+constexpr float kKivNoMax = -1e30f;   // reference maximum before the first group
 
 __host__ __device__ constexpr size_t kivi_qattn_smem(int G) {
     (void)G;
@@ -211,11 +218,48 @@ __device__ inline uint32_t bf16_pack2(float x, float y) {
 __device__ inline float bf16_lo_half(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ inline float bf16_hi_half(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
 
-// Every wave walks its own groups (w, w + 4, ...) with its own running max,
-// sums and P.V accumulators; the waves merge once at the end.  Per group the
-// wave stages the group's grids in its own LDS, builds the scaled query
-// operand there, runs the K products, the softmax update and the P.V
+// x.lo * y.lo + x.hi * y.hi + c on a pair of bf16 values (v_dot2_f32_bf16)
+__device__ inline float dot2_bf16(uint32_t x, uint32_t y, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                           __builtin_bit_cast(bf16x2_t, y), c, false);
+}
+constexpr uint32_t kBfNegLo = 0x0000BF80u;     // (-1, 0)
+constexpr uint32_t kBfNegHi = 0xBF800000u;     // (0, -1)
+constexpr uint32_t kBfNegBoth = 0xBF80BF80u;   // (-1, -1)
+// The pair operands of dot2_bf16 reach it in registers, never as constants:
+// this toolchain encodes the pair (-1, 0) as the inline constant -1.0, which
+// the instruction reads as the 32-bit pattern of -1.0, i.e. the pair (0, -1)
+// (measured on every residue of 4M random values).
+__device__ inline uint32_t bf16_pair_reg(uint32_t x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// One bf16 pair of (a0, a1) for an operand whose rows 0..7 carry the values'
+// bf16 roundings and rows 8..15 the roundings of what is left over: with
+// sel0 = sel1 = 0 the pair is bf16(a0), bf16(a1); with sel0 = (-1, 0) and
+// sel1 = (0, -1) it is bf16(a0 - bf16(a0)), bf16(a1 - bf16(a1)), the
+// differences taken exactly by the dot product with the rounded pair.
+__device__ inline uint32_t bf16_part2(float a0, float a1, uint32_t sel0, uint32_t sel1) {
+    const uint32_t hp = bf16_pack2(a0, a1);
+    return bf16_pack2(dot2_bf16(hp, sel0, a0), dot2_bf16(hp, sel1, a1));
+}
+
+// Every wave walks its own groups (w, w + 4, ...) with its own reference
+// maxima, sums and P.V accumulators; the waves merge once at the end.  Per
+// group the wave stages the group's grids in its own LDS, builds the scaled
+// query operand there, runs the K products, the softmax weights and the P.V
 // products; LDS traffic of one wave needs no workgroup barrier.
+//  * The K products take the query operand's high and low parts as two halves
+//    of a 256-long contraction (rows of the A tile are heads; rows 8..15 of
+//    the MFMA operand repeat rows 0..7), so each head's logit is whole in one
+//    accumulator and the lanes of rows 8..15 hold the same logits as rows
+//    0..7: the weights' rescaling below needs no exchange between the wave's
+//    halves.  The per-head constant starts the accumulator.
+//  * Logits are in base-2 units (scale * log2 e).  A head's reference maximum
+//    moves only when a group's logit exceeds it by more than kKivLazy; then
+//    the whole wave takes the exact maxima and rescales (a wave-uniform
+//    branch).
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kKivWavesPerEU)))
 void kivi_qattn_kernel(KiviArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -227,28 +271,33 @@ void kivi_qattn_kernel(KiviArgs a) {
     const int r = lane >> 4, col = lane & 15;
     const int G = a.G;
     const int ga = col & 7;          // A row: query head (rows 8..15 carry low parts)
-    const bool arow = ga < G;
     const bool hi_lane = col < 8;
+    const float sc2 = a.scale * 1.44269504088896340736f;   // logits in base-2 units
 
     unsigned char *wl = smem + (size_t)w * kKivWaveLds;
-    uint16_t *ast = reinterpret_cast<uint16_t *>(wl);                      // [16][kKivAS]
-    float *kg = reinterpret_cast<float *>(wl + 16 * kKivAS * 2);           // [2][kHD]
+    uint16_t *ast = reinterpret_cast<uint16_t *>(wl);                      // [8][kKivAS]
+    float *kg = reinterpret_cast<float *>(wl + 8 * kKivAS * 2);            // [2][kHD]
     float *vg = kg + 2 * kHD;                                              // [32][8]
     float *pt = vg + kKivGroup * 2 * kKivVG;                               // [8][kKivPL]
     float *al = pt + 8 * kKivPL;                                           // [8]
+    float *csb = al + 8;                                                   // [8]
     KivSmall &sm = *reinterpret_cast<KivSmall *>(smem + (size_t)kFWaves * kKivWaveLds);
 
     // the query slice this lane scales for the K products: head gh, dims d0 .. d0 + 15
     const int gh = lane >> 3, d0 = 16 * (lane & 7);
-    uint32_t qw[8];
+    float qf[16];
     {
         const bool ok = gh < G;
         const uint16_t *qp = a.q + ((size_t)b * a.Hq + (size_t)h * G + (ok ? gh : 0)) * kHD + d0;
         const uint4 z4 = {0, 0, 0, 0};
         const uint4 q0 = ok ? *reinterpret_cast<const uint4 *>(qp) : z4;
         const uint4 q1 = ok ? *reinterpret_cast<const uint4 *>(qp + 8) : z4;
-        qw[0] = q0.x; qw[1] = q0.y; qw[2] = q0.z; qw[3] = q0.w;
-        qw[4] = q1.x; qw[5] = q1.y; qw[6] = q1.z; qw[7] = q1.w;
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            qf[2 * i] = bf16_lo_half(qw[i]);
+            qf[2 * i + 1] = bf16_hi_half(qw[i]);
+        }
     }
 
     int nq = __builtin_amdgcn_readfirstlane(a.n_quant[u]);
@@ -262,17 +311,24 @@ void kivi_qattn_kernel(KiviArgs a) {
     const size_t ubase = (size_t)u * a.max_quant;
     const size_t gbase = (size_t)u * (a.max_quant / kKivGroup);
     const KivMagic km;
+    const uint32_t neg_lo = bf16_pair_reg(kBfNegLo), neg_hi = bf16_pair_reg(kBfNegHi);
+    const uint32_t neg_both = bf16_pair_reg(kBfNegBoth);
 
     f32x4_t oacc[8];
 #pragma unroll
     for (int m8 = 0; m8 < 8; ++m8) oacc[m8] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f32x4_t cacc = {0.f, 0.f, 0.f, 0.f};   // sum_j p_j x_j for the columns of the V grids
     float lsum = 0.f;                        // A-layout lanes: head ga
-    float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // C-layout rows' heads
+    // C-layout rows' heads 4 (r & 1) + ii: reference maxima and their thresholds
+    float mref[4] = {kKivNoMax, kKivNoMax, kKivNoMax, kKivNoMax};
+    float thr[4] = {kKivNoMax, kKivNoMax, kKivNoMax, kKivNoMax};
     // this lane's column of the V-grid product: n < 8 the lo of grid n & 3,
     // n >= 8 the 128x scale; n & 4 selects the low bf16 part
     const int vcol = (col & 8) ? (col & 3) : kKivVG + (col & 3);
     const bool vlow = (col & 4) != 0;
+    // selectors of bf16_part2: P rows 8..15 and the low columns of the V-grid B
+    const uint32_t pa0 = hi_lane ? 0u : kBfNegLo, pa1 = hi_lane ? 0u : kBfNegHi;
+    const uint32_t pb0 = vlow ? kBfNegLo : 0u, pb1 = vlow ? kBfNegHi : 0u;
 
     // the group's data for this lane: K codes of both tiles, V codes (dword
     // col of keys 16 tt + 4 e + r), 16 B of the K grids and of the V grids
@@ -321,103 +377,106 @@ void kivi_qattn_kernel(KiviArgs a) {
             for (int j = 0; j < 16; j += 2) {
                 const float2 s2 = *reinterpret_cast<const float2 *>(kg + d0 + j);
                 const float2 l2 = *reinterpret_cast<const float2 *>(kg + kHD + d0 + j);
-                const float q0 = bf16_lo_half(qw[j / 2]), q1 = bf16_hi_half(qw[j / 2]);
-                const float a0 = q0 * s2.x, a1 = q1 * s2.y;
+                const float a0 = qf[j] * s2.x, a1 = qf[j + 1] * s2.y;
                 const uint32_t hp = bf16_pack2(a0, a1);
-                const float h0 = bf16_lo_half(hp), h1 = bf16_hi_half(hp);
-                const uint32_t lp = bf16_pack2(a0 - h0, a1 - h1);
+                const uint32_t lp = bf16_pack2(dot2_bf16(hp, neg_lo, a0), dot2_bf16(hp, neg_hi, a1));
                 hw[j / 2] = hp;
                 lw[j / 2] = lp;
-                cst += (q0 * l2.x + q1 * l2.y) - ((h0 + bf16_lo_half(lp)) + (h1 + bf16_hi_half(lp)));
+                cst = fmaf(qf[j], l2.x, cst);
+                cst = fmaf(qf[j + 1], l2.y, cst);
+                cst = dot2_bf16(hp, neg_both, cst);
+                cst = dot2_bf16(lp, neg_both, cst);
             }
             uint4 *ah = reinterpret_cast<uint4 *>(ast + gh * kKivAS + d0);
-            uint4 *alo = reinterpret_cast<uint4 *>(ast + (gh + 8) * kKivAS + d0);
+            uint4 *alo = reinterpret_cast<uint4 *>(ast + gh * kKivAS + kHD + d0);
             ah[0] = uint4{hw[0], hw[1], hw[2], hw[3]};
             ah[1] = uint4{hw[4], hw[5], hw[6], hw[7]};
             alo[0] = uint4{lw[0], lw[1], lw[2], lw[3]};
             alo[1] = uint4{lw[4], lw[5], lw[6], lw[7]};
         }
-        cst += __shfl_xor(cst, 1, 64);
-        cst += __shfl_xor(cst, 2, 64);
-        cst += __shfl_xor(cst, 4, 64);   // lanes 8 gh .. 8 gh + 7: head gh's constant
+        cst += lane_xor_f<1>(cst);
+        cst += lane_xor_f<2>(cst);
+        cst += lane_xor_f<4>(cst);   // lanes 8 gh .. 8 gh + 7: head gh's constant
+        if ((lane & 7) == 0) csb[gh] = gh < G ? cst : -INFINITY;
         __builtin_amdgcn_wave_barrier();
-        // ---- logits of the group's 32 keys (C layout: rows 4 (r & 1) + ii)
+        // ---- base-2 logits of the group's 32 keys (C layout: rows 4 (r & 1) + ii)
         float z[2][4];
         {
-            u16x8_t aop[4];
+            const f32x4_t c0 = *reinterpret_cast<const f32x4_t *>(csb + 4 * (r & 1));
+            f32x4_t acc[2] = {c0, c0};
+            const uint16_t *arow = ast + ga * kKivAS + 8 * r;
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4)
-                aop[c4] = *reinterpret_cast<const u16x8_t *>(ast + col * kKivAS + 32 * c4 + 8 * r);
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const u16x8_t ahi = *reinterpret_cast<const u16x8_t *>(arow + 32 * c4);
+                const u16x8_t alo = *reinterpret_cast<const u16x8_t *>(arow + kHD + 32 * c4);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const uint4 kc = cur.kc[tt];
-                const u16x8_t kop[4] = {kiv_widen8(kc.x, km), kiv_widen8(kc.y, km),
-                                        kiv_widen8(kc.z, km), kiv_widen8(kc.w, km)};
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aop[c4]),
-                                                                  as_bf16x8(kop[c4]), acc, 0, 0, 0);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int g = 4 * (r & 1) + ii;
-                    // every lane takes part in both exchanges (a read from an
-                    // inactive lane is not defined)
-                    const float tot = acc[ii] + __shfl_xor(acc[ii], 32, 64);
-                    const float cb = __shfl(cst, 8 * g, 64);
-                    z[tt][ii] = (g < G) ? (tot + cb) * a.scale : -INFINITY;
+                for (int tt = 0; tt < 2; ++tt) {
+                    const uint4 kc = cur.kc[tt];
+                    const u16x8_t kop = kiv_widen8(c4 == 0 ? kc.x : c4 == 1 ? kc.y : c4 == 2 ? kc.z : kc.w, km);
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ahi), as_bf16x8(kop),
+                                                                      acc[tt], 0, 0, 0);
+                    acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(alo), as_bf16x8(kop),
+                                                                      acc[tt], 0, 0, 0);
                 }
             }
-        }
-        // ---- softmax update: the group max per head, the rescale, the weights
-        float alpha[4];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            float m = fmaxf(z[0][ii], z[1][ii]);
-            m = fmaxf(m, __shfl_xor(m, 8, 64));
-            m = fmaxf(m, __shfl_xor(m, 4, 64));
-            m = fmaxf(m, __shfl_xor(m, 2, 64));
-            m = fmaxf(m, __shfl_xor(m, 1, 64));
-            const float mnew = fmaxf(mrun[ii], m);
-            alpha[ii] = (mrun[ii] == -INFINITY) ? 0.f : __expf(mrun[ii] - mnew);
-            mrun[ii] = mnew;
-            const int g = 4 * (r & 1) + ii;
-            if (r < 2 && g < G) {
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) z[tt][ii] = acc[tt][ii] * sc2;
+        }
+        // ---- reference maxima: a wave-uniform rescale when a logit passes its threshold
+        {
+            bool over = false;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) over |= fmaxf(z[0][ii], z[1][ii]) > thr[ii];
+            if (__builtin_amdgcn_ballot_w64(over) != 0) {
+                float alpha[4];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    float m = fmaxf(z[0][ii], z[1][ii]);
+                    m = fmaxf(m, lane_xor_f<8>(m));
+                    m = fmaxf(m, lane_xor_f<4>(m));
+                    m = fmaxf(m, lane_xor_f<2>(m));
+                    m = fmaxf(m, lane_xor_f<1>(m));
+                    const float mnew = fmaxf(mref[ii], m);
+                    alpha[ii] = __builtin_amdgcn_exp2f(mref[ii] - mnew);
+                    mref[ii] = mnew;
+                    thr[ii] = mnew + kKivLazy;
+                }
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+                    for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] *= alpha[ii];
+                    cacc[ii] *= alpha[ii];
+                }
+                if (r < 2 && col == 0)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) al[4 * r + ii] = alpha[ii];
+                __builtin_amdgcn_wave_barrier();
+                lsum *= al[ga];
+            }
+        }
+        // ---- the weights 2^(z - reference) into the P tile (heads past G: 0)
+        if (r < 2) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int g = 4 * r + ii;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     // key col of tile tt at column lg_col(16 tt + col)
                     const int jc = 16 * tt + (((col & 3) << 2) | (col >> 2));
-                    pt[g * kKivPL + jc] = (mnew == -INFINITY) ? 0.f : __expf(z[tt][ii] - mnew);
+                    pt[g * kKivPL + jc] = __builtin_amdgcn_exp2f(z[tt][ii] - mref[ii]);
                 }
-                if (col == 0) al[g] = alpha[ii];
             }
         }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-#pragma unroll
-            for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] *= alpha[ii];
-            cacc[ii] *= alpha[ii];
-        }
         __builtin_amdgcn_wave_barrier();
-        lsum *= arow ? al[ga] : 0.f;
         // ---- P.V of the two tiles
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            float p[4];
-            {
-                const f32x4_t pv = *reinterpret_cast<const f32x4_t *>(pt + (arow ? ga : 0) * kKivPL +
-                                                                      16 * tt + 4 * r);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = arow ? pv[e] : 0.f;
-            }
-            if (hi_lane) lsum += (p[0] + p[1]) + (p[2] + p[3]);
-            s16x4_t ap;
-            {
-                const uint32_t h01 = bf16_pack2(p[0], p[1]), h23 = bf16_pack2(p[2], p[3]);
-                const uint32_t l01 = bf16_pack2(p[0] - bf16_lo_half(h01), p[1] - bf16_hi_half(h01));
-                const uint32_t l23 = bf16_pack2(p[2] - bf16_lo_half(h23), p[3] - bf16_hi_half(h23));
-                ap = __builtin_bit_cast(s16x4_t, hi_lane ? uint2{h01, h23} : uint2{l01, l23});
-            }
+            const f32x4_t p = *reinterpret_cast<const f32x4_t *>(pt + ga * kKivPL + 16 * tt + 4 * r);
+            lsum += (p[0] + p[1]) + (p[2] + p[3]);   // read from the rows 0..7 lanes
+            const s16x4_t ap = __builtin_bit_cast(
+                s16x4_t, uint2{bf16_part2(p[0], p[1], pa0, pa1), bf16_part2(p[2], p[3], pa0, pa1)});
             const uint32_t *x = cur.vc[tt];
             const uint32_t za = (x[0] & 0xFFFFu) | (x[1] << 16), zb = (x[0] >> 16) | (x[1] & 0xFFFF0000u);
             const uint32_t zc = (x[2] & 0xFFFFu) | (x[3] << 16), zd = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
@@ -439,19 +498,11 @@ void kivi_qattn_kernel(KiviArgs a) {
 #pragma unroll
                 for (int hpair = 0; hpair < 2; ++hpair) {
                     const int e0 = 2 * hpair;
-                    const float a0 = p[e0] * sv[e0][c], a1 = p[e0 + 1] * sv[e0 + 1][c];
-                    const uint32_t hp = bf16_pack2(a0, a1);
-                    const uint32_t lp = bf16_pack2(a0 - bf16_lo_half(hp), a1 - bf16_hi_half(hp));
-                    avw[c][hpair] = hi_lane ? hp : lp;
+                    avw[c][hpair] = bf16_part2(p[e0] * sv[e0][c], p[e0 + 1] * sv[e0 + 1][c], pa0, pa1);
                 }
             }
-            s16x4_t bc;
-            {
-                const uint32_t h01 = bf16_pack2(bx[0], bx[1]), h23 = bf16_pack2(bx[2], bx[3]);
-                const uint32_t l01 = bf16_pack2(bx[0] - bf16_lo_half(h01), bx[1] - bf16_hi_half(h01));
-                const uint32_t l23 = bf16_pack2(bx[2] - bf16_lo_half(h23), bx[3] - bf16_hi_half(h23));
-                bc = __builtin_bit_cast(s16x4_t, vlow ? uint2{l01, l23} : uint2{h01, h23});
-            }
+            const s16x4_t bc = __builtin_bit_cast(
+                s16x4_t, uint2{bf16_part2(bx[0], bx[1], pb0, pb1), bf16_part2(bx[2], bx[3], pb0, pb1)});
             cacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, bc, cacc, 0, 0, 0);
 #pragma unroll
             for (int m8 = 0; m8 < 8; ++m8)
@@ -481,7 +532,7 @@ void kivi_qattn_kernel(KiviArgs a) {
     if (r < 2 && col == 0)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            if (4 * r + ii < G) sm.m[w][4 * r + ii] = mrun[ii];
+            if (4 * r + ii < G) sm.m[w][4 * r + ii] = mref[ii];
     if (lane < G) sm.l[w][lane] = lsum;
     __syncthreads();   // every wave is done with its LDS: partial P.V of the waves go there
     float *opart = reinterpret_cast<float *>(smem);   // [waves][G][kHD] (G <= 8: 16 KB)
@@ -498,28 +549,26 @@ void kivi_qattn_kernel(KiviArgs a) {
         }
     }
     __syncthreads();
+    // the partial's maximum goes out in natural-log units, like the other splits'
+    constexpr float kLn2 = 0.69314718055994530942f;
     float *pp = a.part_q + ((size_t)u * ns + s) * G * (kHD + 2);
     for (int e = tid; e < G * kHD; e += kFThreads) {
         const int g = e / kHD, d = e % kHD;
-        float M = -INFINITY;
+        float M = kKivNoMax;
         for (int v = 0; v < kFWaves; ++v) M = fmaxf(M, sm.m[v][g]);
         float o = 0.f;
         for (int v = 0; v < kFWaves; ++v) {
-            const float mv = sm.m[v][g];
-            const float f = (mv == -INFINITY) ? 0.f : __expf(mv - M);
+            const float f = __builtin_amdgcn_exp2f(sm.m[v][g] - M);
             o += f * (opart[((size_t)v * G + g) * kHD + d] + sm.corr[v][g][d / 32]);
         }
         pp[g * (kHD + 2) + d] = o;
     }
     if (tid < G) {
-        float M = -INFINITY;
+        float M = kKivNoMax;
         for (int v = 0; v < kFWaves; ++v) M = fmaxf(M, sm.m[v][tid]);
         float l = 0.f;
-        for (int v = 0; v < kFWaves; ++v) {
-            const float mv = sm.m[v][tid];
-            l += (mv == -INFINITY) ? 0.f : __expf(mv - M) * sm.l[v][tid];
-        }
-        pp[tid * (kHD + 2) + kHD] = M;
+        for (int v = 0; v < kFWaves; ++v) l += __builtin_amdgcn_exp2f(sm.m[v][tid] - M) * sm.l[v][tid];
+        pp[tid * (kHD + 2) + kHD] = M * kLn2;
         pp[tid * (kHD + 2) + kHD + 1] = l;
     }
 }
