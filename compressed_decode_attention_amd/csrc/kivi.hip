@@ -29,10 +29,13 @@
 //  * the weights of a group's 32 keys go from the product layout to the P.V
 //    operand layout through the wave's LDS; the group's grids are staged
 //    there too.
-// The residual and the new token go through split_kernel (bf16, attend
-// only).  kivi_update_kernel merges the partials, turns a full residual's 32
-// oldest tokens into a group, and appends the new token; kivi_prefill_kernel
-// quantizes a prompt.  The quantizer takes every decision in binary32.
+// The unit's last share also attends the bf16 residual and the new token on
+// the same running softmax.  With one share per unit the workgroup then
+// writes the output, turns a full residual's 32 oldest tokens into a group
+// and appends the new token: the whole step is one launch.  With several,
+// kivi_update_kernel merges the shares' partials and does the same update.
+// kivi_prefill_kernel quantizes a prompt.  The quantizer takes every decision
+// in binary32.
 #include "mfma_tiles.h"
 
 namespace kvc {
@@ -73,14 +76,29 @@ __device__ inline u16x8_t kiv_widen8(uint32_t x, const KivMagic &km) {
                                              kiv_pair<2>(x, km), kiv_pair<3>(x, km)});
 }
 
+// Residual V rows keep dim d at element 8 (d % 16) + d / 16, the order of
+// the V code words: the 16 bytes at 16 c of a row are dims c, 16 + c, ..,
+// 112 + c, one lane's B operand of the P.V products.
+__device__ inline int kiv_vres_elem(int d) { return 8 * (d % 16) + d / 16; }
+// the 16 bytes at 16 c of a residual V row, from a row in dim order
+__device__ inline uint4 kiv_vres_chunk(const uint16_t *row, int c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)row[32 * i + c] | ((uint32_t)row[32 * i + 16 + c] << 16);
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
 // Quantize one group of kKivGroup tokens, K rows Kr and V rows Vr (bf16,
-// consecutive rows of kHD), into group slot g of unit u.  256 threads: the
-// first 128 take one K channel each, the others one (token, channel group)
-// of V; codes go through LDS to be packed into the layout.
+// consecutive rows of kHD; V in dim order, or in the residual's element
+// order when VRES), into group slot g of unit u.  256 threads: the first 128
+// take one K channel each, the others one (token, channel group) of V; codes
+// go through LDS to be packed into the layout.
 struct KivQuantLds {
     uint8_t kc[kKivGroup][kHD], vc[kKivGroup][kHD];
 };
 
+template <bool VRES>
 __device__ inline void kivi_quantize_group(const KiviArgs &a, int u, int g, const uint16_t *Kr,
                                            const uint16_t *Vr, KivQuantLds &L) {
     const int tid = threadIdx.x;
@@ -112,7 +130,8 @@ __device__ inline void kivi_quantize_group(const KiviArgs &a, int u, int g, cons
         float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-            x[j] = __uint_as_float((uint32_t)Vr[(size_t)i * kHD + 32 * c + j] << 16);
+            const int d = 32 * c + j;
+            x[j] = __uint_as_float((uint32_t)Vr[(size_t)i * kHD + (VRES ? kiv_vres_elem(d) : d)] << 16);
             mn = fminf(mn, x[j]);
             mx = fmaxf(mx, x[j]);
         }
@@ -165,22 +184,79 @@ __global__ __launch_bounds__(256) void kivi_prefill_kernel(KiviArgs a) {
     const uint16_t *V = a.pv + (size_t)u * a.max_len * kHD;
     if (y < ny) {
         if (y * kKivGroup >= nq) return;
-        kivi_quantize_group(a, u, y, K + (size_t)y * kKivGroup * kHD,
-                            V + (size_t)y * kKivGroup * kHD, L);
+        kivi_quantize_group<false>(a, u, y, K + (size_t)y * kKivGroup * kHD,
+                                   V + (size_t)y * kKivGroup * kHD, L);
         return;
     }
     const int nr = len - nq;
     const uint4 *ks = reinterpret_cast<const uint4 *>(K + (size_t)nq * kHD);
-    const uint4 *vs = reinterpret_cast<const uint4 *>(V + (size_t)nq * kHD);
     uint4 *kd = reinterpret_cast<uint4 *>(a.k_res + (size_t)u * kKivResidual * kHD);
     uint4 *vd = reinterpret_cast<uint4 *>(a.v_res + (size_t)u * kKivResidual * kHD);
     for (int i = threadIdx.x; i < nr * (kHD / 8); i += blockDim.x) {
         kd[i] = ks[i];
-        vd[i] = vs[i];
+        vd[i] = kiv_vres_chunk(V + (size_t)(nq + i / (kHD / 8)) * kHD, i % (kHD / 8));
     }
     if (threadIdx.x == 0) {
         a.n_quant[u] = nq;
         a.n_res[u] = nr;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// cache update after a step's attention: if the residual is full, its 32
+// oldest tokens become the next group and the rest move down; then the new
+// token joins the residual.  All threads of a 256-thread block.
+// ---------------------------------------------------------------------------
+__device__ inline void kivi_cache_update(const KiviArgs &a, int u, KivQuantLds &L) {
+    const int tid = threadIdx.x;
+    const int b = u / a.Hkv, h = u % a.Hkv;
+    int nq = a.n_quant[u], nr = a.n_res[u];
+    const bool bad = nq < 0 || nq > a.max_quant || (nq % kKivGroup) != 0 || nr < 0 ||
+                     nr > kKivResidual;
+    if (bad) {
+        if (tid == 0 && a.flags) atomicOr(a.flags, KVC_FLAG_BAD_COUNT);
+        return;
+    }
+    uint16_t *Kr = a.k_res + (size_t)u * kKivResidual * kHD;
+    uint16_t *Vr = a.v_res + (size_t)u * kKivResidual * kHD;
+    if (nr == kKivResidual) {
+        if (nq + kKivGroup > a.max_quant) {
+            if (tid == 0 && a.flags) atomicOr(a.flags, KVC_FLAG_FULL);
+            return;
+        }
+        kivi_quantize_group<true>(a, u, nq / kKivGroup, Kr, Vr, L);
+        // rows 32..127 move down to 0..95: all reads before any write
+        constexpr int kMove = (kKivResidual - kKivGroup) * (kHD / 8);   // uint4 per tensor
+        static_assert(kMove % 256 == 0, "the row move takes whole passes of 256 threads");
+        constexpr int kPer = kMove / 256;
+        // (plain vectors, so that the copies stay in registers)
+        typedef uint32_t row16_t __attribute__((ext_vector_type(4)));
+        row16_t tk[kPer], tv[kPer];
+        const row16_t *ks = reinterpret_cast<const row16_t *>(Kr + kKivGroup * kHD);
+        const row16_t *vs = reinterpret_cast<const row16_t *>(Vr + kKivGroup * kHD);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            tk[k] = ks[tid + 256 * k];
+            tv[k] = vs[tid + 256 * k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            reinterpret_cast<row16_t *>(Kr)[tid + 256 * k] = tk[k];
+            reinterpret_cast<row16_t *>(Vr)[tid + 256 * k] = tv[k];
+        }
+        nq += kKivGroup;
+        nr -= kKivGroup;
+    }
+    if (tid < kHD / 8) {
+        const size_t src = ((size_t)b * a.Hkv + h) * kHD;
+        reinterpret_cast<uint4 *>(Kr + (size_t)nr * kHD)[tid] =
+            reinterpret_cast<const uint4 *>(a.k_new + src)[tid];
+        reinterpret_cast<uint4 *>(Vr + (size_t)nr * kHD)[tid] = kiv_vres_chunk(a.v_new + src, tid);
+    }
+    if (tid == 0) {
+        a.n_quant[u] = nq;
+        a.n_res[u] = nr + 1;
     }
 }
 
@@ -191,6 +267,7 @@ struct KivSmall {
     float m[kFWaves][8];             // each wave's reference maximum per head (base-2 logits)
     float l[kFWaves][8];             // each wave's running sum per head
     float corr[kFWaves][8][kKivVG];
+    float M[8], il[8];               // the share's maximum per head, 1 / its sum
 };
 // A tile: one row per head, the high parts of its 128 (scaled) query values in
 // columns 0..127 and their low parts in 128..255 (padded against bank clashes)
@@ -256,10 +333,12 @@ __device__ inline uint32_t bf16_part2(float a0, float a1, uint32_t sel0, uint32_
 //    accumulator and the lanes of rows 8..15 hold the same logits as rows
 //    0..7: the weights' rescaling below needs no exchange between the wave's
 //    halves.  The per-head constant starts the accumulator.
-//  * Logits are in base-2 units (scale * log2 e).  A head's reference maximum
-//    moves only when a group's logit exceeds it by more than kKivLazy; then
-//    the whole wave takes the exact maxima and rescales (a wave-uniform
-//    branch).
+//  * Logits are in base-2 units (scale * log2 e); rows of heads past G get
+//    -inf after the scaling.  A head's reference maximum moves only when a
+//    logit exceeds it by more than kKivLazy; then the whole wave takes the
+//    exact maxima and rescales (a wave-uniform branch).
+//  * After its groups, the unit's last share takes the residual and the new
+//    token in 16-key bf16 tiles on the same running softmax (below).
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kKivWavesPerEU)))
 void kivi_qattn_kernel(KiviArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -322,6 +401,9 @@ void kivi_qattn_kernel(KiviArgs a) {
     // C-layout rows' heads 4 (r & 1) + ii: reference maxima and their thresholds
     float mref[4] = {kKivNoMax, kKivNoMax, kKivNoMax, kKivNoMax};
     float thr[4] = {kKivNoMax, kKivNoMax, kKivNoMax, kKivNoMax};
+    float zb[4];   // 0, or -inf for the rows of heads past G
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) zb[ii] = 4 * (r & 1) + ii < G ? 0.f : -INFINITY;
     // this lane's column of the V-grid product: n < 8 the lo of grid n & 3,
     // n >= 8 the 128x scale; n & 4 selects the low bf16 part
     const int vcol = (col & 8) ? (col & 3) : kKivVG + (col & 3);
@@ -353,6 +435,40 @@ void kivi_qattn_kernel(KiviArgs a) {
         // V grids: lanes 0..31 token lane's scales, 32..63 its lo
         const float *vgsrc = (lane < 32 ? a.v_scale : a.v_lo) + (tok + (lane & 31)) * kKivVG;
         d.vgr = kiv_load(reinterpret_cast<const float4 *>(vgsrc));
+    };
+
+    // Reference maxima: lm[ii] is the lane's largest logit of row ii in the
+    // current keys.  When one passes its threshold anywhere in the wave, every
+    // row takes its exact maximum so far and the sums are rescaled.
+    auto update_max = [&](const float (&lm)[4]) {
+        bool over = false;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) over |= lm[ii] > thr[ii];
+        if (__builtin_amdgcn_ballot_w64(over) == 0) return;
+        float alpha[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            float m = lm[ii];
+            m = fmaxf(m, lane_xor_f<8>(m));
+            m = fmaxf(m, lane_xor_f<4>(m));
+            m = fmaxf(m, lane_xor_f<2>(m));
+            m = fmaxf(m, lane_xor_f<1>(m));
+            const float mnew = fmaxf(mref[ii], m);
+            alpha[ii] = __builtin_amdgcn_exp2f(mref[ii] - mnew);
+            mref[ii] = mnew;
+            thr[ii] = mnew + kKivLazy;
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+            for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] *= alpha[ii];
+            cacc[ii] *= alpha[ii];
+        }
+        if (r < 2 && col == 0)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) al[4 * r + ii] = alpha[ii];
+        __builtin_amdgcn_wave_barrier();
+        lsum *= al[ga];
     };
 
 #pragma unroll 1
@@ -397,7 +513,7 @@ void kivi_qattn_kernel(KiviArgs a) {
         cst += lane_xor_f<1>(cst);
         cst += lane_xor_f<2>(cst);
         cst += lane_xor_f<4>(cst);   // lanes 8 gh .. 8 gh + 7: head gh's constant
-        if ((lane & 7) == 0) csb[gh] = gh < G ? cst : -INFINITY;
+        if ((lane & 7) == 0) csb[gh] = cst;
         __builtin_amdgcn_wave_barrier();
         // ---- base-2 logits of the group's 32 keys (C layout: rows 4 (r & 1) + ii)
         float z[2][4];
@@ -422,39 +538,13 @@ void kivi_qattn_kernel(KiviArgs a) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) z[tt][ii] = acc[tt][ii] * sc2;
+                for (int ii = 0; ii < 4; ++ii) z[tt][ii] = fmaf(acc[tt][ii], sc2, zb[ii]);
         }
-        // ---- reference maxima: a wave-uniform rescale when a logit passes its threshold
         {
-            bool over = false;
+            float lm[4];
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) over |= fmaxf(z[0][ii], z[1][ii]) > thr[ii];
-            if (__builtin_amdgcn_ballot_w64(over) != 0) {
-                float alpha[4];
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    float m = fmaxf(z[0][ii], z[1][ii]);
-                    m = fmaxf(m, lane_xor_f<8>(m));
-                    m = fmaxf(m, lane_xor_f<4>(m));
-                    m = fmaxf(m, lane_xor_f<2>(m));
-                    m = fmaxf(m, lane_xor_f<1>(m));
-                    const float mnew = fmaxf(mref[ii], m);
-                    alpha[ii] = __builtin_amdgcn_exp2f(mref[ii] - mnew);
-                    mref[ii] = mnew;
-                    thr[ii] = mnew + kKivLazy;
-                }
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-#pragma unroll
-                    for (int m8 = 0; m8 < 8; ++m8) oacc[m8][ii] *= alpha[ii];
-                    cacc[ii] *= alpha[ii];
-                }
-                if (r < 2 && col == 0)
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) al[4 * r + ii] = alpha[ii];
-                __builtin_amdgcn_wave_barrier();
-                lsum *= al[ga];
-            }
+            for (int ii = 0; ii < 4; ++ii) lm[ii] = fmaxf(z[0][ii], z[1][ii]);
+            update_max(lm);
         }
         // ---- the weights 2^(z - reference) into the P tile (heads past G: 0)
         if (r < 2) {
@@ -512,7 +602,86 @@ void kivi_qattn_kernel(KiviArgs a) {
         }
     }
 
-    // ---------------- merge the four waves into the split's partial (o, m, l)
+    // ---------------- the residual and the new token (the unit's last share):
+    // bf16 rows in 16-key tiles, tile t to wave t % 4, on the same running
+    // softmax.  Keys 0 .. nr-1 are the residual rows, key nr the new token,
+    // later keys of the last tile weigh nothing.  K products: A = the query
+    // rows as given (bf16 x bf16 products are exact), B = the K rows (lane:
+    // dims 32 c4 + 8 r .. of key 16 t + col).  P.V: B of MFMA m8 is element
+    // m8 of the four V rows the lane holds (keys 16 t + 4 e + r); the
+    // residual's element order puts dim 16 m8 + col there, the column of the
+    // quantized products.
+    if (s == ns - 1) {
+        int nr = __builtin_amdgcn_readfirstlane(a.n_res[u]);
+        if (nr < 0 || nr > kKivResidual) {
+            if (tid == 0 && a.flags) atomicOr(a.flags, KVC_FLAG_BAD_COUNT);
+            nr = nr < 0 ? 0 : kKivResidual;
+        }
+        const int ntile = (nr + 16) / 16;   // nr + 1 keys
+        if (w < ntile) {
+            u16x8_t qa[4];
+            {
+                const bool ok = ga < G;
+                const uint16_t *qp = a.q + ((size_t)b * a.Hq + (size_t)h * G + (ok ? ga : 0)) * kHD + 8 * r;
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    qa[c4] = ok ? *reinterpret_cast<const u16x8_t *>(qp + 32 * c4)
+                                : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+            // rows past nr read as zeros
+            const uint32_t rbytes = (uint32_t)nr * kHD * 2;
+            const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k_res + (size_t)u * kKivResidual * kHD, rbytes);
+            const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v_res + (size_t)u * kKivResidual * kHD, rbytes);
+            const uint16_t *kn = a.k_new + ((size_t)b * a.Hkv + h) * kHD;
+            const uint16_t *vn = a.v_new + ((size_t)b * a.Hkv + h) * kHD;
+#pragma unroll 1
+            for (int t = w; t < ntile; t += kFWaves) {
+                const int key = 16 * t + col;
+                u16x8_t kr[4], vr[4];
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    kr[c4] = buffer_row<false, false>(krs, key * (2 * kHD) + 64 * c4 + 16 * r);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    vr[e] = buffer_row<false, false>(vrs, (16 * t + 4 * e + r) * (2 * kHD) + 16 * col);
+                if (key == nr)
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4)
+                        kr[c4] = *reinterpret_cast<const u16x8_t *>(kn + 32 * c4 + 8 * r);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * t + 4 * e + r == nr) vr[e] = __builtin_bit_cast(u16x8_t, kiv_vres_chunk(vn, col));
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kr[c4]),
+                                                                  acc, 0, 0, 0);
+                const float kb = key <= nr ? 0.f : -INFINITY;
+                float zt[4];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) zt[ii] = fmaf(acc[ii], sc2, zb[ii] + kb);
+                update_max(zt);
+                if (r < 2)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        pt[(4 * r + ii) * kKivPL + (((col & 3) << 2) | (col >> 2))] =
+                            __builtin_amdgcn_exp2f(zt[ii] - mref[ii]);
+                __builtin_amdgcn_wave_barrier();
+                const f32x4_t p = *reinterpret_cast<const f32x4_t *>(pt + ga * kKivPL + 4 * r);
+                lsum += (p[0] + p[1]) + (p[2] + p[3]);
+                const s16x4_t ap = __builtin_bit_cast(
+                    s16x4_t, uint2{bf16_part2(p[0], p[1], pa0, pa1), bf16_part2(p[2], p[3], pa0, pa1)});
+#pragma unroll
+                for (int m8 = 0; m8 < 8; ++m8)
+                    oacc[m8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        ap, s16x4_t{(short)vr[0][m8], (short)vr[1][m8], (short)vr[2][m8], (short)vr[3][m8]},
+                        oacc[m8], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---------------- merge the four waves: the output (one share per unit)
+    // or the share's partial (o, m, l)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
 #pragma unroll
@@ -549,37 +718,46 @@ void kivi_qattn_kernel(KiviArgs a) {
         }
     }
     __syncthreads();
-    // the partial's maximum goes out in natural-log units, like the other splits'
-    constexpr float kLn2 = 0.69314718055994530942f;
-    float *pp = a.part_q + ((size_t)u * ns + s) * G * (kHD + 2);
-    for (int e = tid; e < G * kHD; e += kFThreads) {
-        const int g = e / kHD, d = e % kHD;
-        float M = kKivNoMax;
-        for (int v = 0; v < kFWaves; ++v) M = fmaxf(M, sm.m[v][g]);
-        float o = 0.f;
-        for (int v = 0; v < kFWaves; ++v) {
-            const float f = __builtin_amdgcn_exp2f(sm.m[v][g] - M);
-            o += f * (opart[((size_t)v * G + g) * kHD + d] + sm.corr[v][g][d / 32]);
-        }
-        pp[g * (kHD + 2) + d] = o;
-    }
+    const bool direct = ns == 1;
     if (tid < G) {
         float M = kKivNoMax;
         for (int v = 0; v < kFWaves; ++v) M = fmaxf(M, sm.m[v][tid]);
         float l = 0.f;
         for (int v = 0; v < kFWaves; ++v) l += __builtin_amdgcn_exp2f(sm.m[v][tid] - M) * sm.l[v][tid];
-        pp[tid * (kHD + 2) + kHD] = M * kLn2;
-        pp[tid * (kHD + 2) + kHD + 1] = l;
+        sm.M[tid] = M;
+        sm.il[tid] = 1.f / l;
+        if (!direct) {
+            // the partial's maximum goes out in natural-log units
+            float *pp = a.part_q + ((size_t)u * ns + s) * G * (kHD + 2);
+            pp[tid * (kHD + 2) + kHD] = M * 0.69314718055994530942f;
+            pp[tid * (kHD + 2) + kHD + 1] = l;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * kHD; e += kFThreads) {
+        const int g = e / kHD, d = e % kHD;
+        const float M = sm.M[g];
+        float o = 0.f;
+        for (int v = 0; v < kFWaves; ++v) {
+            const float f = __builtin_amdgcn_exp2f(sm.m[v][g] - M);
+            o += f * (opart[((size_t)v * G + g) * kHD + d] + sm.corr[v][g][d / 32]);
+        }
+        if (direct) a.out[((size_t)b * a.Hq + (size_t)h * G + g) * kHD + d] = o * sm.il[g];
+        else a.part_q[(((size_t)u * ns + s) * G + g) * (kHD + 2) + d] = o;
+    }
+    if (direct) {
+        __syncthreads();   // the wave partials are read: the LDS serves the conversion
+        kivi_cache_update(a, u, *reinterpret_cast<KivQuantLds *>(smem));
     }
 }
 
 // ---------------------------------------------------------------------------
-// combine, residual conversion, append: one workgroup per unit
+// several shares per unit: combine their partials, then the cache update;
+// one workgroup per unit
 // ---------------------------------------------------------------------------
 struct KivUpdLds {
-    float fac[kMaxSplit + 1][kMaxGroup];
-    float ms[kMaxSplit + 1][kMaxGroup], ls[kMaxSplit + 1][kMaxGroup];
-    float lsum[kMaxGroup];
+    float fac[kMaxSplit][kMaxGroup];
+    float ms[kMaxSplit][kMaxGroup], ls[kMaxSplit][kMaxGroup];
     KivQuantLds q;
 };
 
@@ -587,12 +765,9 @@ __global__ __launch_bounds__(256) void kivi_update_kernel(KiviArgs a) {
     __shared__ KivUpdLds L;
     const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
     const int tid = threadIdx.x;
-    const int G = a.G, ns = a.nsq, nt = ns + 1;   // split ns: residual + new token
-    auto part = [&](int s) -> const float * {
-        return s < ns ? a.part_q + ((size_t)u * ns + s) * G * (kHD + 2)
-                      : a.part_r + (size_t)u * G * (kHD + 2);
-    };
-    for (int i = tid; i < nt * G; i += blockDim.x) {
+    const int G = a.G, ns = a.nsq;
+    auto part = [&](int s) -> const float * { return a.part_q + ((size_t)u * ns + s) * G * (kHD + 2); };
+    for (int i = tid; i < ns * G; i += blockDim.x) {
         const int s = i / G, g = i % G;
         L.ms[s][g] = part(s)[g * (kHD + 2) + kHD];
         L.ls[s][g] = part(s)[g * (kHD + 2) + kHD + 1];
@@ -600,75 +775,20 @@ __global__ __launch_bounds__(256) void kivi_update_kernel(KiviArgs a) {
     __syncthreads();
     if (tid < G) {
         float M = -INFINITY;
-        for (int s = 0; s < nt; ++s) M = fmaxf(M, L.ms[s][tid]);
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, L.ms[s][tid]);
         float S = 0.f;
-        for (int s = 0; s < nt; ++s)
-            S += (L.ms[s][tid] == -INFINITY) ? 0.f : L.ls[s][tid] * __expf(L.ms[s][tid] - M);
-        for (int s = 0; s < nt; ++s)
-            L.fac[s][tid] = (L.ms[s][tid] == -INFINITY) ? 0.f : __expf(L.ms[s][tid] - M) / S;
+        for (int s = 0; s < ns; ++s) S += L.ls[s][tid] * __expf(L.ms[s][tid] - M);
+        for (int s = 0; s < ns; ++s) L.fac[s][tid] = __expf(L.ms[s][tid] - M) / S;
     }
     __syncthreads();
     for (int e = tid; e < G * kHD; e += blockDim.x) {
         const int g = e / kHD, d = e % kHD;
         float o = 0.f;
 #pragma unroll 8
-        for (int s = 0; s < nt; ++s) o += part(s)[g * (kHD + 2) + d] * L.fac[s][g];
+        for (int s = 0; s < ns; ++s) o += part(s)[g * (kHD + 2) + d] * L.fac[s][g];
         a.out[((size_t)b * a.Hq + (size_t)h * G + g) * kHD + d] = o;
     }
-
-    // ---- the cache update
-    int nq = a.n_quant[u], nr = a.n_res[u];
-    const bool bad = nq < 0 || nq > a.max_quant || (nq % kKivGroup) != 0 || nr < 0 ||
-                     nr > kKivResidual;
-    if (bad) {
-        if (tid == 0 && a.flags) atomicOr(a.flags, KVC_FLAG_BAD_COUNT);
-        return;
-    }
-    uint16_t *Kr = a.k_res + (size_t)u * kKivResidual * kHD;
-    uint16_t *Vr = a.v_res + (size_t)u * kKivResidual * kHD;
-    if (nr == kKivResidual) {
-        if (nq + kKivGroup > a.max_quant) {
-            if (tid == 0 && a.flags) atomicOr(a.flags, KVC_FLAG_FULL);
-            return;
-        }
-        kivi_quantize_group(a, u, nq / kKivGroup, Kr, Vr, L.q);
-        // rows 32..127 move down to 0..95: all reads before any write
-        constexpr int kMove = (kKivResidual - kKivGroup) * (kHD / 8);   // uint4 per tensor
-        constexpr int kPer = (kMove + 255) / 256;
-        uint4 tk[kPer], tv[kPer];
-        const uint4 *ks = reinterpret_cast<const uint4 *>(Kr + kKivGroup * kHD);
-        const uint4 *vs = reinterpret_cast<const uint4 *>(Vr + kKivGroup * kHD);
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int i = tid + 256 * k;
-            if (i < kMove) {
-                tk[k] = ks[i];
-                tv[k] = vs[i];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) {
-            const int i = tid + 256 * k;
-            if (i < kMove) {
-                reinterpret_cast<uint4 *>(Kr)[i] = tk[k];
-                reinterpret_cast<uint4 *>(Vr)[i] = tv[k];
-            }
-        }
-        nq += kKivGroup;
-        nr -= kKivGroup;
-    }
-    if (tid < kHD / 8) {
-        const size_t src = ((size_t)b * a.Hkv + h) * kHD;
-        reinterpret_cast<uint4 *>(Kr + (size_t)nr * kHD)[tid] =
-            reinterpret_cast<const uint4 *>(a.k_new + src)[tid];
-        reinterpret_cast<uint4 *>(Vr + (size_t)nr * kHD)[tid] =
-            reinterpret_cast<const uint4 *>(a.v_new + src)[tid];
-    }
-    if (tid == 0) {
-        a.n_quant[u] = nq;
-        a.n_res[u] = nr + 1;
-    }
+    kivi_cache_update(a, u, L.q);
 }
 
 // ---------------------------------------------------------------------------
@@ -681,47 +801,14 @@ hipError_t launch_kivi_prefill(const KiviArgs &a, hipStream_t s) {
 
 hipError_t launch_kivi_decode(const KiviArgs &a, hipStream_t s) {
     const int units = a.B * a.Hkv;
-    if (a.nsq > 0) {
-        static hipError_t attr = hipFuncSetAttribute((const void *)kivi_qattn_kernel,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)kivi_qattn_smem(kMaxGroup));
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(kivi_qattn_kernel, dim3(units * a.nsq), dim3(kFThreads),
-                           kivi_qattn_smem(a.G), s, a);
-    }
-    // the residual and the new token: bf16 rows, attended only
-    AttnArgs r;
-    r.c.B = a.B;
-    r.c.Hq = a.Hq;
-    r.c.Hkv = a.Hkv;
-    r.c.D = kHD;
-    r.c.cap = kKivResidual;
-    r.c.G = a.G;
-    r.c.bs = 0;
-    r.c.max_blocks = 0;
-    r.c.num_blocks = 0;
-    r.c.k = a.k_res;
-    r.c.v = a.v_res;
-    r.c.bt = nullptr;
-    r.c.pos = nullptr;
-    r.c.n_slots = a.n_res;
-    r.c.flags = a.flags;
-    r.new_pos = nullptr;
-    r.q = a.q;
-    r.k_new = a.k_new;
-    r.v_new = a.v_new;
-    r.out = nullptr;
-    r.scores = nullptr;
-    r.scale = a.scale;
-    r.decay = 0.f;
-    r.nsplit = 1;
-    r.max_len = kKivResidual + 1;
-    r.append = false;
-    r.part = a.part_r;
-    r.logits = nullptr;
-    hipError_t e = launch_split(r, false, r.max_len, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kivi_update_kernel, dim3(units), dim3(256), 0, s, a);
+    if (a.nsq < 1 || a.nsq > kMaxSplit) return hipErrorInvalidValue;
+    static hipError_t attr = hipFuncSetAttribute((const void *)kivi_qattn_kernel,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)kivi_qattn_smem(kMaxGroup));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(kivi_qattn_kernel, dim3(units * a.nsq), dim3(kFThreads),
+                       kivi_qattn_smem(a.G), s, a);
+    if (a.nsq > 1) hipLaunchKernelGGL(kivi_update_kernel, dim3(units), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

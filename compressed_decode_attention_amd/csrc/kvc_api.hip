@@ -625,11 +625,11 @@ kvc_status check_kivi(const kvc_kivi_cache *c, const char *what) {
 // splits of the quantized tokens: shares of at most 64 groups (2,048 tokens;
 // each wave walks its own groups, so a long share costs no LDS), enough
 // splits for about 4,096 workgroups, no share under 4 groups, at most 64
-// splits
+// splits; the last share of a unit also attends the residual and the new
+// token, so there is always one
 int kivi_nsq(const kvc_kivi_cache *c, int hint) {
     const int mq = (hint <= 0 || hint > c->max_quant) ? c->max_quant : hint;
     const int groups = mq / kvc::kKivGroup;
-    if (c->max_quant == 0) return 0;
     if (groups == 0) return 1;
 constexpr int kKivSplitGroups = 64;   // quantized groups per workgroup of the KIVI attention
     const int units = c->batch * c->kv_heads;
@@ -640,8 +640,9 @@ constexpr int kKivSplitGroups = 64;   // quantized groups per workgroup of the K
     return ns > 64 ? 64 : (ns < 1 ? 1 : ns);
 }
 
+// the shares' partials (read by the combine when a unit has several shares)
 struct KiviWs {
-    size_t part_q, part_r, total;
+    size_t part_q, total;
     int nsq;
 };
 
@@ -651,10 +652,8 @@ KiviWs kivi_layout(const kvc_kivi_cache *c, int hint) {
     const size_t G = (size_t)(c->q_heads / c->kv_heads);
     w.nsq = kivi_nsq(c, hint);
     const size_t pq = units * (size_t)w.nsq * G * (c->head_dim + 2) * sizeof(float);
-    const size_t pr = units * G * (c->head_dim + 2) * sizeof(float);
     w.part_q = 0;
-    w.part_r = align_up(pq);
-    w.total = w.part_r + align_up(pr);
+    w.total = align_up(pq);
     return w;
 }
 
@@ -738,6 +737,5 @@ KVC_EXPORT kvc_status kvc_kivi_decode(const kvc_kivi_cache *c, const void *q, co
     a.scale = scale;
     a.nsq = w.nsq;
     a.part_q = (float *)((char *)workspace + w.part_q);
-    a.part_r = (float *)((char *)workspace + w.part_r);
     return hip_status(kvc::launch_kivi_decode(a, (hipStream_t)stream), what);
 }

@@ -521,9 +521,9 @@ struct KiviArgs {
     const uint16_t *q, *k_new, *v_new;
     float *out;
     float scale;
-    int nsq;              // splits of the quantized tokens per unit (0: none)
-    float *part_q;        // [units][nsq][G][D+2]
-    float *part_r;        // [units][G][D+2]: the residual and the new token
+    int nsq;              // shares of the quantized tokens per unit (>= 1; the last one
+                          // also attends the residual and the new token)
+    float *part_q;        // [units][nsq][G][D+2] when nsq > 1
     // prefill
     const uint16_t *pk, *pv;
     const int32_t *lengths;

@@ -370,10 +370,14 @@ kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink, void *
  *   v_codes [u][T][64] uint8.  Dim d of a token: dword d % 16 of its row,
  *           nibble slot k with m = d / 16 = 2k (k < 4) or 2(k-4)+1 (k >= 4).
  *   v_scale, v_lo [u][T][4] float: the grid of channels 32c..32c+31 of a token.
- *   k_res, v_res [u][128][128] bf16: residual rows 0 .. n_res-1, oldest first.
+ *   k_res, v_res [u][128][128] bf16: residual rows 0 .. n_res-1, oldest first;
+ *           a k_res row in dim order, a v_res row with dim d at element
+ *           8*(d%16) + d/16 (the dim order of the V code words).
  *   n_quant, n_res [u] int32.
  * These layouts put one lane's matrix-core operands in one load and widen
- * two codes with two ALU instructions.
+ * two codes with two ALU instructions.  The workspace holds the partials of
+ * a unit's shares of the quantised tokens when max_quant_hint gives it more
+ * than one; with one share per unit a step is a single launch.
  * ========================================================================== */
 typedef struct kvc_kivi_cache {
     int32_t batch, q_heads, kv_heads, head_dim;  /* head_dim 128; q_heads / kv_heads <= 8;

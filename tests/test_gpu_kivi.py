@@ -43,6 +43,8 @@ def _nibble_index():
 
 
 K_IDX, V_IDX = _nibble_index()
+# residual V rows keep dim d at element 8 (d % 16) + d // 16 (kvc.h)
+V_RES_ELEM = np.array([8 * (d % 16) + d // 16 for d in range(D)])
 
 
 def _unpack(rows: np.ndarray, idx) -> np.ndarray:
@@ -71,7 +73,7 @@ def _check_state(cache, orc, B, Hkv):
     ks, kl = cache.k_scale.cpu().numpy(), cache.k_lo.cpu().numpy()
     vs, vl = cache.v_scale.cpu().numpy(), cache.v_lo.cpu().numpy()
     kr = host(cache.k_res, "bf16")
-    vr = host(cache.v_res, "bf16")
+    vr = host(cache.v_res, "bf16")[..., V_RES_ELEM]
     for b in range(B):
         for h in range(Hkv):
             u, ou = b * Hkv + h, orc.units[b][h]
