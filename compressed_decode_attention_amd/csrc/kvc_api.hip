@@ -622,16 +622,17 @@ kvc_status check_kivi(const kvc_kivi_cache *c, const char *what) {
     return KVC_OK;
 }
 
-// splits of the quantized tokens: shares of at most 64 groups (2,048 tokens;
-// each wave walks its own groups, so a long share costs no LDS), enough
-// splits for about 4,096 workgroups, no share under 4 groups, at most 64
-// splits; the last share of a unit also attends the residual and the new
-// token, so there is always one
+// splits of the quantized tokens: shares of at most 128 groups (4,096
+// tokens; each wave walks its own groups, so a long share costs no LDS, and
+// one share per unit makes the step a single launch), enough splits for
+// about 4,096 workgroups, no share under 4 groups, at most 64 splits; the
+// last share of a unit also attends the residual and the new token, so there
+// is always one
 int kivi_nsq(const kvc_kivi_cache *c, int hint) {
     const int mq = (hint <= 0 || hint > c->max_quant) ? c->max_quant : hint;
     const int groups = mq / kvc::kKivGroup;
     if (groups == 0) return 1;
-constexpr int kKivSplitGroups = 64;   // quantized groups per workgroup of the KIVI attention
+constexpr int kKivSplitGroups = 128;   // quantized groups per workgroup of the KIVI attention
     const int units = c->batch * c->kv_heads;
     int ns = (groups + kKivSplitGroups - 1) / kKivSplitGroups;
     const int fill = (4096 + units - 1) / units, by_len = (groups + 3) / 4;
