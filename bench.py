@@ -438,8 +438,9 @@ def kivi_bench(torch, kvc, synth, args):
                    "tokens_per_s": B * 1e3 / ms},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "kvc_kivi_decode (whole step: quantized attention, residual "
-                               "attention, combine + conversion + append)",
+                     "kernel": "kvc_kivi_decode (whole step; one launch at one share per "
+                               "unit: quantized tokens, residual and new token, output, "
+                               "conversion, append)",
                      "bytes_per_unit": unit, "units_per_launch": B * Hkv, "launch_ms": launch_ms,
                      "attainable_read_gbs": attain["gbs"],
                      "frac_of_attainable": achieved / attain["gbs"]},
