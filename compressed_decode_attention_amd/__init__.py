@@ -434,7 +434,8 @@ class KiviCache:
         U, T, D = batch * kv_heads, max_quant, head_dim
         row = D * bits // 8
         self.k_codes = torch.zeros((U, T, row), dtype=torch.uint8, device=device)
-        self.v_codes = torch.zeros((U, T, row), dtype=torch.uint8, device=device)
+        # 16-token tiles of 1,024 bytes (kvc.h): the same bytes as T rows of 64
+        self.v_codes = torch.zeros((U, T // 16, 16 * row), dtype=torch.uint8, device=device)
         self.k_scale = torch.zeros((U, T // KIVI_GROUP, D), dtype=torch.float32, device=device)
         self.k_lo = torch.zeros_like(self.k_scale)
         self.v_scale = torch.zeros((U, T, D // 32), dtype=torch.float32, device=device)

@@ -54,10 +54,10 @@ __device__ inline T kiv_load(const T *p) {
 }
 
 // Two codes of one dword -> two bf16 values 1 + c/128 (the code in the low
-// mantissa bits: bits 0x3F80 | c).  A dword holds eight codes, slots 0..3
-// (bits 0..15) the even elements and slots 4..7 the odd ones, so pair J
-// (elements 2J and 2J + 1) sits at bits 4J and 16 + 4J: one shift and one
-// bit-field select.
+// mantissa bits: bits 0x3F80 | c).  A K dword holds eight codes of one key,
+// slots 0..3 (bits 0..15) the even elements and slots 4..7 the odd ones; a V
+// word holds four codes of each of two keys, one key per half.  Either way
+// pair J sits at bits 4J and 16 + 4J: one shift and one bit-field select.
 // The mask and the bits of 1.0 are passed in registers (KivMagic) so that
 // each pair is one v_and_or_b32 (VOP3 takes no literal constants here).
 struct KivMagic {
@@ -76,9 +76,9 @@ __device__ inline u16x8_t kiv_widen8(uint32_t x, const KivMagic &km) {
                                              kiv_pair<2>(x, km), kiv_pair<3>(x, km)});
 }
 
-// Residual V rows keep dim d at element 8 (d % 16) + d / 16, the order of
-// the V code words: the 16 bytes at 16 c of a row are dims c, 16 + c, ..,
-// 112 + c, one lane's B operand of the P.V products.
+// Residual V rows keep dim d at element 8 (d % 16) + d / 16: the 16 bytes
+// at 16 c of a row are dims c, 16 + c, .., 112 + c, one lane's B operand of
+// the P.V products (the dims of lane column c in the quantized tiles too).
 __device__ inline int kiv_vres_elem(int d) { return 8 * (d % 16) + d / 16; }
 // the 16 bytes at 16 c of a residual V row, from a row in dim order
 __device__ inline uint4 kiv_vres_chunk(const uint16_t *row, int c) {
@@ -146,22 +146,37 @@ __device__ inline void kivi_quantize_group(const KiviArgs &a, int u, int g, cons
         a.v_lo[(tok0 + i) * kKivVG + c] = mn;
     }
     __syncthreads();
-    // pack: 32 tokens x 16 dwords for K, then for V
+    // pack: 512 words of K codes (token rows), then 512 of V codes (tiles)
     for (int idx = tid; idx < 2 * kKivGroup * 16; idx += blockDim.x) {
         const bool isv = idx >= kKivGroup * 16;
         const int rem = idx % (kKivGroup * 16);
-        const int i = rem / 16, wd = rem % 16;
         uint32_t word = 0;
+        uint8_t *dst;
+        if (!isv) {
+            // token i, dword wd: dim 32 * (wd % 4) + 8 * (wd / 4) + e at slot k,
+            // e = 2k (k < 4) or 2 (k - 4) + 1
+            const int i = rem / 16, wd = rem % 16;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = (k < 4) ? 2 * k : 2 * (k - 4) + 1;
-            // K: dword wd = 4 * ((d % 32) / 8) + d / 32, element d % 8;
-            // V: dword d % 16, element d / 16
-            const int d = isv ? 16 * e + wd : 32 * (wd % 4) + 8 * (wd / 4) + e;
-            const uint32_t cq = isv ? L.vc[i][d] : L.kc[i][d];
-            word |= cq << (4 * k);
+            for (int k = 0; k < 8; ++k) {
+                const int e = (k < 4) ? 2 * k : 2 * (k - 4) + 1;
+                word |= (uint32_t)L.kc[i][32 * (wd % 4) + 8 * (wd / 4) + e] << (4 * k);
+            }
+            dst = a.k_codes + (tok0 + i) * kKivRow + 4 * wd;
+        } else {
+            // tile t, lane (r, c), word w: tokens 16 t + r + 8 (w / 2) (low
+            // half) and 4 more (high half), dims c + 16 (2 k + (w & 1)) at
+            // bits 4 k of each half
+            const int t = rem / 256, lr = (rem / 4) % 64, w = rem % 4;
+            const int r = lr / 16, c = lr % 16;
+            const int i0 = 16 * t + r + 8 * (w / 2);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int d = c + 16 * (2 * k + (w & 1));
+                word |= (uint32_t)L.vc[i0][d] << (4 * k);
+                word |= (uint32_t)L.vc[i0 + 4][d] << (16 + 4 * k);
+            }
+            dst = a.v_codes + (tok0 + 16 * t) * kKivRow + 16 * lr + 4 * w;
         }
-        uint8_t *dst = (isv ? a.v_codes : a.k_codes) + (tok0 + i) * kKivRow + 4 * wd;
         *reinterpret_cast<uint32_t *>(dst) = word;
     }
     __syncthreads();
@@ -333,10 +348,12 @@ __device__ inline uint32_t bf16_part2(float a0, float a1, uint32_t sel0, uint32_
 //    accumulator and the lanes of rows 8..15 hold the same logits as rows
 //    0..7: the weights' rescaling below needs no exchange between the wave's
 //    halves.  The per-head constant starts the accumulator.
-//  * Logits are in base-2 units (scale * log2 e); rows of heads past G get
-//    -inf after the scaling.  A head's reference maximum moves only when a
-//    logit exceeds it by more than kKivLazy; then the whole wave takes the
-//    exact maxima and rescales (a wave-uniform branch).
+//  * Logits are in base-2 units (scale * log2 e, folded into the query for
+//    the quantized groups); rows of heads past G get -inf (the quantized
+//    groups' constant, the residual's bias after its scaling).  A head's
+//    reference maximum moves only when a logit exceeds it by more than
+//    kKivLazy; then the whole wave takes the exact maxima and rescales (a
+//    wave-uniform branch).
 //  * After its groups, the unit's last share takes the residual and the new
 //    token in 16-key bf16 tiles on the same running softmax (below).
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(kKivWavesPerEU)))
@@ -362,7 +379,9 @@ void kivi_qattn_kernel(KiviArgs a) {
     float *csb = al + 8;                                                   // [8]
     KivSmall &sm = *reinterpret_cast<KivSmall *>(smem + (size_t)kFWaves * kKivWaveLds);
 
-    // the query slice this lane scales for the K products: head gh, dims d0 .. d0 + 15
+    // the query slice this lane scales for the K products: head gh, dims
+    // d0 .. d0 + 15, times the logit scale in base-2 units (so the products
+    // are the base-2 logits themselves)
     const int gh = lane >> 3, d0 = 16 * (lane & 7);
     float qf[16];
     {
@@ -374,8 +393,8 @@ void kivi_qattn_kernel(KiviArgs a) {
         const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            qf[2 * i] = bf16_lo_half(qw[i]);
-            qf[2 * i + 1] = bf16_hi_half(qw[i]);
+            qf[2 * i] = bf16_lo_half(qw[i]) * sc2;
+            qf[2 * i + 1] = bf16_hi_half(qw[i]) * sc2;
         }
     }
 
@@ -401,9 +420,6 @@ void kivi_qattn_kernel(KiviArgs a) {
     // C-layout rows' heads 4 (r & 1) + ii: reference maxima and their thresholds
     float mref[4] = {kKivNoMax, kKivNoMax, kKivNoMax, kKivNoMax};
     float thr[4] = {kKivNoMax, kKivNoMax, kKivNoMax, kKivNoMax};
-    float zb[4];   // 0, or -inf for the rows of heads past G
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) zb[ii] = 4 * (r & 1) + ii < G ? 0.f : -INFINITY;
     // this lane's column of the V-grid product: n < 8 the lo of grid n & 3,
     // n >= 8 the 128x scale; n & 4 selects the low bf16 part
     const int vcol = (col & 8) ? (col & 3) : kKivVG + (col & 3);
@@ -412,11 +428,12 @@ void kivi_qattn_kernel(KiviArgs a) {
     const uint32_t pa0 = hi_lane ? 0u : kBfNegLo, pa1 = hi_lane ? 0u : kBfNegHi;
     const uint32_t pb0 = vlow ? kBfNegLo : 0u, pb1 = vlow ? kBfNegHi : 0u;
 
-    // the group's data for this lane: K codes of both tiles, V codes (dword
-    // col of keys 16 tt + 4 e + r), 16 B of the K grids and of the V grids
+    // the group's data for this lane: K codes of both tiles (16 B of key
+    // 16 tt + col), V codes (the lane's 16 B of each tile: dims col + 16 m of
+    // keys 16 tt + 4 e + r), 16 B of the K grids and of the V grids
     struct GroupData {
         uint4 kc[2];
-        uint32_t vc[2][4];
+        uint4 vz[2];
         float4 kgr, vgr;
     };
     auto gload = [&](int g, GroupData &d) {
@@ -424,10 +441,8 @@ void kivi_qattn_kernel(KiviArgs a) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             d.kc[tt] = kiv_load(reinterpret_cast<const uint4 *>(a.k_codes + (tok + 16 * tt + col) * kKivRow + 16 * r));
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                d.vc[tt][e] = kiv_load(reinterpret_cast<const uint32_t *>(
-                    a.v_codes + (tok + 16 * tt + 4 * e + r) * kKivRow + 4 * col));
+            d.vz[tt] = kiv_load(reinterpret_cast<const uint4 *>(a.v_codes + (tok + 16 * tt) * kKivRow +
+                                                                 16 * (16 * r + col)));
         }
         // K grids: lanes 0..31 the scales (4 each), 32..63 the lo
         const float *kgsrc = (lane < 32 ? a.k_scale : a.k_lo) + (gbase + g) * kHD + 4 * (lane & 31);
@@ -513,7 +528,7 @@ void kivi_qattn_kernel(KiviArgs a) {
         cst += lane_xor_f<1>(cst);
         cst += lane_xor_f<2>(cst);
         cst += lane_xor_f<4>(cst);   // lanes 8 gh .. 8 gh + 7: head gh's constant
-        if ((lane & 7) == 0) csb[gh] = cst;
+        if ((lane & 7) == 0) csb[gh] = gh < G ? cst : -INFINITY;
         __builtin_amdgcn_wave_barrier();
         // ---- base-2 logits of the group's 32 keys (C layout: rows 4 (r & 1) + ii)
         float z[2][4];
@@ -538,7 +553,7 @@ void kivi_qattn_kernel(KiviArgs a) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) z[tt][ii] = fmaf(acc[tt][ii], sc2, zb[ii]);
+                for (int ii = 0; ii < 4; ++ii) z[tt][ii] = acc[tt][ii];
         }
         {
             float lm[4];
@@ -567,9 +582,7 @@ void kivi_qattn_kernel(KiviArgs a) {
             lsum += (p[0] + p[1]) + (p[2] + p[3]);   // read from the rows 0..7 lanes
             const s16x4_t ap = __builtin_bit_cast(
                 s16x4_t, uint2{bf16_part2(p[0], p[1], pa0, pa1), bf16_part2(p[2], p[3], pa0, pa1)});
-            const uint32_t *x = cur.vc[tt];
-            const uint32_t za = (x[0] & 0xFFFFu) | (x[1] << 16), zb = (x[0] >> 16) | (x[1] & 0xFFFF0000u);
-            const uint32_t zc = (x[2] & 0xFFFFu) | (x[3] << 16), zd = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
+            const uint32_t za = cur.vz[tt].x, zb = cur.vz[tt].y, zc = cur.vz[tt].z, zd = cur.vz[tt].w;
             const uint2 bw[8] = {{kiv_pair<0>(za, km), kiv_pair<0>(zc, km)}, {kiv_pair<0>(zb, km), kiv_pair<0>(zd, km)},
                                  {kiv_pair<1>(za, km), kiv_pair<1>(zc, km)}, {kiv_pair<1>(zb, km), kiv_pair<1>(zd, km)},
                                  {kiv_pair<2>(za, km), kiv_pair<2>(zc, km)}, {kiv_pair<2>(zb, km), kiv_pair<2>(zd, km)},
@@ -657,9 +670,10 @@ void kivi_qattn_kernel(KiviArgs a) {
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[c4]), as_bf16x8(kr[c4]),
                                                                   acc, 0, 0, 0);
                 const float kb = key <= nr ? 0.f : -INFINITY;
-                float zt[4];
+                float zt[4];   // rows of heads past G and keys past nr: -inf
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) zt[ii] = fmaf(acc[ii], sc2, zb[ii] + kb);
+                for (int ii = 0; ii < 4; ++ii)
+                    zt[ii] = fmaf(acc[ii], sc2, 4 * (r & 1) + ii < G ? kb : -INFINITY);
                 update_max(zt);
                 if (r < 2)
 #pragma unroll

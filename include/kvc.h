@@ -367,15 +367,20 @@ kvc_status kvc_stream_read(const void *src, size_t bytes, uint32_t *sink, void *
  *           that dword (bits 4k..4k+3) with e = d % 8 = 2k (k < 4) or
  *           2(k-4)+1 (k >= 4).
  *   k_scale, k_lo [u][T/32][128] float: the grid of channel d of group g.
- *   v_codes [u][T][64] uint8.  Dim d of a token: dword d % 16 of its row,
- *           nibble slot k with m = d / 16 = 2k (k < 4) or 2(k-4)+1 (k >= 4).
+ *   v_codes [u][T/16][1024] uint8: tiles of 16 consecutive tokens.  The 16
+ *           bytes at 16*(16r + c) of a tile (r < 4, c < 16) hold dims c + 16m
+ *           (m < 8) of the tile's tokens r, r+4, r+8, r+12 as four little-
+ *           endian words: word 0 even m of tokens r (bits 0..15) and r+4
+ *           (bits 16..31), word 1 odd m of the same two, words 2 and 3 the
+ *           same for tokens r+8 and r+12; in a half, dim c + 16m at bits
+ *           4*(m/2).
  *   v_scale, v_lo [u][T][4] float: the grid of channels 32c..32c+31 of a token.
  *   k_res, v_res [u][128][128] bf16: residual rows 0 .. n_res-1, oldest first;
  *           a k_res row in dim order, a v_res row with dim d at element
- *           8*(d%16) + d/16 (the dim order of the V code words).
+ *           8*(d%16) + d/16 (the dims of a V code lane's 16 bytes).
  *   n_quant, n_res [u] int32.
- * These layouts put one lane's matrix-core operands in one load and widen
- * two codes with two ALU instructions.  The workspace holds the partials of
+ * These layouts put one lane's matrix-core operands of a 16-token tile in
+ * one 16-byte load and widen two codes with two ALU instructions.  The workspace holds the partials of
  * a unit's shares of the quantised tokens when max_quant_hint gives it more
  * than one; with one share per unit a step is a single launch.
  * ========================================================================== */

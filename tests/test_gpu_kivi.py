@@ -27,19 +27,28 @@ D = 128
 
 
 def _nibble_index():
-    """(byte, shift) of each dim's code in a 64-byte K row and V row."""
+    """(byte, shift) of each dim's code in a 64-byte K row; for V, of each
+    (token, dim) of a 32-token group in its two 1,024-byte tiles (kvc.h)."""
     def place(word, elem):
         slot = elem // 2 if elem % 2 == 0 else 4 + elem // 2
         return 4 * word + slot // 2, 4 * (slot % 2)
-    kb, ks, vb, vs = [], [], [], []
+    kb, ks = [], []
     for d in range(D):
         b, s = place(4 * ((d % 32) // 8) + d // 32, d % 8)
         kb.append(b)
         ks.append(s)
-        b, s = place(d % 16, d // 16)
-        vb.append(b)
-        vs.append(s)
-    return (np.array(kb), np.array(ks, np.uint8)), (np.array(vb), np.array(vs, np.uint8))
+    vb = np.zeros((32, D), np.int64)
+    vs = np.zeros((32, D), np.uint8)
+    for i in range(32):
+        t, q = divmod(i, 16)
+        r, e = q % 4, q // 4          # token 4e + r of its tile
+        for d in range(D):
+            c, m = d % 16, d // 16
+            w = 2 * (e // 2) + m % 2   # words 0/1: tokens r, r+4; 2/3: r+8, r+12
+            bit = 16 * (e % 2) + 4 * (m // 2)
+            vb[i, d] = 1024 * t + 16 * (16 * r + c) + 4 * w + bit // 8
+            vs[i, d] = bit % 8
+    return (np.array(kb), np.array(ks, np.uint8)), (vb, vs)
 
 
 K_IDX, V_IDX = _nibble_index()
@@ -81,7 +90,8 @@ def _check_state(cache, orc, B, Hkv):
             for g, grp in enumerate(ou.groups):
                 t = slice(32 * g, 32 * g + 32)
                 np.testing.assert_array_equal(_unpack(kc[u, t], K_IDX), grp.k_codes)
-                np.testing.assert_array_equal(_unpack(vc[u, t], V_IDX), grp.v_codes)
+                vgrp = vc[u].reshape(-1)[2048 * g:2048 * (g + 1)]
+                np.testing.assert_array_equal((vgrp[V_IDX[0]] >> V_IDX[1]) & 0xF, grp.v_codes)
                 np.testing.assert_array_equal(ks[u, g], grp.k_scale)
                 np.testing.assert_array_equal(kl[u, g], grp.k_lo)
                 np.testing.assert_array_equal(vs[u, t], grp.v_scale)
