@@ -101,7 +101,7 @@ def _check_state(cache, orc, B, Hkv):
             np.testing.assert_array_equal(oracle.decode(vr[u, :n], "bf16"), ou.res_v)
 
 
-def _run(w, lengths, steps, max_quant=None, hint=0, check_every=1):
+def _run(w, lengths, steps, max_quant=None, hint=0, check_every=1, scale=None):
     B, Hq, Hkv = len(lengths), w.q_heads, w.kv_heads
     k, v, parts = _prompts(w, lengths)
     longest = max(lengths) + steps
@@ -109,7 +109,7 @@ def _run(w, lengths, steps, max_quant=None, hint=0, check_every=1):
     cache = kvc.KiviCache(B, Hq, Hkv, D, mq)
     kvc.kivi_prefill(cache, dev(k, "bf16"), dev(v, "bf16"),
                      torch.tensor(lengths, dtype=torch.int32, device="cuda"))
-    orc = oracle.Kivi(Hq, Hkv, D)
+    orc = oracle.Kivi(Hq, Hkv, D, scale=scale)
     for b in range(B):
         orc.load(b, *parts[b])
     _check_state(cache, orc, B, Hkv)
@@ -119,7 +119,7 @@ def _run(w, lengths, steps, max_quant=None, hint=0, check_every=1):
     for t in range(1, steps + 1):
         q, kn, vn = synth.batch_step_inputs(w, t, B)
         kvc.kivi_decode(cache, dev(q, "bf16"), dev(kn, "bf16"), dev(vn, "bf16"), out,
-                        max_quant_hint=hint, workspace=ws)
+                        scale=scale, max_quant_hint=hint, workspace=ws)
         o = out.cpu().numpy()
         for b in range(B):
             ref = orc.step(b, q[b], kn[b], vn[b])
@@ -155,9 +155,19 @@ def test_single_query_head_group():
 
 
 def test_long_share_runs_in_pieces():
-    # a length bound of one group gives one split per unit, so a unit of
-    # 2,100 tokens (61 groups) runs in four LDS pieces with online rescaling
+    # a length bound of one group gives one share per unit, so a unit of
+    # 2,100 tokens (61 groups) runs in one workgroup whose waves each walk
+    # about 15 groups on their own running softmax
     _run(W8, [2100, 700, 129], steps=3, hint=32)
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+@pytest.mark.parametrize("hint", [0, 32])
+def test_negative_and_zero_scale(scale, hint):
+    # any finite scale: the heads past G and the keys past the residual must
+    # still weigh nothing when the logits flip sign or vanish, with one share
+    # per unit (the output written by the attention) and with several
+    _run(W5, [150, 400, 620], steps=3, hint=hint, scale=scale)
 
 
 def test_many_splits_and_empty_splits():
