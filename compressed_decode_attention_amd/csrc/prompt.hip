@@ -193,7 +193,17 @@ void prompt_stats_kernel(PromptArgs a) {
         qmin[t] = __builtin_amdgcn_readfirstlane(wave_min_i(qp[t]));
         rows_full[t] = blk * kStatRows + 16 * kRT * w + 16 * t + 15 < nrows;
     }
-    const float c2 = a.scale * kLog2e;
+    // a negative scale: the same logits from the negated query rows and
+    // |scale|, so the running maxima of the raw dot products stay maxima of
+    // the logits (bf16 negation is exact); a zero scale: every logit 0, from
+    // zero rows and a positive factor (masked slots stay -inf, never -inf * 0)
+    if (a.scale <= 0.f)
+#pragma unroll
+        for (int t = 0; t < kRT; ++t)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                qb[t][c4] = a.scale < 0.f ? qb[t][c4] ^ (uint16_t)0x8000 : u16x8_p{0, 0, 0, 0, 0, 0, 0, 0};
+    const float c2 = (a.scale == 0.f ? 1.f : fabsf(a.scale)) * kLog2e;
     // next tile (from kt on) that some row of the block sees (uniform)
     auto next_active = [&](int kt) {
         while (kt < ntile && tmin_s[kt] > qmax) ++kt;
@@ -216,7 +226,7 @@ void prompt_stats_kernel(PromptArgs a) {
         ppos = (j0 + (tid & (kTile - 1)) < n) ? p : INT_MAX;
     };
 
-    // running maximum of the raw dot products (c2 > 0 keeps the order) and
+    // running maximum of the raw dot products (c2 >= 0 keeps the order) and
     // the sum of exp2(c2 * (dot - maximum)), per lane and row tile
     float mm[kRT], ll[kRT];
 #pragma unroll
@@ -408,7 +418,15 @@ void prompt_scores_kernel(PromptArgs a) {
         kmaxw[t] = __builtin_amdgcn_readfirstlane(wave_max_i(kp[t]));
         slots_full[t] = blk * kScoreSlots + 16 * kST * w + 16 * t + 15 < n;
     }
-    const float c2 = a.scale * kLog2e;
+    // a negative or zero scale: negated or zero slot rows and a positive
+    // factor, as the statistics pass does with the query rows
+    if (a.scale <= 0.f)
+#pragma unroll
+        for (int t = 0; t < kST; ++t)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                kb[t][c4] = a.scale < 0.f ? kb[t][c4] ^ (uint16_t)0x8000 : u16x8_p{0, 0, 0, 0, 0, 0, 0, 0};
+    const float c2 = (a.scale == 0.f ? 1.f : fabsf(a.scale)) * kLog2e;
     auto next_active = [&](int rt) {
         if (track)
             while (rt < nrt) {

@@ -74,6 +74,17 @@ def test_causal_prompt_rows(w, m):
     _check(w, cache, q, [np.arange(m), np.arange(m)])
 
 
+@pytest.mark.parametrize("w", [W_G4, W_G8, W_F32], ids=lambda w: w.name)
+@pytest.mark.parametrize("scale", [-0.18, 0.0])
+def test_negative_and_zero_scale(w, scale):
+    # any finite scale: a negative one flips which slots dominate, zero spreads
+    # every row evenly over the slots it sees
+    m = 150
+    cache = make_cache(w, [m, m], capacity=m + 5)
+    q = _rows(w, 2, m)
+    _check(w, cache, q, [np.arange(m), np.arange(m)], scale=scale, check_mass=True)
+
+
 def test_group_of_sixteen_and_one():
     for q_heads in (128, 8):   # G = 16, G = 1
         w = synth.workload("heavy_load_b512_l2048", q_heads=q_heads)
