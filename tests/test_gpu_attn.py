@@ -37,7 +37,7 @@ def _path(path, lengths, capacity):
 
 
 def _run(w, lengths, capacity, with_scores=True, hint=0, paged=0, step=1, q_zero=False,
-         path=None):
+         path=None, scale=None):
     if path is not None:
         capacity, hint = _path(path, lengths, capacity)
     B = len(lengths)
@@ -54,12 +54,12 @@ def _run(w, lengths, capacity, with_scores=True, hint=0, paged=0, step=1, q_zero
     out = torch.full((B, w.q_heads, D), float("nan"), device="cuda")
     new_pos = torch.tensor(lengths, dtype=torch.int32, device="cuda")
     ws = cache.workspace(hint)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
     kvc.decode_attn(cache, new_pos, dev(q, w.dtype), dev(kn, w.dtype), dev(vn, w.dtype), out,
-                    scores, max_len_hint=hint, workspace=ws)
+                    scores, scale=scale, max_len_hint=hint, workspace=ws)
     post = Snapshot(cache, w.dtype, scores)
     assert int(cache.flags.item()) == 0
     out_h = out.cpu().numpy()
-    scale = 1.0 / math.sqrt(D)
     worst = 0.0
     for b in range(B):
         for h in range(w.kv_heads):
@@ -114,6 +114,13 @@ def test_without_scores(path):
 @pytest.mark.parametrize("path", PATHS)
 def test_zero_query_spreads_probability_uniformly(path):
     _run(W_GQA, [100, 255], capacity=300, q_zero=True, path=path)
+
+
+@pytest.mark.parametrize("path", PATHS + ["fallback"])
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_negative_and_zero_scale(path, scale):
+    # any finite scale: the masked rows and slots still weigh nothing
+    _run(W_G5, [129, 700, 2], capacity=1000, path=path, scale=scale)
 
 
 def test_long_units_split_across_workgroups():
