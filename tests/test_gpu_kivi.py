@@ -142,6 +142,13 @@ def test_prefill_ragged_lengths_around_the_residual():
     _run(W4, [0, 20, 128, 129, 160, 200, 700], steps=0)
 
 
+def test_short_prompts_decode_from_the_residual_alone():
+    # units with no quantized group (an empty one included) attend the residual
+    # and the new token only; the 128-token unit converts its first group at
+    # the first step
+    _run(W4, [0, 1, 20, 127, 128], steps=3)
+
+
 @pytest.mark.parametrize("w", [W4, W5, W8], ids=lambda w: w.name)
 def test_decode_steps_with_conversions(w):
     # units at 128 convert on step 1, at 127 on step 2; 40 steps cross a
