@@ -11,18 +11,19 @@
 // the waves merge once at the end, so the loop has no workgroup barrier:
 //  * K of group g, channel d: k = c * s_gd + lo_gd, so
 //        q . k_j = sum_d (q_d s_gd) c_jd + sum_d q_d lo_gd.
-//    The scale folds into the query: A = 128 q_d s_gd as a bf16 high part in
-//    rows 0..7 and the bf16 rounding of the rest in rows 8..15; a code enters
-//    B exactly as the bf16 value 1 + c/128 (bits 0x3F80 | c).  The product is
-//    then sum_d A_d + sum_d (A_d / 128) c_jd, and the first sum with the lo
-//    term is one constant per (group, head) added to the group's logits.  The
-//    operand is built once per (wave, group): each lane scales 16 of the
-//    group's (head, dim) pairs into the wave's LDS tile and reads its own
-//    operand back.
+//    The scale folds into the query: A = 128 q_d s_gd as a bf16 high part
+//    and the bf16 rounding of the rest, the two halves of one 256-long
+//    contraction; a code enters B exactly as the bf16 value 1 + c/128 (bits
+//    0x3F80 | c).  The product is then sum_d A_d + sum_d (A_d / 128) c_jd,
+//    and the first sum with the lo term is one constant per (group, head)
+//    that starts the group's accumulators.  The operand is built once per
+//    (wave, group): each lane scales 16 of the group's (head, dim) pairs into
+//    the wave's LDS tile and reads its own operand back.
 //  * V of token j, channel group c (32 channels): v = code * s_jc + lo_jc.  In
 //    the P.V tile MFMA m covers dims 16m .. 16m + 15, inside one channel
 //    group, so the token scale folds into P: A = 128 p_j s_jc (high / low
-//    rows), B the codes as above, and sum_j (p_j lo_jc - A_j) is added per
+//    rows), B the codes as above (one 16-byte load per lane and tile from
+//    the tiled V layout), and sum_j (p_j lo_jc - A_j) is added per
 //    (head, channel group) at the end; those two sums come from one more MFMA
 //    per tile, P against a B of the tile's lo and 128 s values (high / low
 //    columns), whose error is that of the bf16 pairs, 2^-17 relative.
