@@ -336,14 +336,17 @@ KVC_EXPORT kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos
     return hip_status(kvc::launch_attn(a, c->dtype, (hipStream_t)stream), what);
 }
 
-// the matrix-core prompt scoring: bf16 K, head_dim 128
-static bool use_prompt_mfma(const kvc_cache *c) {
-    return c->dtype == KVC_BF16 && c->head_dim == 128;
+// the matrix-core prompt scoring: bf16 K, head_dim 128, and a sequence's
+// query rows and a unit's K rows each within the 2 GiB its buffer loads address
+static bool use_prompt_mfma(const kvc_cache *c, int32_t m_rows) {
+    const size_t limit = (size_t)1 << 31;
+    return c->dtype == KVC_BF16 && c->head_dim == 128 &&
+           (size_t)m_rows * (size_t)c->q_heads * 256 < limit && (size_t)c->capacity * 256 < limit;
 }
 
 KVC_EXPORT size_t kvc_h2o_accumulate_workspace_bytes(const kvc_cache *c, int32_t m_rows) {
     if (check_cache(c, "kvc_h2o_accumulate_workspace_bytes") != KVC_OK || m_rows <= 0) return 0;
-    if (!use_prompt_mfma(c)) return 0;
+    if (!use_prompt_mfma(c, m_rows)) return 0;
     return align_up(kvc::prompt_workspace_bytes(c->batch * c->kv_heads, m_rows,
                                                 c->q_heads / c->kv_heads));
 }
@@ -360,7 +363,7 @@ KVC_EXPORT kvc_status kvc_h2o_accumulate(const kvc_cache *c, const void *q_rows,
     if (!q_rows || !h2o_scores)
         return fail(KVC_ERR_INVALID_ARG, "%s: q_rows and h2o_scores must not be NULL", what);
     if (!isfinite(scale)) return fail(KVC_ERR_INVALID_ARG, "%s: scale is not finite", what);
-    if (use_prompt_mfma(c)) {
+    if (use_prompt_mfma(c, m_rows)) {
         if ((uintptr_t)q_rows % 16)
             return fail(KVC_ERR_INVALID_ARG, "%s: q_rows must be 16-byte aligned", what);
         Workspace w{};

@@ -15,10 +15,12 @@
 //     are staged in LDS (XOR swizzle, conflict-free reads) and enter
 //     v_mfma_f32_16x16x32_bf16 as the A operand; the rows are the B operand,
 //     held in registers (64 rows per wave, so each A operand read from LDS
-//     feeds four row tiles).  Each lane keeps a running maximum of the raw dot
-//     products (the scale is positive, so the order is the same) and a sum
-//     of exp2(c2 * (dot - maximum)), rescaled once per two 16-slot tiles;
-//     four lanes merge into the row's log-sum-exp, written to the workspace.
+//     feeds four row tiles).  Each lane keeps a sum of exp2(c2 * dot + nb)
+//     against a reference nb that moves only when a group of terms passes a
+//     cap (2^64): no maximum or rescale per group, one wave-uniform test per
+//     two 16-slot tiles instead (the scale is made positive, so references
+//     follow the largest dot products); four lanes merge into the row's
+//     log-sum-exp, written to the workspace.
 //  2. scores: one workgroup per 256 slots of a unit.  The slots are the B
 //     operand, held in registers (64 slots per wave); query tiles (64 consecutive positions of
 //     one head, so a tile's rows share one stride through q) are staged in
@@ -60,7 +62,9 @@ constexpr int kST = 4;            // pass 2: 16-slot tiles per wave (B operands 
 constexpr int kScoreSlots = 64 * kST;   // slots per workgroup, pass 2
 constexpr int kTile = 64;         // slots (pass 1) or rows (pass 2) staged per step
 constexpr int kMaxRowTilesLds = 4096;   // pass 2: position tiles whose largest position fits in LDS
-constexpr int kSG = 2;            // pass 1: 16-slot tiles per maximum and rescale
+constexpr int kSG = 2;            // pass 1: 16-slot tiles per test of the references
+constexpr float kLazyCap = 0x1p64f;   // pass 1: a group's sum past this moves the reference
+constexpr float kNoRef = 0x1p100f;    // pass 1: offset before any slot is seen
 
 __device__ inline bf16x8_p as_bf(u16x8_p x) { return __builtin_bit_cast(bf16x8_p, x); }
 
@@ -109,15 +113,6 @@ __device__ inline int row_pos(const PromptArgs &a, int b, int R) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Maximum of three floats in one v_max3_f32.  The operands here are dot
-// products of finite values or -inf, never NaN, so the quieting the compiler
-// puts before an IEEE maximum of each MFMA result (one more instruction per
-// operand) is not needed.
-__device__ inline float max3_f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
 __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }   // v_exp_f32
 
 }  // namespace
@@ -129,6 +124,7 @@ __device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }  
 // (found up front from each tile's smallest position): while the MFMAs run on
 // one LDS buffer, the next active tile's K rows are already in registers on
 // their way; one barrier per tile.
+template <bool kPaged>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void prompt_stats_kernel(PromptArgs a) {
     __shared__ __align__(16) unsigned char ktile[2][kTile * 256];
@@ -148,8 +144,14 @@ void prompt_stats_kernel(PromptArgs a) {
     const int32_t *P = c.pos + (size_t)u * c.cap;
     const int ntile = (n + kTile - 1) / kTile;
     int *tmin_s = tile_pos, *tmax_s = tile_pos + (c.cap + kTile - 1) / kTile;
-    // contiguous caches: the unit's first row; slot j is row j after it
-    const uint16_t *Ku = c.bs == 0 ? K + (size_t)u * c.cap * kPD : nullptr;
+    // contiguous caches: buffer resources over the unit's n filled rows and
+    // positions (loads past them return zeros; such slots are masked), so a
+    // tile's loads take a scalar offset and one per-lane offset fixed for the
+    // whole kernel
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(kPaged ? K : K + (size_t)u * c.cap * kPD, kPaged ? 0u : (uint32_t)n * (kPD * 2));
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(P, kPaged ? 0u : (uint32_t)n * 4);
+    const int koff = (tid >> 4) * (kPD * 2) + 16 * (tid & 15);
 
     // B operands: kRT 16-row tiles per wave; lane (col, r) holds dims
     // 32c + 8r .. 32c + 8r + 7 of row col
@@ -209,28 +211,42 @@ void prompt_stats_kernel(PromptArgs a) {
         while (kt < ntile && tmin_s[kt] > qmax) ++kt;
         return kt;
     };
-    // the tile's K rows and positions into registers; rows past n read row
-    // n - 1 (every load unconditional, in bounds; such slots are masked)
+    // the tile's K rows and positions into registers, unconditionally and in
+    // bounds (paged caches read row n - 1 for slots past n, contiguous ones
+    // zeros); such slots are masked.  Nothing reads the loaded values before
+    // the next tile is staged, so the loads stay in flight while this tile
+    // computes (the position of a slot past n is set when it is staged).
     u16x8_p pre[kTile / 16];
     int ppos = 0;
     auto fetch = [&](int kt) {
         const int j0 = kt * kTile;
+        if constexpr (kPaged) {
 #pragma unroll
-        for (int pass = 0; pass < kTile / 16; ++pass) {
-            const int j = min(j0 + 16 * pass + (tid >> 4), n - 1);
-            const size_t row = Ku ? (size_t)j : row_of(c, b, h, j);
-            pre[pass] = *reinterpret_cast<const u16x8_p *>((Ku ? Ku : K) + row * kPD + 8 * (tid & 15));
+            for (int pass = 0; pass < kTile / 16; ++pass) {
+                const int j = min(j0 + 16 * pass + (tid >> 4), n - 1);
+                pre[pass] = *reinterpret_cast<const u16x8_p *>(K + row_of(c, b, h, j) * kPD +
+                                                               8 * (tid & 15));
+            }
+            ppos = P[min(j0 + (tid & (kTile - 1)), n - 1)];
+        } else {
+#pragma unroll
+            for (int pass = 0; pass < kTile / 16; ++pass)
+                pre[pass] = __builtin_bit_cast(
+                    u16x8_p, __builtin_amdgcn_raw_buffer_load_b128(
+                                 krs, koff, (j0 + 16 * pass) * (kPD * 2), 0));
+            ppos = __builtin_amdgcn_raw_buffer_load_b32(prs, 4 * (tid & (kTile - 1)), 4 * j0, 0);
         }
-        const int jp = min(j0 + (tid & (kTile - 1)), n - 1);
-        const int p = P[jp];
-        ppos = (j0 + (tid & (kTile - 1)) < n) ? p : INT_MAX;
     };
 
-    // running maximum of the raw dot products (c2 >= 0 keeps the order) and
-    // the sum of exp2(c2 * (dot - maximum)), per lane and row tile
-    float mm[kRT], ll[kRT];
+    // per lane and row tile: the sum of exp2(c2 * dot + nb) over the slots
+    // seen, nb the base-2 offset of a reference that moves only when a
+    // group's sum passes kLazyCap (a row's first visible group, or a logit
+    // far above the reference); the log-sum-exp is log2(sum) - nb.  Before the
+    // first visible group nb is kNoRef, so every visible term overflows and
+    // sets the reference.
+    float nb[kRT], ll[kRT];
 #pragma unroll
-    for (int t = 0; t < kRT; ++t) { mm[t] = -INFINITY; ll[t] = 0.f; }
+    for (int t = 0; t < kRT; ++t) { nb[t] = kNoRef; ll[t] = 0.f; }
     int cur = next_active(0);
     if (cur < ntile) fetch(cur);
     int buf = 0;
@@ -240,7 +256,7 @@ void prompt_stats_kernel(PromptArgs a) {
         for (int pass = 0; pass < kTile / 16; ++pass)
             *reinterpret_cast<u16x8_p *>(ktile[buf] + tile_off(16 * pass + (tid >> 4), tid & 15)) =
                 pre[pass];
-        if (tid < kTile) kpos[buf][tid] = ppos;
+        if (tid < kTile) kpos[buf][tid] = j0 + tid < n ? ppos : INT_MAX;
         __syncthreads();
         const int nxt = next_active(cur + 1);
         if (nxt < ntile) fetch(nxt);   // lands while this tile computes
@@ -252,9 +268,10 @@ void prompt_stats_kernel(PromptArgs a) {
 #pragma unroll
         for (int t = 0; t < kRT; ++t) inner[t] = slots_full && rows_full[t] && kmax <= qmin[t];
         // two 16-slot tiles' dot products at a time (8 per lane and row
-        // tile, for each of the wave's row tiles), then one maximum and one
-        // rescale per row tile.  The mask
-        // decision is uniform per tile, so each variant is straight-line code.
+        // tile, for each of the wave's row tiles), their terms against the
+        // current references, and one wave-uniform test whether a reference
+        // has to move.  The mask decision is uniform per tile, so each
+        // variant is straight-line code.
         auto tile_body = [&](auto masked_c) {
             constexpr bool kMasked = decltype(masked_c)::value;
 #pragma unroll
@@ -292,26 +309,48 @@ void prompt_stats_kernel(PromptArgs a) {
                                 acc[t][s][i] = (live && kp <= qp[t]) ? acc[t][s][i] : -INFINITY;
                         }
                 }
+                // the group's terms against the current reference (a masked
+                // slot's term is exp2(-inf) = 0)
+                float gs[kRT];
+                bool move = false;
 #pragma unroll
                 for (int t = 0; t < kRT; ++t) {
-                    float mx = mm[t];
-#pragma unroll
-                    for (int s = 0; s < kSG; ++s) {
-                        mx = max3_f(mx, acc[t][s][0], acc[t][s][1]);
-                        mx = max3_f(mx, acc[t][s][2], acc[t][s][3]);
-                    }
-                    // base-2 weights exp2(c2 * (dot - max)) (scale * log2 e in
-                    // c2); a row with nothing seen yet keeps a zero sum (a
-                    // mask-free tile gives every row a finite maximum)
-                    const float ms = (!kMasked || mx != -INFINITY) ? mx : 0.f;
-                    const float nb = -ms * c2;
-                    float sum = 0.f;
+                    float e[kSG][4];
 #pragma unroll
                     for (int s = 0; s < kSG; ++s)
-                        sum += (exp2_hw(fmaf(acc[t][s][0], c2, nb)) + exp2_hw(fmaf(acc[t][s][1], c2, nb))) +
-                               (exp2_hw(fmaf(acc[t][s][2], c2, nb)) + exp2_hw(fmaf(acc[t][s][3], c2, nb)));
-                    ll[t] = ll[t] * exp2_hw(fmaf(mm[t], c2, nb)) + sum;
-                    mm[t] = mx;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) e[s][i] = exp2_hw(fmaf(acc[t][s][i], c2, nb[t]));
+                    gs[t] = ((e[0][0] + e[0][1]) + (e[0][2] + e[0][3])) +
+                            ((e[1][0] + e[1][1]) + (e[1][2] + e[1][3]));
+                    move = move || !(gs[t] < kLazyCap);
+                }
+                if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                    // some lane's group passed the cap: those lanes take the
+                    // group's largest dot product as the new reference,
+                    // rescale their sum and recount the group's terms
+#pragma unroll
+                    for (int t = 0; t < kRT; ++t) {
+                        if (!(gs[t] < kLazyCap)) {
+                            float gm = acc[t][0][0];
+#pragma unroll
+                            for (int s = 0; s < kSG; ++s)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) gm = fmaxf(gm, acc[t][s][i]);
+                            const float nbn = -gm * c2;
+                            float g2 = 0.f;
+#pragma unroll
+                            for (int s = 0; s < kSG; ++s)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) g2 += exp2_hw(fmaf(acc[t][s][i], c2, nbn));
+                            ll[t] = ll[t] * exp2_hw(nbn - nb[t]) + g2;
+                            nb[t] = nbn;
+                        } else {
+                            ll[t] += gs[t];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < kRT; ++t) ll[t] += gs[t];
                 }
             }
         };
@@ -325,22 +364,25 @@ void prompt_stats_kernel(PromptArgs a) {
         buf ^= 1;
         cur = nxt;
     }
-    // merge the four lanes of each row, then log-sum-exp
+    // merge the four lanes of each row (references as base-2 logits -nb),
+    // then the log-sum-exp: the sum's binary exponent is split off exactly,
+    // so the logarithm is taken of a mantissa in [1, 2)
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
-        float m = mm[t], l = ll[t];
+        float ref = -nb[t], l = ll[t];
 #pragma unroll
         for (int off = 16; off <= 32; off <<= 1) {
-            const float mo = __shfl_xor(m, off, 64), lo = __shfl_xor(l, off, 64);
-            const float mn = fmaxf(m, mo);
-            if (mn != -INFINITY) {
-                l = l * exp2_hw((m - mn) * c2) + lo * exp2_hw((mo - mn) * c2);
-                m = mn;
-            }
+            const float ro = __shfl_xor(ref, off, 64), lo = __shfl_xor(l, off, 64);
+            const float rn = fmaxf(ref, ro);
+            l = l * exp2_hw(ref - rn) + lo * exp2_hw(ro - rn);
+            ref = rn;
         }
-        // base-2 log-sum-exp of the row's base-2 logits c2 * dot
-        if (r == 0 && Rw[t] < nrows)
-            a.lse[(size_t)u * nrows + Rw[t]] = (l > 0.f) ? m * c2 + log2f(l) : -INFINITY;
+        if (r == 0 && Rw[t] < nrows) {
+            int ex;
+            const float mant = frexpf(l, &ex);   // l = mant * 2^ex, mant in [0.5, 1)
+            a.lse[(size_t)u * nrows + Rw[t]] =
+                (l > 0.f) ? (ref + (float)(ex - 1)) + log2f(2.f * mant) : -INFINITY;
+        }
     }
 }
 
@@ -436,30 +478,37 @@ void prompt_scores_kernel(PromptArgs a) {
             }
         return rt;
     };
-    // the tile's query rows, positions and base-2 log-sum-exps into registers;
-    // rows past the last read the last one (unconditional, in bounds; such
-    // rows are masked)
+    // the tile's query rows, positions and base-2 log-sum-exps into
+    // registers.  Position rr of head g (of this kv head's group) is query row
+    // (b m + rr) Hq + h G + g of q_rows and statistic rr G + g of the unit;
+    // buffer resources end at the sequence's last row, its last position and
+    // the unit's last statistic, so rows past m_rows read zeros (such rows
+    // are masked: their position and statistic are set when the tile is
+    // staged).  Nothing reads the loaded values before then, so the loads stay
+    // in flight while the current tile computes.
     u16x8_p pre[kTile / 16];
     int ppos = 0;
     float plse = 0.f;
-    // position rr of head g (of this kv head's group) is query row
-    // (b m + rr) Hq + h G + g of q_rows, and statistic rr G + g of the unit
-    const uint16_t *qbase = static_cast<const uint16_t *>(a.q_rows) +
-                            ((size_t)b * a.m_rows * c.Hq + (size_t)h * G) * kPD;
+    const size_t q_first = ((size_t)b * a.m_rows * c.Hq + (size_t)h * G) * kPD;
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc(static_cast<const uint16_t *>(a.q_rows) + q_first,
+                  (uint32_t)(((size_t)a.m_rows * c.Hq - (size_t)h * G) * (kPD * 2)));
+    const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse + (size_t)u * nrows, (uint32_t)nrows * 4);
+    const __amdgpu_buffer_rsrc_t prs =
+        make_rsrc(a.q_pos ? a.q_pos + (size_t)b * a.m_rows : nullptr, a.q_pos ? (uint32_t)a.m_rows * 4 : 0u);
+    const int qoff = (tid >> 4) * c.Hq * (kPD * 2) + 16 * (tid & 15);
+    const int lane_row = tid & (kTile - 1);
     auto fetch = [&](int rt) {
         const int k = rt / G, g = rt - k * G;
         const int rr0 = kTile * k;
 #pragma unroll
-        for (int pass = 0; pass < kTile / 16; ++pass) {
-            const int rr = min(rr0 + 16 * pass + (tid >> 4), a.m_rows - 1);
-            pre[pass] = *reinterpret_cast<const u16x8_p *>(
-                qbase + ((size_t)rr * c.Hq + g) * kPD + 8 * (tid & 15));
-        }
-        const int rr = rr0 + (tid & (kTile - 1)), rc = min(rr, a.m_rows - 1);
-        const int p = a.q_pos ? a.q_pos[(size_t)b * a.m_rows + rc] : INT_MAX;
-        const float l = a.lse[(size_t)u * nrows + (size_t)rc * G + g];
-        ppos = rr < a.m_rows ? p : INT_MIN;
-        plse = rr < a.m_rows ? l : -INFINITY;
+        for (int pass = 0; pass < kTile / 16; ++pass)
+            pre[pass] = __builtin_bit_cast(
+                u16x8_p, __builtin_amdgcn_raw_buffer_load_b128(
+                             qrs, qoff, ((rr0 + 16 * pass) * c.Hq + g) * (kPD * 2), 0));
+        ppos = __builtin_amdgcn_raw_buffer_load_b32(prs, 4 * lane_row, 4 * rr0, 0);
+        plse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             lrs, 4 * G * lane_row, 4 * (rr0 * G + g), 0));
     };
 
     double cs[kST];
@@ -474,8 +523,9 @@ void prompt_scores_kernel(PromptArgs a) {
             *reinterpret_cast<u16x8_p *>(qtile[buf] + tile_off(16 * pass + (tid >> 4), tid & 15)) =
                 pre[pass];
         if (tid < kTile) {
-            rpos[buf][tid] = ppos;
-            rlse[buf][tid] = plse;
+            const bool row = kTile * (cur / G) + tid < a.m_rows;
+            rpos[buf][tid] = row ? (a.q_pos ? ppos : INT_MAX) : INT_MIN;
+            rlse[buf][tid] = row ? plse : -INFINITY;
         }
         __syncthreads();
         const int nxt = next_active(cur + 1);
@@ -561,8 +611,12 @@ hipError_t launch_prompt_scores(const PromptArgs &a, hipStream_t s) {
     const int nb1 = (nrows + kStatRows - 1) / kStatRows;
     const int nb2 = (a.c.cap + kScoreSlots - 1) / kScoreSlots;
     const size_t tile_bytes = 2 * (size_t)((a.c.cap + kTile - 1) / kTile) * sizeof(int);
-    hipLaunchKernelGGL(prompt_stats_kernel, dim3(groups * 8 * nb1), dim3(kPThreads), tile_bytes, s,
-                       a);
+    if (a.c.bs == 0)
+        hipLaunchKernelGGL(prompt_stats_kernel<false>, dim3(groups * 8 * nb1), dim3(kPThreads),
+                           tile_bytes, s, a);
+    else
+        hipLaunchKernelGGL(prompt_stats_kernel<true>, dim3(groups * 8 * nb1), dim3(kPThreads),
+                           tile_bytes, s, a);
     // position tiles whose largest position is tracked in LDS (up to 16 KB)
     PromptArgs a2 = a;
     const int nrt_g = (a.m_rows + kTile - 1) / kTile;

@@ -228,7 +228,9 @@ kvc_status kvc_decode_attn(const kvc_cache *c, const int32_t *new_pos,
  *            0 bytes and NULL allowed otherwise).
  * bf16 caches with head_dim 128 run on the matrix cores (two exact passes:
  * the rows' softmax statistics, then every slot's probability sum in fp64,
- * a fixed summation order); other shapes use a VALU pass.
+ * a fixed summation order) when one sequence's query rows
+ * (m_rows * q_heads * 256 bytes) and one unit's K rows (capacity * 256 bytes)
+ * are each under 2 GiB; other shapes use a VALU pass.
  */
 size_t kvc_h2o_accumulate_workspace_bytes(const kvc_cache *c, int32_t m_rows);
 kvc_status kvc_h2o_accumulate(const kvc_cache *c, const void *q_rows,
