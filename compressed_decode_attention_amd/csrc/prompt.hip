@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void prompt_scores_kernel(PromptArgs a) {
     __shared__ __align__(16) unsigned char qtile[2][kTile * 256];
     __shared__ int rpos[2][kTile];
-    __shared__ float rlse[2][kTile];
+    __shared__ __align__(16) float rlse[2][kTile];
     __shared__ int red[kPThreads / 64];
     extern __shared__ int rtile_max[];   // [position tiles] largest position, when tracked
     const CacheDev &c = a.c;
@@ -450,6 +450,9 @@ void prompt_scores_kernel(PromptArgs a) {
             const int hi = wave_max_i(p);
             if (lane == 0) rtile_max[k] = hi;
         }
+    // smallest position among the wave's slots (a row tile whose positions
+    // all precede it adds nothing to this wave's slots)
+    const int kmin_w = __builtin_amdgcn_readfirstlane(wave_min_i(kmin));
     kmin = block_min(kmin, red);   // (its barriers also publish the tile bounds)
     // largest position of each 16-slot tile of the wave, and whether all its
     // slots are filled (only such tiles may skip the mask)
@@ -553,13 +556,11 @@ void prompt_scores_kernel(PromptArgs a) {
                 for (int c4 = 0; c4 < 4; ++c4)
                     qa[c4] = *reinterpret_cast<const u16x8_p *>(qtile[buf] + tile_off(q, 4 * c4 + r));
                 // C[row 4r + i][slot col]
-                float rl[4];
+                const f32x4_p rl = *reinterpret_cast<const f32x4_p *>(&rlse[buf][16 * s + 4 * r]);   // base 2
                 int rp[4];
+                if constexpr (kMasked)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    rl[i] = rlse[buf][16 * s + 4 * r + i];   // base 2
-                    if constexpr (kMasked) rp[i] = rpos[buf][16 * s + 4 * r + i];
-                }
+                    for (int i = 0; i < 4; ++i) rp[i] = rpos[buf][16 * s + 4 * r + i];
 #pragma unroll
                 for (int t = 0; t < kST; ++t) {
                     f32x4_p acc = {0.f, 0.f, 0.f, 0.f};
@@ -580,9 +581,12 @@ void prompt_scores_kernel(PromptArgs a) {
         bool all_inner = true;
 #pragma unroll
         for (int t = 0; t < kST; ++t) all_inner = all_inner && inner[t];
+        // (a causal prompt: the block's row tiles before this wave's first
+        // slot are staged for the other waves but skipped here)
+        const bool wave_sees = !track || rtile_max[cur / G] >= kmin_w;
         if (all_inner)
             tile_body(std::integral_constant<bool, false>());
-        else
+        else if (wave_sees)
             tile_body(std::integral_constant<bool, true>());
 #pragma unroll
         for (int t = 0; t < kST; ++t) cs[t] += (double)ts[t];
