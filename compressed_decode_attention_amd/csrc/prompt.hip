@@ -36,8 +36,9 @@
 // one multiply-add and one v_exp_f32.  Each slot tile's smallest and largest
 // position come from a wave reduction (a wave's 64 lanes hold one tile).  All
 // blocks of one unit run on one XCD (workgroups are dealt round-robin over the
-// eight XCDs), so the K (pass 1) or Q (pass 2) rows they share are read from
-// that XCD's L2.  Both kernels run three waves per SIMD: the larger register
+// eight XCDs, so the rows they share can come from its L2), and both passes
+// start every unit's longest block first: a causal prompt's blocks differ up
+// to 32-fold in work, and a long block started last would run alone.  Both kernels run three waves per SIMD: the larger register
 // tiles halve the LDS reads and the per-tile fixed work (staging, barrier,
 // next-tile search) per product, which pays more than a fourth wave.
 #include "kvc_internal.h"
@@ -70,10 +71,22 @@ __device__ inline bf16x8_p as_bf(u16x8_p x) { return __builtin_bit_cast(bf16x8_p
 
 // Unit and block index of this workgroup; every block of a unit gets the same
 // blockIdx % 8, hence the same XCD.  False for the padding of the last group.
-__device__ inline bool unit_block(int nblk, int units, int &u, int &blk) {
+// Workgroups start roughly in blockIdx order, so both passes deal them
+// block-major with the longest blocks first (for a causal prompt, every
+// unit's last row block in the statistics pass and its first slot block in
+// the scores pass), and the launch's tail is a short block.
+__device__ inline bool stats_unit_block(int nblk, int units, int &u, int &blk) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    u = 8 * (slot / nblk) + xcd;
-    blk = slot % nblk;
+    const int groups = (units + 7) / 8;
+    u = 8 * (slot % groups) + xcd;
+    blk = nblk - 1 - slot / groups;
+    return u < units;
+}
+__device__ inline bool scores_unit_block(int units, int &u, int &blk) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int groups = (units + 7) / 8;
+    u = 8 * (slot % groups) + xcd;
+    blk = slot / groups;
     return u < units;
 }
 
@@ -135,7 +148,7 @@ void prompt_stats_kernel(PromptArgs a) {
     const int nrows = a.m_rows * c.G;
     const int nblk = (nrows + kStatRows - 1) / kStatRows;
     int u, blk;
-    if (!unit_block(nblk, c.B * c.Hkv, u, blk)) return;
+    if (!stats_unit_block(nblk, c.B * c.Hkv, u, blk)) return;
     const int b = u / c.Hkv, h = u % c.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane >> 4, col = lane & 15;
@@ -404,9 +417,8 @@ void prompt_scores_kernel(PromptArgs a) {
     extern __shared__ int rtile_max[];   // [position tiles] largest position, when tracked
     const CacheDev &c = a.c;
     const int nrows = a.m_rows * c.G;
-    const int nblk = (c.cap + kScoreSlots - 1) / kScoreSlots;
     int u, blk;
-    if (!unit_block(nblk, c.B * c.Hkv, u, blk)) return;
+    if (!scores_unit_block(c.B * c.Hkv, u, blk)) return;
     const int b = u / c.Hkv, h = u % c.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane >> 4, col = lane & 15;
