@@ -366,7 +366,7 @@ void finish_kernel(AttnArgs a, SelectArgs sa, CompactArgs ca) {
     const int e = select_unit<Cfg::SEL, Cfg::NT>(sa, u, F.sel);
     __syncthreads();
     if (e >= -1) compact_one<T, D>(ca, u, e);
-    else compact_unit<T, D, Cfg::NT>(ca, u, F.comp);
+    else compact_unit<T, D, Cfg::NT, true>(ca, u, F.comp);
 }
 
 template <typename T, int D>

@@ -18,7 +18,7 @@ namespace kvc {
 template <typename T, int D>
 __global__ __launch_bounds__(kCompThreads) void compact_kernel(CompactArgs a) {
     __shared__ CompLds CL;
-    compact_unit<T, D>(a, blockIdx.x, CL);
+    compact_unit<T, D, kCompThreads, true>(a, blockIdx.x, CL);
 }
 
 template <typename T, int D>

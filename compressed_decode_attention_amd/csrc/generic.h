@@ -526,7 +526,10 @@ __device__ inline void compact_one(const CompactArgs &a, int u, int e) {
     if (tid == 0) c.n_slots[u] = src;
 }
 
-template <typename T, int D, int NT = kCompThreads>
+// WAVE_COPY: the waves copy the rows together with batched loads (the
+// compaction and finish kernels); without it each lane with a move copies its
+// row alone (kept for callers whose registers are at their limit).
+template <typename T, int D, int NT = kCompThreads, bool WAVE_COPY = false>
 __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
     const CacheDev &c = a.c;
     const int b = u / c.Hkv, h = u % c.Hkv;
@@ -560,6 +563,19 @@ __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
 
     int32_t *P = c.pos + (size_t)u * c.cap;
     float *S = a.scores ? a.scores + (size_t)u * c.cap : nullptr;
+    // WAVE_COPY: each wave copies its lanes' moves together: kParts lanes per row, one
+    // 16-byte part each of K and V, the row addresses taken from the lane that
+    // owns the move; a lane's loads of kBatch such steps go out before its
+    // stores (a move's source is a kept slot >= m and its destination a hole
+    // below m, so no row is both read and written), instead of one lane
+    // copying a row with a round trip per part.
+    constexpr int kParts = (int)(D * sizeof(T) / 16);
+    static_assert(64 % kParts == 0, "a row's 16-byte parts must tile a wave");
+    constexpr int kPerStep = 64 / kParts;   // moves per wave step
+    constexpr int kBatch = 4;               // wave steps whose loads go out together
+    static_assert(kParts % kBatch == 0, "steps per wave must be a multiple of the batch");
+    const int lane = tid & 63, part = lane % kParts, which = lane / kParts;
+    uint4 *Kq = reinterpret_cast<uint4 *>(c.k), *Vq = reinterpret_cast<uint4 *>(c.v);
     int base = 0;
     for (int j0 = 0; j0 < m; j0 += NT) {
         const int j = j0 + tid;
@@ -567,14 +583,48 @@ __device__ inline void compact_unit(const CompactArgs &a, int u, CompLds &CL) {
         int t;
         const int r = block_excl_scan(hole, red, &t);
         const int idx = below + base + r;
+        if constexpr (!WAVE_COPY) {
+            if (hole && idx < m) {
+                const int src = ks[idx];
+                if (src >= m && src < n) {
+                    copy_row<T, D>((T *)c.k + row_of(c, b, h, j) * D, (T *)c.k + row_of(c, b, h, src) * D);
+                    copy_row<T, D>((T *)c.v + row_of(c, b, h, j) * D, (T *)c.v + row_of(c, b, h, src) * D);
+                    P[j] = P[src];
+                    if (S) S[j] = S[src];
+                }
+            }
+            base += t;
+            continue;
+        }
+        // this lane's move: destination and source rows in 16-byte units
+        long long dq = -1, sq = 0;
         if (hole && idx < m) {
             const int src = ks[idx];
             if (src >= m && src < n) {
-                copy_row<T, D>((T *)c.k + row_of(c, b, h, j) * D, (T *)c.k + row_of(c, b, h, src) * D);
-                copy_row<T, D>((T *)c.v + row_of(c, b, h, j) * D, (T *)c.v + row_of(c, b, h, src) * D);
+                dq = (long long)row_of(c, b, h, j) * kParts;
+                sq = (long long)row_of(c, b, h, src) * kParts;
                 P[j] = P[src];
                 if (S) S[j] = S[src];
             }
+        }
+        // (the batch is written out: arrays indexed in loops here were kept on
+        // the stack)
+        for (int s0 = 0; s0 < kParts; s0 += kBatch) {   // kParts steps cover the wave's 64 lanes
+            const int o0 = s0 * kPerStep + which;
+            const long long d0 = __shfl(dq, o0, 64), d1 = __shfl(dq, o0 + kPerStep, 64);
+            const long long d2 = __shfl(dq, o0 + 2 * kPerStep, 64), d3 = __shfl(dq, o0 + 3 * kPerStep, 64);
+            const long long r0 = __shfl(sq, o0, 64) + part, r1 = __shfl(sq, o0 + kPerStep, 64) + part;
+            const long long r2 = __shfl(sq, o0 + 2 * kPerStep, 64) + part;
+            const long long r3 = __shfl(sq, o0 + 3 * kPerStep, 64) + part;
+            uint4 k0{}, k1{}, k2{}, k3{}, v0{}, v1{}, v2{}, v3{};
+            if (d0 >= 0) { k0 = Kq[r0]; v0 = Vq[r0]; }
+            if (d1 >= 0) { k1 = Kq[r1]; v1 = Vq[r1]; }
+            if (d2 >= 0) { k2 = Kq[r2]; v2 = Vq[r2]; }
+            if (d3 >= 0) { k3 = Kq[r3]; v3 = Vq[r3]; }
+            if (d0 >= 0) { Kq[d0 + part] = k0; Vq[d0 + part] = v0; }
+            if (d1 >= 0) { Kq[d1 + part] = k1; Vq[d1 + part] = v1; }
+            if (d2 >= 0) { Kq[d2 + part] = k2; Vq[d2 + part] = v2; }
+            if (d3 >= 0) { Kq[d3 + part] = k3; Vq[d3 + part] = v3; }
         }
         base += t;
     }
