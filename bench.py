@@ -32,18 +32,18 @@ HBM_PEAK_GBS = 8000.0
 # rocprofv3 --pmc runs of this script per case (FETCH_SIZE, then WRITE_SIZE, KiB
 # per dispatch, mean over the steady-state dispatches), each scaled by what the
 # same counter reads for a plain 1 GiB device copy (--copy-probe-mb 1024):
-# FETCH_SIZE reads 524,302.6 KiB for 1,048,576 KiB copied (x 2.000),
+# FETCH_SIZE reads 524,301.2 KiB for 1,048,576 KiB copied (x 2.000),
 # WRITE_SIZE reads 1,048,576 KiB (x 1.000).  A record is valid only for the
 # fused kernel's sources whose digest it holds; otherwise the bench reports null.
-FETCH_SCALE = 1048576.0 / 524302.61
+FETCH_SCALE = 1048576.0 / 524301.20
 WRITE_SCALE = 1.0
 PROFILED_TRAFFIC = [
-    {"sources_digest": "cb437634e64ec7cb", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "bf16", "fetch_kib": 538442.43, "write_kib": 26995.67},
-    {"sources_digest": "cb437634e64ec7cb", "workload": "heavy_load_b512_l2048", "policy": "streaming",
-     "kv_dtype": "bf16", "fetch_kib": 534092.53, "write_kib": 18688.10},
-    {"sources_digest": "cb437634e64ec7cb", "workload": "heavy_load_b512_l2048", "policy": "h2o",
-     "kv_dtype": "e5m2", "fetch_kib": 276357.22, "write_kib": 25968.04},
+    {"sources_digest": "c0791d2f6fa3568a", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "bf16", "fetch_kib": 538442.26, "write_kib": 26995.57},
+    {"sources_digest": "c0791d2f6fa3568a", "workload": "heavy_load_b512_l2048", "policy": "streaming",
+     "kv_dtype": "bf16", "fetch_kib": 534098.69, "write_kib": 18688.10},
+    {"sources_digest": "c0791d2f6fa3568a", "workload": "heavy_load_b512_l2048", "policy": "h2o",
+     "kv_dtype": "e5m2", "fetch_kib": 276357.07, "write_kib": 25968.04},
 ]
 
 
