@@ -146,15 +146,18 @@ def test_large_units_leave_the_lds_path():
         np.testing.assert_array_equal(got[u], want)
 
 
-@pytest.mark.parametrize("dtype", [kvc.BF16, kvc.F32])
-def test_compaction_moves_survivors_bit_exactly(dtype):
+# every row size of the copy (64 to 512 bytes: 4 to 32 parts of 16 bytes, so
+# 16 to 2 moves per wave step)
+@pytest.mark.parametrize("dtype,D", [(kvc.BF16, 128), (kvc.F32, 128), (kvc.BF16, 64), (kvc.F32, 64),
+                                     (kvc.FP8_E5M2, 128), (kvc.FP8_E5M2, 64)])
+def test_compaction_moves_survivors_bit_exactly(dtype, D):
     rng = np.random.default_rng(400)
-    Hkv, cap, D = 2, 600, 128
+    Hkv, cap = 2, 600
     units_pos = _units(rng, 4 * Hkv, 590, 1500)
     cache = _pos_cache(units_pos, cap, Hkv, D=D, dtype=dtype, fill_kv=True)
     sc = rng.random((4, Hkv, cap)).astype(np.float32)
     scores = torch.from_numpy(sc).cuda()
-    dn = "bf16" if dtype == kvc.BF16 else "f32"
+    dn = {kvc.BF16: "bf16", kvc.F32: "f32", kvc.FP8_E5M2: "e5m2"}[dtype]
     pre = Snapshot(cache, dn, scores)
     keep = torch.empty((4, Hkv, cap), dtype=torch.int32, device="cuda")
     nout = torch.empty((4, Hkv), dtype=torch.int32, device="cuda")
