@@ -22,11 +22,13 @@
 //     follow the largest dot products); four lanes merge into the row's
 //     log-sum-exp, written to the workspace.
 //  2. scores: one workgroup per 256 slots of a unit.  The slots are the B
-//     operand, held in registers (64 slots per wave); query tiles (64 consecutive positions of
-//     one head, so a tile's rows share one stride through q) are staged in
-//     LDS.  Each lane sums exp2(c2 * dot - lse) over its 16 rows of a tile in
-//     fp32, adds that to an fp64 column sum (a fixed order: the scores are
-//     deterministic), and one lane per slot adds the total to the score.
+//     operand, held in registers (64 slots per wave); query tiles (64
+//     consecutive positions of one head, so a tile's rows share one stride
+//     through q) are staged in LDS.  Each lane sums exp2(c2 * dot - lse) over
+//     its 16 rows of a tile in fp32, adds that to an fp64 column sum (a fixed
+//     order: the scores are deterministic), and one lane per slot adds the
+//     total to the score.  A wave skips the row tiles whose positions all
+//     precede its own slots.
 // Tiles that no row of a block can see (from the positions alone) are
 // skipped, which halves the work of a causal prompt; tiles that every row sees
 // whole (most of a causal triangle) run a mask-free variant of the tile's
@@ -38,9 +40,12 @@
 // blocks of one unit run on one XCD (workgroups are dealt round-robin over the
 // eight XCDs, so the rows they share can come from its L2), and both passes
 // start every unit's longest block first: a causal prompt's blocks differ up
-// to 32-fold in work, and a long block started last would run alone.  Both kernels run three waves per SIMD: the larger register
-// tiles halve the LDS reads and the per-tile fixed work (staging, barrier,
-// next-tile search) per product, which pays more than a fourth wave.
+// to 32-fold in work, and a long block started last would run alone.  Per-tile
+// loads are buffer loads with a scalar tile offset, their validity applied
+// when the tile is staged, so the next tile's loads stay in flight through
+// the current one.  Both kernels run three waves per SIMD: the larger
+// register tiles halve the LDS reads and the per-tile fixed work (staging,
+// barrier, next-tile search) per product, which pays more than a fourth wave.
 #include "kvc_internal.h"
 
 #include <limits.h>
