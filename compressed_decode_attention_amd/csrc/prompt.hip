@@ -76,22 +76,25 @@ __device__ inline bf16x8_p as_bf(u16x8_p x) { return __builtin_bit_cast(bf16x8_p
 
 // Unit and block index of this workgroup; every block of a unit gets the same
 // blockIdx % 8, hence the same XCD.  False for the padding of the last group.
-// Workgroups start roughly in blockIdx order, so both passes deal them
-// block-major with the longest blocks first (for a causal prompt, every
-// unit's last row block in the statistics pass and its first slot block in
-// the scores pass), and the launch's tail is a short block.
-__device__ inline bool stats_unit_block(int nblk, int units, int &u, int &blk) {
+// Workgroups start roughly in blockIdx order, so both passes deal them with
+// the longest blocks first (for a causal prompt, a unit's last row block in
+// the statistics pass and its first slot block in the scores pass), and the
+// launch's tail is a short block.  Both do so within windows of W units per
+// XCD (all their blocks, longest first, then the next window), so that the
+// units whose rows are read at a time fit the XCD's L2 (K rows in the
+// statistics pass, query rows in the scores pass).
+constexpr int kStatsWindow = 8;
+constexpr int kScoresWindow = 16;
+template <int W, bool LONG_LAST>
+__device__ inline bool windowed_unit_block(int nblk, int units, int &u, int &blk) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int groups = (units + 7) / 8;
-    u = 8 * (slot % groups) + xcd;
-    blk = nblk - 1 - slot / groups;
-    return u < units;
-}
-__device__ inline bool scores_unit_block(int units, int &u, int &blk) {
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int groups = (units + 7) / 8;
-    u = 8 * (slot % groups) + xcd;
-    blk = slot / groups;
+    const int groups = (units + 7) / 8;   // units per XCD
+    const int full = groups / W, wsize = W * nblk;
+    const int win = slot / wsize;
+    const int within = win < full ? slot % wsize : slot - full * wsize;
+    const int wc = win < full ? W : groups - full * W;   // units in this window
+    blk = LONG_LAST ? nblk - 1 - within / wc : within / wc;
+    u = 8 * (win * W + within % wc) + xcd;
     return u < units;
 }
 
@@ -153,7 +156,7 @@ void prompt_stats_kernel(PromptArgs a) {
     const int nrows = a.m_rows * c.G;
     const int nblk = (nrows + kStatRows - 1) / kStatRows;
     int u, blk;
-    if (!stats_unit_block(nblk, c.B * c.Hkv, u, blk)) return;
+    if (!windowed_unit_block<kStatsWindow, true>(nblk, c.B * c.Hkv, u, blk)) return;
     const int b = u / c.Hkv, h = u % c.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane >> 4, col = lane & 15;
@@ -423,7 +426,8 @@ void prompt_scores_kernel(PromptArgs a) {
     const CacheDev &c = a.c;
     const int nrows = a.m_rows * c.G;
     int u, blk;
-    if (!scores_unit_block(c.B * c.Hkv, u, blk)) return;
+    const int nblk = (c.cap + kScoreSlots - 1) / kScoreSlots;
+    if (!windowed_unit_block<kScoresWindow, false>(nblk, c.B * c.Hkv, u, blk)) return;
     const int b = u / c.Hkv, h = u % c.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane >> 4, col = lane & 15;
