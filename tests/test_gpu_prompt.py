@@ -125,6 +125,18 @@ def test_several_blocks_ragged_tails_and_unsorted_rows():
     _check(w, cache, _rows(w, len(lengths), m), q_pos)
 
 
+def test_partial_windows_of_the_block_order():
+    # 160 units = 20 per XCD: the statistics pass's windows of 8 units and the
+    # scores pass's windows of 16 both end with a partial window of 4; units
+    # sampled from full and partial windows of several XCDs, each against the
+    # oracle and the probability mass
+    w = W_G4
+    B, L = 20, 300
+    cache = make_cache(w, [L] * B, capacity=L)
+    units = [divmod(u, w.kv_heads) for u in (0, 7, 8 * 8 + 3, 8 * 15 + 6, 8 * 16 + 5, 8 * 17 + 1, 159)]
+    _check(w, cache, _rows(w, B, L), [np.arange(L)] * B, units=units, check_mass=True)
+
+
 def test_paged_cache_matches_contiguous_bit_for_bit():
     w = W_G8
     lengths, m = [200, 33, 129], 160
